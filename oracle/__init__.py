@@ -1,0 +1,231 @@
+"""TEST INFRASTRUCTURE ONLY — the oracle for submanifold sparse convolution.
+
+Plain, slow CPU implementations of what the GPU path computes, used to judge
+it.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package; the product library never does.  It
+shares no code with the GPU path.
+
+Contents
+--------
+``OracleMap`` / ``build_map`` / ``forward`` / ``forward_rows``
+    ctypes front end of ``spconv_oracle.cpp`` (ordered-tree coordinate lookup,
+    per-entry fp64 vector-matrix products).  See that file for the passages
+    each step follows.
+``brute_map``
+    O(N^2) pair test for tiny inputs: (j, q) is an entry of offset d iff
+    coords[j] = coords[q] + (0, d).  Independent of the tree lookup.
+``dense_grow``
+    The regular ("dilating") output definition, for the dilation pins:
+    "Sparse inputs and sparse convolution", section "What a dense convolution
+    does to empty space", and the SparseConvNet blog, section 2 (regular
+    output definition).
+``mac_count``
+    Entries x Cin x Cout: "Sparse inputs and sparse convolution", section
+    "A symmetry you can check on the slide" (MACs per layer).
+
+Every function here has a pin in ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import itertools
+import os
+from typing import Dict, Iterable, List, Optional, Sequence, Set, Tuple
+
+import numpy as np
+
+from . import build as _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB: Optional[ctypes.CDLL] = None
+
+STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "DUPLICATE_COORD", 3: "COORD_RANGE"}
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+class OracleError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"oracle status {status} ({STATUS_NAMES.get(status, '?')})")
+        self.status = status
+        self.name = STATUS_NAMES.get(status, "?")
+
+
+def _lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        path = _build.LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build()
+        lib = ctypes.CDLL(path)
+        lib.oracle_build_map.argtypes = [_i32p, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
+        lib.oracle_build_map.restype = ctypes.c_int
+        lib.oracle_map_free.argtypes = [ctypes.c_void_p]
+        lib.oracle_map_free.restype = None
+        lib.oracle_map_kernel.argtypes = [ctypes.c_void_p]
+        lib.oracle_map_kernel.restype = ctypes.c_int32
+        lib.oracle_map_count.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+        lib.oracle_map_count.restype = ctypes.c_int64
+        lib.oracle_map_list.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, _i32p]
+        lib.oracle_map_list.restype = ctypes.c_int
+        lib.oracle_forward.argtypes = [ctypes.c_void_p, _f64p, _f64p, ctypes.c_int32, ctypes.c_int32, _f64p]
+        lib.oracle_forward.restype = ctypes.c_int
+        lib.oracle_forward_rows.argtypes = [ctypes.c_void_p, _f64p, _f64p, ctypes.c_int32, ctypes.c_int32,
+                                            _i64p, ctypes.c_int64, _f64p]
+        lib.oracle_forward_rows.restype = ctypes.c_int
+        lib.oracle_neighbours.argtypes = [ctypes.c_void_p, _i64p, ctypes.c_int64, _i32p]
+        lib.oracle_neighbours.restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def _ptr(a: np.ndarray, t):
+    return a.ctypes.data_as(t)
+
+
+class OracleMap:
+    """Map built by the oracle.  ``lists[k]`` is ``(in_idx, out_idx)`` int32
+    arrays ordered by output row."""
+
+    def __init__(self, coords: np.ndarray, K: int):
+        coords = np.ascontiguousarray(np.asarray(coords, dtype=np.int32).reshape(-1, 4))
+        self.coords = coords
+        self.K = int(K)
+        self.N = int(coords.shape[0])
+        h = ctypes.c_void_p()
+        st = _lib().oracle_build_map(_ptr(coords, _i32p), self.N, self.K, ctypes.byref(h))
+        if st != 0:
+            raise OracleError(st)
+        self._h = h
+        kv = self.K ** 3
+        self.counts = np.array([_lib().oracle_map_count(h, k) for k in range(kv)], dtype=np.int64)
+        self.lists: List[Tuple[np.ndarray, np.ndarray]] = []
+        for k in range(kv):
+            a = np.empty(self.counts[k], np.int32)
+            b = np.empty(self.counts[k], np.int32)
+            if self.counts[k] > 0:
+                st = _lib().oracle_map_list(h, k, _ptr(a, _i32p), _ptr(b, _i32p))
+                if st != 0:
+                    raise OracleError(st)
+            self.lists.append((a, b))
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _LIB is not None:
+            _LIB.oracle_map_free(h)
+            self._h = None
+
+    @property
+    def total_entries(self) -> int:
+        return int(self.counts.sum())
+
+    def forward(self, feats: np.ndarray, weights: np.ndarray) -> np.ndarray:
+        """fp64 forward over the whole map.  ``feats`` [N, Cin] and ``weights``
+        [K^3, Cin, Cout] are widened to fp64 exactly before the call."""
+        f = np.ascontiguousarray(np.asarray(feats, dtype=np.float64))
+        w = np.ascontiguousarray(np.asarray(weights, dtype=np.float64))
+        cin, cout = w.shape[1], w.shape[2]
+        assert f.shape == (self.N, cin) and w.shape[0] == self.K ** 3
+        out = np.empty((self.N, cout), np.float64)
+        st = _lib().oracle_forward(self._h, _ptr(f, _f64p), _ptr(w, _f64p), cin, cout, _ptr(out, _f64p))
+        if st != 0:
+            raise OracleError(st)
+        return out
+
+    def forward_rows(self, feats: np.ndarray, weights: np.ndarray, rows: Sequence[int]) -> np.ndarray:
+        """fp64 forward for selected output rows, evaluated from the coordinate
+        table one row at a time."""
+        f = np.ascontiguousarray(np.asarray(feats, dtype=np.float64))
+        w = np.ascontiguousarray(np.asarray(weights, dtype=np.float64))
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        cin, cout = w.shape[1], w.shape[2]
+        out = np.empty((r.shape[0], cout), np.float64)
+        st = _lib().oracle_forward_rows(self._h, _ptr(f, _f64p), _ptr(w, _f64p), cin, cout,
+                                        _ptr(r, _i64p), r.shape[0], _ptr(out, _f64p))
+        if st != 0:
+            raise OracleError(st)
+        return out
+
+    def neighbours(self, rows: Sequence[int]) -> np.ndarray:
+        """[len(rows), K^3] neighbour rows (or -1) of selected outputs."""
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nbr = np.empty((r.shape[0], self.K ** 3), np.int32)
+        st = _lib().oracle_neighbours(self._h, _ptr(r, _i64p), r.shape[0], _ptr(nbr, _i32p))
+        if st != 0:
+            raise OracleError(st)
+        return nbr
+
+
+def build_map(coords: np.ndarray, K: int) -> OracleMap:
+    return OracleMap(coords, K)
+
+
+def offset_index(dz: int, dy: int, dx: int, K: int) -> int:
+    """k(d) = ((dz + r) K + (dy + r)) K + (dx + r), r = (K - 1) / 2."""
+    r = (K - 1) // 2
+    return ((dz + r) * K + (dy + r)) * K + (dx + r)
+
+
+def offset_of(k: int, K: int) -> Tuple[int, int, int]:
+    r = (K - 1) // 2
+    return (k // (K * K) - r, (k // K) % K - r, k % K - r)
+
+
+def brute_map(coords: np.ndarray, K: int) -> Dict[int, Set[Tuple[int, int]]]:
+    """Per-offset entry sets by an O(N^2) pair test: (j, q) belongs to offset
+    d = coords[j] - coords[q] when both share b and max |d| <= r.  For tiny
+    inputs only."""
+    c = np.asarray(coords, dtype=np.int64).reshape(-1, 4)
+    r = (K - 1) // 2
+    res: Dict[int, Set[Tuple[int, int]]] = {k: set() for k in range(K ** 3)}
+    for q in range(c.shape[0]):
+        d = c - c[q]
+        ok = (d[:, 0] == 0) & (np.abs(d[:, 1:]).max(axis=1) <= r)
+        for j in np.nonzero(ok)[0]:
+            dz, dy, dx = (int(v) for v in d[j, 1:])
+            res[offset_index(dz, dy, dx, K)].add((int(j), int(q)))
+    return res
+
+
+def dense_grow(active: Iterable[Tuple[int, ...]], layers: int, shape: Optional[Tuple[int, ...]] = None,
+               K: int = 3) -> Set[Tuple[int, ...]]:
+    """Active sites after ``layers`` dense K^d convolutions under the regular
+    output definition: an output is active when its window touches any active
+    input.  ``shape`` clips to a grid (the slide grid); None means unbounded."""
+    cur = set(tuple(int(v) for v in a) for a in active)
+    if not cur:
+        return cur
+    d = len(next(iter(cur)))
+    r = (K - 1) // 2
+    offs = list(itertools.product(range(-r, r + 1), repeat=d))
+    for _ in range(layers):
+        nxt = set()
+        for a in cur:
+            for o in offs:
+                p = tuple(a[i] + o[i] for i in range(d))
+                if shape is None or all(0 <= p[i] < shape[i] for i in range(d)):
+                    nxt.add(p)
+        cur = nxt
+    return cur
+
+
+def conventional_entries(active: Iterable[Tuple[int, ...]], shape: Tuple[int, ...], K: int = 3) -> int:
+    """Entries of a conventional (zero-skipping) layer: one per active input
+    and in-grid output position its window reaches."""
+    act = [tuple(int(v) for v in a) for a in active]
+    d = len(act[0])
+    r = (K - 1) // 2
+    n = 0
+    for a in act:
+        for o in itertools.product(range(-r, r + 1), repeat=d):
+            if all(0 <= a[i] + o[i] < shape[i] for i in range(d)):
+                n += 1
+    return n
+
+
+def mac_count(entries: int, cin: int, cout: int) -> int:
+    """Multiply-accumulates of a layer: entries x Cin x Cout, independent of
+    how the entries are grouped."""
+    return int(entries) * int(cin) * int(cout)

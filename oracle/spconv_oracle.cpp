@@ -1,0 +1,225 @@
+// TEST INFRASTRUCTURE ONLY — the oracle for submanifold sparse convolution.
+//
+// A plain, slow, obviously correct CPU implementation of what the GPU path
+// computes.  Only the tests, the smoke check and the bench's CPU-baseline leg
+// load it; the product path never does.  It shares no code, header, table or
+// helper with the GPU library.
+//
+// What it follows (page titles as published; sections named on each page):
+//  * Map ("kernel map" / "rulebook"): "Sparse inputs and sparse convolution",
+//    sections "The map is the computation" (for each output q and offset d,
+//    look up q + d; a hit p joins the map as (p, q, W_d)) and "The fix: compute
+//    only where an input exists" (submanifold rule: the outputs are exactly the
+//    inputs).  Offset sign from "Sparse convolution for point clouds", section
+//    "The map and the update rule" (input P = output Q + offset), which is also
+//    the GetOffset result of section 3 of the SparseConvNet blog
+//    ("编织计算规则：Rulebook的生成与核心作用": offset = input - output).
+//  * Coordinate table: SparseConvNet blog, section 2 ("构建计算地图"): one
+//    increasing index per unique coordinate.  Here an ordered tree, on purpose
+//    not a hash, so it cannot share the GPU's packing or probing.
+//  * Forward: "Sparse convolution for point clouds", section "The map and the
+//    update rule": for every entry, f_out(Q) += f_in(P) x W_d, starting from
+//    zero, no bias.  Evaluated in fp64 on the exactly widened stored inputs.
+//
+// Conventions (the readings the pages leave open):
+//  * coordinates are (b, z, y, x); b in [0, 2^15), z, y, x in [0, 2^16);
+//  * offset index k = ((dz + r) K + (dy + r)) K + (dx + r), r = (K - 1) / 2;
+//  * entries never cross batch index b;
+//  * a neighbour coordinate outside the active set is a miss (no wrap);
+//  * duplicate coordinates are an error, not merged.
+//
+// Build: g++ -O2 -std=c++17 -shared -fPIC (no fast-math: the fp64 sums keep
+// their written order).
+
+#include <array>
+#include <cstddef>
+#include <cstdint>
+#include <map>
+#include <new>
+#include <vector>
+
+namespace {
+
+enum OracleStatus : int {
+  kOk = 0,
+  kInvalidArg = 1,
+  kDuplicateCoord = 2,
+  kCoordRange = 3,
+};
+
+using Coord = std::array<int64_t, 4>;  // (b, z, y, x)
+
+struct OracleMap {
+  int32_t K = 0;
+  int64_t N = 0;
+  std::vector<Coord> coords;
+  std::map<Coord, int64_t> row_of;               // coordinate -> row index
+  std::vector<std::vector<int32_t>> in_idx;      // per offset k
+  std::vector<std::vector<int32_t>> out_idx;     // per offset k
+};
+
+// Offset (dz, dy, dx) of index k for an odd kernel size K.
+void offset_of(int32_t k, int32_t K, int64_t* dz, int64_t* dy, int64_t* dx) {
+  const int32_t r = (K - 1) / 2;
+  *dz = k / (K * K) - r;
+  *dy = (k / K) % K - r;
+  *dx = k % K - r;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Builds the map of a submanifold convolution with a K^3 kernel over the N
+// voxels in coords (row-major int32 [N][4], (b, z, y, x)).  Returns a status;
+// on success *out holds an opaque handle to release with oracle_map_free.
+int oracle_build_map(const int32_t* coords, int64_t N, int32_t K, void** out) {
+  if (out == nullptr) return kInvalidArg;
+  *out = nullptr;
+  if (coords == nullptr || N <= 0 || K < 1 || K % 2 == 0) return kInvalidArg;
+  OracleMap* m = new (std::nothrow) OracleMap;
+  if (m == nullptr) return kInvalidArg;
+  m->K = K;
+  m->N = N;
+  m->coords.resize(static_cast<size_t>(N));
+  // Step 1: validate ranges and fill the coordinate -> row table.
+  for (int64_t i = 0; i < N; ++i) {
+    Coord c = {coords[4 * i + 0], coords[4 * i + 1], coords[4 * i + 2], coords[4 * i + 3]};
+    if (c[0] < 0 || c[0] >= (int64_t(1) << 15)) { delete m; return kCoordRange; }
+    for (int d = 1; d < 4; ++d) {
+      if (c[d] < 0 || c[d] >= (int64_t(1) << 16)) { delete m; return kCoordRange; }
+    }
+    m->coords[static_cast<size_t>(i)] = c;
+  }
+  for (int64_t i = 0; i < N; ++i) {
+    auto ins = m->row_of.emplace(m->coords[static_cast<size_t>(i)], i);
+    if (!ins.second) { delete m; return kDuplicateCoord; }
+  }
+  // Step 2: the double loop over outputs q and offsets k with a lookup of
+  // q + d; a hit p adds (in = p, out = q) to list k.
+  const int32_t KV = K * K * K;
+  m->in_idx.assign(static_cast<size_t>(KV), {});
+  m->out_idx.assign(static_cast<size_t>(KV), {});
+  for (int64_t q = 0; q < N; ++q) {
+    const Coord& cq = m->coords[static_cast<size_t>(q)];
+    for (int32_t k = 0; k < KV; ++k) {
+      int64_t dz, dy, dx;
+      offset_of(k, K, &dz, &dy, &dx);
+      const Coord p = {cq[0], cq[1] + dz, cq[2] + dy, cq[3] + dx};
+      auto it = m->row_of.find(p);
+      if (it != m->row_of.end()) {
+        m->in_idx[static_cast<size_t>(k)].push_back(static_cast<int32_t>(it->second));
+        m->out_idx[static_cast<size_t>(k)].push_back(static_cast<int32_t>(q));
+      }
+    }
+  }
+  *out = m;
+  return kOk;
+}
+
+void oracle_map_free(void* h) { delete static_cast<OracleMap*>(h); }
+
+int32_t oracle_map_kernel(const void* h) { return static_cast<const OracleMap*>(h)->K; }
+
+// Number of entries in the list of offset k (-1 if k is out of range).
+int64_t oracle_map_count(const void* h, int32_t k) {
+  const OracleMap* m = static_cast<const OracleMap*>(h);
+  if (k < 0 || k >= static_cast<int32_t>(m->in_idx.size())) return -1;
+  return static_cast<int64_t>(m->in_idx[static_cast<size_t>(k)].size());
+}
+
+// Copies list k into caller buffers of oracle_map_count(h, k) entries each.
+// The list is ordered by output row (the order of the double loop).
+int oracle_map_list(const void* h, int32_t k, int32_t* in_idx, int32_t* out_idx) {
+  const OracleMap* m = static_cast<const OracleMap*>(h);
+  if (k < 0 || k >= static_cast<int32_t>(m->in_idx.size())) return kInvalidArg;
+  const auto& a = m->in_idx[static_cast<size_t>(k)];
+  const auto& b = m->out_idx[static_cast<size_t>(k)];
+  for (size_t e = 0; e < a.size(); ++e) { in_idx[e] = a[e]; out_idx[e] = b[e]; }
+  return kOk;
+}
+
+// The forward over the whole map: out[N][Cout] = sum over k, over entries
+// (j, q) of list k, of feats[j][:] x W[k] (W[k] is Cin x Cout, row-major), in
+// fp64, from zero.  feats is [N][Cin], weights is [K^3][Cin][Cout].
+int oracle_forward(const void* h, const double* feats, const double* weights,
+                   int32_t Cin, int32_t Cout, double* out) {
+  const OracleMap* m = static_cast<const OracleMap*>(h);
+  if (feats == nullptr || weights == nullptr || out == nullptr || Cin <= 0 || Cout <= 0) {
+    return kInvalidArg;
+  }
+  for (int64_t i = 0; i < m->N * Cout; ++i) out[i] = 0.0;
+  const int32_t KV = m->K * m->K * m->K;
+  for (int32_t k = 0; k < KV; ++k) {
+    const auto& ins = m->in_idx[static_cast<size_t>(k)];
+    const auto& outs = m->out_idx[static_cast<size_t>(k)];
+    const double* Wk = weights + static_cast<int64_t>(k) * Cin * Cout;
+    for (size_t e = 0; e < ins.size(); ++e) {
+      const double* fj = feats + static_cast<int64_t>(ins[e]) * Cin;
+      double* oq = out + static_cast<int64_t>(outs[e]) * Cout;
+      for (int32_t ci = 0; ci < Cin; ++ci) {
+        for (int32_t co = 0; co < Cout; ++co) {
+          oq[co] += fj[ci] * Wk[static_cast<int64_t>(ci) * Cout + co];
+        }
+      }
+    }
+  }
+  return kOk;
+}
+
+// The same definition evaluated for selected output rows only, straight from
+// the coordinate table: out[i][:] = sum over offsets d with q_i + d active of
+// feats[row(q_i + d)][:] x W[k(d)].  Used where the whole map is too large to
+// evaluate in seconds.  rows holds n_rows output row indices.
+int oracle_forward_rows(const void* h, const double* feats, const double* weights,
+                        int32_t Cin, int32_t Cout, const int64_t* rows, int64_t n_rows,
+                        double* out) {
+  const OracleMap* m = static_cast<const OracleMap*>(h);
+  if (feats == nullptr || weights == nullptr || out == nullptr || rows == nullptr ||
+      Cin <= 0 || Cout <= 0 || n_rows < 0) {
+    return kInvalidArg;
+  }
+  const int32_t KV = m->K * m->K * m->K;
+  for (int64_t i = 0; i < n_rows; ++i) {
+    const int64_t q = rows[i];
+    if (q < 0 || q >= m->N) return kInvalidArg;
+    double* oq = out + i * Cout;
+    for (int32_t co = 0; co < Cout; ++co) oq[co] = 0.0;
+    const Coord& cq = m->coords[static_cast<size_t>(q)];
+    for (int32_t k = 0; k < KV; ++k) {
+      int64_t dz, dy, dx;
+      offset_of(k, m->K, &dz, &dy, &dx);
+      auto it = m->row_of.find(Coord{cq[0], cq[1] + dz, cq[2] + dy, cq[3] + dx});
+      if (it == m->row_of.end()) continue;
+      const double* fj = feats + it->second * Cin;
+      const double* Wk = weights + static_cast<int64_t>(k) * Cin * Cout;
+      for (int32_t ci = 0; ci < Cin; ++ci) {
+        for (int32_t co = 0; co < Cout; ++co) {
+          oq[co] += fj[ci] * Wk[static_cast<int64_t>(ci) * Cout + co];
+        }
+      }
+    }
+  }
+  return kOk;
+}
+
+// Neighbour rows of selected outputs: nbr[i][k] = row of q_i + d(k), or -1.
+int oracle_neighbours(const void* h, const int64_t* rows, int64_t n_rows, int32_t* nbr) {
+  const OracleMap* m = static_cast<const OracleMap*>(h);
+  if (rows == nullptr || nbr == nullptr || n_rows < 0) return kInvalidArg;
+  const int32_t KV = m->K * m->K * m->K;
+  for (int64_t i = 0; i < n_rows; ++i) {
+    const int64_t q = rows[i];
+    if (q < 0 || q >= m->N) return kInvalidArg;
+    const Coord& cq = m->coords[static_cast<size_t>(q)];
+    for (int32_t k = 0; k < KV; ++k) {
+      int64_t dz, dy, dx;
+      offset_of(k, m->K, &dz, &dy, &dx);
+      auto it = m->row_of.find(Coord{cq[0], cq[1] + dz, cq[2] + dy, cq[3] + dx});
+      nbr[i * KV + k] = (it == m->row_of.end()) ? -1 : static_cast<int32_t>(it->second);
+    }
+  }
+  return kOk;
+}
+
+}  // extern "C"
