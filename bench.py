@@ -1,0 +1,181 @@
+"""Benchmark of the submanifold sparse convolution hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+the kernel-map build (hash insert, half-offset probe with mirror emission,
+per-offset scan and compaction) followed by the fused forward (centre GEMM,
+gathered offsets on MFMA, output-stationary accumulation, epilogue).  Inputs
+are resident in HBM before timing starts.
+
+Prints ONE JSON line.  ``value`` is the whole-step effective throughput
+2 |map| C_in C_out / t_step in TFLOP/s (|map| counts real entries only,
+including the centre ones); the map-build rate and the forward-only rate are
+reported beside it.  ``roofline`` describes the fused forward kernel measured
+with HIP events on the stream it runs on; ``cpu_baseline`` times the CPU
+oracle on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
+DEFAULT_WORKLOAD = 1  # the indoor scene: 150k voxels, K=3, C=32, fp16
+
+ELEM = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def algorithmic_forward_bytes(n, e, kv, cin, cout, dtype):
+    """Minimum HBM bytes of one forward: each input row read once, each output
+    row written once, the weights once, and the (in, out) int32 index pair of
+    every non-centre entry once."""
+    s = ELEM[dtype]
+    return n * cin * s + n * cout * s + kv * cin * cout * s + 8 * (e - n)
+
+
+def cpu_baseline(layer, feats, w, budget_s=10.0, max_passes=5):
+    """The oracle, as it stands, on the same workload: map build (ordered-tree
+    lookups) plus fp64 forward, single-threaded, repeated until ~budget_s."""
+    import oracle
+
+    fd, wd = feats.double().numpy(), w.double().numpy()
+    times = []
+    e = 0
+    while len(times) < max_passes and sum(times) < budget_s:
+        t0 = time.perf_counter()
+        m = oracle.build_map(layer.coords, layer.k)
+        m.forward(fd, wd)
+        times.append(time.perf_counter() - t0)
+        e = m.total_entries
+    t = sum(times) / len(times)
+    return {
+        "value": 2.0 * e * layer.cin * layer.cout / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"whole workload (map build + fp64 forward), {len(times)} pass(es), "
+                  f"{t:.2f} s per pass",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD,
+                    help="workload index 0..4 (default: the indoor scene)")
+    ap.add_argument("--layer", type=int, default=0, help="layer of the workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
+              "multi-GPU path; see the sharding notes in DESIGN.md", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import submanifold_sparse_convolution_device_amd as sp
+    import workloads
+
+    sp.lib()
+    dev = torch.device("cuda:0")
+    wl = workloads.make_workload(args.workload)
+    layer = wl.layers[args.layer]
+    feats_h, w_h = workloads.layer_inputs(layer)
+    coords = torch.from_numpy(layer.coords).to(dev)
+    feats = feats_h.to(dev)
+    w = w_h.to(dev)
+    out = torch.empty((layer.n, layer.cout), dtype=feats.dtype, device=dev)
+    print(f"[bench] workload={wl.name} layer={args.layer} N={layer.n} K={layer.k} "
+          f"C={layer.cin}->{layer.cout} {layer.dtype}", file=sys.stderr, flush=True)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        kmap = sp.build_map(coords, layer.k)
+        if ev is not None:
+            ev[1].record()
+        sp.forward(feats, w, kmap, out=out)
+        if ev is not None:
+            ev[2].record()
+        return kmap
+
+    maps = [step() for _ in range(args.warmup)]
+    torch.cuda.synchronize()
+    e_total = maps[-1].total_entries
+    kv = layer.k ** 3
+    del maps
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    keep = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        keep.append(step(events[i]))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    build_ms = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in events]))
+    fwd_ms = float(np.mean([ev[1].elapsed_time(ev[2]) for ev in events]))
+    del keep
+
+    flops = 2.0 * e_total * layer.cin * layer.cout
+    value = flops / (ms_step * 1e-3) / 1e12
+    fwd_bytes = algorithmic_forward_bytes(layer.n, e_total, kv, layer.cin, layer.cout, layer.dtype)
+    achieved = fwd_bytes / (fwd_ms * 1e-3) / 1e9
+    result = {
+        "metric": "sparse-conv effective TFLOP/s (2*|map|*Cin*Cout/t) + map build Mvoxel/s",
+        "value": round(value, 4),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": layer.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "description": wl.description,
+            "n_voxels": layer.n,
+            "map_entries": e_total,
+            "kernel": layer.k,
+            "c_in": layer.cin,
+            "c_out": layer.cout,
+        },
+        "map_build_mvoxel_per_s": round(layer.n / (build_ms * 1e-3) / 1e6, 2),
+        "map_build_ms": round(build_ms, 4),
+        "forward_ms": round(fwd_ms, 4),
+        "forward_tflops": round(flops / (fwd_ms * 1e-3) / 1e12, 4),
+        "roofline": {
+            "kernel": "k_forward (fused gather-MFMA-accumulate)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": int(fwd_bytes),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(layer, feats_h, w_h)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

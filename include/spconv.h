@@ -1,0 +1,150 @@
+/*
+ * spconv.h — C ABI of the MI355X (gfx950) submanifold sparse convolution library.
+ *
+ * The operation (page titles as published, section names on each page):
+ *
+ *   Sparse tensor: a coordinate list of active voxels (b, z, y, x) and a
+ *   feature list with one row per voxel — SparseConvNet blog
+ *   ("图解稀疏卷积SparseConvNet：从哈希表到Rulebook的完整实现原理"), section 1.
+ *
+ *   Submanifold rule: an output exists exactly where an input exists
+ *   (P_out = P_in; odd kernel, stride 1, same padding) — "Sparse inputs and
+ *   sparse convolution", section "The fix: compute only where an input
+ *   exists"; "Sparse convolution for point clouds", section "Submanifold
+ *   sparse convolution".
+ *
+ *   Map (rulebook): for each output Q and offset d, the input P = Q + d, if
+ *   active, adds the entry (P, Q, W_d) — "Sparse inputs and sparse
+ *   convolution", section "The map is the computation"; offset sign as in
+ *   "Sparse convolution for point clouds", section "The map and the update
+ *   rule" (P = Q + offset), and in the GetOffset derivation of the blog's
+ *   section 3 (offset = input - output).  Entries are grouped by offset
+ *   ("sorted by weight offset", section "Nine entries become two").
+ *
+ *   Forward: f_out(Q) = sum over the map's entries (P, Q, W_d) of
+ *   f_in(P) x W_d, from zero, no bias — "Sparse convolution for point clouds",
+ *   section "The map and the update rule".
+ *
+ * Conventions of this ABI:
+ *   - coordinates: int32 [N][4] rows (b, z, y, x), row-major, b in [0, 2^15),
+ *     z, y, x in [0, 2^16); rows must be unique; entries never cross b;
+ *   - kernel size K in {1, 3, 5, 7}; r = (K - 1) / 2;
+ *   - offset index k(dz, dy, dx) = ((dz + r) K + (dy + r)) K + (dx + r), so the
+ *     centre is k = (K^3 - 1) / 2 and k(-d) = K^3 - 1 - k(d);
+ *   - weights: [K^3][C_in][C_out] row-major, the same dtype as the features;
+ *     W[k] multiplies the input at Q + d(k) (cross-correlation);
+ *   - a neighbour coordinate outside [0, 2^16) or not in the set is a miss.
+ *
+ * Memory and streams: every d_ pointer is device memory owned by the caller,
+ * except the map's lists, which the map owns.  hip_stream is a hipStream_t
+ * (NULL = the null stream).  spconv_build_map synchronises hip_stream once (to
+ * read the per-offset counts and the device-side error flags);
+ * spconv_forward is asynchronous on its stream.  The map's device buffers come
+ * from a library-owned stream-ordered memory pool on the current device.
+ *
+ * Errors: functions return a status; nothing throws across the ABI.  Host-
+ * checkable errors are reported before any device work.  On error, output
+ * handles are set to NULL and nothing leaks.  spconv_last_error() returns a
+ * thread-local message describing the last failure.
+ */
+#ifndef SPCONV_H_
+#define SPCONV_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spconv_status {
+  SPCONV_OK = 0,
+  SPCONV_ERR_INVALID_ARG = 1,     /* null pointer, bad size, misaligned buffer, K/C mismatch   */
+  SPCONV_ERR_DUPLICATE_COORD = 2, /* two rows share one (b, z, y, x) (detected on the device)  */
+  SPCONV_ERR_COORD_RANGE = 3,     /* a coordinate outside the ranges above (device-detected)   */
+  SPCONV_ERR_UNSUPPORTED = 4,     /* K not in {1,3,5,7}, dtype or channel count not supported  */
+  SPCONV_ERR_OUT_OF_MEMORY = 5,   /* device allocation failed                                  */
+  SPCONV_ERR_DEVICE = 6           /* a HIP runtime call failed                                 */
+} spconv_status;
+
+typedef enum spconv_dtype {
+  SPCONV_F32 = 0,  /* fp32 features and weights, fp32 products and accumulation                */
+  SPCONV_F16 = 1,  /* fp16 features and weights, fp32 accumulation, output rounded to nearest even */
+  SPCONV_BF16 = 2  /* bf16 features and weights, fp32 accumulation, output rounded to nearest even */
+} spconv_dtype;
+
+/* Opaque kernel map.  Owns its device buffers until spconv_map_free. */
+typedef struct spconv_map spconv_map;
+
+/* Version of this ABI (incremented on any incompatible change). */
+int32_t spconv_abi_version(void);
+
+/*
+ * Builds the kernel map of a submanifold convolution with a K x K x K kernel
+ * over the N voxels at d_coords (device int32 [N][4], (b, z, y, x)).
+ *
+ * The map holds, for every offset k, the list of entries (in_idx, out_idx)
+ * with coords[in_idx] = coords[out_idx] + d(k) (same b).  The centre list is
+ * the identity (q, q) for every row.  Within one offset the entries are in
+ * increasing out_idx.  Work: a device hash insert of all N keys, a probe of
+ * the (K^3 - 1) / 2 offsets with k > centre for every voxel, each hit also
+ * emitting its mirror entry (P, Q, d) <-> (Q, P, -d) ("Sparse inputs and
+ * sparse convolution", section "A symmetry you can check on the slide"), and
+ * a prefix-scan compaction per offset.
+ *
+ * Errors: INVALID_ARG (d_coords or out_map NULL, N <= 0, N x K^3 >= 2^31),
+ * UNSUPPORTED (K not in {1,3,5,7}), DUPLICATE_COORD, COORD_RANGE,
+ * OUT_OF_MEMORY, DEVICE.  On success *out_map is a new map, else NULL.
+ */
+spconv_status spconv_build_map(const int32_t* d_coords, int64_t n, int32_t kernel_size,
+                               void* hip_stream, spconv_map** out_map);
+
+/* Kernel size, number of voxels and total entries (sum of all counts,
+ * including the N centre entries).  Any output pointer may be NULL. */
+spconv_status spconv_map_info(const spconv_map* map, int32_t* kernel_size, int64_t* n,
+                              int64_t* total_entries);
+
+/* Copies the per-offset entry counts h_counts[K^3] and list offsets
+ * h_offsets[K^3 + 1] (host arrays; either may be NULL).  The entries of
+ * offset k lie at [h_offsets[k], h_offsets[k+1]) of the lists. */
+spconv_status spconv_map_counts(const spconv_map* map, int64_t* h_counts, int64_t* h_offsets);
+
+/* Borrowed device pointers to the map's int32 lists (total_entries each),
+ * valid until spconv_map_free.  Reading them is ordered after the build on the
+ * build's stream. */
+spconv_status spconv_map_lists(const spconv_map* map, const int32_t** d_in_idx,
+                               const int32_t** d_out_idx);
+
+/*
+ * Forward of one submanifold convolution over a map:
+ *   d_out[q][:] = sum_k sum_{(j, q) in list k} d_feats[j][:] x W[k]
+ * with d_feats [N][c_in], d_weights [K^3][c_in][c_out] and d_out [N][c_out]
+ * (caller-allocated, overwritten), all row-major in dtype and 16-byte aligned.
+ * Products accumulate in fp32; the result is rounded to dtype (to nearest
+ * even).  Runs as one fused kernel per call: the centre offset is a dense
+ * (identity-indexed) GEMM and every other offset gathers its input rows by
+ * index; each output row is accumulated on chip and written once.
+ *
+ * Requirements: c_in, c_out multiples of 8 in [8, 1024] (F16/BF16), or
+ * multiples of 4 in [4, 512] (F32).  Errors: INVALID_ARG (NULL or misaligned pointers, channel counts out
+ * of range), UNSUPPORTED (dtype, channel multiple), DEVICE.
+ */
+spconv_status spconv_forward(const void* d_feats, const void* d_weights, const spconv_map* map,
+                             int32_t c_in, int32_t c_out, spconv_dtype dtype, void* d_out,
+                             void* hip_stream);
+
+/* Releases a map.  Its buffers return to the pool in the order of the build's
+ * stream; the caller must not free a map while work on another stream still
+ * reads it.  NULL is ignored. */
+void spconv_map_free(spconv_map* map);
+
+/* Static name of a status ("SPCONV_OK", ...). */
+const char* spconv_status_string(spconv_status status);
+
+/* Thread-local detail of the last error on this thread ("" if none). */
+const char* spconv_last_error(void);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif /* SPCONV_H_ */

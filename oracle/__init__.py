@@ -62,6 +62,8 @@ def _lib() -> ctypes.CDLL:
         lib = ctypes.CDLL(path)
         lib.oracle_build_map.argtypes = [_i32p, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
         lib.oracle_build_map.restype = ctypes.c_int
+        lib.oracle_build_table.argtypes = lib.oracle_build_map.argtypes
+        lib.oracle_build_table.restype = ctypes.c_int
         lib.oracle_map_free.argtypes = [ctypes.c_void_p]
         lib.oracle_map_free.restype = None
         lib.oracle_map_kernel.argtypes = [ctypes.c_void_p]
@@ -87,15 +89,19 @@ def _ptr(a: np.ndarray, t):
 
 class OracleMap:
     """Map built by the oracle.  ``lists[k]`` is ``(in_idx, out_idx)`` int32
-    arrays ordered by output row."""
+    arrays ordered by output row.  With ``lists=False`` only the coordinate
+    table is built: ``forward_rows`` and ``neighbours`` still work, the lists
+    stay empty."""
 
-    def __init__(self, coords: np.ndarray, K: int):
+    def __init__(self, coords: np.ndarray, K: int, lists: bool = True):
         coords = np.ascontiguousarray(np.asarray(coords, dtype=np.int32).reshape(-1, 4))
         self.coords = coords
         self.K = int(K)
         self.N = int(coords.shape[0])
         h = ctypes.c_void_p()
-        st = _lib().oracle_build_map(_ptr(coords, _i32p), self.N, self.K, ctypes.byref(h))
+        fn = _lib().oracle_build_map if lists else _lib().oracle_build_table
+        st = fn(_ptr(coords, _i32p), self.N, self.K, ctypes.byref(h))
+        self.has_lists = bool(lists)
         if st != 0:
             raise OracleError(st)
         self._h = h
@@ -122,8 +128,10 @@ class OracleMap:
         return int(self.counts.sum())
 
     def forward(self, feats: np.ndarray, weights: np.ndarray) -> np.ndarray:
-        """fp64 forward over the whole map.  ``feats`` [N, Cin] and ``weights``
+        """fp64 forward over the whole map (needs the lists).  ``feats`` [N, Cin] and ``weights``
         [K^3, Cin, Cout] are widened to fp64 exactly before the call."""
+        if not self.has_lists:
+            raise ValueError("built with lists=False: use forward_rows")
         f = np.ascontiguousarray(np.asarray(feats, dtype=np.float64))
         w = np.ascontiguousarray(np.asarray(weights, dtype=np.float64))
         cin, cout = w.shape[1], w.shape[2]
@@ -160,6 +168,11 @@ class OracleMap:
 
 def build_map(coords: np.ndarray, K: int) -> OracleMap:
     return OracleMap(coords, K)
+
+
+def build_table(coords: np.ndarray, K: int) -> OracleMap:
+    """Coordinate table only, for row-at-a-time evaluation."""
+    return OracleMap(coords, K, lists=False)
 
 
 def offset_index(dz: int, dy: int, dx: int, K: int) -> int:

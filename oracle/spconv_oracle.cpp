@@ -73,7 +73,20 @@ extern "C" {
 // Builds the map of a submanifold convolution with a K^3 kernel over the N
 // voxels in coords (row-major int32 [N][4], (b, z, y, x)).  Returns a status;
 // on success *out holds an opaque handle to release with oracle_map_free.
+int oracle_build_map_impl(const int32_t* coords, int64_t N, int32_t K, bool with_lists, void** out);
+
 int oracle_build_map(const int32_t* coords, int64_t N, int32_t K, void** out) {
+  return oracle_build_map_impl(coords, N, K, true, out);
+}
+
+// The coordinate table only (step 1 below), for row-at-a-time evaluation with
+// oracle_forward_rows / oracle_neighbours on inputs too large for the full
+// double loop; the per-offset lists stay empty.
+int oracle_build_table(const int32_t* coords, int64_t N, int32_t K, void** out) {
+  return oracle_build_map_impl(coords, N, K, false, out);
+}
+
+int oracle_build_map_impl(const int32_t* coords, int64_t N, int32_t K, bool with_lists, void** out) {
   if (out == nullptr) return kInvalidArg;
   *out = nullptr;
   if (coords == nullptr || N <= 0 || K < 1 || K % 2 == 0) return kInvalidArg;
@@ -100,7 +113,7 @@ int oracle_build_map(const int32_t* coords, int64_t N, int32_t K, void** out) {
   const int32_t KV = K * K * K;
   m->in_idx.assign(static_cast<size_t>(KV), {});
   m->out_idx.assign(static_cast<size_t>(KV), {});
-  for (int64_t q = 0; q < N; ++q) {
+  for (int64_t q = 0; with_lists && q < N; ++q) {
     const Coord& cq = m->coords[static_cast<size_t>(q)];
     for (int32_t k = 0; k < KV; ++k) {
       int64_t dz, dy, dx;

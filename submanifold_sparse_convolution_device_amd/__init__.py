@@ -1,0 +1,248 @@
+"""Submanifold sparse convolution on AMD MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libspconv.so`` (declared in
+``include/spconv.h``).  It only marshals arguments: PyTorch tensors supply
+device memory and the current HIP stream; every step of the map build and the
+forward runs in the library's HIP kernels.  There is no CPU fallback: if the
+library is missing, every entry point raises.
+
+The raw C functions are exposed under their C names (``spconv_build_map``,
+``spconv_forward``, ...) through :func:`lib`; :func:`build_map` and
+:func:`forward` wrap them for torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspconv.so")
+
+STATUS = {
+    0: "SPCONV_OK",
+    1: "SPCONV_ERR_INVALID_ARG",
+    2: "SPCONV_ERR_DUPLICATE_COORD",
+    3: "SPCONV_ERR_COORD_RANGE",
+    4: "SPCONV_ERR_UNSUPPORTED",
+    5: "SPCONV_ERR_OUT_OF_MEMORY",
+    6: "SPCONV_ERR_DEVICE",
+}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+
+# Every symbol include/spconv.h declares.
+EXPORTED = (
+    "spconv_abi_version", "spconv_build_map", "spconv_map_info", "spconv_map_counts",
+    "spconv_map_lists", "spconv_forward", "spconv_map_free", "spconv_status_string",
+    "spconv_last_error",
+)
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+class SpconvError(RuntimeError):
+    """A non-OK status from the C ABI."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, f"status {status}")
+        super().__init__(f"{self.name}: {detail}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``libspconv.so`` with argument types declared."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc for gfx950) first")
+    # torch ships its own HIP runtime under the same soname (libamdhip64.so.7).
+    # Loading torch first makes the library bind to that one runtime, so
+    # torch's stream handles and allocations are valid in both.
+    _torch()
+    L = ctypes.CDLL(LIB_PATH)
+    runtimes = _mapped_hip_runtimes()
+    if len(runtimes) > 1:
+        raise RuntimeError(f"two HIP runtimes are mapped in this process: {runtimes}")
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.spconv_abi_version.argtypes, L.spconv_abi_version.restype = [], i32
+    L.spconv_build_map.argtypes = [vp, i64, i32, vp, ctypes.POINTER(vp)]
+    L.spconv_build_map.restype = ctypes.c_int
+    L.spconv_map_info.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.spconv_map_info.restype = ctypes.c_int
+    L.spconv_map_counts.argtypes = [vp, vp, vp]
+    L.spconv_map_counts.restype = ctypes.c_int
+    L.spconv_map_lists.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp)]
+    L.spconv_map_lists.restype = ctypes.c_int
+    L.spconv_forward.argtypes = [vp, vp, vp, i32, i32, ctypes.c_int, vp, vp]
+    L.spconv_forward.restype = ctypes.c_int
+    L.spconv_map_free.argtypes, L.spconv_map_free.restype = [vp], None
+    L.spconv_status_string.argtypes, L.spconv_status_string.restype = [ctypes.c_int], ctypes.c_char_p
+    L.spconv_last_error.argtypes, L.spconv_last_error.restype = [], ctypes.c_char_p
+    # the runtime's own copy routine, resolved through the library's dependencies
+    L.hipMemcpyAsync.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
+    L.hipMemcpyAsync.restype = ctypes.c_int
+    _LIB = L
+    return L
+
+
+def _mapped_hip_runtimes():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({l.split()[-1] for l in f if "libamdhip64" in l})
+    except OSError:
+        return []
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise SpconvError(status, lib().spconv_last_error().decode(errors="replace"))
+
+
+# ------------------------------------------------------------------ raw C names
+
+
+def spconv_abi_version() -> int:
+    return int(lib().spconv_abi_version())
+
+
+def spconv_build_map(d_coords: int, n: int, kernel_size: int, hip_stream: int) -> int:
+    """Raw call: returns the map handle (int) or raises SpconvError."""
+    h = ctypes.c_void_p()
+    _check(lib().spconv_build_map(d_coords, n, kernel_size, hip_stream, ctypes.byref(h)))
+    return int(h.value)
+
+
+def spconv_map_info(handle: int) -> Tuple[int, int, int]:
+    K, n, e = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().spconv_map_info(handle, ctypes.byref(K), ctypes.byref(n), ctypes.byref(e)))
+    return K.value, n.value, e.value
+
+
+def spconv_map_counts(handle: int, kernel_volume: int) -> Tuple[np.ndarray, np.ndarray]:
+    counts = np.zeros(kernel_volume, np.int64)
+    offsets = np.zeros(kernel_volume + 1, np.int64)
+    _check(lib().spconv_map_counts(handle, counts.ctypes.data, offsets.ctypes.data))
+    return counts, offsets
+
+
+def spconv_map_lists(handle: int) -> Tuple[int, int]:
+    a, b = ctypes.c_void_p(), ctypes.c_void_p()
+    _check(lib().spconv_map_lists(handle, ctypes.byref(a), ctypes.byref(b)))
+    return int(a.value or 0), int(b.value or 0)
+
+
+def spconv_forward(d_feats: int, d_weights: int, handle: int, c_in: int, c_out: int, dtype: int,
+                   d_out: int, hip_stream: int) -> None:
+    _check(lib().spconv_forward(d_feats, d_weights, handle, c_in, c_out, dtype, d_out, hip_stream))
+
+
+def spconv_map_free(handle: int) -> None:
+    lib().spconv_map_free(handle)
+
+
+def spconv_status_string(status: int) -> str:
+    return lib().spconv_status_string(status).decode()
+
+
+def spconv_last_error() -> str:
+    return lib().spconv_last_error().decode(errors="replace")
+
+
+# ------------------------------------------------------------------ torch front end
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if t.dtype not in m:
+        raise SpconvError(4, f"dtype {t.dtype} not supported")
+    return m[t.dtype]
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+class SpconvMap:
+    """A kernel map on the GPU (owns the C handle)."""
+
+    def __init__(self, handle: int, device):
+        self.handle = handle
+        self.device = device
+        self.kernel_size, self.n, self.total_entries = spconv_map_info(handle)
+        self.kernel_volume = self.kernel_size ** 3
+        self.counts, self.offsets = spconv_map_counts(handle, self.kernel_volume)
+
+    def lists(self):
+        """(in_idx, out_idx) as int32 device tensors: stream-ordered copies of
+        the map's lists (the map owns the originals)."""
+        torch = _torch()
+        a, b = spconv_map_lists(self.handle)
+        e = self.total_entries
+        out = torch.empty((2, e), dtype=torch.int32, device=self.device)
+        if e:
+            stream = _stream(self.device)
+            for dst, src in ((out[0].data_ptr(), a), (out[1].data_ptr(), b)):
+                rc = lib().hipMemcpyAsync(dst, src, 4 * e, 3, stream)  # device to device
+                if rc != 0:
+                    raise SpconvError(6, f"hipMemcpyAsync failed with {rc}")
+        return out[0], out[1]
+
+    def free(self):
+        if self.handle:
+            spconv_map_free(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def build_map(coords, kernel_size: int) -> SpconvMap:
+    """Kernel map of a K^3 submanifold convolution over int32 [N, 4]
+    (b, z, y, x) coordinates resident on a HIP device."""
+    torch = _torch()
+    if not (isinstance(coords, torch.Tensor) and coords.is_cuda and coords.dtype == torch.int32
+            and coords.dim() == 2 and coords.shape[1] == 4 and coords.is_contiguous()):
+        raise SpconvError(1, "coords must be a contiguous int32 [N, 4] tensor on a HIP device")
+    with torch.cuda.device(coords.device):
+        h = spconv_build_map(coords.data_ptr(), coords.shape[0], int(kernel_size), _stream(coords.device))
+    return SpconvMap(h, coords.device)
+
+
+def forward(feats, weights, kmap: SpconvMap, out=None):
+    """f_out = submanifold convolution of feats [N, C_in] with weights
+    [K^3, C_in, C_out] over ``kmap``; returns out [N, C_out] (same dtype)."""
+    torch = _torch()
+    for name, t in (("feats", feats), ("weights", weights)):
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
+            raise SpconvError(1, f"{name} must be a contiguous tensor on a HIP device")
+    if feats.dim() != 2 or weights.dim() != 3:
+        raise SpconvError(1, "feats must be [N, C_in] and weights [K^3, C_in, C_out]")
+    n, cin = feats.shape
+    kv, wcin, cout = weights.shape
+    if n != kmap.n or kv != kmap.kernel_volume or wcin != cin:
+        raise SpconvError(1, f"shape mismatch: feats {tuple(feats.shape)}, weights "
+                             f"{tuple(weights.shape)}, map N={kmap.n} K^3={kmap.kernel_volume}")
+    if weights.dtype != feats.dtype:
+        raise SpconvError(1, "feats and weights must share one dtype")
+    if out is None:
+        out = torch.empty((n, cout), dtype=feats.dtype, device=feats.device)
+    elif not (out.is_cuda and out.is_contiguous() and out.dtype == feats.dtype and out.shape == (n, cout)):
+        raise SpconvError(1, "out must be a contiguous [N, C_out] tensor of the feature dtype")
+    with torch.cuda.device(feats.device):
+        spconv_forward(feats.data_ptr(), weights.data_ptr(), kmap.handle, cin, cout,
+                       _dtype_code(feats), out.data_ptr(), _stream(feats.device))
+    return out

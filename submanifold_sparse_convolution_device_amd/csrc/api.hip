@@ -1,0 +1,310 @@
+// Host side of the C ABI declared in include/spconv.h: argument validation,
+// stream-ordered memory, the single read-back of the map build, and kernel
+// launches.  No compute happens here.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/spconv.h"
+#include "internal.h"
+
+struct spconv_map {
+  int device = 0;
+  hipStream_t stream = nullptr;
+  int32_t K = 0;
+  int32_t KV = 0;
+  int64_t n = 0;
+  int64_t total = 0;
+  int64_t tiles = 0;
+  std::vector<int64_t> counts;   // KV
+  std::vector<int64_t> offsets;  // KV + 1
+  void* block = nullptr;         // one pool allocation: in_idx | out_idx | tile_off
+  int32_t* in_idx = nullptr;
+  int32_t* out_idx = nullptr;
+  int32_t* tile_off = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+spconv_status fail(spconv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+spconv_status hip_fail(hipError_t e, const char* what) {
+  const spconv_status st =
+      (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) ? SPCONV_ERR_OUT_OF_MEMORY
+                                                                   : SPCONV_ERR_DEVICE;
+  return fail(st, "%s: %s (%d)", what, hipGetErrorString(e), static_cast<int>(e));
+}
+
+#define SPCONV_HIP(call, what)                 \
+  do {                                         \
+    const hipError_t e_ = (call);              \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+// One stream-ordered pool per device, kept warm (no release at sync points),
+// so per-build workspace and map buffers cost no driver allocation once the
+// pool has grown.
+std::mutex g_pool_mu;
+std::vector<hipMemPool_t> g_pools;
+
+spconv_status pool_for(int device, hipMemPool_t* out) {
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  if (static_cast<int>(g_pools.size()) <= device) g_pools.resize(device + 1, nullptr);
+  if (g_pools[device] == nullptr) {
+    hipMemPoolProps props;
+    std::memset(&props, 0, sizeof(props));
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = device;
+    hipMemPool_t pool = nullptr;
+    SPCONV_HIP(hipMemPoolCreate(&pool, &props), "hipMemPoolCreate");
+    uint64_t keep = ~0ull;
+    SPCONV_HIP(hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep),
+               "hipMemPoolSetAttribute");
+    g_pools[device] = pool;
+  }
+  *out = g_pools[device];
+  return SPCONV_OK;
+}
+
+// Pinned host staging for the build's read-back, one per thread.
+spconv_status host_staging(size_t bytes, long long** out) {
+  thread_local long long* buf = nullptr;
+  thread_local size_t cap = 0;
+  if (cap < bytes) {
+    if (buf != nullptr) (void)hipHostFree(buf);
+    buf = nullptr;
+    cap = 0;
+    void* p = nullptr;
+    SPCONV_HIP(hipHostMalloc(&p, bytes, hipHostMallocPortable), "hipHostMalloc");
+    buf = static_cast<long long*>(p);
+    cap = bytes;
+  }
+  *out = buf;
+  return SPCONV_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t next_pow2(int64_t v) {
+  int64_t p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t spconv_abi_version(void) { return 1; }
+
+const char* spconv_status_string(spconv_status s) {
+  switch (s) {
+    case SPCONV_OK: return "SPCONV_OK";
+    case SPCONV_ERR_INVALID_ARG: return "SPCONV_ERR_INVALID_ARG";
+    case SPCONV_ERR_DUPLICATE_COORD: return "SPCONV_ERR_DUPLICATE_COORD";
+    case SPCONV_ERR_COORD_RANGE: return "SPCONV_ERR_COORD_RANGE";
+    case SPCONV_ERR_UNSUPPORTED: return "SPCONV_ERR_UNSUPPORTED";
+    case SPCONV_ERR_OUT_OF_MEMORY: return "SPCONV_ERR_OUT_OF_MEMORY";
+    case SPCONV_ERR_DEVICE: return "SPCONV_ERR_DEVICE";
+  }
+  return "SPCONV_ERR_UNKNOWN";
+}
+
+const char* spconv_last_error(void) { return g_last_error.c_str(); }
+
+spconv_status spconv_build_map(const int32_t* d_coords, int64_t n, int32_t kernel_size,
+                               void* hip_stream, spconv_map** out_map) {
+  g_last_error.clear();
+  if (out_map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "out_map is NULL");
+  *out_map = nullptr;
+  if (d_coords == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "d_coords is NULL");
+  if (!aligned16(d_coords)) return fail(SPCONV_ERR_INVALID_ARG, "d_coords is not 16-byte aligned");
+  if (n <= 0) return fail(SPCONV_ERR_INVALID_ARG, "n = %lld must be positive", (long long)n);
+  if (kernel_size != 1 && kernel_size != 3 && kernel_size != 5 && kernel_size != 7) {
+    return fail(SPCONV_ERR_UNSUPPORTED, "kernel_size = %d not in {1, 3, 5, 7}", kernel_size);
+  }
+  const int32_t KV = kernel_size * kernel_size * kernel_size;
+  if (n >= (int64_t(1) << 31) / KV) {
+    return fail(SPCONV_ERR_INVALID_ARG, "n x K^3 = %lld x %d must stay below 2^31",
+                (long long)n, KV);
+  }
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+
+  spconv::BuildPlan p;
+  p.n = n;
+  p.K = kernel_size;
+  p.KV = KV;
+  p.centre = (KV - 1) / 2;
+  p.half = (KV - 1) / 2;
+  p.mask_words = (KV + 31) / 32;
+  p.tiles = (n + spconv::kTileRows - 1) / spconv::kTileRows;
+  p.chunks = (p.tiles + spconv::kChunkTiles - 1) / spconv::kChunkTiles;
+  p.table_slots = next_pow2(2 * n);
+  if (p.table_slots < 64) p.table_slots = 64;
+
+  int device = 0;
+  SPCONV_HIP(hipGetDevice(&device), "hipGetDevice");
+  hipMemPool_t pool = nullptr;
+  spconv_status st = pool_for(device, &pool);
+  if (st != SPCONV_OK) return st;
+  long long* staging = nullptr;
+  st = host_staging(sizeof(long long) * (spconv::kSummaryHead + KV), &staging);
+  if (st != SPCONV_OK) return st;
+
+  void* ws = nullptr;
+  SPCONV_HIP(hipMallocFromPoolAsync(&ws, spconv::build_scratch_bytes(p), pool, stream),
+             "workspace allocation");
+  spconv::BuildScratch s;
+  spconv::carve_build_scratch(p, ws, &s);
+
+  auto release_ws = [&]() { (void)hipFreeAsync(ws, stream); };
+  hipError_t e = spconv::launch_build_front(p, d_coords, s, stream);
+  if (e != hipSuccess) { release_ws(); return hip_fail(e, "map build launch"); }
+  e = hipMemcpyAsync(staging, s.summary, sizeof(long long) * (spconv::kSummaryHead + KV),
+                     hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) { release_ws(); return hip_fail(e, "summary read-back"); }
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) { release_ws(); return hip_fail(e, "map build"); }
+
+  const unsigned long long flags = static_cast<unsigned long long>(staging[0]);
+  if (flags & spconv::kFlagRange) {
+    release_ws();
+    return fail(SPCONV_ERR_COORD_RANGE,
+                "a coordinate is outside b in [0, 2^15), z, y, x in [0, 2^16)");
+  }
+  if (flags & spconv::kFlagDuplicate) {
+    release_ws();
+    return fail(SPCONV_ERR_DUPLICATE_COORD, "two rows share one (b, z, y, x) coordinate");
+  }
+  if (flags & spconv::kFlagTableFull) {
+    release_ws();
+    return fail(SPCONV_ERR_DEVICE, "internal: hash table probe exceeded its bound");
+  }
+  const int64_t total = staging[1];
+
+  spconv_map* m = new (std::nothrow) spconv_map;
+  if (m == nullptr) { release_ws(); return fail(SPCONV_ERR_OUT_OF_MEMORY, "host allocation"); }
+  m->device = device;
+  m->stream = stream;
+  m->K = kernel_size;
+  m->KV = KV;
+  m->n = n;
+  m->total = total;
+  m->tiles = p.tiles;
+  m->counts.assign(staging + spconv::kSummaryHead, staging + spconv::kSummaryHead + KV);
+  m->offsets.resize(KV + 1);
+  m->offsets[0] = 0;
+  for (int k = 0; k < KV; ++k) m->offsets[k + 1] = m->offsets[k] + m->counts[k];
+
+  const size_t list_bytes = (static_cast<size_t>(total) * sizeof(int32_t) + 255) / 256 * 256;
+  const size_t tile_bytes = static_cast<size_t>(KV * p.tiles + 1) * sizeof(int32_t);
+  e = hipMallocFromPoolAsync(&m->block, 2 * list_bytes + tile_bytes, pool, stream);
+  if (e != hipSuccess) {
+    delete m;
+    release_ws();
+    return hip_fail(e, "map allocation");
+  }
+  char* b = static_cast<char*>(m->block);
+  m->in_idx = reinterpret_cast<int32_t*>(b);
+  m->out_idx = reinterpret_cast<int32_t*>(b + list_bytes);
+  m->tile_off = reinterpret_cast<int32_t*>(b + 2 * list_bytes);
+  e = spconv::launch_build_compact(p, s, total, m->in_idx, m->out_idx, m->tile_off, stream);
+  release_ws();
+  if (e != hipSuccess) {
+    (void)hipFreeAsync(m->block, stream);
+    delete m;
+    return hip_fail(e, "map compaction launch");
+  }
+  *out_map = m;
+  return SPCONV_OK;
+}
+
+spconv_status spconv_map_info(const spconv_map* map, int32_t* kernel_size, int64_t* n,
+                              int64_t* total_entries) {
+  if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
+  if (kernel_size) *kernel_size = map->K;
+  if (n) *n = map->n;
+  if (total_entries) *total_entries = map->total;
+  return SPCONV_OK;
+}
+
+spconv_status spconv_map_counts(const spconv_map* map, int64_t* h_counts, int64_t* h_offsets) {
+  if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
+  if (h_counts) std::memcpy(h_counts, map->counts.data(), sizeof(int64_t) * map->KV);
+  if (h_offsets) std::memcpy(h_offsets, map->offsets.data(), sizeof(int64_t) * (map->KV + 1));
+  return SPCONV_OK;
+}
+
+spconv_status spconv_map_lists(const spconv_map* map, const int32_t** d_in_idx,
+                               const int32_t** d_out_idx) {
+  if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
+  if (d_in_idx) *d_in_idx = map->in_idx;
+  if (d_out_idx) *d_out_idx = map->out_idx;
+  return SPCONV_OK;
+}
+
+spconv_status spconv_forward(const void* d_feats, const void* d_weights, const spconv_map* map,
+                             int32_t c_in, int32_t c_out, spconv_dtype dtype, void* d_out,
+                             void* hip_stream) {
+  g_last_error.clear();
+  if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
+  if (d_feats == nullptr || d_weights == nullptr || d_out == nullptr) {
+    return fail(SPCONV_ERR_INVALID_ARG, "NULL feature, weight or output pointer");
+  }
+  if (!aligned16(d_feats) || !aligned16(d_weights) || !aligned16(d_out)) {
+    return fail(SPCONV_ERR_INVALID_ARG, "feature, weight and output buffers must be 16-byte aligned");
+  }
+  if (dtype != SPCONV_F32 && dtype != SPCONV_F16 && dtype != SPCONV_BF16) {
+    return fail(SPCONV_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(dtype));
+  }
+  const int32_t cmax = (dtype == SPCONV_F32) ? 512 : 1024;
+  if (c_in < 1 || c_out < 1 || c_in > cmax || c_out > cmax) {
+    return fail(SPCONV_ERR_INVALID_ARG, "c_in = %d, c_out = %d must lie in [1, %d]", c_in, c_out, cmax);
+  }
+  const int32_t mult = (dtype == SPCONV_F32) ? 4 : 8;
+  if (c_in % mult != 0 || c_out % mult != 0) {
+    return fail(SPCONV_ERR_UNSUPPORTED, "c_in = %d and c_out = %d must be multiples of %d", c_in,
+                c_out, mult);
+  }
+  spconv::ForwardArgs a;
+  a.feats = d_feats;
+  a.weights = d_weights;
+  a.out = d_out;
+  a.in_idx = map->in_idx;
+  a.out_idx = map->out_idx;
+  a.tile_off = map->tile_off;
+  a.n = map->n;
+  a.tiles = map->tiles;
+  a.KV = map->KV;
+  a.cin = c_in;
+  a.cout = c_out;
+  a.dtype = static_cast<int32_t>(dtype);
+  const hipError_t e = spconv::launch_forward(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  return SPCONV_OK;
+}
+
+void spconv_map_free(spconv_map* map) {
+  if (map == nullptr) return;
+  if (map->block != nullptr) (void)hipFreeAsync(map->block, map->stream);
+  delete map;
+}
+
+}  // extern "C"

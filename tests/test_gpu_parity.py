@@ -1,0 +1,296 @@
+"""GPU parity: the HIP path through the C ABI against the oracle.
+
+Maps must match bit-exactly as per-offset sets (the order inside a list is
+the library's choice; it is also checked to be increasing in out_idx).
+Features must satisfy max |gpu - oracle| <= tol x RMS(oracle) with tol = 2e-2
+for fp16/bf16 and 1e-5 for fp32, the oracle computing in fp64 on the exactly
+widened stored inputs.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module")
+def sp():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    import submanifold_sparse_convolution_device_amd as m
+    m.lib()
+    return m
+
+
+DEV = "cuda:0"
+
+
+@functools.lru_cache(maxsize=None)
+def _workload(index):
+    return workloads.make_workload(index)
+
+
+def _gpu_map(sp, coords, K):
+    return sp.build_map(torch.from_numpy(np.ascontiguousarray(coords, dtype=np.int32)).to(DEV), K)
+
+
+def _gpu_lists(kmap):
+    a, b = kmap.lists()
+    torch.cuda.synchronize()
+    return a.cpu().numpy(), b.cpu().numpy()
+
+
+def assert_map_equal(kmap, ref):
+    """Per-offset set equality, counts and offsets, plus the ordering contract."""
+    kv = ref.K ** 3
+    assert kmap.kernel_size == ref.K and kmap.n == ref.N
+    assert np.array_equal(kmap.counts, ref.counts)
+    assert kmap.offsets[0] == 0 and np.array_equal(np.diff(kmap.offsets), kmap.counts)
+    assert kmap.total_entries == ref.total_entries
+    a, b = _gpu_lists(kmap)
+    for k in range(kv):
+        lo, hi = kmap.offsets[k], kmap.offsets[k + 1]
+        ga, gb = a[lo:hi], b[lo:hi]
+        assert np.all(np.diff(gb) > 0), f"offset {k}: out_idx not increasing"
+        ra, rb = ref.lists[k]  # the oracle's lists are ordered by output row too
+        assert np.array_equal(gb, rb) and np.array_equal(ga, ra), f"offset {k} differs"
+
+
+def _forward_check(sp, kmap, coords, K, cin, cout, dtype, seed, ref_map=None, rows=None):
+    f = workloads.features(coords.shape[0], cin, dtype, seed)
+    w = workloads.weights(K, cin, cout, dtype, seed + 1)
+    out = sp.forward(f.to(DEV), w.to(DEV), kmap)
+    got = out.double().cpu().numpy()
+    ref_map = ref_map or oracle.build_map(coords, K)
+    fd, wd = f.double().numpy(), w.double().numpy()
+    if rows is None:
+        ref = ref_map.forward(fd, wd)
+        sel = got
+    else:
+        ref = ref_map.forward_rows(fd, wd, rows)
+        sel = got[rows]
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = float(np.max(np.abs(sel - ref)))
+    assert np.all(np.isfinite(got))
+    assert err <= TOL[dtype] * rms, f"max|err| {err:.3e} > {TOL[dtype]} x RMS {rms:.3e}"
+    return err / rms
+
+
+# ------------------------------------------------------------------ maps
+
+
+def test_worked_5x5_map(sp):
+    pts = [(1, 1), (2, 2), (2, 4), (3, 2), (4, 3)]
+    c = np.array([[0, 0, r, col] for r, col in pts], np.int32)
+    kmap = _gpu_map(sp, c, 3)
+    assert_map_equal(kmap, oracle.build_map(c, 3))
+    assert kmap.total_entries == 11 and int((kmap.counts > 0).sum()) == 5
+
+
+@pytest.mark.parametrize("seed,extent,occ,batches,K", [
+    (1, 6, 0.05, 1, 3), (2, 10, 0.2, 2, 3), (3, 9, 0.4, 1, 5), (4, 16, 0.1, 3, 3),
+    (5, 8, 0.3, 1, 1), (6, 12, 0.05, 2, 5), (7, 7, 0.5, 1, 7), (8, 20, 0.15, 2, 3),
+])
+def test_map_random_grids(sp, seed, extent, occ, batches, K):
+    c = workloads.permuted(workloads.random_grid(seed, extent, occ, batches), seed)
+    assert_map_equal(_gpu_map(sp, c, K), oracle.build_map(c, K))
+
+
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 127, 4095, 4096, 4097, 8193])
+def test_map_ragged_sizes(sp, n):
+    """Sizes around the 64-row tile and 4096-row chunk edges."""
+    rng = np.random.default_rng(n)
+    cells = rng.choice(40 ** 3, size=n, replace=False)
+    c = np.stack([np.zeros(n), cells // 1600, (cells // 40) % 40, cells % 40], 1).astype(np.int32)
+    assert_map_equal(_gpu_map(sp, c, 3), oracle.build_map(c, 3))
+
+
+def test_map_extreme_coordinates(sp):
+    """In-range extremes; neighbours past 2^16 - 1 or below 0 are misses, never wraps."""
+    c = np.array([[32767, 65535, 65535, 65535], [32767, 65535, 65535, 65534], [32767, 0, 0, 0],
+                  [0, 65535, 65535, 65535], [0, 0, 0, 0], [0, 0, 0, 1], [1, 0, 0, 0]], np.int32)
+    assert_map_equal(_gpu_map(sp, c, 3), oracle.build_map(c, 3))
+    assert_map_equal(_gpu_map(sp, c, 5), oracle.build_map(c, 5))
+
+
+def test_map_dense_cube_closed_form(sp):
+    """Fully active 100^3 cube (1M voxels): count(d) = prod (100 - |d_i|)."""
+    n = 100
+    ax = np.arange(n)
+    z, y, x = np.meshgrid(ax, ax, ax, indexing="ij")
+    c = np.stack([np.zeros(n ** 3), z.ravel(), y.ravel(), x.ravel()], 1).astype(np.int32)
+    kmap = _gpu_map(sp, c, 3)
+    for k in range(27):
+        dz, dy, dx = oracle.offset_of(k, 3)
+        assert kmap.counts[k] == (n - abs(dz)) * (n - abs(dy)) * (n - abs(dx))
+
+
+def test_map_device_errors(sp):
+    dup = np.array([[0, 1, 2, 3], [0, 5, 5, 5], [0, 1, 2, 3]], np.int32)
+    with pytest.raises(sp.SpconvError) as e:
+        _gpu_map(sp, dup, 3)
+    assert e.value.name == "SPCONV_ERR_DUPLICATE_COORD"
+    for bad in ([0, 0, 70000, 0], [0, -1, 0, 0], [40000, 0, 0, 0]):
+        c = np.array([[0, 0, 0, 0], bad], np.int32)
+        with pytest.raises(sp.SpconvError) as e:
+            _gpu_map(sp, c, 3)
+        assert e.value.name == "SPCONV_ERR_COORD_RANGE"
+    # the library stays usable after device-detected errors
+    ok = np.array([[0, 1, 2, 3], [0, 1, 2, 4]], np.int32)
+    assert _gpu_map(sp, ok, 3).total_entries == 4
+
+
+def test_map_deterministic(sp):
+    c = workloads.permuted(workloads.random_grid(99, 30, 0.1, 2), 99)
+    a1, b1 = _gpu_lists(_gpu_map(sp, c, 3))
+    a2, b2 = _gpu_lists(_gpu_map(sp, c, 3))
+    assert np.array_equal(a1, a2) and np.array_equal(b1, b2)
+
+
+# ------------------------------------------------------------------ forward
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("K,cin,cout", [(3, 16, 16), (3, 32, 48), (3, 8, 24), (5, 40, 16), (1, 64, 32),
+                                        (3, 96, 136), (7, 16, 8)])
+def test_forward_random_grids(sp, dtype, K, cin, cout):
+    if dtype == "f32" and (cin > 512 or cout > 512):
+        pytest.skip("fp32 channels are limited to 512")
+    c = workloads.permuted(workloads.random_grid(K * 100 + cin, 14, 0.2, 2), cin)
+    kmap = _gpu_map(sp, c, K)
+    _forward_check(sp, kmap, c, K, cin, cout, dtype, seed=cin * 7 + cout)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_forward_routing_is_exact(sp, dtype):
+    """Identity weights route rows exactly in any dtype (one product by 1.0)."""
+    c = workloads.permuted(workloads.random_grid(5, 12, 0.3, 1), 5)
+    n, ch = c.shape[0], 32
+    kmap = _gpu_map(sp, c, 3)
+    ref = oracle.build_map(c, 3)
+    f = workloads.features(n, ch, dtype, 11)
+    for k in (13, 0, 17, 26):
+        w = torch.zeros((27, ch, ch), dtype=TORCH_DT[dtype])
+        w[k] = torch.eye(ch, dtype=TORCH_DT[dtype])
+        out = sp.forward(f.to(DEV), w.to(DEV), kmap).cpu()
+        exp = torch.zeros_like(f)
+        j, q = ref.lists[k]
+        exp[torch.from_numpy(q).long()] = f[torch.from_numpy(j).long()]
+        assert torch.equal(out, exp), f"offset {k}"
+
+
+def test_forward_all_ones_degree(sp):
+    """All-ones features and weights: f_out[q][c] = Cin x deg(q), exact in fp16."""
+    c = workloads.random_grid(17, 10, 0.5, 1)
+    kmap = _gpu_map(sp, c, 3)
+    n, ch = c.shape[0], 16
+    out = sp.forward(torch.ones((n, ch), dtype=torch.float16, device=DEV),
+                     torch.ones((27, ch, 8), dtype=torch.float16, device=DEV), kmap).cpu()
+    ref = oracle.build_map(c, 3)
+    deg = np.zeros(n)
+    for k in range(27):
+        np.add.at(deg, ref.lists[k][1], 1)
+    assert torch.equal(out, torch.from_numpy(np.repeat((ch * deg)[:, None], 8, 1)).half())
+
+
+def test_forward_single_voxel_and_isolated(sp):
+    c = np.array([[0, 5, 5, 5]], np.int32)
+    kmap = _gpu_map(sp, c, 3)
+    _forward_check(sp, kmap, c, 3, 32, 32, "f16", seed=1)
+    iso = np.array([[0, 3 * i, 3 * j, 0] for i in range(9) for j in range(9)], np.int32)
+    _forward_check(sp, _gpu_map(sp, iso, 3), iso, 3, 32, 16, "bf16", seed=2)
+
+
+def test_forward_is_repeatable_and_overwrites(sp):
+    c = workloads.random_grid(23, 16, 0.2, 1)
+    kmap = _gpu_map(sp, c, 3)
+    f = workloads.features(c.shape[0], 32, "f16", 1).to(DEV)
+    w = workloads.weights(3, 32, 32, "f16", 2).to(DEV)
+    out = torch.full((c.shape[0], 32), float("nan"), dtype=torch.float16, device=DEV)
+    a = sp.forward(f, w, kmap, out=out).clone()
+    b = sp.forward(f, w, kmap)
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ the five workloads
+
+
+@pytest.mark.parametrize("index", [0, 1, 2])
+def test_workload_map_and_forward(sp, index):
+    wl = _workload(index)
+    layer = wl.layers[0]
+    ref = oracle.build_map(layer.coords, layer.k)
+    kmap = _gpu_map(sp, layer.coords, layer.k)
+    assert_map_equal(kmap, ref)
+    _forward_check(sp, kmap, layer.coords, layer.k, layer.cin, layer.cout, layer.dtype,
+                   seed=layer.feat_seed, ref_map=ref)
+
+
+def test_workload_unet_stack(sp):
+    """Four levels x two chained convs; conv 2 takes conv 1's GPU output as
+    stored (bf16), and the oracle takes that same tensor, so parity is per
+    layer."""
+    wl = _workload(3)
+    prev = None
+    for layer in wl.layers:
+        if not layer.chain:
+            ref = oracle.build_map(layer.coords, layer.k)
+            kmap = _gpu_map(sp, layer.coords, layer.k)
+            assert_map_equal(kmap, ref)
+            f = workloads.features(layer.n, layer.cin, layer.dtype, layer.feat_seed)
+        else:
+            f = prev.cpu()
+        w = workloads.weights(layer.k, layer.cin, layer.cout, layer.dtype, layer.weight_seed)
+        out = sp.forward(f.to(DEV), w.to(DEV), kmap)
+        r = ref.forward(f.double().numpy(), w.double().numpy())
+        rms = float(np.sqrt(np.mean(r ** 2)))
+        err = float(np.max(np.abs(out.double().cpu().numpy() - r)))
+        assert err <= TOL[layer.dtype] * rms, f"level {layer.level}: {err:.3e} vs RMS {rms:.3e}"
+        prev = out
+
+
+@pytest.mark.parametrize("li", [0, 1])
+def test_workload_batched_frames_sampled(sp, li):
+    """640k voxels: map invariants at full size, oracle rows sampled (neighbour
+    sets and features computed one row at a time)."""
+    wl = _workload(4)
+    layer = wl.layers[li]
+    c = layer.coords
+    kv = layer.k ** 3
+    kmap = _gpu_map(sp, c, layer.k)
+    a, b = _gpu_lists(kmap)
+    counts = kmap.counts
+    assert counts[kv // 2] == layer.n
+    assert np.array_equal(counts, counts[::-1])  # count(d) = count(-d)
+    # every entry at full size: coords[in] - coords[out] is its offset, same batch
+    ci = c.astype(np.int64)
+    r = (layer.k - 1) // 2
+    for k in range(kv):
+        lo, hi = kmap.offsets[k], kmap.offsets[k + 1]
+        d = ci[a[lo:hi]] - ci[b[lo:hi]]
+        dz, dy, dx = oracle.offset_of(k, layer.k)
+        assert np.all(d == np.array([0, dz, dy, dx]))
+        assert np.all(np.diff(b[lo:hi]) > 0)
+    # sampled rows against the oracle's lookups
+    rng = np.random.default_rng(li)
+    rows = np.sort(rng.choice(layer.n, 2000, replace=False))
+    ref = oracle.build_table(c, layer.k)
+    nbr = ref.neighbours(rows)
+    gnbr = np.full((rows.shape[0], kv), -1, np.int64)
+    pos = {int(q): i for i, q in enumerate(rows)}
+    for k in range(kv):
+        lo, hi = kmap.offsets[k], kmap.offsets[k + 1]
+        sel = np.isin(b[lo:hi], rows)
+        for j, q in zip(a[lo:hi][sel], b[lo:hi][sel]):
+            gnbr[pos[int(q)], k] = j
+    assert np.array_equal(gnbr, nbr)
+    _forward_check(sp, kmap, c, layer.k, layer.cin, layer.cout, layer.dtype, seed=layer.feat_seed,
+                   ref_map=ref, rows=rows)

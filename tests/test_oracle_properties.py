@@ -142,6 +142,10 @@ def test_forward_rows_matches_full_forward():
     full = m.forward(f, w)
     rows = rng.choice(c.shape[0], 40, replace=False)
     assert np.allclose(m.forward_rows(f, w, rows), full[rows], rtol=0, atol=1e-12)
+    t = oracle.build_table(c, 3)
+    assert t.total_entries == 0
+    assert np.allclose(t.forward_rows(f, w, rows), full[rows], rtol=0, atol=1e-12)
+    assert np.array_equal(t.neighbours(rows), m.neighbours(rows))
     nbr = m.neighbours(rows)
     for i, q in enumerate(rows):
         for k in range(27):
