@@ -160,17 +160,30 @@ def _torch():
     return torch
 
 
-def _dtype_code(t) -> int:
-    torch = _torch()
-    m = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-    if t.dtype not in m:
-        raise SpconvError(4, f"dtype {t.dtype} not supported")
-    return m[t.dtype]
+def _stream() -> int:
+    """Handle of torch's current stream on the current device."""
+    return int(_torch().cuda.current_stream().cuda_stream)
 
 
-def _stream(device) -> int:
-    torch = _torch()
-    return int(torch.cuda.current_stream(device).cuda_stream)
+class _OnDevice:
+    """Makes ``device`` current for the call only when it is not already."""
+
+    __slots__ = ("idx", "prev")
+
+    def __init__(self, device):
+        self.idx = device.index if device.index is not None else 0
+        self.prev = None
+
+    def __enter__(self):
+        torch = _torch()
+        cur = torch.cuda.current_device()
+        if cur != self.idx:
+            self.prev = cur
+            torch.cuda.set_device(self.idx)
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            _torch().cuda.set_device(self.prev)
 
 
 class SpconvMap:
@@ -181,7 +194,22 @@ class SpconvMap:
         self.device = device
         self.kernel_size, self.n, self.total_entries = spconv_map_info(handle)
         self.kernel_volume = self.kernel_size ** 3
-        self.counts, self.offsets = spconv_map_counts(handle, self.kernel_volume)
+        self._counts = None
+
+    def _load_counts(self):
+        if self._counts is None:
+            self._counts = spconv_map_counts(self.handle, self.kernel_volume)
+        return self._counts
+
+    @property
+    def counts(self) -> np.ndarray:
+        """Entries per offset, int64 [K^3]."""
+        return self._load_counts()[0]
+
+    @property
+    def offsets(self) -> np.ndarray:
+        """List offsets, int64 [K^3 + 1]."""
+        return self._load_counts()[1]
 
     def lists(self):
         """(in_idx, out_idx) as int32 device tensors: stream-ordered copies of
@@ -191,11 +219,12 @@ class SpconvMap:
         e = self.total_entries
         out = torch.empty((2, e), dtype=torch.int32, device=self.device)
         if e:
-            stream = _stream(self.device)
-            for dst, src in ((out[0].data_ptr(), a), (out[1].data_ptr(), b)):
-                rc = lib().hipMemcpyAsync(dst, src, 4 * e, 3, stream)  # device to device
-                if rc != 0:
-                    raise SpconvError(6, f"hipMemcpyAsync failed with {rc}")
+            with _OnDevice(self.device):
+                stream = _stream()
+                for dst, src in ((out[0].data_ptr(), a), (out[1].data_ptr(), b)):
+                    rc = lib().hipMemcpyAsync(dst, src, 4 * e, 3, stream)  # device to device
+                    if rc != 0:
+                        raise SpconvError(6, f"hipMemcpyAsync failed with {rc}")
         return out[0], out[1]
 
     def free(self):
@@ -217,18 +246,23 @@ def build_map(coords, kernel_size: int) -> SpconvMap:
     if not (isinstance(coords, torch.Tensor) and coords.is_cuda and coords.dtype == torch.int32
             and coords.dim() == 2 and coords.shape[1] == 4 and coords.is_contiguous()):
         raise SpconvError(1, "coords must be a contiguous int32 [N, 4] tensor on a HIP device")
-    with torch.cuda.device(coords.device):
-        h = spconv_build_map(coords.data_ptr(), coords.shape[0], int(kernel_size), _stream(coords.device))
+    with _OnDevice(coords.device):
+        h = spconv_build_map(coords.data_ptr(), coords.shape[0], int(kernel_size), _stream())
     return SpconvMap(h, coords.device)
+
+
+_DT = None
 
 
 def forward(feats, weights, kmap: SpconvMap, out=None):
     """f_out = submanifold convolution of feats [N, C_in] with weights
     [K^3, C_in, C_out] over ``kmap``; returns out [N, C_out] (same dtype)."""
+    global _DT
     torch = _torch()
-    for name, t in (("feats", feats), ("weights", weights)):
-        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
-            raise SpconvError(1, f"{name} must be a contiguous tensor on a HIP device")
+    if _DT is None:
+        _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if not (feats.is_cuda and weights.is_cuda and feats.is_contiguous() and weights.is_contiguous()):
+        raise SpconvError(1, "feats and weights must be contiguous tensors on a HIP device")
     if feats.dim() != 2 or weights.dim() != 3:
         raise SpconvError(1, "feats must be [N, C_in] and weights [K^3, C_in, C_out]")
     n, cin = feats.shape
@@ -236,13 +270,17 @@ def forward(feats, weights, kmap: SpconvMap, out=None):
     if n != kmap.n or kv != kmap.kernel_volume or wcin != cin:
         raise SpconvError(1, f"shape mismatch: feats {tuple(feats.shape)}, weights "
                              f"{tuple(weights.shape)}, map N={kmap.n} K^3={kmap.kernel_volume}")
-    if weights.dtype != feats.dtype:
+    dt = feats.dtype
+    if weights.dtype != dt:
         raise SpconvError(1, "feats and weights must share one dtype")
+    code = _DT.get(dt)
+    if code is None:
+        raise SpconvError(4, f"dtype {dt} not supported")
     if out is None:
-        out = torch.empty((n, cout), dtype=feats.dtype, device=feats.device)
-    elif not (out.is_cuda and out.is_contiguous() and out.dtype == feats.dtype and out.shape == (n, cout)):
+        out = torch.empty((n, cout), dtype=dt, device=feats.device)
+    elif not (out.is_cuda and out.is_contiguous() and out.dtype == dt and tuple(out.shape) == (n, cout)):
         raise SpconvError(1, "out must be a contiguous [N, C_out] tensor of the feature dtype")
-    with torch.cuda.device(feats.device):
-        spconv_forward(feats.data_ptr(), weights.data_ptr(), kmap.handle, cin, cout,
-                       _dtype_code(feats), out.data_ptr(), _stream(feats.device))
+    with _OnDevice(feats.device):
+        spconv_forward(feats.data_ptr(), weights.data_ptr(), kmap.handle, cin, cout, code,
+                       out.data_ptr(), _stream())
     return out

@@ -24,10 +24,8 @@ struct spconv_map {
   int64_t tiles = 0;
   std::vector<int64_t> counts;   // KV
   std::vector<int64_t> offsets;  // KV + 1
-  void* block = nullptr;         // one pool allocation: in_idx | out_idx | tile_off
-  int32_t* in_idx = nullptr;
-  int32_t* out_idx = nullptr;
-  int32_t* tile_off = nullptr;
+  void* block = nullptr;         // one pool allocation holding the MapBuffers
+  spconv::MapBuffers buf;
 };
 
 namespace {
@@ -100,6 +98,16 @@ spconv_status host_staging(size_t bytes, long long** out) {
   return SPCONV_OK;
 }
 
+// One reusable timing-free event per thread for the build's completion.
+spconv_status build_event(hipEvent_t* out) {
+  thread_local hipEvent_t ev = nullptr;
+  if (ev == nullptr) {
+    SPCONV_HIP(hipEventCreateWithFlags(&ev, hipEventDisableTiming), "hipEventCreateWithFlags");
+  }
+  *out = ev;
+  return SPCONV_OK;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int64_t next_pow2(int64_t v) {
@@ -152,7 +160,6 @@ spconv_status spconv_build_map(const int32_t* d_coords, int64_t n, int32_t kerne
   p.K = kernel_size;
   p.KV = KV;
   p.centre = (KV - 1) / 2;
-  p.half = (KV - 1) / 2;
   p.mask_words = (KV + 31) / 32;
   p.tiles = (n + spconv::kTileRows - 1) / spconv::kTileRows;
   p.chunks = (p.tiles + spconv::kChunkTiles - 1) / spconv::kChunkTiles;
@@ -168,70 +175,77 @@ spconv_status spconv_build_map(const int32_t* d_coords, int64_t n, int32_t kerne
   st = host_staging(sizeof(long long) * (spconv::kSummaryHead + KV), &staging);
   if (st != SPCONV_OK) return st;
 
+  spconv_map* m = new (std::nothrow) spconv_map;
+  if (m == nullptr) return fail(SPCONV_ERR_OUT_OF_MEMORY, "host allocation");
   void* ws = nullptr;
-  SPCONV_HIP(hipMallocFromPoolAsync(&ws, spconv::build_scratch_bytes(p), pool, stream),
-             "workspace allocation");
+  hipError_t e = hipMallocFromPoolAsync(&ws, spconv::build_scratch_bytes(p), pool, stream);
+  if (e != hipSuccess) {
+    delete m;
+    return hip_fail(e, "workspace allocation");
+  }
+  e = hipMallocFromPoolAsync(&m->block, spconv::map_buffer_bytes(p), pool, stream);
+  if (e != hipSuccess) {
+    (void)hipFreeAsync(ws, stream);
+    delete m;
+    return hip_fail(e, "map allocation");
+  }
   spconv::BuildScratch s;
   spconv::carve_build_scratch(p, ws, &s);
+  spconv::carve_map_buffers(p, m->block, &m->buf);
+  auto discard = [&](spconv_status st) {
+    (void)hipFreeAsync(ws, stream);
+    (void)hipFreeAsync(m->block, stream);
+    delete m;
+    return st;
+  };
 
-  auto release_ws = [&]() { (void)hipFreeAsync(ws, stream); };
-  hipError_t e = spconv::launch_build_front(p, d_coords, s, stream);
-  if (e != hipSuccess) { release_ws(); return hip_fail(e, "map build launch"); }
+  e = spconv::launch_build(p, d_coords, s, m->buf, stream);
+  if (e != hipSuccess) return discard(hip_fail(e, "map build launch"));
   e = hipMemcpyAsync(staging, s.summary, sizeof(long long) * (spconv::kSummaryHead + KV),
                      hipMemcpyDeviceToHost, stream);
-  if (e != hipSuccess) { release_ws(); return hip_fail(e, "summary read-back"); }
-  e = hipStreamSynchronize(stream);
-  if (e != hipSuccess) { release_ws(); return hip_fail(e, "map build"); }
+  if (e != hipSuccess) return discard(hip_fail(e, "summary read-back"));
+  hipEvent_t done = nullptr;
+  st = build_event(&done);
+  if (st != SPCONV_OK) return discard(st);
+  e = hipEventRecord(done, stream);
+  if (e != hipSuccess) return discard(hip_fail(e, "hipEventRecord"));
+  (void)hipFreeAsync(ws, stream);
+  ws = nullptr;
+  // The one wait of a build.  Spinning on the event keeps the wake-up latency
+  // of a blocking wait off the critical path.
+  while ((e = hipEventQuery(done)) == hipErrorNotReady) {
+  }
+  if (e != hipSuccess) {
+    (void)hipFreeAsync(m->block, stream);
+    delete m;
+    return hip_fail(e, "map build");
+  }
 
   const unsigned long long flags = static_cast<unsigned long long>(staging[0]);
+  spconv_status err = SPCONV_OK;
   if (flags & spconv::kFlagRange) {
-    release_ws();
-    return fail(SPCONV_ERR_COORD_RANGE,
-                "a coordinate is outside b in [0, 2^15), z, y, x in [0, 2^16)");
+    err = fail(SPCONV_ERR_COORD_RANGE, "a coordinate is outside b in [0, 2^15), z, y, x in [0, 2^16)");
+  } else if (flags & spconv::kFlagDuplicate) {
+    err = fail(SPCONV_ERR_DUPLICATE_COORD, "two rows share one (b, z, y, x) coordinate");
+  } else if (flags & spconv::kFlagTableFull) {
+    err = fail(SPCONV_ERR_DEVICE, "internal: hash table probe exceeded its bound");
   }
-  if (flags & spconv::kFlagDuplicate) {
-    release_ws();
-    return fail(SPCONV_ERR_DUPLICATE_COORD, "two rows share one (b, z, y, x) coordinate");
+  if (err != SPCONV_OK) {
+    (void)hipFreeAsync(m->block, stream);
+    delete m;
+    return err;
   }
-  if (flags & spconv::kFlagTableFull) {
-    release_ws();
-    return fail(SPCONV_ERR_DEVICE, "internal: hash table probe exceeded its bound");
-  }
-  const int64_t total = staging[1];
-
-  spconv_map* m = new (std::nothrow) spconv_map;
-  if (m == nullptr) { release_ws(); return fail(SPCONV_ERR_OUT_OF_MEMORY, "host allocation"); }
   m->device = device;
   m->stream = stream;
   m->K = kernel_size;
   m->KV = KV;
   m->n = n;
-  m->total = total;
+  m->total = staging[1];
   m->tiles = p.tiles;
   m->counts.assign(staging + spconv::kSummaryHead, staging + spconv::kSummaryHead + KV);
   m->offsets.resize(KV + 1);
   m->offsets[0] = 0;
   for (int k = 0; k < KV; ++k) m->offsets[k + 1] = m->offsets[k] + m->counts[k];
-
-  const size_t list_bytes = (static_cast<size_t>(total) * sizeof(int32_t) + 255) / 256 * 256;
-  const size_t tile_bytes = static_cast<size_t>(KV * p.tiles + 1) * sizeof(int32_t);
-  e = hipMallocFromPoolAsync(&m->block, 2 * list_bytes + tile_bytes, pool, stream);
-  if (e != hipSuccess) {
-    delete m;
-    release_ws();
-    return hip_fail(e, "map allocation");
-  }
-  char* b = static_cast<char*>(m->block);
-  m->in_idx = reinterpret_cast<int32_t*>(b);
-  m->out_idx = reinterpret_cast<int32_t*>(b + list_bytes);
-  m->tile_off = reinterpret_cast<int32_t*>(b + 2 * list_bytes);
-  e = spconv::launch_build_compact(p, s, total, m->in_idx, m->out_idx, m->tile_off, stream);
-  release_ws();
-  if (e != hipSuccess) {
-    (void)hipFreeAsync(m->block, stream);
-    delete m;
-    return hip_fail(e, "map compaction launch");
-  }
   *out_map = m;
   return SPCONV_OK;
 }
@@ -255,8 +269,8 @@ spconv_status spconv_map_counts(const spconv_map* map, int64_t* h_counts, int64_
 spconv_status spconv_map_lists(const spconv_map* map, const int32_t** d_in_idx,
                                const int32_t** d_out_idx) {
   if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
-  if (d_in_idx) *d_in_idx = map->in_idx;
-  if (d_out_idx) *d_out_idx = map->out_idx;
+  if (d_in_idx) *d_in_idx = map->buf.in_idx;
+  if (d_out_idx) *d_out_idx = map->buf.out_idx;
   return SPCONV_OK;
 }
 
@@ -287,9 +301,10 @@ spconv_status spconv_forward(const void* d_feats, const void* d_weights, const s
   a.feats = d_feats;
   a.weights = d_weights;
   a.out = d_out;
-  a.in_idx = map->in_idx;
-  a.out_idx = map->out_idx;
-  a.tile_off = map->tile_off;
+  a.in_idx = map->buf.in_idx;
+  a.out_idx = map->buf.out_idx;
+  a.tile_off = map->buf.tile_off;
+  a.tile_mask = map->buf.tile_mask;
   a.n = map->n;
   a.tiles = map->tiles;
   a.KV = map->KV;

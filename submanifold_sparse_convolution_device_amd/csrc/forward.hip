@@ -239,6 +239,309 @@ __global__ __launch_bounds__(kThreads) void k_forward(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small-channel kernel: every W_d fits in LDS at once.
+//
+// A workgroup of 16 waves stages all K^3 weight matrices into LDS once,
+// already in MFMA operand order (per offset, co-block and ci-chunk, 64 lanes x
+// 16 bytes), so a lane's A operand is one conflict-free 16-byte read.  Each
+// wave then owns one 64-row output tile at a time, independently of the other
+// waves:
+//   1. lanes k < K^3 read the tile's row mask and list start for offset k
+//      (written by the map build); the tile's own rows are loaded straight
+//      into B-operand registers and the centre offset runs on them as a dense
+//      GEMM;
+//   2. the tile's non-centre entries are numbered in offset order (a wave
+//      prefix sum of the mask popcounts) and gathered in one burst: each lane
+//      fetches whole input rows by index into the wave's LDS stage;
+//   3. per offset present in the tile, per 16-row block that uses it, one
+//      MFMA per (co-block, ci-chunk) with B read from the stage (zero for
+//      rows without that neighbour);
+//   4. the accumulators are rounded to the output dtype and each output row is
+//      written once.
+// A tile with more entries than the stage holds is processed in slot ranges;
+// an entry belongs to exactly one range.
+// ---------------------------------------------------------------------------
+constexpr int kSmallWaves = 16;
+constexpr int kStageEntries = 92;  // plus one zero row per wave
+constexpr size_t kSmallLdsCap = 160 * 1024;  // one workgroup per CU
+
+template <typename T, int CIN, int COUT>
+struct SmallShape {
+  static constexpr int CHUNK = Elem<T>::kChunk;
+  static constexpr int VEC = Elem<T>::kVec;
+  static constexpr int NCH = CIN / CHUNK;
+  static constexpr int NCB = COUT / 16;
+  static constexpr int ROWV = CIN * static_cast<int>(sizeof(T)) / 16;  // 16-byte vectors per row
+  static_assert(CIN % CHUNK == 0 && COUT % 16 == 0, "shape");
+  static size_t wbytes(int KV) { return static_cast<size_t>(KV) * NCB * NCH * 64 * 16; }
+  static size_t lds_bytes(int KV) {
+    return wbytes(KV) + static_cast<size_t>(kSmallWaves) * (kStageEntries + 1) * ROWV * 16;
+  }
+};
+
+template <typename T, int NCB>
+__device__ __forceinline__ void mfma_block(floatx4 (&acc)[NCB], const uint4 (&a)[NCB], uint4 b) {
+  if constexpr (sizeof(T) == 4) {
+    const floatx4 bv = __builtin_bit_cast(floatx4, b);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const floatx4 av = __builtin_bit_cast(floatx4, a[cb]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc[cb], 0, 0, 0);
+    }
+  } else if constexpr (__is_same(T, _Float16)) {
+    const half8 bv = __builtin_bit_cast(half8, b);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a[cb]), bv, acc[cb], 0, 0, 0);
+    }
+  } else {
+    const bf16x8 bv = __builtin_bit_cast(bf16x8, b);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[cb]), bv, acc[cb], 0, 0, 0);
+    }
+  }
+}
+
+// Orders this wave's LDS writes before its later LDS reads by other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int lane_i32(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+__device__ __forceinline__ unsigned long long lane_u64(unsigned long long v, int src) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), src));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), src));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+// Stages every W_d into operand order: element i of lane (g, r) of block
+// (k, cb, ch) is W[k][ch * CHUNK + g * VEC + i][cb * 16 + r].  Each thread
+// reads a VEC x VEC block (VEC rows of ci, VEC columns of co, 16 bytes per
+// row), transposes it in registers, and writes VEC 16-byte operand vectors.
+template <typename T, int CIN, int COUT>
+__device__ __forceinline__ void stage_weights(const T* __restrict__ weights, uint4* wl, int KV) {
+  using Sh = SmallShape<T, CIN, COUT>;
+  constexpr int CHUNK = Sh::CHUNK, VEC = Sh::VEC, NCH = Sh::NCH, NCB = Sh::NCB;
+  constexpr int RB = CIN / VEC, CBK = COUT / VEC;  // blocks along ci and co
+  const int nblk = KV * RB * CBK;
+  for (int b = threadIdx.x; b < nblk; b += blockDim.x) {
+    const int k = b / (RB * CBK);
+    const int rem = b - k * RB * CBK;
+    const int ci0 = (rem / CBK) * VEC, co0 = (rem % CBK) * VEC;
+    T blk[VEC][VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(weights + (static_cast<int64_t>(k) * CIN + ci0 + i) * COUT + co0);
+      __builtin_memcpy(blk[i], &raw, sizeof(raw));
+    }
+    const int ch = ci0 / CHUNK, g = (ci0 % CHUNK) / VEC;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      T col[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) col[i] = blk[i][j];
+      const int co = co0 + j;
+      const size_t slot = ((static_cast<size_t>(k) * NCB + (co >> 4)) * NCH + ch) * 64 + g * 16 + (co & 15);
+      uint4 v;
+      __builtin_memcpy(&v, col, sizeof(v));
+      wl[slot] = v;
+    }
+  }
+}
+
+template <typename T, int CIN, int COUT>
+__global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
+    const T* __restrict__ feats, const T* __restrict__ weights, T* __restrict__ out,
+    const int32_t* __restrict__ in_idx, const int32_t* __restrict__ tile_off,
+    const unsigned long long* __restrict__ tile_mask, int64_t n, int64_t tiles, int KV) {
+  using Sh = SmallShape<T, CIN, COUT>;
+  constexpr int CHUNK = Sh::CHUNK, VEC = Sh::VEC, NCH = Sh::NCH, NCB = Sh::NCB, ROWV = Sh::ROWV;
+  extern __shared__ uint4 smem4[];
+  uint4* wl = smem4;  // [KV][NCB][NCH][64] A operands
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, g = lane >> 4;
+  uint4* stage = wl + static_cast<size_t>(KV) * NCB * NCH * 64 +
+                 static_cast<size_t>(wave) * (kStageEntries + 1) * ROWV;
+  const int centre = (KV - 1) / 2;
+  if (lane < ROWV) stage[kStageEntries * ROWV + lane] = make_uint4(0u, 0u, 0u, 0u);  // zero row
+
+  stage_weights<T, CIN, COUT>(weights, wl, KV);
+  __syncthreads();
+
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kSmallWaves;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * kSmallWaves + wave; t < tiles; t += nwaves) {
+    const int64_t q0 = t * kTileRows;
+    // 1. per-offset mask and list start (lane k holds offset k), own rows
+    unsigned long long mk = 0ull;
+    int lok = 0;
+    if (lane < KV) {
+      mk = tile_mask[static_cast<int64_t>(lane) * tiles + t];
+      lok = tile_off[static_cast<int64_t>(lane) * tiles + t];
+    }
+    floatx4 acc[4][NCB];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[qb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    {
+      uint4 bc[4][NCH];
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) {
+        const int64_t q = q0 + qb * 16 + r;
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) {
+          bc[qb][ch] = (q < n) ? *reinterpret_cast<const uint4*>(feats + q * CIN + ch * CHUNK + g * VEC)
+                               : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        uint4 a[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) a[cb] = wl[((static_cast<size_t>(centre) * NCB + cb) * NCH + ch) * 64 + lane];
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) mfma_block<T, NCB>(acc[qb], a, bc[qb][ch]);
+      }
+    }
+    // 2. entry numbering: exclusive prefix of the non-centre counts over offsets
+    const int cnt = (lane < KV && lane != centre) ? __popcll(mk) : 0;
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int up = __shfl_up(incl, d);
+      if (lane >= d) incl += up;
+    }
+    const int basek = incl - cnt;  // lane k: first slot of offset k
+    const int total = lane_i32(incl, 63);
+    const uint32_t below16 = (1u << r) - 1u;  // rows of this lane's 16-row block before it
+
+    for (int s0 = 0; s0 < total; s0 += kStageEntries) {
+      const int s1 = (total - s0 < kStageEntries) ? total : s0 + kStageEntries;
+      // gather slots [s0, s1): slot s belongs to the last offset k with
+      // base_k <= s (binary search over the lanes holding base_k)
+#pragma unroll
+      for (int round = 0; round < (kStageEntries + 63) / 64; ++round) {
+        const int s = s0 + lane + 64 * round;
+        // Binary lifting with every lane active at every shuffle (a shuffle
+        // from a lane outside the active mask does not return its register).
+        int lo = 0;
+#pragma unroll
+        for (int step = 32; step > 0; step >>= 1) {
+          const int cand = lo + step;
+          const int b = __shfl(basek, cand < KV ? cand : KV - 1);
+          if (cand < KV && b <= s) lo = cand;
+        }
+        const int bk = __shfl(basek, lo);
+        const int lk = __shfl(lok, lo);
+        if (s < s1) {
+          const int32_t src = in_idx[static_cast<int64_t>(lk) + (s - bk)];
+          const uint4* rowp = reinterpret_cast<const uint4*>(feats + static_cast<int64_t>(src) * CIN);
+#pragma unroll
+          for (int v = 0; v < ROWV; ++v) stage[(s - s0) * ROWV + v] = rowp[v];
+        }
+      }
+      wave_lds_sync();
+      // 3. MFMA over the offsets with entries in [s0, s1)
+      for (int k = 0; k < KV; ++k) {
+        if (k == centre) continue;
+        const int bk = lane_i32(basek, k);
+        const unsigned long long m = lane_u64(mk, k);
+        if (m == 0ull || bk >= s1 || bk + __popcll(m) <= s0) continue;
+        uint4 a[NCH][NCB];
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            a[ch][cb] = wl[((static_cast<size_t>(k) * NCB + cb) * NCH + ch) * 64 + lane];
+        uint4 b[4][NCH];
+        int before = bk;  // slot of the first row of block qb
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+          const uint32_t sub = static_cast<uint32_t>(m >> (qb * 16)) & 0xffffu;
+          const int slot = before + __popc(sub & below16);
+          const bool has = ((sub >> r) & 1u) && slot >= s0 && slot < s1;
+          const int ls = has ? slot - s0 : kStageEntries;  // row kStageEntries of the stage is zero
+#pragma unroll
+          for (int ch = 0; ch < NCH; ++ch) b[qb][ch] = stage[ls * ROWV + ch * 4 + g];
+          before += __popc(sub);
+        }
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+          if (((m >> (qb * 16)) & 0xffffull) == 0ull) continue;
+#pragma unroll
+          for (int ch = 0; ch < NCH; ++ch) mfma_block<T, NCB>(acc[qb], a[ch], b[qb][ch]);
+        }
+      }
+      wave_lds_sync();
+    }
+    // 4. epilogue
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const int64_t q = q0 + qb * 16 + r;
+      if (q < n) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) Elem<T>::store4(out + q * COUT + cb * 16 + 4 * g, acc[qb][cb]);
+      }
+    }
+  }
+}
+
+int device_cu_count() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) {
+      cus = v;
+    } else {
+      cus = 256;
+    }
+  }
+  return cus;
+}
+
+template <typename T, int CIN, int COUT>
+hipError_t launch_small(const ForwardArgs& a, hipStream_t stream) {
+  using Sh = SmallShape<T, CIN, COUT>;
+  const size_t lds = Sh::lds_bytes(a.KV);
+  const int64_t want = (a.tiles + kSmallWaves - 1) / kSmallWaves;
+  const int64_t cap = device_cu_count();
+  const unsigned grid = static_cast<unsigned>(want < cap ? want : cap);
+  static bool lds_raised = false;  // raise the dynamic-LDS limit once per instantiation
+  if (!lds_raised) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_forward_small<T, CIN, COUT>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(kSmallLdsCap));
+    if (e != hipSuccess) return e;
+    lds_raised = true;
+  }
+  hipLaunchKernelGGL((k_forward_small<T, CIN, COUT>), dim3(grid), dim3(kSmallWaves * 64), lds, stream,
+                     static_cast<const T*>(a.feats), static_cast<const T*>(a.weights),
+                     static_cast<T*>(a.out), a.in_idx, a.tile_off, a.tile_mask, a.n, a.tiles, a.KV);
+  return hipGetLastError();
+}
+
+// Small kernel shapes; returns hipErrorNotSupported when the shape has none.
+template <typename T>
+hipError_t try_small(const ForwardArgs& a, hipStream_t stream) {
+  if (a.KV > 64) return hipErrorNotSupported;
+  constexpr size_t kBudget = kSmallLdsCap;
+  if constexpr (sizeof(T) == 2) {
+    if (a.cin == 32 && a.cout == 32 && SmallShape<T, 32, 32>::lds_bytes(a.KV) <= kBudget) return launch_small<T, 32, 32>(a, stream);
+    if (a.cin == 32 && a.cout == 16 && SmallShape<T, 32, 16>::lds_bytes(a.KV) <= kBudget) return launch_small<T, 32, 16>(a, stream);
+  } else {
+    if (a.cin == 16 && a.cout == 16 && SmallShape<T, 16, 16>::lds_bytes(a.KV) <= kBudget) return launch_small<T, 16, 16>(a, stream);
+    if (a.cin == 16 && a.cout == 32 && SmallShape<T, 16, 32>::lds_bytes(a.KV) <= kBudget) return launch_small<T, 16, 32>(a, stream);
+  }
+  return hipErrorNotSupported;
+}
+
 template <typename T, int CB>
 hipError_t launch_typed(const ForwardArgs& a, hipStream_t stream) {
   const size_t lds = static_cast<size_t>(kOffsetsPerStage) * (kTileRows + 2) * sizeof(int32_t) +
@@ -264,11 +567,18 @@ hipError_t launch_dispatch_cb(const ForwardArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+template <typename T>
+hipError_t dispatch(const ForwardArgs& a, hipStream_t stream) {
+  const hipError_t e = try_small<T>(a, stream);
+  if (e != hipErrorNotSupported) return e;
+  return launch_dispatch_cb<T>(a, stream);
+}
+
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream) {
   switch (a.dtype) {
-    case 0: return launch_dispatch_cb<float>(a, stream);
-    case 1: return launch_dispatch_cb<_Float16>(a, stream);
-    case 2: return launch_dispatch_cb<__bf16>(a, stream);
+    case 0: return dispatch<float>(a, stream);
+    case 1: return dispatch<_Float16>(a, stream);
+    case 2: return dispatch<__bf16>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -12,12 +12,13 @@ namespace spconv {
 // (one ballot per tile and offset), and the forward's workgroup owns whole
 // tiles, so per-tile list ranges are all the forward needs from the map.
 constexpr int kTileRows = 64;
-// Tiles per chunk of the count / compaction grid (4 waves x 16 tiles).
-constexpr int kChunkTiles = 64;
+// Tiles per chunk of the count / compaction grid (one count workgroup of 16
+// waves, one tile each).
+constexpr int kChunkTiles = 16;
 constexpr int kChunkRows = kTileRows * kChunkTiles;
 
-// Hash table: open addressing over 16-byte slots {key, row}, probed in
-// aligned windows of 4 slots (64 bytes) by a group of 4 lanes.
+// Coordinate table: open addressing over 64-bit keys, probed in aligned
+// windows of 4 keys (32 bytes); a key's row sits in a parallel array.
 constexpr int kWindowSlots = 4;
 constexpr uint64_t kEmptyKey = ~0ull;
 
@@ -26,19 +27,13 @@ constexpr unsigned long long kFlagDuplicate = 1ull;
 constexpr unsigned long long kFlagRange = 2ull;
 constexpr unsigned long long kFlagTableFull = 4ull;
 
-struct Slot {
-  unsigned long long key;
-  int32_t row;
-  int32_t pad;
-};
-
 // Layout of the small device summary the host reads once per build:
 //   [0] error flags, [1] total entries E, [2 + k] entries of offset k.
 constexpr int kSummaryHead = 2;
 
 struct BuildPlan {
   int64_t n = 0;
-  int32_t K = 0, KV = 0, centre = 0, half = 0, mask_words = 0;
+  int32_t K = 0, KV = 0, centre = 0, mask_words = 0;
   int64_t tiles = 0;        // ceil(n / kTileRows)
   int64_t chunks = 0;       // ceil(tiles / kChunkTiles)
   int64_t table_slots = 0;  // power of two >= 2n, >= 64
@@ -46,7 +41,8 @@ struct BuildPlan {
 
 // Workspace of one build (carved from a single allocation).
 struct BuildScratch {
-  Slot* table = nullptr;            // table_slots
+  unsigned long long* keys = nullptr;  // table_slots
+  int32_t* rows = nullptr;             // table_slots
   uint32_t* masks = nullptr;        // mask_words x n, word-major
   int32_t* nbr = nullptr;           // KV x n, offset-major; only entries whose mask bit is set are valid
   int64_t* chunk_sum = nullptr;     // KV x chunks, then its exclusive scan in place
@@ -56,12 +52,20 @@ struct BuildScratch {
 size_t build_scratch_bytes(const BuildPlan& p);
 void carve_build_scratch(const BuildPlan& p, void* base, BuildScratch* s);
 
-// Map-build launches (all asynchronous on `stream`).
-hipError_t launch_build_front(const BuildPlan& p, const int32_t* coords, const BuildScratch& s,
-                              hipStream_t stream);
-hipError_t launch_build_compact(const BuildPlan& p, const BuildScratch& s, int64_t total,
-                                int32_t* in_idx, int32_t* out_idx, int32_t* tile_off,
-                                hipStream_t stream);
+// Device buffers owned by a map (one allocation).
+struct MapBuffers {
+  int32_t* in_idx = nullptr;                // capacity KV * n
+  int32_t* out_idx = nullptr;               // capacity KV * n
+  int32_t* tile_off = nullptr;              // KV * tiles + 1
+  unsigned long long* tile_mask = nullptr;  // KV * tiles
+};
+size_t map_buffer_bytes(const BuildPlan& p);
+void carve_map_buffers(const BuildPlan& p, void* base, MapBuffers* m);
+
+// The whole map build (all asynchronous on `stream`); the summary in the
+// scratch holds the flags, E and the per-offset counts when it completes.
+hipError_t launch_build(const BuildPlan& p, const int32_t* coords, const BuildScratch& s,
+                        const MapBuffers& m, hipStream_t stream);
 
 // Forward launch.  dtype: 0 f32, 1 f16, 2 bf16.
 struct ForwardArgs {
@@ -70,7 +74,8 @@ struct ForwardArgs {
   void* out;
   const int32_t* in_idx;
   const int32_t* out_idx;
-  const int32_t* tile_off;  // KV * tiles + 1
+  const int32_t* tile_off;                  // KV * tiles + 1
+  const unsigned long long* tile_mask;      // KV * tiles
   int64_t n;
   int64_t tiles;
   int32_t KV;

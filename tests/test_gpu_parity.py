@@ -159,8 +159,9 @@ def test_map_deterministic(sp):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("K,cin,cout", [(3, 16, 16), (3, 32, 48), (3, 8, 24), (5, 40, 16), (1, 64, 32),
-                                        (3, 96, 136), (7, 16, 8)])
+@pytest.mark.parametrize("K,cin,cout", [(3, 16, 16), (3, 32, 32), (3, 32, 16), (3, 16, 32), (1, 32, 32),
+                                        (3, 32, 48), (3, 8, 24), (5, 40, 16), (1, 64, 32),
+                                        (3, 96, 136), (7, 16, 8), (5, 32, 32)])
 def test_forward_random_grids(sp, dtype, K, cin, cout):
     if dtype == "f32" and (cin > 512 or cout > 512):
         pytest.skip("fp32 channels are limited to 512")
@@ -169,22 +170,35 @@ def test_forward_random_grids(sp, dtype, K, cin, cout):
     _forward_check(sp, kmap, c, K, cin, cout, dtype, seed=cin * 7 + cout)
 
 
+@pytest.mark.parametrize("dtype,ch", [("f16", 32), ("bf16", 32), ("f32", 16)])
+@pytest.mark.parametrize("extent", [12, 20])
+def test_forward_dense_block(sp, dtype, ch, extent):
+    """Fully active cube: up to 26 neighbours per row, so a 64-row tile holds
+    far more gathered rows than one stage batch."""
+    ax = np.arange(extent)
+    z, y, x = np.meshgrid(ax, ax, ax, indexing="ij")
+    c = np.stack([np.zeros(extent ** 3), z.ravel(), y.ravel(), x.ravel()], 1).astype(np.int32)
+    kmap = _gpu_map(sp, c, 3)
+    _forward_check(sp, kmap, c, 3, ch, ch, dtype, seed=extent)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
 def test_forward_routing_is_exact(sp, dtype):
     """Identity weights route rows exactly in any dtype (one product by 1.0)."""
     c = workloads.permuted(workloads.random_grid(5, 12, 0.3, 1), 5)
-    n, ch = c.shape[0], 32
+    n = c.shape[0]
     kmap = _gpu_map(sp, c, 3)
     ref = oracle.build_map(c, 3)
-    f = workloads.features(n, ch, dtype, 11)
-    for k in (13, 0, 17, 26):
-        w = torch.zeros((27, ch, ch), dtype=TORCH_DT[dtype])
-        w[k] = torch.eye(ch, dtype=TORCH_DT[dtype])
-        out = sp.forward(f.to(DEV), w.to(DEV), kmap).cpu()
-        exp = torch.zeros_like(f)
-        j, q = ref.lists[k]
-        exp[torch.from_numpy(q).long()] = f[torch.from_numpy(j).long()]
-        assert torch.equal(out, exp), f"offset {k}"
+    for ch in ((16, 48) if dtype == "f32" else (32, 48)):
+        f = workloads.features(n, ch, dtype, 11)
+        for k in (13, 0, 17, 26):
+            w = torch.zeros((27, ch, ch), dtype=TORCH_DT[dtype])
+            w[k] = torch.eye(ch, dtype=TORCH_DT[dtype])
+            out = sp.forward(f.to(DEV), w.to(DEV), kmap).cpu()
+            exp = torch.zeros_like(f)
+            j, q = ref.lists[k]
+            exp[torch.from_numpy(q).long()] = f[torch.from_numpy(j).long()]
+            assert torch.equal(out, exp), f"offset {k}, {ch} channels"
 
 
 def test_forward_all_ones_degree(sp):
