@@ -311,7 +311,21 @@ spconv_status spconv_forward(const void* d_feats, const void* d_weights, const s
   a.cin = c_in;
   a.cout = c_out;
   a.dtype = static_cast<int32_t>(dtype);
-  const hipError_t e = spconv::launch_forward(a, static_cast<hipStream_t>(hip_stream));
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (!spconv::small_supported(a) && spconv::tiled_supported(a)) {
+    hipMemPool_t pool = nullptr;
+    const spconv_status st = pool_for(map->device, &pool);
+    if (st != SPCONV_OK) return st;
+    void* ws = nullptr;
+    hipError_t e = hipMallocFromPoolAsync(&ws, spconv::tiled_workspace_bytes(a), pool, stream);
+    if (e != hipSuccess) return hip_fail(e, "forward workspace allocation");
+    e = spconv::launch_forward_tiled(a, ws, stream);
+    const hipError_t ef = hipFreeAsync(ws, stream);
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+    if (ef != hipSuccess) return hip_fail(ef, "forward workspace release");
+    return SPCONV_OK;
+  }
+  const hipError_t e = spconv::launch_forward(a, stream);
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return SPCONV_OK;
 }

@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void k_forward(
 // ---------------------------------------------------------------------------
 // Small-channel kernel: every W_d fits in LDS at once.
 //
-// A workgroup of 16 waves stages all K^3 weight matrices into LDS once,
+// A workgroup of 12 waves stages all K^3 weight matrices into LDS once,
 // already in MFMA operand order (per offset, co-block and ci-chunk, 64 lanes x
 // 16 bytes), so a lane's A operand is one conflict-free 16-byte read.  Each
 // wave then owns one 64-row output tile at a time, independently of the other
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void k_forward(
 // A tile with more entries than the stage holds is processed in slot ranges;
 // an entry belongs to exactly one range.
 // ---------------------------------------------------------------------------
-constexpr int kSmallWaves = 16;
+constexpr int kSmallWaves = 12;
 constexpr int kStageEntries = 92;  // plus one zero row per wave
 constexpr size_t kSmallLdsCap = 160 * 1024;  // one workgroup per CU
 
@@ -276,7 +276,8 @@ struct SmallShape {
   static_assert(CIN % CHUNK == 0 && COUT % 16 == 0, "shape");
   static size_t wbytes(int KV) { return static_cast<size_t>(KV) * NCB * NCH * 64 * 16; }
   static size_t lds_bytes(int KV) {
-    return wbytes(KV) + static_cast<size_t>(kSmallWaves) * (kStageEntries + 1) * ROWV * 16;
+    // per wave: ROWV x (kStageEntries + 1) chunks plus kStageEntries slot positions
+    return wbytes(KV) + static_cast<size_t>(kSmallWaves) * (ROWV * (kStageEntries + 1) * 16 + kStageEntries * 4);
   }
 };
 
@@ -321,36 +322,186 @@ __device__ __forceinline__ unsigned long long lane_u64(unsigned long long v, int
 
 // Stages every W_d into operand order: element i of lane (g, r) of block
 // (k, cb, ch) is W[k][ch * CHUNK + g * VEC + i][cb * 16 + r].  Each thread
-// reads a VEC x VEC block (VEC rows of ci, VEC columns of co, 16 bytes per
-// row), transposes it in registers, and writes VEC 16-byte operand vectors.
+// reads VEC x VEC blocks (VEC rows of ci, VEC columns of co, 16 bytes per
+// row), transposes them in registers, and writes VEC 16-byte operand vectors.
+// The first block of a thread is split into a load (weight_block_load) and a
+// store (weight_block_store) so that the caller can overlap its latency.
 template <typename T, int CIN, int COUT>
-__device__ __forceinline__ void stage_weights(const T* __restrict__ weights, uint4* wl, int KV) {
+struct WeightBlock {
+  static constexpr int VEC = Elem<T>::kVec;
+  uint4 rows[VEC];
+  int b;
+};
+
+template <typename T, int CIN, int COUT>
+__device__ __forceinline__ void weight_block_load(WeightBlock<T, CIN, COUT>& wb, const T* __restrict__ weights,
+                                                  int b, int nblk) {
+  constexpr int VEC = Elem<T>::kVec, RB = CIN / VEC, CBK = COUT / VEC;
+  wb.b = b;
+  if (b >= nblk) return;
+  const int k = b / (RB * CBK);
+  const int rem = b - k * RB * CBK;
+  const int ci0 = (rem / CBK) * VEC, co0 = (rem % CBK) * VEC;
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    wb.rows[i] = *reinterpret_cast<const uint4*>(weights + (static_cast<int64_t>(k) * CIN + ci0 + i) * COUT + co0);
+  }
+}
+
+template <typename T, int CIN, int COUT>
+__device__ __forceinline__ void weight_block_store(const WeightBlock<T, CIN, COUT>& wb, uint4* wl, int nblk) {
   using Sh = SmallShape<T, CIN, COUT>;
   constexpr int CHUNK = Sh::CHUNK, VEC = Sh::VEC, NCH = Sh::NCH, NCB = Sh::NCB;
-  constexpr int RB = CIN / VEC, CBK = COUT / VEC;  // blocks along ci and co
-  const int nblk = KV * RB * CBK;
-  for (int b = threadIdx.x; b < nblk; b += blockDim.x) {
-    const int k = b / (RB * CBK);
-    const int rem = b - k * RB * CBK;
-    const int ci0 = (rem / CBK) * VEC, co0 = (rem % CBK) * VEC;
-    T blk[VEC][VEC];
+  constexpr int RB = CIN / VEC, CBK = COUT / VEC;
+  if (wb.b >= nblk) return;
+  const int k = wb.b / (RB * CBK);
+  const int rem = wb.b - k * RB * CBK;
+  const int ci0 = (rem / CBK) * VEC, co0 = (rem % CBK) * VEC;
+  T blk[VEC][VEC];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(weights + (static_cast<int64_t>(k) * CIN + ci0 + i) * COUT + co0);
-      __builtin_memcpy(blk[i], &raw, sizeof(raw));
+  for (int i = 0; i < VEC; ++i) __builtin_memcpy(blk[i], &wb.rows[i], sizeof(uint4));
+  const int ch = ci0 / CHUNK, g = (ci0 % CHUNK) / VEC;
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    T col[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) col[i] = blk[i][j];
+    const int co = co0 + j;
+    const size_t slot = ((static_cast<size_t>(k) * NCB + (co >> 4)) * NCH + ch) * 64 + g * 16 + (co & 15);
+    uint4 v;
+    __builtin_memcpy(&v, col, sizeof(v));
+    wl[slot] = v;
+  }
+}
+
+// Per-wave state of one tile: offset k's row mask, list start and first
+// stage slot live in lane k.
+struct TileMeta {
+  unsigned long long mk;
+  int lok;
+  int basek;
+  int total;
+};
+
+template <typename T, int CIN>
+__device__ __forceinline__ TileMeta tile_meta(const unsigned long long* __restrict__ tile_mask,
+                                              const int32_t* __restrict__ tile_off, int64_t t,
+                                              int64_t tiles, int KV, int centre, int lane) {
+  TileMeta tm;
+  tm.mk = 0ull;
+  tm.lok = 0;
+  if (lane < KV) {
+    tm.mk = tile_mask[static_cast<int64_t>(lane) * tiles + t];
+    tm.lok = tile_off[static_cast<int64_t>(lane) * tiles + t];
+  }
+  const int cnt = (lane < KV && lane != centre) ? __popcll(tm.mk) : 0;
+  int incl = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int up = __shfl_up(incl, d);
+    if (lane >= d) incl += up;
+  }
+  tm.basek = incl - cnt;
+  tm.total = lane_i32(incl, 63);
+  return tm;
+}
+
+// Stage layout of a wave: chunk-major, stage[v * kStageStride + slot] is the
+// 16-byte chunk v of the row in stage slot `slot`; slot kStageEntries is a
+// zero row.  Consecutive slots are consecutive 16-byte words, so lanes reading
+// one chunk of consecutive slots hit distinct banks.
+constexpr int kStageStride = kStageEntries + 1;
+
+// Gathers the input rows of the tile's entries with stage slots in [s0, s1)
+// (s1 - s0 <= kStageEntries).  Pass 1 (lanes = rows): for each offset present,
+// the lane of a row that has it records its list position in slot_pos.  Pass 2
+// (lanes = slots): index loads, then row loads, then stage writes.
+template <typename T, int CIN>
+__device__ __forceinline__ void gather_stage(const T* __restrict__ feats,
+                                             const int32_t* __restrict__ in_idx, const TileMeta& tm,
+                                             int s0, int s1, int centre, int KV, int lane,
+                                             uint4* stage, int* slot_pos) {
+  constexpr int ROWV = CIN * static_cast<int>(sizeof(T)) / 16;
+  constexpr int ROUNDS = (kStageEntries + 63) / 64;
+  const int cnt = (lane < KV && lane != centre) ? __popcll(tm.mk) : 0;
+  unsigned long long todo = __ballot(cnt > 0 && tm.basek < s1 && tm.basek + cnt > s0);
+  while (todo) {
+    const int k = __ffsll(static_cast<long long>(todo)) - 1;
+    todo &= todo - 1ull;
+    const unsigned long long m = lane_u64(tm.mk, k);
+    const int bk = lane_i32(tm.basek, k);
+    const int lk = lane_i32(tm.lok, k);
+    const int rank = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+        static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+    const int slot = bk + rank;
+    if (((m >> lane) & 1ull) && slot >= s0 && slot < s1) slot_pos[slot - s0] = lk + rank;
+  }
+  wave_lds_sync();
+  int32_t src[ROUNDS];
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    const int ls = lane + 64 * rd;
+    src[rd] = (ls < s1 - s0) ? in_idx[slot_pos[ls]] : 0;
+  }
+  uint4 row[ROUNDS][ROWV];
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    const uint4* rowp = reinterpret_cast<const uint4*>(feats + static_cast<int64_t>(src[rd]) * CIN);
+#pragma unroll
+    for (int v = 0; v < ROWV; ++v) row[rd][v] = rowp[v];
+  }
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    const int ls = lane + 64 * rd;
+    if (ls < s1 - s0) {
+#pragma unroll
+      for (int v = 0; v < ROWV; ++v) stage[v * kStageStride + ls] = row[rd][v];
     }
-    const int ch = ci0 / CHUNK, g = (ci0 % CHUNK) / VEC;
+  }
+}
+
+// A and B operands of one offset for the wave's four 16-row blocks.
+template <int NCH, int NCB>
+struct OffsetOps {
+  uint4 a[NCH][NCB];
+  uint4 b[4][NCH];
+  unsigned long long m;
+};
+
+template <typename T, int CIN, int COUT>
+__device__ __forceinline__ void load_offset(OffsetOps<CIN / Elem<T>::kChunk, COUT / 16>& op,
+                                            const uint4* wl, const uint4* stage_g,
+                                            const TileMeta& tm, int k, int s0, int s1, int lane) {
+  constexpr int NCH = CIN / Elem<T>::kChunk, NCB = COUT / 16;
+  const int r = lane & 15;
+  const int bk = lane_i32(tm.basek, k) - s0;
+  op.m = lane_u64(tm.mk, k);
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      T col[VEC];
+  for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) col[i] = blk[i][j];
-      const int co = co0 + j;
-      const size_t slot = ((static_cast<size_t>(k) * NCB + (co >> 4)) * NCH + ch) * 64 + g * 16 + (co & 15);
-      uint4 v;
-      __builtin_memcpy(&v, col, sizeof(v));
-      wl[slot] = v;
-    }
+    for (int cb = 0; cb < NCB; ++cb) op.a[ch][cb] = wl[((static_cast<size_t>(k) * NCB + cb) * NCH + ch) * 64 + lane];
+  const uint32_t below16 = (1u << r) - 1u;
+  int before = bk;
+  const int lim = s1 - s0;
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb) {
+    const uint32_t sub = static_cast<uint32_t>(op.m >> (qb * 16)) & 0xffffu;
+    const int ls0 = before + __popc(sub & below16);
+    const bool has = ((sub >> r) & 1u) && ls0 >= 0 && ls0 < lim;
+    const int ls = has ? ls0 : kStageEntries;  // the zero row
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) op.b[qb][ch] = stage_g[ch * 4 * kStageStride + ls];
+    before += __popc(sub);
+  }
+}
+
+template <typename T, int NCH, int NCB>
+__device__ __forceinline__ void run_offset(floatx4 (&acc)[4][NCB], const OffsetOps<NCH, NCB>& op) {
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb) {
+    if (((op.m >> (qb * 16)) & 0xffffull) == 0ull) continue;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) mfma_block<T, NCB>(acc[qb], op.a[ch], op.b[qb][ch]);
   }
 }
 
@@ -367,28 +518,45 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
   const int wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
   uint4* stage = wl + static_cast<size_t>(KV) * NCB * NCH * 64 +
-                 static_cast<size_t>(wave) * (kStageEntries + 1) * ROWV;
+                 static_cast<size_t>(wave) * (ROWV * kStageStride + kStageEntries / 4);
+  int* slot_pos = reinterpret_cast<int*>(stage + ROWV * kStageStride);
+  const uint4* stage_g = stage + g * kStageStride;  // this lane's chunk (of ci-chunk 0)
   const int centre = (KV - 1) / 2;
-  if (lane < ROWV) stage[kStageEntries * ROWV + lane] = make_uint4(0u, 0u, 0u, 0u);  // zero row
+  if (lane < ROWV) stage[lane * kStageStride + kStageEntries] = make_uint4(0u, 0u, 0u, 0u);  // zero row
 
-  stage_weights<T, CIN, COUT>(weights, wl, KV);
+  // The weight loads of this thread's first block and the first tile's index
+  // and row gathers are independent: issue both before waiting on either.
+  constexpr int kRB = CIN / VEC, kCBK = COUT / VEC;
+  const int nblk = KV * kRB * kCBK;
+  WeightBlock<T, CIN, COUT> wb;
+  weight_block_load<T, CIN, COUT>(wb, weights, tid, nblk);
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kSmallWaves;
+  int64_t t = static_cast<int64_t>(blockIdx.x) * kSmallWaves + wave;
+  TileMeta tm{0ull, 0, 0, 0};
+  if (t < tiles) {
+    tm = tile_meta<T, CIN>(tile_mask, tile_off, t, tiles, KV, centre, lane);
+    if (tm.total > 0) {
+      gather_stage<T, CIN>(feats, in_idx, tm, 0, tm.total < kStageEntries ? tm.total : kStageEntries,
+                           centre, KV, lane, stage, slot_pos);
+    }
+  }
+  weight_block_store<T, CIN, COUT>(wb, wl, nblk);
+  for (int b = tid + blockDim.x; b < nblk; b += blockDim.x) {
+    weight_block_load<T, CIN, COUT>(wb, weights, b, nblk);
+    weight_block_store<T, CIN, COUT>(wb, wl, nblk);
+  }
   __syncthreads();
 
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kSmallWaves;
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * kSmallWaves + wave; t < tiles; t += nwaves) {
+  bool first = true;
+  for (; t < tiles; t += nwaves) {
     const int64_t q0 = t * kTileRows;
-    // 1. per-offset mask and list start (lane k holds offset k), own rows
-    unsigned long long mk = 0ull;
-    int lok = 0;
-    if (lane < KV) {
-      mk = tile_mask[static_cast<int64_t>(lane) * tiles + t];
-      lok = tile_off[static_cast<int64_t>(lane) * tiles + t];
-    }
+    if (!first) tm = tile_meta<T, CIN>(tile_mask, tile_off, t, tiles, KV, centre, lane);
     floatx4 acc[4][NCB];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) acc[qb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // centre offset: a dense GEMM on the tile's own rows
     {
       uint4 bc[4][NCH];
 #pragma unroll
@@ -409,78 +577,36 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
         for (int qb = 0; qb < 4; ++qb) mfma_block<T, NCB>(acc[qb], a, bc[qb][ch]);
       }
     }
-    // 2. entry numbering: exclusive prefix of the non-centre counts over offsets
-    const int cnt = (lane < KV && lane != centre) ? __popcll(mk) : 0;
-    int incl = cnt;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int up = __shfl_up(incl, d);
-      if (lane >= d) incl += up;
-    }
-    const int basek = incl - cnt;  // lane k: first slot of offset k
-    const int total = lane_i32(incl, 63);
-    const uint32_t below16 = (1u << r) - 1u;  // rows of this lane's 16-row block before it
-
-    for (int s0 = 0; s0 < total; s0 += kStageEntries) {
-      const int s1 = (total - s0 < kStageEntries) ? total : s0 + kStageEntries;
-      // gather slots [s0, s1): slot s belongs to the last offset k with
-      // base_k <= s (binary search over the lanes holding base_k)
-#pragma unroll
-      for (int round = 0; round < (kStageEntries + 63) / 64; ++round) {
-        const int s = s0 + lane + 64 * round;
-        // Binary lifting with every lane active at every shuffle (a shuffle
-        // from a lane outside the active mask does not return its register).
-        int lo = 0;
-#pragma unroll
-        for (int step = 32; step > 0; step >>= 1) {
-          const int cand = lo + step;
-          const int b = __shfl(basek, cand < KV ? cand : KV - 1);
-          if (cand < KV && b <= s) lo = cand;
-        }
-        const int bk = __shfl(basek, lo);
-        const int lk = __shfl(lok, lo);
-        if (s < s1) {
-          const int32_t src = in_idx[static_cast<int64_t>(lk) + (s - bk)];
-          const uint4* rowp = reinterpret_cast<const uint4*>(feats + static_cast<int64_t>(src) * CIN);
-#pragma unroll
-          for (int v = 0; v < ROWV; ++v) stage[(s - s0) * ROWV + v] = rowp[v];
-        }
+    const int cntk = (lane < KV && lane != centre) ? __popcll(tm.mk) : 0;
+    for (int s0 = 0; s0 < tm.total; s0 += kStageEntries) {
+      const int s1 = (tm.total - s0 < kStageEntries) ? tm.total : s0 + kStageEntries;
+      if (!(first && s0 == 0)) {
+        wave_lds_sync();  // earlier reads of the stage are done
+        gather_stage<T, CIN>(feats, in_idx, tm, s0, s1, centre, KV, lane, stage, slot_pos);
       }
       wave_lds_sync();
-      // 3. MFMA over the offsets with entries in [s0, s1)
-      for (int k = 0; k < KV; ++k) {
-        if (k == centre) continue;
-        const int bk = lane_i32(basek, k);
-        const unsigned long long m = lane_u64(mk, k);
-        if (m == 0ull || bk >= s1 || bk + __popcll(m) <= s0) continue;
-        uint4 a[NCH][NCB];
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb)
-            a[ch][cb] = wl[((static_cast<size_t>(k) * NCB + cb) * NCH + ch) * 64 + lane];
-        uint4 b[4][NCH];
-        int before = bk;  // slot of the first row of block qb
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-          const uint32_t sub = static_cast<uint32_t>(m >> (qb * 16)) & 0xffffu;
-          const int slot = before + __popc(sub & below16);
-          const bool has = ((sub >> r) & 1u) && slot >= s0 && slot < s1;
-          const int ls = has ? slot - s0 : kStageEntries;  // row kStageEntries of the stage is zero
-#pragma unroll
-          for (int ch = 0; ch < NCH; ++ch) b[qb][ch] = stage[ls * ROWV + ch * 4 + g];
-          before += __popc(sub);
-        }
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-          if (((m >> (qb * 16)) & 0xffffull) == 0ull) continue;
-#pragma unroll
-          for (int ch = 0; ch < NCH; ++ch) mfma_block<T, NCB>(acc[qb], a[ch], b[qb][ch]);
-        }
+      // offsets with entries in [s0, s1), in order, ping-ponging between two
+      // operand sets: the next offset's loads are in flight while the current
+      // one runs on MFMA
+      unsigned long long todo = __ballot(cntk > 0 && tm.basek < s1 && tm.basek + cntk > s0);
+      OffsetOps<NCH, NCB> x, y;
+      int k = todo ? __ffsll(static_cast<long long>(todo)) - 1 : -1;
+      todo &= todo - 1ull;
+      if (k >= 0) load_offset<T, CIN, COUT>(x, wl, stage_g, tm, k, s0, s1, lane);
+      while (k >= 0) {
+        k = todo ? __ffsll(static_cast<long long>(todo)) - 1 : -1;
+        todo &= todo - 1ull;
+        if (k >= 0) load_offset<T, CIN, COUT>(y, wl, stage_g, tm, k, s0, s1, lane);
+        run_offset<T, NCH, NCB>(acc, x);
+        if (k < 0) break;
+        k = todo ? __ffsll(static_cast<long long>(todo)) - 1 : -1;
+        todo &= todo - 1ull;
+        if (k >= 0) load_offset<T, CIN, COUT>(x, wl, stage_g, tm, k, s0, s1, lane);
+        run_offset<T, NCH, NCB>(acc, y);
       }
-      wave_lds_sync();
     }
-    // 4. epilogue
+    first = false;
+    // epilogue: round to the output dtype, each row written once
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       const int64_t q = q0 + qb * 16 + r;
@@ -489,6 +615,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
         for (int cb = 0; cb < NCB; ++cb) Elem<T>::store4(out + q * COUT + cb * 16 + 4 * g, acc[qb][cb]);
       }
     }
+    wave_lds_sync();
   }
 }
 
@@ -510,6 +637,8 @@ template <typename T, int CIN, int COUT>
 hipError_t launch_small(const ForwardArgs& a, hipStream_t stream) {
   using Sh = SmallShape<T, CIN, COUT>;
   const size_t lds = Sh::lds_bytes(a.KV);
+  // One workgroup per CU (LDS-bound); a workgroup takes consecutive tiles, so
+  // the rows its waves gather overlap in the CU's and the XCD's caches.
   const int64_t want = (a.tiles + kSmallWaves - 1) / kSmallWaves;
   const int64_t cap = device_cu_count();
   const unsigned grid = static_cast<unsigned>(want < cap ? want : cap);
@@ -572,6 +701,14 @@ hipError_t dispatch(const ForwardArgs& a, hipStream_t stream) {
   const hipError_t e = try_small<T>(a, stream);
   if (e != hipErrorNotSupported) return e;
   return launch_dispatch_cb<T>(a, stream);
+}
+
+bool small_supported(const ForwardArgs& a) {
+  if (a.KV > 64) return false;
+  if (a.dtype == 0) {
+    return a.cin == 16 && (a.cout == 16 || a.cout == 32);
+  }
+  return a.cin == 32 && (a.cout == 16 || a.cout == 32);
 }
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream) {

@@ -85,4 +85,12 @@ struct ForwardArgs {
 };
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream);
 
+// Mid / large channel path (forward_tiled.hip): needs a workspace of
+// tiled_workspace_bytes(a) bytes for the weights in MFMA operand order.
+bool tiled_supported(const ForwardArgs& a);
+size_t tiled_workspace_bytes(const ForwardArgs& a);
+hipError_t launch_forward_tiled(const ForwardArgs& a, void* workspace, hipStream_t stream);
+// True when the small-channel kernel (every W_d resident in LDS) serves `a`.
+bool small_supported(const ForwardArgs& a);
+
 }  // namespace spconv

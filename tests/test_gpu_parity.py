@@ -170,7 +170,21 @@ def test_forward_random_grids(sp, dtype, K, cin, cout):
     _forward_check(sp, kmap, c, K, cin, cout, dtype, seed=cin * 7 + cout)
 
 
-@pytest.mark.parametrize("dtype,ch", [("f16", 32), ("bf16", 32), ("f32", 16)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("K,cin,cout", [(3, 64, 64), (3, 128, 128), (3, 256, 256), (5, 64, 64),
+                                        (3, 128, 48), (3, 256, 16), (1, 128, 128), (5, 32, 64),
+                                        (3, 64, 208), (7, 64, 32)])
+def test_forward_mid_large_channels(sp, dtype, K, cin, cout):
+    """Channel counts of the tiled path: whole W_d no longer fits on chip, so
+    slices are staged per offset; C_in 256 splits a 64-row tile over two
+    waves; ragged grids leave partial tiles and offsets absent from blocks."""
+    c = workloads.permuted(workloads.random_grid(K * 31 + cin + cout, 13, 0.25, 2), cin + 1)
+    kmap = _gpu_map(sp, c, K)
+    _forward_check(sp, kmap, c, K, cin, cout, dtype, seed=cin * 5 + cout + K)
+
+
+@pytest.mark.parametrize("dtype,ch", [("f16", 32), ("bf16", 32), ("f32", 16), ("f16", 128),
+                                      ("bf16", 256)])
 @pytest.mark.parametrize("extent", [12, 20])
 def test_forward_dense_block(sp, dtype, ch, extent):
     """Fully active cube: up to 26 neighbours per row, so a 64-row tile holds
@@ -189,7 +203,7 @@ def test_forward_routing_is_exact(sp, dtype):
     n = c.shape[0]
     kmap = _gpu_map(sp, c, 3)
     ref = oracle.build_map(c, 3)
-    for ch in ((16, 48) if dtype == "f32" else (32, 48)):
+    for ch in ((16, 48) if dtype == "f32" else (32, 48, 64, 256)):
         f = workloads.features(n, ch, dtype, 11)
         for k in (13, 0, 17, 26):
             w = torch.zeros((27, ch, ch), dtype=TORCH_DT[dtype])
