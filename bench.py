@@ -6,6 +6,11 @@ per-offset scan and compaction) followed by the fused forward (centre GEMM,
 gathered offsets on MFMA, output-stationary accumulation, epilogue).  Inputs
 are resident in HBM before timing starts.
 
+Steps are pipelined the way a network would run them: each map build is
+enqueued without a host wait, the forward follows on the same stream, and the
+previous step's map is waited on (its device status checked) and released
+once this step's work is queued.
+
 Prints ONE JSON line.  ``value`` is the whole-step effective throughput
 2 |map| C_in C_out / t_step in TFLOP/s (|map| counts real entries only,
 including the centre ones); the map-build rate and the forward-only rate are
@@ -99,29 +104,42 @@ def main(argv=None):
     print(f"[bench] workload={wl.name} layer={args.layer} N={layer.n} K={layer.k} "
           f"C={layer.cin}->{layer.cout} {layer.dtype}", file=sys.stderr, flush=True)
 
+    # One step: the map build, enqueued without a host wait, then the forward
+    # on the same stream.  The previous step's map is waited on (its device
+    # status checked) and released after this step's work is enqueued, so the
+    # device never idles between steps and every map is still checked.
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        kmap = sp.build_map(coords, layer.k)
+        kmap = sp.build_map(coords, layer.k, wait=False)
         if ev is not None:
             ev[1].record()
         sp.forward(feats, w, kmap, out=out)
         if ev is not None:
             ev[2].record()
+        return kmap
+
+    def retire(kmap):
+        kmap.wait()  # raises on a device-detected build error
         e = kmap.total_entries
         kmap.free()  # stream-ordered release, as a network layer would do
         return e
 
     for _ in range(args.warmup):
-        e_total = step()
+        e_total = retire(step())
     torch.cuda.synchronize()
     kv = layer.k ** 3
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    prev = None
     for i in range(args.steps):
-        step(events[i])
+        kmap = step(events[i])
+        if prev is not None:
+            assert retire(prev) == e_total
+        prev = kmap
+    assert retire(prev) == e_total
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps

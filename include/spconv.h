@@ -39,8 +39,10 @@
  * except the map's lists, which the map owns.  hip_stream is a hipStream_t
  * (NULL = the null stream).  spconv_build_map synchronises hip_stream once (to
  * read the per-offset counts and the device-side error flags);
- * spconv_forward is asynchronous on its stream.  The map's device buffers come
- * from a library-owned stream-ordered memory pool on the current device.
+ * spconv_build_map_async only enqueues, and the counts and device errors are
+ * read by the first call that needs them.  spconv_forward is asynchronous on
+ * its stream.  The map's device buffers come from a library-owned
+ * stream-ordered memory pool on the current device.
  *
  * Errors: functions return a status; nothing throws across the ABI.  Host-
  * checkable errors are reported before any device work.  On error, output
@@ -98,15 +100,34 @@ int32_t spconv_abi_version(void);
 spconv_status spconv_build_map(const int32_t* d_coords, int64_t n, int32_t kernel_size,
                                void* hip_stream, spconv_map** out_map);
 
+/*
+ * The same map build, without the wait: returns as soon as the work is
+ * enqueued on hip_stream, so that a forward can follow on the device without
+ * an idle gap.  Host-checkable errors are returned as by spconv_build_map.
+ * The device-detected ones (DUPLICATE_COORD, COORD_RANGE) and the counts
+ * become known when the build completes; spconv_map_wait, spconv_map_info
+ * (for total_entries) and spconv_map_counts wait for that and return such an
+ * error.  A forward over a map whose build reports an error is memory-safe
+ * but its output is meaningless.  On success *out_map is a new map (to be
+ * freed with spconv_map_free whatever its build reports), else NULL.
+ */
+spconv_status spconv_build_map_async(const int32_t* d_coords, int64_t n, int32_t kernel_size,
+                                     void* hip_stream, spconv_map** out_map);
+
+/* Waits until the map's build has completed on the device (no-op for a map
+ * from spconv_build_map) and returns its device status: OK, DUPLICATE_COORD,
+ * COORD_RANGE or DEVICE.  The map stays valid either way. */
+spconv_status spconv_map_wait(spconv_map* map);
+
 /* Kernel size, number of voxels and total entries (sum of all counts,
  * including the N centre entries).  Any output pointer may be NULL. */
-spconv_status spconv_map_info(const spconv_map* map, int32_t* kernel_size, int64_t* n,
+spconv_status spconv_map_info(spconv_map* map, int32_t* kernel_size, int64_t* n,
                               int64_t* total_entries);
 
 /* Copies the per-offset entry counts h_counts[K^3] and list offsets
  * h_offsets[K^3 + 1] (host arrays; either may be NULL).  The entries of
  * offset k lie at [h_offsets[k], h_offsets[k+1]) of the lists. */
-spconv_status spconv_map_counts(const spconv_map* map, int64_t* h_counts, int64_t* h_offsets);
+spconv_status spconv_map_counts(spconv_map* map, int64_t* h_counts, int64_t* h_offsets);
 
 /* Borrowed device pointers to the map's int32 lists (total_entries each),
  * valid until spconv_map_free.  Reading them is ordered after the build on the
@@ -120,13 +141,17 @@ spconv_status spconv_map_lists(const spconv_map* map, const int32_t** d_in_idx,
  * with d_feats [N][c_in], d_weights [K^3][c_in][c_out] and d_out [N][c_out]
  * (caller-allocated, overwritten), all row-major in dtype and 16-byte aligned.
  * Products accumulate in fp32; the result is rounded to dtype (to nearest
- * even).  Runs as one fused kernel per call: the centre offset is a dense
+ * even).  The work is one fused kernel: the centre offset is a dense
  * (identity-indexed) GEMM and every other offset gathers its input rows by
- * index; each output row is accumulated on chip and written once.
+ * index; each output row is accumulated on chip and written once.  For
+ * F16/BF16 with c_in in {32, 64, 128, 256} outside the small-channel shapes,
+ * a short kernel first copies W into MFMA operand order in a workspace from
+ * the library's stream-ordered pool.
  *
  * Requirements: c_in, c_out multiples of 8 in [8, 1024] (F16/BF16), or
- * multiples of 4 in [4, 512] (F32).  Errors: INVALID_ARG (NULL or misaligned pointers, channel counts out
- * of range), UNSUPPORTED (dtype, channel multiple), DEVICE.
+ * multiples of 4 in [4, 512] (F32).  Errors: INVALID_ARG (NULL or misaligned
+ * pointers, channel counts out of range), UNSUPPORTED (dtype, channel
+ * multiple), OUT_OF_MEMORY (workspace), DEVICE.
  */
 spconv_status spconv_forward(const void* d_feats, const void* d_weights, const spconv_map* map,
                              int32_t c_in, int32_t c_out, spconv_dtype dtype, void* d_out,

@@ -34,9 +34,9 @@ DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 
 # Every symbol include/spconv.h declares.
 EXPORTED = (
-    "spconv_abi_version", "spconv_build_map", "spconv_map_info", "spconv_map_counts",
-    "spconv_map_lists", "spconv_forward", "spconv_map_free", "spconv_status_string",
-    "spconv_last_error",
+    "spconv_abi_version", "spconv_build_map", "spconv_build_map_async", "spconv_map_wait",
+    "spconv_map_info", "spconv_map_counts", "spconv_map_lists", "spconv_forward",
+    "spconv_map_free", "spconv_status_string", "spconv_last_error",
 )
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -71,6 +71,9 @@ def lib() -> ctypes.CDLL:
     L.spconv_abi_version.argtypes, L.spconv_abi_version.restype = [], i32
     L.spconv_build_map.argtypes = [vp, i64, i32, vp, ctypes.POINTER(vp)]
     L.spconv_build_map.restype = ctypes.c_int
+    L.spconv_build_map_async.argtypes = [vp, i64, i32, vp, ctypes.POINTER(vp)]
+    L.spconv_build_map_async.restype = ctypes.c_int
+    L.spconv_map_wait.argtypes, L.spconv_map_wait.restype = [vp], ctypes.c_int
     L.spconv_map_info.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.spconv_map_info.restype = ctypes.c_int
     L.spconv_map_counts.argtypes = [vp, vp, vp]
@@ -114,6 +117,18 @@ def spconv_build_map(d_coords: int, n: int, kernel_size: int, hip_stream: int) -
     h = ctypes.c_void_p()
     _check(lib().spconv_build_map(d_coords, n, kernel_size, hip_stream, ctypes.byref(h)))
     return int(h.value)
+
+
+def spconv_build_map_async(d_coords: int, n: int, kernel_size: int, hip_stream: int) -> int:
+    """Raw call: enqueues the build and returns the map handle (int); device
+    errors surface in spconv_map_wait / spconv_map_info / spconv_map_counts."""
+    h = ctypes.c_void_p()
+    _check(lib().spconv_build_map_async(d_coords, n, kernel_size, hip_stream, ctypes.byref(h)))
+    return int(h.value)
+
+
+def spconv_map_wait(handle: int) -> None:
+    _check(lib().spconv_map_wait(handle))
 
 
 def spconv_map_info(handle: int) -> Tuple[int, int, int]:
@@ -189,12 +204,23 @@ class _OnDevice:
 class SpconvMap:
     """A kernel map on the GPU (owns the C handle)."""
 
-    def __init__(self, handle: int, device):
+    def __init__(self, handle: int, device, kernel_size: int, n: int):
         self.handle = handle
         self.device = device
-        self.kernel_size, self.n, self.total_entries = spconv_map_info(handle)
+        self.kernel_size, self.n = kernel_size, n
         self.kernel_volume = self.kernel_size ** 3
         self._counts = None
+        self._total = None
+
+    def wait(self) -> None:
+        """Waits for the build (a no-op once done); raises its device error."""
+        spconv_map_wait(self.handle)
+
+    @property
+    def total_entries(self) -> int:
+        if self._total is None:
+            self._total = spconv_map_info(self.handle)[2]
+        return self._total
 
     def _load_counts(self):
         if self._counts is None:
@@ -239,16 +265,19 @@ class SpconvMap:
             pass
 
 
-def build_map(coords, kernel_size: int) -> SpconvMap:
+def build_map(coords, kernel_size: int, wait: bool = True) -> SpconvMap:
     """Kernel map of a K^3 submanifold convolution over int32 [N, 4]
-    (b, z, y, x) coordinates resident on a HIP device."""
+    (b, z, y, x) coordinates resident on a HIP device.  With wait=False the
+    build is only enqueued (device errors then surface in ``SpconvMap.wait``
+    or the first query of counts)."""
     torch = _torch()
     if not (isinstance(coords, torch.Tensor) and coords.is_cuda and coords.dtype == torch.int32
             and coords.dim() == 2 and coords.shape[1] == 4 and coords.is_contiguous()):
         raise SpconvError(1, "coords must be a contiguous int32 [N, 4] tensor on a HIP device")
+    call = spconv_build_map if wait else spconv_build_map_async
     with _OnDevice(coords.device):
-        h = spconv_build_map(coords.data_ptr(), coords.shape[0], int(kernel_size), _stream())
-    return SpconvMap(h, coords.device)
+        h = call(coords.data_ptr(), coords.shape[0], int(kernel_size), _stream())
+    return SpconvMap(h, coords.device, int(kernel_size), int(coords.shape[0]))
 
 
 _DT = None

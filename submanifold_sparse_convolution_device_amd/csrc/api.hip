@@ -14,18 +14,34 @@
 #include "../../include/spconv.h"
 #include "internal.h"
 
+namespace {
+
+// Pinned host slot that receives one build's summary, with the event that
+// marks its arrival.  Slots are reused; a slot released while its copy may
+// still be in flight is reclaimed only once its event has completed.
+struct SummarySlot {
+  long long* host = nullptr;
+  hipEvent_t done = nullptr;
+};
+
+}  // namespace
+
 struct spconv_map {
   int device = 0;
   hipStream_t stream = nullptr;
   int32_t K = 0;
   int32_t KV = 0;
   int64_t n = 0;
-  int64_t total = 0;
   int64_t tiles = 0;
+  void* block = nullptr;  // one pool allocation holding the MapBuffers
+  spconv::MapBuffers buf;
+  // Filled when the build's summary has been read (see finish_build).
+  SummarySlot* slot = nullptr;   // non-null while the summary is not yet read
+  spconv_status status = SPCONV_OK;
+  std::string error;             // detail of a device-detected error
+  int64_t total = 0;
   std::vector<int64_t> counts;   // KV
   std::vector<int64_t> offsets;  // KV + 1
-  void* block = nullptr;         // one pool allocation holding the MapBuffers
-  spconv::MapBuffers buf;
 };
 
 namespace {
@@ -81,30 +97,87 @@ spconv_status pool_for(int device, hipMemPool_t* out) {
   return SPCONV_OK;
 }
 
-// Pinned host staging for the build's read-back, one per thread.
-spconv_status host_staging(size_t bytes, long long** out) {
-  thread_local long long* buf = nullptr;
-  thread_local size_t cap = 0;
-  if (cap < bytes) {
-    if (buf != nullptr) (void)hipHostFree(buf);
-    buf = nullptr;
-    cap = 0;
-    void* p = nullptr;
-    SPCONV_HIP(hipHostMalloc(&p, bytes, hipHostMallocPortable), "hipHostMalloc");
-    buf = static_cast<long long*>(p);
-    cap = bytes;
+// Summary slots, one free list per device.  A slot holds enough for the
+// largest kernel (K = 7).
+constexpr size_t kSlotBytes = sizeof(long long) * (spconv::kSummaryHead + 343);
+constexpr int kSlotsPerBatch = 16;
+
+struct SlotPool {
+  std::vector<SummarySlot*> free;
+  std::vector<SummarySlot*> pending;  // released while their copy may be in flight
+};
+std::mutex g_slot_mu;
+std::vector<SlotPool> g_slots;
+
+spconv_status acquire_slot(int device, SummarySlot** out) {
+  std::lock_guard<std::mutex> lock(g_slot_mu);
+  if (static_cast<int>(g_slots.size()) <= device) g_slots.resize(device + 1);
+  SlotPool& pool = g_slots[device];
+  for (size_t i = 0; i < pool.pending.size();) {
+    if (hipEventQuery(pool.pending[i]->done) == hipSuccess) {
+      pool.free.push_back(pool.pending[i]);
+      pool.pending[i] = pool.pending.back();
+      pool.pending.pop_back();
+    } else {
+      ++i;
+    }
   }
-  *out = buf;
+  if (pool.free.empty()) {
+    void* p = nullptr;
+    SPCONV_HIP(hipHostMalloc(&p, kSlotBytes * kSlotsPerBatch, hipHostMallocPortable), "hipHostMalloc");
+    for (int i = 0; i < kSlotsPerBatch; ++i) {
+      SummarySlot* slot = new (std::nothrow) SummarySlot;
+      if (slot == nullptr) return fail(SPCONV_ERR_OUT_OF_MEMORY, "host allocation");
+      slot->host = reinterpret_cast<long long*>(static_cast<char*>(p) + kSlotBytes * i);
+      SPCONV_HIP(hipEventCreateWithFlags(&slot->done, hipEventDisableTiming), "hipEventCreateWithFlags");
+      pool.free.push_back(slot);
+    }
+  }
+  *out = pool.free.back();
+  pool.free.pop_back();
   return SPCONV_OK;
 }
 
-// One reusable timing-free event per thread for the build's completion.
-spconv_status build_event(hipEvent_t* out) {
-  thread_local hipEvent_t ev = nullptr;
-  if (ev == nullptr) {
-    SPCONV_HIP(hipEventCreateWithFlags(&ev, hipEventDisableTiming), "hipEventCreateWithFlags");
+void release_slot(int device, SummarySlot* slot) {
+  std::lock_guard<std::mutex> lock(g_slot_mu);
+  g_slots[device].pending.push_back(slot);
+}
+
+// Waits for the build's summary (once) and records the counts or the device
+// error it reports.
+spconv_status finish_build(spconv_map* m) {
+  if (m->slot != nullptr) {
+    hipError_t e;
+    // Spinning keeps the wake-up latency of a blocking wait off the critical path.
+    while ((e = hipEventQuery(m->slot->done)) == hipErrorNotReady) {
+    }
+    const long long* sum = m->slot->host;
+    if (e != hipSuccess) {
+      m->status = hip_fail(e, "map build");
+      m->error = g_last_error;
+    } else {
+      const unsigned long long flags = static_cast<unsigned long long>(sum[0]);
+      if (flags & spconv::kFlagRange) {
+        m->status = SPCONV_ERR_COORD_RANGE;
+        m->error = "a coordinate is outside b in [0, 2^15), z, y, x in [0, 2^16)";
+      } else if (flags & spconv::kFlagDuplicate) {
+        m->status = SPCONV_ERR_DUPLICATE_COORD;
+        m->error = "two rows share one (b, z, y, x) coordinate";
+      } else if (flags & spconv::kFlagTableFull) {
+        m->status = SPCONV_ERR_DEVICE;
+        m->error = "internal: hash table probe exceeded its bound";
+      } else {
+        m->total = sum[1];
+        m->counts.assign(sum + spconv::kSummaryHead, sum + spconv::kSummaryHead + m->KV);
+        m->offsets.resize(m->KV + 1);
+        m->offsets[0] = 0;
+        for (int k = 0; k < m->KV; ++k) m->offsets[k + 1] = m->offsets[k] + m->counts[k];
+      }
+    }
+    release_slot(m->device, m->slot);
+    m->slot = nullptr;
   }
-  *out = ev;
+  if (m->status != SPCONV_OK) return fail(m->status, "%s", m->error.c_str());
   return SPCONV_OK;
 }
 
@@ -137,8 +210,8 @@ const char* spconv_status_string(spconv_status s) {
 
 const char* spconv_last_error(void) { return g_last_error.c_str(); }
 
-spconv_status spconv_build_map(const int32_t* d_coords, int64_t n, int32_t kernel_size,
-                               void* hip_stream, spconv_map** out_map) {
+spconv_status spconv_build_map_async(const int32_t* d_coords, int64_t n, int32_t kernel_size,
+                                     void* hip_stream, spconv_map** out_map) {
   g_last_error.clear();
   if (out_map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "out_map is NULL");
   *out_map = nullptr;
@@ -171,21 +244,25 @@ spconv_status spconv_build_map(const int32_t* d_coords, int64_t n, int32_t kerne
   hipMemPool_t pool = nullptr;
   spconv_status st = pool_for(device, &pool);
   if (st != SPCONV_OK) return st;
-  long long* staging = nullptr;
-  st = host_staging(sizeof(long long) * (spconv::kSummaryHead + KV), &staging);
-  if (st != SPCONV_OK) return st;
 
   spconv_map* m = new (std::nothrow) spconv_map;
   if (m == nullptr) return fail(SPCONV_ERR_OUT_OF_MEMORY, "host allocation");
+  st = acquire_slot(device, &m->slot);
+  if (st != SPCONV_OK) {
+    delete m;
+    return st;
+  }
   void* ws = nullptr;
   hipError_t e = hipMallocFromPoolAsync(&ws, spconv::build_scratch_bytes(p), pool, stream);
   if (e != hipSuccess) {
+    release_slot(device, m->slot);
     delete m;
     return hip_fail(e, "workspace allocation");
   }
   e = hipMallocFromPoolAsync(&m->block, spconv::map_buffer_bytes(p), pool, stream);
   if (e != hipSuccess) {
     (void)hipFreeAsync(ws, stream);
+    release_slot(device, m->slot);
     delete m;
     return hip_fail(e, "map allocation");
   }
@@ -195,72 +272,64 @@ spconv_status spconv_build_map(const int32_t* d_coords, int64_t n, int32_t kerne
   auto discard = [&](spconv_status st) {
     (void)hipFreeAsync(ws, stream);
     (void)hipFreeAsync(m->block, stream);
+    release_slot(device, m->slot);
     delete m;
     return st;
   };
 
   e = spconv::launch_build(p, d_coords, s, m->buf, stream);
   if (e != hipSuccess) return discard(hip_fail(e, "map build launch"));
-  e = hipMemcpyAsync(staging, s.summary, sizeof(long long) * (spconv::kSummaryHead + KV),
+  e = hipMemcpyAsync(m->slot->host, s.summary, sizeof(long long) * (spconv::kSummaryHead + KV),
                      hipMemcpyDeviceToHost, stream);
   if (e != hipSuccess) return discard(hip_fail(e, "summary read-back"));
-  hipEvent_t done = nullptr;
-  st = build_event(&done);
-  if (st != SPCONV_OK) return discard(st);
-  e = hipEventRecord(done, stream);
+  e = hipEventRecord(m->slot->done, stream);
   if (e != hipSuccess) return discard(hip_fail(e, "hipEventRecord"));
   (void)hipFreeAsync(ws, stream);
-  ws = nullptr;
-  // The one wait of a build.  Spinning on the event keeps the wake-up latency
-  // of a blocking wait off the critical path.
-  while ((e = hipEventQuery(done)) == hipErrorNotReady) {
-  }
-  if (e != hipSuccess) {
-    (void)hipFreeAsync(m->block, stream);
-    delete m;
-    return hip_fail(e, "map build");
-  }
 
-  const unsigned long long flags = static_cast<unsigned long long>(staging[0]);
-  spconv_status err = SPCONV_OK;
-  if (flags & spconv::kFlagRange) {
-    err = fail(SPCONV_ERR_COORD_RANGE, "a coordinate is outside b in [0, 2^15), z, y, x in [0, 2^16)");
-  } else if (flags & spconv::kFlagDuplicate) {
-    err = fail(SPCONV_ERR_DUPLICATE_COORD, "two rows share one (b, z, y, x) coordinate");
-  } else if (flags & spconv::kFlagTableFull) {
-    err = fail(SPCONV_ERR_DEVICE, "internal: hash table probe exceeded its bound");
-  }
-  if (err != SPCONV_OK) {
-    (void)hipFreeAsync(m->block, stream);
-    delete m;
-    return err;
-  }
   m->device = device;
   m->stream = stream;
   m->K = kernel_size;
   m->KV = KV;
   m->n = n;
-  m->total = staging[1];
   m->tiles = p.tiles;
-  m->counts.assign(staging + spconv::kSummaryHead, staging + spconv::kSummaryHead + KV);
-  m->offsets.resize(KV + 1);
-  m->offsets[0] = 0;
-  for (int k = 0; k < KV; ++k) m->offsets[k + 1] = m->offsets[k] + m->counts[k];
   *out_map = m;
   return SPCONV_OK;
 }
 
-spconv_status spconv_map_info(const spconv_map* map, int32_t* kernel_size, int64_t* n,
+spconv_status spconv_build_map(const int32_t* d_coords, int64_t n, int32_t kernel_size,
+                               void* hip_stream, spconv_map** out_map) {
+  spconv_status st = spconv_build_map_async(d_coords, n, kernel_size, hip_stream, out_map);
+  if (st != SPCONV_OK) return st;
+  st = finish_build(*out_map);
+  if (st != SPCONV_OK) {
+    spconv_map_free(*out_map);
+    *out_map = nullptr;
+  }
+  return st;
+}
+
+spconv_status spconv_map_wait(spconv_map* map) {
+  if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
+  return finish_build(map);
+}
+
+spconv_status spconv_map_info(spconv_map* map, int32_t* kernel_size, int64_t* n,
                               int64_t* total_entries) {
   if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
   if (kernel_size) *kernel_size = map->K;
   if (n) *n = map->n;
-  if (total_entries) *total_entries = map->total;
+  if (total_entries) {
+    const spconv_status st = finish_build(map);
+    if (st != SPCONV_OK) return st;
+    *total_entries = map->total;
+  }
   return SPCONV_OK;
 }
 
-spconv_status spconv_map_counts(const spconv_map* map, int64_t* h_counts, int64_t* h_offsets) {
+spconv_status spconv_map_counts(spconv_map* map, int64_t* h_counts, int64_t* h_offsets) {
   if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
+  const spconv_status st = finish_build(map);
+  if (st != SPCONV_OK) return st;
   if (h_counts) std::memcpy(h_counts, map->counts.data(), sizeof(int64_t) * map->KV);
   if (h_offsets) std::memcpy(h_offsets, map->offsets.data(), sizeof(int64_t) * (map->KV + 1));
   return SPCONV_OK;
@@ -333,6 +402,7 @@ spconv_status spconv_forward(const void* d_feats, const void* d_weights, const s
 void spconv_map_free(spconv_map* map) {
   if (map == nullptr) return;
   if (map->block != nullptr) (void)hipFreeAsync(map->block, map->stream);
+  if (map->slot != nullptr) release_slot(map->device, map->slot);
   delete map;
 }
 

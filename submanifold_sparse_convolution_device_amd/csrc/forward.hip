@@ -242,28 +242,31 @@ __global__ __launch_bounds__(kThreads) void k_forward(
 // ---------------------------------------------------------------------------
 // Small-channel kernel: every W_d fits in LDS at once.
 //
-// A workgroup of 12 waves stages all K^3 weight matrices into LDS once,
-// already in MFMA operand order (per offset, co-block and ci-chunk, 64 lanes x
-// 16 bytes), so a lane's A operand is one conflict-free 16-byte read.  Each
-// wave then owns one 64-row output tile at a time, independently of the other
-// waves:
+// A workgroup stages all K^3 weight matrices into LDS once, already in MFMA
+// operand order (per offset, co-block and ci-chunk, 64 lanes x 16 bytes), so
+// a lane's A operand is one 16-byte read.  Each wave then owns one 64-row
+// output tile at a time, independently of the other waves:
 //   1. lanes k < K^3 read the tile's row mask and list start for offset k
 //      (written by the map build); the tile's own rows are loaded straight
 //      into B-operand registers and the centre offset runs on them as a dense
 //      GEMM;
 //   2. the tile's non-centre entries are numbered in offset order (a wave
-//      prefix sum of the mask popcounts) and gathered in one burst: each lane
-//      fetches whole input rows by index into the wave's LDS stage;
+//      prefix sum of the mask popcounts).  Entry s of offset k sits at list
+//      position tile_off[k] + s - base_k, so a lane finds the input row of a
+//      stage slot with one index load, then loads that whole row; the
+//      stage's rows go to the wave's LDS stage in one burst;
 //   3. per offset present in the tile, per 16-row block that uses it, one
 //      MFMA per (co-block, ci-chunk) with B read from the stage (zero for
 //      rows without that neighbour);
 //   4. the accumulators are rounded to the output dtype and each output row is
 //      written once.
-// A tile with more entries than the stage holds is processed in slot ranges;
-// an entry belongs to exactly one range.
+// A tile with more entries than the stage holds is processed in slot ranges
+// of kStageEntries; an entry belongs to exactly one range, and the rows of
+// the next range are in flight while the current one runs on MFMA.
 // ---------------------------------------------------------------------------
-constexpr int kSmallWaves = 12;
-constexpr int kStageEntries = 92;  // plus one zero row per wave
+constexpr int kSmallWaves = 12;    // most waves per workgroup
+constexpr int kStageRounds = 2;    // 64-slot rounds per stage
+constexpr int kStageEntries = 64 * kStageRounds;  // plus one zero row per wave
 constexpr size_t kSmallLdsCap = 160 * 1024;  // one workgroup per CU
 
 template <typename T, int CIN, int COUT>
@@ -275,10 +278,8 @@ struct SmallShape {
   static constexpr int ROWV = CIN * static_cast<int>(sizeof(T)) / 16;  // 16-byte vectors per row
   static_assert(CIN % CHUNK == 0 && COUT % 16 == 0, "shape");
   static size_t wbytes(int KV) { return static_cast<size_t>(KV) * NCB * NCH * 64 * 16; }
-  static size_t lds_bytes(int KV) {
-    // per wave: ROWV x (kStageEntries + 1) chunks plus kStageEntries slot positions
-    return wbytes(KV) + static_cast<size_t>(kSmallWaves) * (ROWV * (kStageEntries + 1) * 16 + kStageEntries * 4);
-  }
+  static size_t stage_bytes() { return static_cast<size_t>(ROWV) * (kStageEntries + 1) * 16; }
+  static size_t lds_bytes(int KV, int waves) { return wbytes(KV) + static_cast<size_t>(waves) * stage_bytes(); }
 };
 
 template <typename T, int NCB>
@@ -319,6 +320,12 @@ __device__ __forceinline__ unsigned long long lane_u64(unsigned long long v, int
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), src));
   return (static_cast<unsigned long long>(hi) << 32) | lo;
 }
+
+// Position of lane l's 16-byte operand inside a 64-lane operand block in LDS.
+// The XOR spreads the eight 16-byte writes that eight consecutive threads make
+// together while staging (slots 8m + j, m = 0..7) over all banks; reads by
+// lanes 8m..8m+7 stay one contiguous 128-byte row.
+__device__ __forceinline__ int operand_slot(int l) { return l ^ ((l >> 3) & 7); }
 
 // Stages every W_d into operand order: element i of lane (g, r) of block
 // (k, cb, ch) is W[k][ch * CHUNK + g * VEC + i][cb * 16 + r].  Each thread
@@ -367,7 +374,7 @@ __device__ __forceinline__ void weight_block_store(const WeightBlock<T, CIN, COU
 #pragma unroll
     for (int i = 0; i < VEC; ++i) col[i] = blk[i][j];
     const int co = co0 + j;
-    const size_t slot = ((static_cast<size_t>(k) * NCB + (co >> 4)) * NCH + ch) * 64 + g * 16 + (co & 15);
+    const size_t slot = ((static_cast<size_t>(k) * NCB + (co >> 4)) * NCH + ch) * 64 + operand_slot(g * 16 + (co & 15));
     uint4 v;
     __builtin_memcpy(&v, col, sizeof(v));
     wl[slot] = v;
@@ -412,97 +419,115 @@ __device__ __forceinline__ TileMeta tile_meta(const unsigned long long* __restri
 // one chunk of consecutive slots hit distinct banks.
 constexpr int kStageStride = kStageEntries + 1;
 
-// Gathers the input rows of the tile's entries with stage slots in [s0, s1)
-// (s1 - s0 <= kStageEntries).  Pass 1 (lanes = rows): for each offset present,
-// the lane of a row that has it records its list position in slot_pos.  Pass 2
-// (lanes = slots): index loads, then row loads, then stage writes.
-template <typename T, int CIN>
-__device__ __forceinline__ void gather_stage(const T* __restrict__ feats,
-                                             const int32_t* __restrict__ in_idx, const TileMeta& tm,
-                                             int s0, int s1, int centre, int KV, int lane,
-                                             uint4* stage, int* slot_pos) {
-  constexpr int ROWV = CIN * static_cast<int>(sizeof(T)) / 16;
-  constexpr int ROUNDS = (kStageEntries + 63) / 64;
-  const int cnt = (lane < KV && lane != centre) ? __popcll(tm.mk) : 0;
-  unsigned long long todo = __ballot(cnt > 0 && tm.basek < s1 && tm.basek + cnt > s0);
+// List positions of stage slots s0 + lane + 64 rd.  Entries are numbered in
+// offset order: offset k's entries of this tile are slots [base_k, base_k +
+// cnt_k) and list positions [tile_off_k, tile_off_k + cnt_k), both in output
+// row order.  Slots past the tile's entries get position 0 (a valid entry; its
+// row lands in a stage slot nothing reads).
+__device__ __forceinline__ void stage_positions(const TileMeta& tm, int cntk, int s0, int lane,
+                                                int (&pos)[kStageRounds]) {
+#pragma unroll
+  for (int rd = 0; rd < kStageRounds; ++rd) pos[rd] = 0;
+  unsigned long long todo = __ballot(cntk > 0 && tm.basek < s0 + kStageEntries && tm.basek + cntk > s0);
   while (todo) {
     const int k = __ffsll(static_cast<long long>(todo)) - 1;
     todo &= todo - 1ull;
-    const unsigned long long m = lane_u64(tm.mk, k);
-    const int bk = lane_i32(tm.basek, k);
-    const int lk = lane_i32(tm.lok, k);
-    const int rank = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-        static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
-    const int slot = bk + rank;
-    if (((m >> lane) & 1ull) && slot >= s0 && slot < s1) slot_pos[slot - s0] = lk + rank;
-  }
-  wave_lds_sync();
-  int32_t src[ROUNDS];
+    const int base = lane_i32(tm.basek, k), c = lane_i32(cntk, k), lo = lane_i32(tm.lok, k);
 #pragma unroll
-  for (int rd = 0; rd < ROUNDS; ++rd) {
-    const int ls = lane + 64 * rd;
-    src[rd] = (ls < s1 - s0) ? in_idx[slot_pos[ls]] : 0;
-  }
-  uint4 row[ROUNDS][ROWV];
-#pragma unroll
-  for (int rd = 0; rd < ROUNDS; ++rd) {
-    const uint4* rowp = reinterpret_cast<const uint4*>(feats + static_cast<int64_t>(src[rd]) * CIN);
-#pragma unroll
-    for (int v = 0; v < ROWV; ++v) row[rd][v] = rowp[v];
-  }
-#pragma unroll
-  for (int rd = 0; rd < ROUNDS; ++rd) {
-    const int ls = lane + 64 * rd;
-    if (ls < s1 - s0) {
-#pragma unroll
-      for (int v = 0; v < ROWV; ++v) stage[v * kStageStride + ls] = row[rd][v];
+    for (int rd = 0; rd < kStageRounds; ++rd) {
+      const int e = s0 + lane + 64 * rd - base;
+      if (e >= 0 && e < c) pos[rd] = lo + e;
     }
   }
 }
 
-// A and B operands of one offset for the wave's four 16-row blocks.
-template <int NCH, int NCB>
-struct OffsetOps {
-  uint4 a[NCH][NCB];
-  uint4 b[4][NCH];
-  unsigned long long m;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Rows of one stage in flight (native vectors, so they stay in registers
+// across the MFMA loop that overlaps their loads).
+template <int ROWV>
+struct StageRows {
+  u32x4 v[kStageRounds][ROWV];
 };
 
-template <typename T, int CIN, int COUT>
-__device__ __forceinline__ void load_offset(OffsetOps<CIN / Elem<T>::kChunk, COUT / 16>& op,
-                                            const uint4* wl, const uint4* stage_g,
-                                            const TileMeta& tm, int k, int s0, int s1, int lane) {
-  constexpr int NCH = CIN / Elem<T>::kChunk, NCB = COUT / 16;
-  const int r = lane & 15;
-  const int bk = lane_i32(tm.basek, k) - s0;
-  op.m = lane_u64(tm.mk, k);
+// Input rows of the slots whose list positions are idx_pos (all loads issued
+// before any is used).
+template <typename T, int CIN>
+__device__ __forceinline__ void load_stage_rows(const T* __restrict__ feats, const int32_t* __restrict__ in_idx,
+                                                const int (&pos)[kStageRounds],
+                                                StageRows<CIN * static_cast<int>(sizeof(T)) / 16>& rows) {
+  constexpr int ROWV = CIN * static_cast<int>(sizeof(T)) / 16;
+  int32_t src[kStageRounds];
 #pragma unroll
-  for (int ch = 0; ch < NCH; ++ch)
+  for (int rd = 0; rd < kStageRounds; ++rd) src[rd] = in_idx[pos[rd]];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) op.a[ch][cb] = wl[((static_cast<size_t>(k) * NCB + cb) * NCH + ch) * 64 + lane];
-  const uint32_t below16 = (1u << r) - 1u;
-  int before = bk;
-  const int lim = s1 - s0;
+  for (int rd = 0; rd < kStageRounds; ++rd) {
+    const u32x4* rowp = reinterpret_cast<const u32x4*>(feats + static_cast<int64_t>(src[rd]) * CIN);
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    const uint32_t sub = static_cast<uint32_t>(op.m >> (qb * 16)) & 0xffffu;
-    const int ls0 = before + __popc(sub & below16);
-    const bool has = ((sub >> r) & 1u) && ls0 >= 0 && ls0 < lim;
-    const int ls = has ? ls0 : kStageEntries;  // the zero row
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) op.b[qb][ch] = stage_g[ch * 4 * kStageStride + ls];
-    before += __popc(sub);
+    for (int v = 0; v < ROWV; ++v) rows.v[rd][v] = rowp[v];
   }
 }
 
+template <int ROWV>
+__device__ __forceinline__ void commit_stage(uint4* stage, const StageRows<ROWV>& rows, int lane) {
+#pragma unroll
+  for (int rd = 0; rd < kStageRounds; ++rd)
+#pragma unroll
+    for (int v = 0; v < ROWV; ++v) *reinterpret_cast<u32x4*>(stage + v * kStageStride + lane + 64 * rd) = rows.v[rd][v];
+}
+
+// One unit of MFMA work: the rows of one 16-row block that have a neighbour
+// at offset k, with at least one of them in the current stage range.  All
+// fields are wave-uniform.  lo is the stage slot of the block's first entry at
+// k relative to the range start; sub has bit i set when row i of the block has
+// that neighbour.  k < 0 marks the end of a walk.
+struct Item {
+  int k;
+  int lo;
+  uint32_t sub;
+};
+
+// A operands (W_k for every co-block) and the B operand of one item.  A lane
+// whose row has no entry in range reads the stage's zero row.  An item with
+// k < 0 reads offset 0 and the zero row (a harmless read that keeps the LDS
+// wait counts the same on every path).
+template <int NCH, int NCB>
+struct ItemOps {
+  uint4 a[NCH][NCB];
+  uint4 b[NCH];
+};
+
+template <typename T, int CIN, int COUT>
+__device__ __forceinline__ void load_item(ItemOps<CIN / Elem<T>::kChunk, COUT / 16>& op, const uint4* wl,
+                                          const uint4* stage_g, const Item& it, int lim, int r,
+                                          uint32_t below_r, int aslot) {
+  constexpr int NCH = CIN / Elem<T>::kChunk, NCB = COUT / 16;
+  const int k = it.k < 0 ? 0 : it.k;
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) op.a[ch][cb] = wl[((static_cast<size_t>(k) * NCB + cb) * NCH + ch) * 64 + aslot];
+  const int ls0 = it.lo + __popc(it.sub & below_r);
+  const bool has = ((it.sub >> r) & 1u) && static_cast<unsigned>(ls0) < static_cast<unsigned>(lim);
+  const int ls = has ? ls0 : kStageEntries;  // the zero row
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) op.b[ch] = stage_g[ch * 4 * kStageStride + ls];
+}
+
 template <typename T, int NCH, int NCB>
-__device__ __forceinline__ void run_offset(floatx4 (&acc)[4][NCB], const OffsetOps<NCH, NCB>& op) {
+__device__ __forceinline__ void run_item(floatx4 (&acc)[NCB], const ItemOps<NCH, NCB>& op) {
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    if (((op.m >> (qb * 16)) & 0xffffull) == 0ull) continue;
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) mfma_block<T, NCB>(acc[qb], op.a[ch], op.b[qb][ch]);
-  }
+  for (int ch = 0; ch < NCH; ++ch) mfma_block<T, NCB>(acc, op.a[ch], op.b[ch]);
+}
+
+// Next item of block qb: the lowest offset left in todo.  lov and subv hold,
+// in lane k, offset k's first slot for this block (relative to the range
+// start) and the block's 16-bit row mask.
+__device__ __forceinline__ Item next_item(unsigned long long& todo, int lov, int subv) {
+  if (todo == 0ull) return Item{-1, 0, 0u};
+  const int k = __ffsll(static_cast<long long>(todo)) - 1;
+  todo &= todo - 1ull;
+  return Item{k, lane_i32(lov, k), static_cast<uint32_t>(lane_i32(subv, k))};
 }
 
 template <typename T, int CIN, int COUT>
@@ -514,12 +539,13 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
   constexpr int CHUNK = Sh::CHUNK, VEC = Sh::VEC, NCH = Sh::NCH, NCB = Sh::NCB, ROWV = Sh::ROWV;
   extern __shared__ uint4 smem4[];
   uint4* wl = smem4;  // [KV][NCB][NCH][64] A operands
+  const int nw = static_cast<int>(blockDim.x >> 6);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
-  uint4* stage = wl + static_cast<size_t>(KV) * NCB * NCH * 64 +
-                 static_cast<size_t>(wave) * (ROWV * kStageStride + kStageEntries / 4);
-  int* slot_pos = reinterpret_cast<int*>(stage + ROWV * kStageStride);
+  const int aslot = operand_slot(lane);
+  const uint32_t below_r = (1u << r) - 1u;
+  uint4* stage = wl + static_cast<size_t>(KV) * NCB * NCH * 64 + static_cast<size_t>(wave) * ROWV * kStageStride;
   const uint4* stage_g = stage + g * kStageStride;  // this lane's chunk (of ci-chunk 0)
   const int centre = (KV - 1) / 2;
   if (lane < ROWV) stage[lane * kStageStride + kStageEntries] = make_uint4(0u, 0u, 0u, 0u);  // zero row
@@ -530,14 +556,33 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
   const int nblk = KV * kRB * kCBK;
   WeightBlock<T, CIN, COUT> wb;
   weight_block_load<T, CIN, COUT>(wb, weights, tid, nblk);
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kSmallWaves;
-  int64_t t = static_cast<int64_t>(blockIdx.x) * kSmallWaves + wave;
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * nw;
+  int64_t t = static_cast<int64_t>(blockIdx.x) * nw + wave;
   TileMeta tm{0ull, 0, 0, 0};
+  int cntk = 0;
+  StageRows<ROWV> rows;
+  int pos_next[kStageRounds];
+  uint4 bc[4][NCH];  // the tile's own rows (centre offset)
+  auto load_centre = [&](int64_t q0) {
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const int64_t q = q0 + qb * 16 + r;
+      const int64_t qs = q < n ? q : n - 1;
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        bc[qb][ch] = *reinterpret_cast<const uint4*>(feats + qs * CIN + ch * CHUNK + g * VEC);
+        if (q >= n) bc[qb][ch] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
   if (t < tiles) {
+    load_centre(t * kTileRows);
     tm = tile_meta<T, CIN>(tile_mask, tile_off, t, tiles, KV, centre, lane);
+    cntk = (lane < KV && lane != centre) ? __popcll(tm.mk) : 0;
     if (tm.total > 0) {
-      gather_stage<T, CIN>(feats, in_idx, tm, 0, tm.total < kStageEntries ? tm.total : kStageEntries,
-                           centre, KV, lane, stage, slot_pos);
+      int pos[kStageRounds];
+      stage_positions(tm, cntk, 0, lane, pos);
+      load_stage_rows<T, CIN>(feats, in_idx, pos, rows);
     }
   }
   weight_block_store<T, CIN, COUT>(wb, wl, nblk);
@@ -550,7 +595,16 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
   bool first = true;
   for (; t < tiles; t += nwaves) {
     const int64_t q0 = t * kTileRows;
-    if (!first) tm = tile_meta<T, CIN>(tile_mask, tile_off, t, tiles, KV, centre, lane);
+    if (!first) {
+      load_centre(q0);
+      tm = tile_meta<T, CIN>(tile_mask, tile_off, t, tiles, KV, centre, lane);
+      cntk = (lane < KV && lane != centre) ? __popcll(tm.mk) : 0;
+      if (tm.total > 0) {
+        int pos[kStageRounds];
+        stage_positions(tm, cntk, 0, lane, pos);
+        load_stage_rows<T, CIN>(feats, in_idx, pos, rows);
+      }
+    }
     floatx4 acc[4][NCB];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
@@ -558,51 +612,55 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
       for (int cb = 0; cb < NCB; ++cb) acc[qb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
     // centre offset: a dense GEMM on the tile's own rows
     {
-      uint4 bc[4][NCH];
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        const int64_t q = q0 + qb * 16 + r;
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) {
-          bc[qb][ch] = (q < n) ? *reinterpret_cast<const uint4*>(feats + q * CIN + ch * CHUNK + g * VEC)
-                               : make_uint4(0u, 0u, 0u, 0u);
-        }
-      }
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
         uint4 a[NCB];
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) a[cb] = wl[((static_cast<size_t>(centre) * NCB + cb) * NCH + ch) * 64 + lane];
+        for (int cb = 0; cb < NCB; ++cb) a[cb] = wl[((static_cast<size_t>(centre) * NCB + cb) * NCH + ch) * 64 + aslot];
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) mfma_block<T, NCB>(acc[qb], a, bc[qb][ch]);
       }
     }
-    const int cntk = (lane < KV && lane != centre) ? __popcll(tm.mk) : 0;
     for (int s0 = 0; s0 < tm.total; s0 += kStageEntries) {
       const int s1 = (tm.total - s0 < kStageEntries) ? tm.total : s0 + kStageEntries;
-      if (!(first && s0 == 0)) {
-        wave_lds_sync();  // earlier reads of the stage are done
-        gather_stage<T, CIN>(feats, in_idx, tm, s0, s1, centre, KV, lane, stage, slot_pos);
-      }
+      wave_lds_sync();  // earlier reads of the stage are done
+      commit_stage<ROWV>(stage, rows, lane);
       wave_lds_sync();
-      // offsets with entries in [s0, s1), in order, ping-ponging between two
-      // operand sets: the next offset's loads are in flight while the current
-      // one runs on MFMA
-      unsigned long long todo = __ballot(cntk > 0 && tm.basek < s1 && tm.basek + cntk > s0);
-      OffsetOps<NCH, NCB> x, y;
-      int k = todo ? __ffsll(static_cast<long long>(todo)) - 1 : -1;
-      todo &= todo - 1ull;
-      if (k >= 0) load_offset<T, CIN, COUT>(x, wl, stage_g, tm, k, s0, s1, lane);
-      while (k >= 0) {
-        k = todo ? __ffsll(static_cast<long long>(todo)) - 1 : -1;
-        todo &= todo - 1ull;
-        if (k >= 0) load_offset<T, CIN, COUT>(y, wl, stage_g, tm, k, s0, s1, lane);
-        run_offset<T, NCH, NCB>(acc, x);
-        if (k < 0) break;
-        k = todo ? __ffsll(static_cast<long long>(todo)) - 1 : -1;
-        todo &= todo - 1ull;
-        if (k >= 0) load_offset<T, CIN, COUT>(x, wl, stage_g, tm, k, s0, s1, lane);
-        run_offset<T, NCH, NCB>(acc, y);
+      // the next range's rows are loaded while this one runs
+      if (s1 < tm.total) {
+        stage_positions(tm, cntk, s1, lane, pos_next);
+        load_stage_rows<T, CIN>(feats, in_idx, pos_next, rows);
+      }
+      // Per 16-row block, the offsets with entries in [s0, s1), ping-ponging
+      // between two operand sets: the next item's LDS reads are in flight
+      // while the current one runs on MFMA.  The block index is static, so
+      // each block's accumulators stay in place.
+      const int lim = s1 - s0;
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) {
+        const bool mine = lane < KV && lane != centre;
+        const int subv = mine ? static_cast<int>((tm.mk >> (16 * qb)) & 0xffffull) : 0;
+        const unsigned long long below = (qb == 0) ? 0ull : (tm.mk & ((1ull << (16 * qb)) - 1ull));
+        const int lov = tm.basek + static_cast<int>(__popcll(below)) - s0;
+        const int c = __popc(static_cast<uint32_t>(subv));
+        unsigned long long todo = __ballot(c > 0 && lov + c > 0 && lov < lim);
+        if (todo == 0ull) continue;
+        // Items go in pairs; an odd count is padded with an end item, whose
+        // B operand is the zero row (it adds nothing).  One loop exit keeps
+        // the LDS wait counts the same on every path.
+        const int items = __popcll(todo);
+        ItemOps<NCH, NCB> x, y;
+        load_item<T, CIN, COUT>(x, wl, stage_g, next_item(todo, lov, subv), lim, r, below_r, aslot);
+        for (int i = 0; i < items; i += 2) {
+          load_item<T, CIN, COUT>(y, wl, stage_g, next_item(todo, lov, subv), lim, r, below_r, aslot);
+          // keep the scheduler from sinking these reads below the MFMAs
+          // (which would reuse one operand set and wait on every item)
+          __builtin_amdgcn_sched_barrier(0);
+          run_item<T, NCH, NCB>(acc[qb], x);
+          load_item<T, CIN, COUT>(x, wl, stage_g, next_item(todo, lov, subv), lim, r, below_r, aslot);
+          __builtin_amdgcn_sched_barrier(0);
+          run_item<T, NCH, NCB>(acc[qb], y);
+        }
       }
     }
     first = false;
@@ -615,7 +673,6 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
         for (int cb = 0; cb < NCB; ++cb) Elem<T>::store4(out + q * COUT + cb * 16 + 4 * g, acc[qb][cb]);
       }
     }
-    wave_lds_sync();
   }
 }
 
@@ -636,12 +693,17 @@ int device_cu_count() {
 template <typename T, int CIN, int COUT>
 hipError_t launch_small(const ForwardArgs& a, hipStream_t stream) {
   using Sh = SmallShape<T, CIN, COUT>;
-  const size_t lds = Sh::lds_bytes(a.KV);
-  // One workgroup per CU (LDS-bound); a workgroup takes consecutive tiles, so
-  // the rows its waves gather overlap in the CU's and the XCD's caches.
-  const int64_t want = (a.tiles + kSmallWaves - 1) / kSmallWaves;
-  const int64_t cap = device_cu_count();
-  const unsigned grid = static_cast<unsigned>(want < cap ? want : cap);
+  // One workgroup per CU (LDS-bound), with just enough waves for every tile to
+  // have its own wave when the CUs allow it; a workgroup takes consecutive
+  // tiles, so the rows its waves gather overlap in the CU's and the XCD's
+  // caches.
+  const int64_t cus = device_cu_count();
+  int64_t waves = (a.tiles + cus - 1) / cus;
+  if (waves < 1) waves = 1;
+  if (waves > kSmallWaves) waves = kSmallWaves;
+  const size_t lds = Sh::lds_bytes(a.KV, static_cast<int>(waves));
+  const int64_t want = (a.tiles + waves - 1) / waves;
+  const unsigned grid = static_cast<unsigned>(want < cus ? want : cus);
   static bool lds_raised = false;  // raise the dynamic-LDS limit once per instantiation
   if (!lds_raised) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_forward_small<T, CIN, COUT>),
@@ -650,7 +712,7 @@ hipError_t launch_small(const ForwardArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
-  hipLaunchKernelGGL((k_forward_small<T, CIN, COUT>), dim3(grid), dim3(kSmallWaves * 64), lds, stream,
+  hipLaunchKernelGGL((k_forward_small<T, CIN, COUT>), dim3(grid), dim3(static_cast<unsigned>(waves) * 64), lds, stream,
                      static_cast<const T*>(a.feats), static_cast<const T*>(a.weights),
                      static_cast<T*>(a.out), a.in_idx, a.tile_off, a.tile_mask, a.n, a.tiles, a.KV);
   return hipGetLastError();
@@ -662,11 +724,11 @@ hipError_t try_small(const ForwardArgs& a, hipStream_t stream) {
   if (a.KV > 64) return hipErrorNotSupported;
   constexpr size_t kBudget = kSmallLdsCap;
   if constexpr (sizeof(T) == 2) {
-    if (a.cin == 32 && a.cout == 32 && SmallShape<T, 32, 32>::lds_bytes(a.KV) <= kBudget) return launch_small<T, 32, 32>(a, stream);
-    if (a.cin == 32 && a.cout == 16 && SmallShape<T, 32, 16>::lds_bytes(a.KV) <= kBudget) return launch_small<T, 32, 16>(a, stream);
+    if (a.cin == 32 && a.cout == 32 && SmallShape<T, 32, 32>::lds_bytes(a.KV, kSmallWaves) <= kBudget) return launch_small<T, 32, 32>(a, stream);
+    if (a.cin == 32 && a.cout == 16 && SmallShape<T, 32, 16>::lds_bytes(a.KV, kSmallWaves) <= kBudget) return launch_small<T, 32, 16>(a, stream);
   } else {
-    if (a.cin == 16 && a.cout == 16 && SmallShape<T, 16, 16>::lds_bytes(a.KV) <= kBudget) return launch_small<T, 16, 16>(a, stream);
-    if (a.cin == 16 && a.cout == 32 && SmallShape<T, 16, 32>::lds_bytes(a.KV) <= kBudget) return launch_small<T, 16, 32>(a, stream);
+    if (a.cin == 16 && a.cout == 16 && SmallShape<T, 16, 16>::lds_bytes(a.KV, kSmallWaves) <= kBudget) return launch_small<T, 16, 16>(a, stream);
+    if (a.cin == 16 && a.cout == 32 && SmallShape<T, 16, 32>::lds_bytes(a.KV, kSmallWaves) <= kBudget) return launch_small<T, 16, 32>(a, stream);
   }
   return hipErrorNotSupported;
 }

@@ -59,6 +59,20 @@ def test_build_map_host_validation():
     assert sp.STATUS[st] == "SPCONV_ERR_INVALID_ARG"
 
 
+def test_build_map_async_host_validation():
+    """The enqueue-only build rejects the same arguments before any device work."""
+    fake = 4096
+    b = sp.spconv_build_map_async
+    assert _status_of(b, 0, 10, 3, 0) == "SPCONV_ERR_INVALID_ARG"
+    assert _status_of(b, fake + 8, 10, 3, 0) == "SPCONV_ERR_INVALID_ARG"
+    assert _status_of(b, fake, 0, 3, 0) == "SPCONV_ERR_INVALID_ARG"
+    for K in (0, 2, 8):
+        assert _status_of(b, fake, 10, K, 0) == "SPCONV_ERR_UNSUPPORTED"
+    assert _status_of(b, fake, (1 << 31) // 343, 7, 0) == "SPCONV_ERR_INVALID_ARG"
+    st = sp.lib().spconv_build_map_async(fake, 10, 3, 0, None)
+    assert sp.STATUS[st] == "SPCONV_ERR_INVALID_ARG"
+
+
 def test_forward_host_validation():
     fake = 4096
     fake_map = 8192  # never dereferenced on these error paths
@@ -77,6 +91,7 @@ def test_forward_host_validation():
 
 
 def test_map_queries_reject_null():
+    assert _status_of(sp.spconv_map_wait, 0) == "SPCONV_ERR_INVALID_ARG"
     assert _status_of(sp.spconv_map_info, 0) == "SPCONV_ERR_INVALID_ARG"
     assert _status_of(sp.spconv_map_lists, 0) == "SPCONV_ERR_INVALID_ARG"
     assert _status_of(sp.spconv_map_counts, 0, 27) == "SPCONV_ERR_INVALID_ARG"

@@ -148,6 +148,44 @@ def test_map_device_errors(sp):
     assert _gpu_map(sp, ok, 3).total_entries == 4
 
 
+def test_async_build_matches_sync_and_defers_errors(sp):
+    """The enqueue-only build gives the same map; a forward may follow before
+    any host wait; device errors surface at the wait, and the map can still
+    be freed."""
+    c = workloads.permuted(workloads.random_grid(77, 16, 0.2, 2), 77)
+    dc = torch.from_numpy(c).to(DEV)
+    ref = oracle.build_map(c, 3)
+    f = workloads.features(c.shape[0], 32, "f16", 5).to(DEV)
+    w = workloads.weights(3, 32, 32, "f16", 6).to(DEV)
+    m_sync = sp.build_map(dc, 3)
+    out_sync = sp.forward(f, w, m_sync)
+    maps = [sp.build_map(dc, 3, wait=False) for _ in range(3)]
+    outs = [sp.forward(f, w, m) for m in maps]  # enqueued before any wait
+    for m, o in zip(maps, outs):
+        m.wait()
+        assert_map_equal(m, ref)
+        assert torch.equal(o, out_sync)
+        m.free()
+    dup = torch.from_numpy(np.array([[0, 1, 2, 3], [0, 5, 5, 5], [0, 1, 2, 3]], np.int32)).to(DEV)
+    m = sp.build_map(dup, 3, wait=False)
+    with pytest.raises(sp.SpconvError) as e:
+        m.wait()
+    assert e.value.name == "SPCONV_ERR_DUPLICATE_COORD"
+    with pytest.raises(sp.SpconvError):
+        m.counts
+    m.free()
+    bad = torch.from_numpy(np.array([[0, 0, 0, 0], [0, 0, 70000, 0]], np.int32)).to(DEV)
+    m = sp.build_map(bad, 3, wait=False)
+    with pytest.raises(sp.SpconvError) as e:
+        _ = m.total_entries
+    assert e.value.name == "SPCONV_ERR_COORD_RANGE"
+    m.free()
+    # freeing a map whose build has not been waited on is fine too
+    for _ in range(40):
+        sp.build_map(dc, 3, wait=False).free()
+    assert sp.build_map(dc, 3).total_entries == ref.total_entries
+
+
 def test_map_deterministic(sp):
     c = workloads.permuted(workloads.random_grid(99, 30, 0.1, 2), 99)
     a1, b1 = _gpu_lists(_gpu_map(sp, c, 3))
