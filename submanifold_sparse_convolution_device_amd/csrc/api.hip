@@ -167,11 +167,11 @@ spconv_status finish_build(spconv_map* m) {
         m->status = SPCONV_ERR_DEVICE;
         m->error = "internal: hash table probe exceeded its bound";
       } else {
-        m->total = sum[1];
         m->counts.assign(sum + spconv::kSummaryHead, sum + spconv::kSummaryHead + m->KV);
         m->offsets.resize(m->KV + 1);
         m->offsets[0] = 0;
         for (int k = 0; k < m->KV; ++k) m->offsets[k + 1] = m->offsets[k] + m->counts[k];
+        m->total = m->offsets[m->KV];
       }
     }
     release_slot(m->device, m->slot);
@@ -182,12 +182,6 @@ spconv_status finish_build(spconv_map* m) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-int64_t next_pow2(int64_t v) {
-  int64_t p = 1;
-  while (p < v) p <<= 1;
-  return p;
-}
 
 }  // namespace
 
@@ -228,16 +222,7 @@ spconv_status spconv_build_map_async(const int32_t* d_coords, int64_t n, int32_t
   }
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
 
-  spconv::BuildPlan p;
-  p.n = n;
-  p.K = kernel_size;
-  p.KV = KV;
-  p.centre = (KV - 1) / 2;
-  p.mask_words = (KV + 31) / 32;
-  p.tiles = (n + spconv::kTileRows - 1) / spconv::kTileRows;
-  p.chunks = (p.tiles + spconv::kChunkTiles - 1) / spconv::kChunkTiles;
-  p.table_slots = next_pow2(2 * n);
-  if (p.table_slots < 64) p.table_slots = 64;
+  const spconv::BuildPlan p = spconv::make_plan(n, kernel_size);
 
   int device = 0;
   SPCONV_HIP(hipGetDevice(&device), "hipGetDevice");

@@ -12,14 +12,20 @@ namespace spconv {
 // (one ballot per tile and offset), and the forward's workgroup owns whole
 // tiles, so per-tile list ranges are all the forward needs from the map.
 constexpr int kTileRows = 64;
-// Tiles per chunk of the count / compaction grid (one count workgroup of 16
-// waves, one tile each).
-constexpr int kChunkTiles = 16;
-constexpr int kChunkRows = kTileRows * kChunkTiles;
+// Tiles per group of the count / compaction grid (one count workgroup of 16
+// waves, one tile each, per group).  A chunk is `group_tiles` consecutive
+// groups, chosen so that an offset has at most kMaxChunks chunks: each
+// compaction workgroup sums the counts of the chunks before it.
+constexpr int kGroupTiles = 16;
+constexpr int kMaxChunks = 128;
 
-// Coordinate table: open addressing over 64-bit keys, probed in aligned
-// windows of 4 keys (32 bytes); a key's row sits in a parallel array.
-constexpr int kWindowSlots = 4;
+// Coordinate table: open addressing over 16-byte slots (64-bit key, int32 row,
+// flags), probed in aligned windows of 8 slots (128 bytes, one L2 line).  A
+// key first claims its preferred slot (x & 3 in a hash-chosen half of its home
+// window); an EMPTY preferred slot therefore means the key is absent.  The
+// table has at least 4 slots per voxel.
+constexpr int kWindowSlots = 8;
+constexpr int kTableSlotsPerVoxel = 4;
 constexpr uint64_t kEmptyKey = ~0ull;
 
 // Device error flags (bit set in summary[0]).
@@ -28,25 +34,34 @@ constexpr unsigned long long kFlagRange = 2ull;
 constexpr unsigned long long kFlagTableFull = 4ull;
 
 // Layout of the small device summary the host reads once per build:
-//   [0] error flags, [1] total entries E, [2 + k] entries of offset k.
+//   [0] error flags, [1] unused, [2 + k] entries of offset k.
 constexpr int kSummaryHead = 2;
 
 struct BuildPlan {
   int64_t n = 0;
-  int32_t K = 0, KV = 0, centre = 0, mask_words = 0;
+  int32_t K = 0, KV = 0, centre = 0;
   int64_t tiles = 0;        // ceil(n / kTileRows)
-  int64_t chunks = 0;       // ceil(tiles / kChunkTiles)
-  int64_t table_slots = 0;  // power of two >= 2n, >= 64
+  int64_t group_tiles = 0;  // tiles per chunk (a multiple of kGroupTiles)
+  int64_t chunks = 0;       // ceil(tiles / group_tiles) <= kMaxChunks
+  int64_t table_slots = 0;  // power of two >= kTableSlotsPerVoxel n, >= 64
 };
+BuildPlan make_plan(int64_t n, int32_t K);
 
 // Workspace of one build (carved from a single allocation).
+// Neighbour flags of a row: offsets after the centre as bits of
+// pos_words(K) 32-bit words (written by the row's own probe lane), offsets
+// before the centre as bytes in a 16-byte aligned record of neg_bytes(K)
+// (written by the lanes of the neighbours, as mirror entries).
+__host__ __device__ constexpr int pos_words(int K) { return ((K * K * K - 1) / 2 + 31) / 32; }
+__host__ __device__ constexpr int neg_bytes(int K) { return ((K * K * K - 1) / 2 + 15) / 16 * 16; }
+
 struct BuildScratch {
-  unsigned long long* keys = nullptr;  // table_slots
-  int32_t* rows = nullptr;             // table_slots
-  uint32_t* masks = nullptr;        // mask_words x n, word-major
-  int32_t* nbr = nullptr;           // KV x n, offset-major; only entries whose mask bit is set are valid
-  int64_t* chunk_sum = nullptr;     // KV x chunks, then its exclusive scan in place
-  long long* summary = nullptr;     // kSummaryHead + KV
+  ulonglong2* table = nullptr;   // table_slots 16-byte slots: .x key, .y row
+  uint32_t* pos_bits = nullptr;  // n x pos_words(K)
+  uint8_t* neg_flags = nullptr;  // n x neg_bytes(K)
+  int32_t* nbr = nullptr;        // KV x n, offset-major; valid where the flag is set
+  int64_t* chunk_sum = nullptr;  // KV x chunks entry counts
+  long long* summary = nullptr;  // kSummaryHead + KV
 };
 
 size_t build_scratch_bytes(const BuildPlan& p);

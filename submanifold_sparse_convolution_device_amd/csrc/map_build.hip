@@ -8,32 +8,38 @@
 // compute only where an input exists"), so one coordinate table serves both
 // sides (the SparseConvNet blog, section 2, builds one table per side).
 //
-// Coordinate table: open addressing over 64-bit keys (b, z, y, x packed in
-// 16-bit fields), probed in aligned windows of 4 keys (32 bytes) with linear
-// probing over windows; the row of a key sits in a parallel array at the same
-// slot and is read only on a hit.  The home window of a key hashes
-// (b, z, y, x >> 2): the four keys of an aligned run of x share a home window,
-// so the x-neighbours a voxel looks up for one (dz, dy) fall into one or two
-// windows, which a lane keeps in registers between lookups.
+// Coordinate table: open addressing over 16-byte slots (64-bit key with b, z,
+// y, x in 16-bit fields; the row; a "displaced" bit), probed in aligned
+// windows of 8 slots (128 bytes) with linear probing over windows.  The home
+// window of a key hashes (b, z, y, x >> 2), so the four keys of an aligned run
+// of x share a window (in a hash-chosen half), and each key first claims its
+// own slot x & 3 there.  A
+// key that loses its preferred slot marks that slot displaced before going
+// elsewhere.  A lookup therefore settles on the preferred slot alone
+// (the key, EMPTY, or another key in an unmarked slot: absent) except in the
+// few marked slots, where the window is scanned.
 //
 // Pipeline (one stream, six launches, then one read-back of a small summary):
-//   k_init     clear the table, the neighbour bitmasks and the summary
-//   k_insert   one lane per voxel: scan the window, claim the first free slot
-//              with a 64-bit CAS; an equal key raises the duplicate flag
-//   k_probe    one lane per (voxel, (dz, dy) row of the positive half): look up
-//              Q + d for the offsets d > 0 (lexicographic in (dz, dy, dx)) of
-//              that row.  A hit also records the mirror entry (Q, P, -d),
-//              since (P, Q, d) <-> (Q, P, -d) ("Sparse inputs and sparse
-//              convolution", section "A symmetry you can check on the slide"),
-//              so (K^3 - 1) / 2 of the K^3 offsets are probed.  Bits go to
-//              per-row neighbour masks, indices to an offset-major scratch
-//              table.
-//   k_count    one workgroup per 1024-row chunk: per-tile row masks of every
-//              offset (ballots of the mask bits) and per-chunk counts
-//   k_scan     one workgroup: exclusive scan of the (offset, chunk) counts in
-//              offset-major order into list offsets and per-offset totals
-//   k_compact  per (offset, chunk): each entry's place from the scan and the
-//              tile mask; lists come out grouped by offset ("sorted by weight
+//   k_init     clear the table, the negative-half neighbour flags and the
+//              summary
+//   k_claim    one lane per voxel: a plain store of its row claims its
+//              preferred slot (last writer wins)
+//   k_insert   one lane per voxel: the winner writes its key; a loser is a
+//              duplicate of the winner or takes the first unreserved free slot
+//              by CAS (the only atomics of the insert)
+//   k_probe    one lane per voxel: look up Q + d for the (K^3 - 1) / 2
+//              offsets d after the centre (lexicographic in (dz, dy, dx)),
+//              their loads in flight together.  A hit also records the mirror
+//              entry (Q, P, -d), since (P, Q, d) <-> (Q, P, -d) ("Sparse
+//              inputs and sparse convolution", section "A symmetry you can
+//              check on the slide"), so half of the offsets are probed.  Each
+//              (row, offset) cell has one writer, so flags and neighbour rows
+//              are plain stores.
+//   k_count    per 64-row tile and offset, a ballot of the flags is the tile's
+//              row mask; per-chunk counts and per-offset totals
+//   k_compact  per (offset, chunk): the list start from the totals and the
+//              counts of earlier chunks, then each entry's place from the tile
+//              masks; lists come out grouped by offset ("sorted by weight
 //              offset", section "Nine entries become two") and ordered by
 //              output row within an offset.
 // The lists are sized for the bound of K^3 entries per voxel, so nothing on
@@ -60,65 +66,117 @@ __device__ __forceinline__ unsigned long long mix64(unsigned long long h) {
   return h;
 }
 
-// Home window of a key: hash of the key without the two low bits of x.
+// Home window of a key: hash of the key without the two low bits of x, so an
+// aligned run of 4 x values shares it.  The run takes the half of the window
+// chosen by a high hash bit (independent of the window index), and each key
+// its slot x & 3 in that half.
+__device__ __forceinline__ unsigned long long key_hash(unsigned long long key) { return mix64(key >> 2); }
 __device__ __forceinline__ unsigned long long home_window(unsigned long long key,
                                                           unsigned long long window_mask) {
-  return mix64(key >> 2) & window_mask;
+  return key_hash(key) & window_mask;
+}
+__device__ __forceinline__ unsigned long long preferred_slot(unsigned long long key,
+                                                             unsigned long long window_mask) {
+  const unsigned long long h = key_hash(key);
+  return (h & window_mask) * kWindowSlots + ((h >> 60) & 4ull) + (key & 3ull);
 }
 
 __device__ __forceinline__ bool coord_in_range(int v) { return v >= 0 && v < 65536; }
+
+__device__ __forceinline__ bool voxel_in_range(int4 c) {
+  return c.x >= 0 && c.x < 32768 && coord_in_range(c.y) && coord_in_range(c.z) && coord_in_range(c.w);
+}
+
+// Slot fields: .x is the key; the low 32 bits of .y the row, the high 32 bits
+// flags (bit 0: a key was displaced from this slot).  Row and flags are
+// separate words so that neither write can clobber the other.
+constexpr uint32_t kSlotDisplaced = 1u;
+__device__ __forceinline__ uint32_t* slot_row(ulonglong2* s) {
+  return reinterpret_cast<uint32_t*>(&s->y);
+}
+__device__ __forceinline__ uint32_t* slot_flags(ulonglong2* s) {
+  return reinterpret_cast<uint32_t*>(&s->y) + 1;
+}
 
 __device__ __forceinline__ void raise_flag(long long* summary, unsigned long long bit) {
   atomicOr(reinterpret_cast<unsigned long long*>(summary), bit);
 }
 
-__global__ __launch_bounds__(256) void k_init(ulonglong2* keys2, int64_t key_pairs,
-                                              uint32_t* masks, int64_t mask_elems,
-                                              long long* summary, int summary_len) {
+__global__ __launch_bounds__(256) void k_init(ulonglong2* table, int64_t slots, uint32_t* flag_words,
+                                              int64_t nwords, long long* summary, int summary_len) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const ulonglong2 empty = make_ulonglong2(kEmptyKey, kEmptyKey);
-  for (int64_t i = t0; i < key_pairs; i += stride) keys2[i] = empty;
-  for (int64_t i = t0; i < mask_elems; i += stride) masks[i] = 0u;
+  const ulonglong2 empty = make_ulonglong2(kEmptyKey, 0x00000000ffffffffull);  // row -1, no flags
+  for (int64_t i = t0; i < slots; i += stride) table[i] = empty;
+  for (int64_t i = t0; i < nwords; i += stride) flag_words[i] = 0u;
   for (int64_t i = t0; i < summary_len; i += stride) summary[i] = 0;
 }
 
-// One lane per voxel.
+// Insert, phase 1 (one lane per voxel): claim the preferred slot of the home
+// window with a plain store of the row; the last writer wins.
+__global__ __launch_bounds__(256) void k_claim(const int4* __restrict__ coords, int64_t n, ulonglong2* table,
+                                               unsigned long long window_mask) {
+  const int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (v >= n) return;
+  const int4 c = coords[v];
+  if (!voxel_in_range(c)) return;  // reported by phase 2
+  const unsigned long long key = pack_key(c.x, c.y, c.z, c.w);
+  *slot_row(&table[preferred_slot(key, window_mask)]) = static_cast<uint32_t>(v);
+}
+
+__device__ __forceinline__ bool same_voxel(int4 a, int4 b) {
+  return a.x == b.x && a.y == b.y && a.z == b.z && a.w == b.w;
+}
+
+// Insert, phase 2 (one lane per voxel; phase 1 is complete, a kernel
+// boundary).  The winner of a preferred slot writes its key there with a
+// plain store.  A loser whose winner has the same coordinates is a duplicate;
+// otherwise it marks the slot displaced and takes, by CAS, the first slot
+// that no phase-1 winner reserved and no other loser took, in a fixed order
+// (increasing slot index, window after window).  Two losers with one key thus
+// always meet on the slot the first one took, so duplicates are always
+// detected.  Views are read with plain loads; a stale view can only show a
+// slot free that has since been taken (slots are never released), and a
+// failed CAS returns the slot's true key.  Every window is left as soon as it
+// is seen full, so the search visits each window at most once.
 __global__ __launch_bounds__(256) void k_insert(const int4* __restrict__ coords, int64_t n,
-                                                unsigned long long* keys, int32_t* rows,
-                                                unsigned long long window_mask,
+                                                ulonglong2* table, unsigned long long window_mask,
                                                 long long* summary) {
   const int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (v >= n) return;
   const int4 c = coords[v];
-  if (c.x < 0 || c.x >= 32768 || !coord_in_range(c.y) || !coord_in_range(c.z) ||
-      !coord_in_range(c.w)) {
+  if (!voxel_in_range(c)) {
     raise_flag(summary, kFlagRange);
     return;
   }
   const unsigned long long key = pack_key(c.x, c.y, c.z, c.w);
   unsigned long long w = home_window(key, window_mask);
-  // Every window is left for the next one as soon as it is seen full, so the
-  // search visits each window at most once; the bound is reached only by a
-  // table without a free slot, which reports a full table.
+  ulonglong2* pslot = &table[preferred_slot(key, window_mask)];
+  const uint32_t claim = *slot_row(pslot);
+  if (claim == static_cast<uint32_t>(v)) {
+    pslot->x = key;
+    return;
+  }
+  // claim is another voxel's row (phase 1 wrote one for every voxel in range)
+  if (claim < static_cast<uint64_t>(n) && same_voxel(coords[claim], c)) {
+    raise_flag(summary, kFlagDuplicate);
+    return;
+  }
+  *slot_flags(pslot) = kSlotDisplaced;  // every writer stores the same value
   const unsigned long long max_steps = window_mask + 1;
-  // Keys of one aligned x-run share a home window; each first tries its own
-  // slot x & 3 so that neighbours inserted together do not contend.  Any free
-  // slot of the first non-full window is valid for linear probing, since a
-  // lookup scans whole windows and stops at the first one with a free slot.
-  //
-  // The window is read with plain (cacheable) loads.  A stale view can only
-  // show EMPTY where a key already sits, never a wrong key; a failed CAS
-  // returns the slot's true key, which replaces the stale one.  Candidates are
-  // tried in a fixed order (the preferred slot, then increasing slot index),
-  // so two inserters of one key always meet on the slot the first one
-  // claimed and the second sees its key: duplicates are always detected.
-  const int pref = c.w & (kWindowSlots - 1);
   for (unsigned long long step = 0; step < max_steps; ++step) {
-    unsigned long long* win = keys + w * kWindowSlots;
-    const ulonglong2 v01 = reinterpret_cast<const ulonglong2*>(win)[0];
-    const ulonglong2 v23 = reinterpret_cast<const ulonglong2*>(win)[1];
-    unsigned long long view[kWindowSlots] = {v01.x, v01.y, v23.x, v23.y};
+    ulonglong2* win = table + w * kWindowSlots;
+    unsigned long long view[kWindowSlots];
+    bool reserved[kWindowSlots];
+    // A slot reserved by a phase-1 winner holds (or is about to hold) that
+    // winner's key, which differs from ours: equal keys prefer the same slot,
+    // and our own slot's winner was compared above.
+#pragma unroll
+    for (int j = 0; j < kWindowSlots; ++j) {
+      const ulonglong2 e = win[j];
+      view[j] = e.x;
+      reserved[j] = (static_cast<uint32_t>(e.y) != 0xffffffffu);
+    }
     bool moved = false;
     for (int attempt = 0; attempt <= kWindowSlots; ++attempt) {
       bool dup = false;
@@ -126,20 +184,20 @@ __global__ __launch_bounds__(256) void k_insert(const int4* __restrict__ coords,
 #pragma unroll
       for (int j = kWindowSlots - 1; j >= 0; --j) {
         dup |= (view[j] == key);
-        if (view[j] == kEmptyKey) target = j;
+        if (view[j] == kEmptyKey && !reserved[j]) target = j;
       }
       if (dup) {
         raise_flag(summary, kFlagDuplicate);
         return;
       }
-      if (view[pref] == kEmptyKey) target = pref;
       if (target < 0) {  // window full: next window
         moved = true;
         break;
       }
-      const unsigned long long old = atomicCAS(&win[target], kEmptyKey, key);
+      const unsigned long long old =
+          atomicCAS(reinterpret_cast<unsigned long long*>(&win[target]), kEmptyKey, key);
       if (old == kEmptyKey) {
-        rows[w * kWindowSlots + target] = static_cast<int32_t>(v);
+        *slot_row(&win[target]) = static_cast<uint32_t>(v);
         return;
       }
       view[target] = old;  // learn the true key and try again
@@ -149,165 +207,218 @@ __global__ __launch_bounds__(256) void k_insert(const int4* __restrict__ coords,
   raise_flag(summary, kFlagTableFull);
 }
 
-// Row of `key`, or -1.  The window at index `cw` (keys in ck[]) is the one
-// loaded last; it is reused when a search reaches it again.
-__device__ __forceinline__ int64_t find_row(unsigned long long key,
-                                            const unsigned long long* __restrict__ keys,
-                                            const int32_t* __restrict__ rows,
-                                            unsigned long long window_mask,
-                                            unsigned long long& cw, ulonglong2 (&ck)[2],
-                                            bool& overflow) {
+// Row of `key` by scanning windows from its home window, or -1.
+__device__ __forceinline__ int64_t find_row_scan(unsigned long long key, const ulonglong2* __restrict__ table,
+                                 unsigned long long window_mask, bool& overflow) {
   unsigned long long w = home_window(key, window_mask);
   for (unsigned long long step = 0; step <= window_mask; ++step) {
-    if (w != cw) {
-      const ulonglong2* p = reinterpret_cast<const ulonglong2*>(keys + w * kWindowSlots);
-      ck[0] = p[0];
-      ck[1] = p[1];
-      cw = w;
+    const ulonglong2* win = table + w * kWindowSlots;
+    int64_t found = -1;
+    bool empty = false;
+#pragma unroll
+    for (int j = 0; j < kWindowSlots; ++j) {
+      const ulonglong2 e = win[j];
+      if (e.x == key) found = static_cast<int64_t>(static_cast<uint32_t>(e.y));
+      empty |= (e.x == kEmptyKey);
     }
-    const unsigned long long k0 = ck[0].x, k1 = ck[0].y, k2 = ck[1].x, k3 = ck[1].y;
-    int hit = -1;
-    if (k3 == key) hit = 3;
-    if (k2 == key) hit = 2;
-    if (k1 == key) hit = 1;
-    if (k0 == key) hit = 0;
-    if (hit >= 0) return rows[w * kWindowSlots + hit];
-    if (k0 == kEmptyKey || k1 == kEmptyKey || k2 == kEmptyKey || k3 == kEmptyKey) return -1;
+    if (found >= 0) return found;
+    if (empty) return -1;
     w = (w + 1) & window_mask;
   }
   overflow = true;
   return -1;
 }
 
-// Grid: x covers voxels, y = index j of a (dz, dy) row of the positive half,
-// in lexicographic order: j = 0 is (0, 0) (probing dx > 0 only), then (0, 1..r),
-// then (1..r, -r..r).
-__global__ __launch_bounds__(256) void k_probe(const int4* __restrict__ coords, int64_t n, int K,
-                                               int KV, const unsigned long long* __restrict__ keys,
-                                               const int32_t* __restrict__ rows,
-                                               unsigned long long window_mask,
-                                               int32_t* __restrict__ nbr, uint32_t* masks,
-                                               long long* summary) {
+// Offset of index j in the positive half (k = centre + 1 + j) as (dz, dy, dx).
+template <int K>
+__device__ __forceinline__ void positive_offset(int j, int& dz, int& dy, int& dx) {
+  constexpr int R = (K - 1) / 2, centre = (K * K * K - 1) / 2;
+  const int k = centre + 1 + j;
+  dz = k / (K * K) - R;
+  dy = (k / K) % K - R;
+  dx = k % K - R;
+}
+
+// Records the entry (P = p, Q = q, offset k) and its mirror (Q, P, -d).
+template <int K>
+__device__ __forceinline__ void emit_pair(int j, int64_t q, int32_t p, int64_t n, int32_t* __restrict__ nbr,
+                                          uint8_t* __restrict__ neg_flags) {
+  constexpr int KV = K * K * K, centre = (KV - 1) / 2, NB = neg_bytes(K);
+  const int k = centre + 1 + j;
+  const int kneg = centre - 1 - j;  // = KV - 1 - k
+  nbr[static_cast<int64_t>(k) * n + q] = p;
+  nbr[static_cast<int64_t>(kneg) * n + p] = static_cast<int32_t>(q);
+  neg_flags[static_cast<int64_t>(p) * NB + kneg] = 1;
+}
+
+// One lane per voxel Q: the (K^3 - 1) / 2 offsets after the centre, in
+// groups of up to 32.  For a group, every preferred-slot load is issued (in
+// batches of 16) and resolved before any store: vector-memory counters retire
+// in order, so a store issued between loads would make the later loads' waits
+// wait for its write acknowledgement too.  The few lookups that land on a
+// displaced slot are finished afterwards from their whole home windows.
+template <int K>
+__global__ __launch_bounds__(256) void k_probe(const int4* __restrict__ coords, int64_t n,
+                                               const ulonglong2* __restrict__ table,
+                                               unsigned long long window_mask, int32_t* __restrict__ nbr,
+                                               uint32_t* __restrict__ pos_bits,
+                                               uint8_t* __restrict__ neg_flags, long long* summary) {
+  constexpr int KV = K * K * K, centre = (KV - 1) / 2, NPOS = (KV - 1) / 2;
+  constexpr int GROUP = 32, BATCH = 16, PW = pos_words(K);
   const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (q >= n) return;
-  const int r = (K - 1) / 2;
-  const int j = blockIdx.y;
-  int dz, dy;
-  if (j == 0) {
-    dz = 0;
-    dy = 0;
-  } else if (j <= r) {
-    dz = 0;
-    dy = j;
-  } else {
-    dz = 1 + (j - r - 1) / K;
-    dy = (j - r - 1) % K - r;
-  }
-  const int dx_lo = (j == 0) ? 1 : -r;
   const int4 c = coords[q];
-  const int z = c.y + dz, y = c.z + dy;
-  if (!coord_in_range(z) || !coord_in_range(y)) return;  // never wraps
-  unsigned long long cw = ~0ull;
-  ulonglong2 ck[2];
+  const bool ok = voxel_in_range(c);  // a voxel out of range (a reported error) gets no entries
   bool overflow = false;
-  // The offsets of one (dz, dy) row are K consecutive indices, so they span at
-  // most two 32-bit mask words.
-  const int krow = (dz + r) * K * K + (dy + r) * K + r;  // k of (dz, dy, 0)
-  const int w0 = (krow - r) >> 5;
-  uint32_t own0 = 0u, own1 = 0u;
-  for (int dx = dx_lo; dx <= r; ++dx) {
-    const int x = c.w + dx;
-    if (!coord_in_range(x)) continue;
-    const int64_t p = find_row(pack_key(c.x, z, y, x), keys, rows, window_mask, cw, ck, overflow);
-    if (p < 0 || p >= n) continue;  // miss (a claimed slot always holds a row in range)
-    const int kpos = krow + dx;
-    const int kneg = KV - 1 - kpos;
-    nbr[static_cast<int64_t>(kpos) * n + q] = static_cast<int32_t>(p);
-    nbr[static_cast<int64_t>(kneg) * n + p] = static_cast<int32_t>(q);
-    if ((kpos >> 5) == w0) {
-      own0 |= 1u << (kpos & 31);
-    } else {
-      own1 |= 1u << (kpos & 31);
+  uint32_t bits[PW > 0 ? PW : 1];
+#pragma unroll
+  for (int w = 0; w < PW; ++w) bits[w] = 0u;
+#pragma unroll
+  for (int g0 = 0; g0 < NPOS; g0 += GROUP) {
+    int32_t row[GROUP];
+    uint32_t pend = 0u;  // bit i: offset g0 + i needs the window scan
+#pragma unroll
+    for (int b0 = g0; b0 < g0 + GROUP && b0 < NPOS; b0 += BATCH) {
+      unsigned long long key[BATCH];
+      bool valid[BATCH];
+      ulonglong2 slot[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        if (b0 + i < NPOS && b0 + i < g0 + GROUP) {
+          int dz, dy, dx;
+          positive_offset<K>(b0 + i, dz, dy, dx);
+          const int z = c.y + dz, y = c.z + dy, x = c.w + dx;
+          valid[i] = ok && coord_in_range(z) && coord_in_range(y) && coord_in_range(x);
+          key[i] = pack_key(c.x, z, y, x);
+          const unsigned long long s = valid[i] ? preferred_slot(key[i], window_mask) : 0ull;
+          slot[i] = table[s];  // unconditional (slot 0 exists), so the loads batch
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        if (b0 + i < NPOS && b0 + i < g0 + GROUP) {
+          int32_t p = -1;
+          if (valid[i]) {
+            if (slot[i].x == key[i]) {
+              p = static_cast<int32_t>(static_cast<uint32_t>(slot[i].y));
+            } else if (slot[i].x != kEmptyKey &&
+                       ((static_cast<uint32_t>(slot[i].y >> 32) & kSlotDisplaced) != 0u)) {
+              pend |= 1u << (b0 + i - g0);
+            }
+          }
+          row[b0 + i - g0] = (p >= 0 && p < n) ? p : -1;  // a claimed slot holds a row in range
+        }
+      }
     }
-    atomicOr(&masks[static_cast<int64_t>(kneg >> 5) * n + p], 1u << (kneg & 31));
+    // Lookups on displaced slots: up to kPend per lane per round, every home
+    // window loaded before any is scanned (one round covers nearly every wave).
+    while (pend != 0u) {
+      constexpr int kPend = 2;
+      int js[kPend];
+      unsigned long long ks[kPend];
+      ulonglong2 wv[kPend][kWindowSlots];
+#pragma unroll
+      for (int u = 0; u < kPend; ++u) {
+        js[u] = -1;
+        ks[u] = 0ull;
+        if (pend != 0u) {
+          js[u] = g0 + __ffs(pend) - 1;
+          pend &= pend - 1u;
+          int dz, dy, dx;
+          positive_offset<K>(js[u], dz, dy, dx);
+          ks[u] = pack_key(c.x, c.y + dz, c.z + dy, c.w + dx);
+          const ulonglong2* win = table + home_window(ks[u], window_mask) * kWindowSlots;
+#pragma unroll
+          for (int s2 = 0; s2 < kWindowSlots; ++s2) wv[u][s2] = win[s2];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kPend; ++u) {
+        if (js[u] >= 0) {
+          int64_t p = -1;
+          bool empty = false;
+#pragma unroll
+          for (int s2 = 0; s2 < kWindowSlots; ++s2) {
+            if (wv[u][s2].x == ks[u]) p = static_cast<int64_t>(static_cast<uint32_t>(wv[u][s2].y));
+            empty |= (wv[u][s2].x == kEmptyKey);
+          }
+          if (p < 0 && !empty) p = find_row_scan(ks[u], table, window_mask, overflow);  // full window
+          if (p >= 0 && p < n) {
+            const int j = js[u];
+            bits[j >> 5] |= 1u << (j & 31);
+            emit_pair<K>(j, q, static_cast<int32_t>(p), n, nbr, neg_flags);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < GROUP; ++i) {
+      if (g0 + i < NPOS && row[i] >= 0) {
+        const int j = g0 + i;
+        bits[j >> 5] |= 1u << (j & 31);
+        emit_pair<K>(j, q, row[i], n, nbr, neg_flags);
+      }
+    }
   }
-  // Other lanes' mirror bits land in this voxel's words too, hence atomics.
-  if (own0) atomicOr(&masks[static_cast<int64_t>(w0) * n + q], own0);
-  if (own1) atomicOr(&masks[static_cast<int64_t>(w0 + 1) * n + q], own1);
+#pragma unroll
+  for (int w = 0; w < PW; ++w) pos_bits[q * PW + w] = bits[w];
   if (overflow) raise_flag(summary, kFlagTableFull);
 }
 
-// Exclusive scan, in place and in offset-major order, of the KV x chunks
-// counts by one 1024-thread workgroup; totals go to the summary, E to
-// *tile_off_end.
-__device__ void scan_chunk_sums(int64_t* a, int KV, int64_t chunks, long long* summary,
-                                int32_t* tile_off_end, int64_t* part) {
-  constexpr int kT = 1024;
-  const int t = threadIdx.x;
-  const int64_t m = static_cast<int64_t>(KV) * chunks;
-  const int64_t per = (m + kT - 1) / kT;
-  const int64_t b = t * per;
-  const int64_t e = (b + per < m) ? b + per : m;
-  int64_t s = 0;
-  for (int64_t i = b; i < e; ++i) s += a[i];
-  part[t] = s;
-  __syncthreads();
-  for (int off = 1; off < kT; off <<= 1) {
-    const int64_t add = (t >= off) ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += add;
-    __syncthreads();
-  }
-  const int64_t total = part[kT - 1];
-  int64_t base = part[t] - s;
-  for (int64_t i = b; i < e; ++i) {
-    const int64_t val = a[i];
-    a[i] = base;
-    base += val;
-  }
-  __syncthreads();
-  if (t == 0) {
-    summary[1] = total;
-    *tile_off_end = static_cast<int32_t>(total);
-  }
-  for (int k = t; k < KV; k += kT) {
-    const int64_t lo = a[static_cast<int64_t>(k) * chunks];
-    const int64_t hi = (k + 1 < KV) ? a[static_cast<int64_t>(k + 1) * chunks] : total;
-    summary[kSummaryHead + k] = hi - lo;
-  }
-}
-
-// One workgroup of 1024 threads (16 waves) per chunk of kChunkTiles = 16
-// tiles, one tile per wave.  Per tile and offset k, a ballot of mask bit k is
-// the tile's row mask; lane k mod 64 keeps it (slot k / 64), stores it to
-// tile_mask[k][t] and counts it.  Per-chunk counts go to chunk_sum[k][chunk].
+// One workgroup of 1024 threads (16 waves) per chunk of group_tiles tiles,
+// one tile per wave at a time.  Per tile and offset k, a ballot of the row
+// flags is the tile's row mask; lane k mod 64 keeps it (slot k / 64) and
+// stores it to tile_mask[k][t].  Per-chunk counts go to chunk_sum[k][chunk]
+// and are added to the per-offset totals in the summary.
 template <int K>
-__global__ __launch_bounds__(1024) void k_count(const uint32_t* __restrict__ masks, int64_t n,
-                                                int64_t tiles, int64_t chunks,
+__global__ __launch_bounds__(1024) void k_count(const uint32_t* __restrict__ pos_bits,
+                                                const uint8_t* __restrict__ neg_flags, int64_t n,
+                                                int64_t tiles, int64_t group_tiles, int64_t chunks,
                                                 unsigned long long* __restrict__ tile_mask,
-                                                int64_t* chunk_sum) {
+                                                int64_t* __restrict__ chunk_sum, long long* summary) {
   constexpr int KV = K * K * K;
   constexpr int centre = (KV - 1) / 2;
-  constexpr int NS = (KV + 63) / 64;          // offsets per lane
-  constexpr int KW = (KV + 31) / 32;          // mask words per row
+  constexpr int NS = (KV + 63) / 64;  // offsets per lane
+  constexpr int PW = pos_words(K), NB = neg_bytes(K), NV = NB / 16;
   const int64_t chunk = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t t = chunk * kChunkTiles + wave;
-  const int64_t q = t * kTileRows + lane;
-  const bool valid = (t < tiles) && (q < n);
-  unsigned long long mine[NS];
+  int cnt[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) mine[s] = 0ull;
-  if (t < tiles) {
+  for (int s = 0; s < NS; ++s) cnt[s] = 0;
+  for (int64_t g = 0; g < group_tiles; g += kGroupTiles) {
+    const int64_t t = chunk * group_tiles + g + wave;
+    if (t >= tiles) break;  // tiles of later groups are past the end too
+    const int64_t q = t * kTileRows + lane;
+    const bool valid = q < n;
+    const int64_t qs = valid ? q : n - 1;
+    uint32_t pw[PW > 0 ? PW : 1];
+    uint4 nv[NV > 0 ? NV : 1];
 #pragma unroll
-    for (int w = 0; w < KW; ++w) {
-      const uint32_t mw = valid ? masks[static_cast<int64_t>(w) * n + q] : 0u;
+    for (int w = 0; w < PW; ++w) pw[w] = pos_bits[qs * PW + w];
 #pragma unroll
-      for (int bit = 0; bit < 32; ++bit) {
-        const int k = 32 * w + bit;
+    for (int v = 0; v < NV; ++v) nv[v] = *reinterpret_cast<const uint4*>(neg_flags + qs * NB + 16 * v);
+    unsigned long long mine[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) mine[s] = 0ull;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+      for (int jj = 0; jj < 64; ++jj) {
+        const int k = s * 64 + jj;
         if (k < KV) {
-          const unsigned long long bal = __ballot(k == centre ? valid : ((mw >> bit) & 1u) != 0u);
-          if (lane == (k & 63)) mine[k >> 6] = bal;
+          bool f;
+          if (k == centre) {
+            f = true;
+          } else if (k < centre) {
+            const uint4 v = nv[k / 16];
+            const uint32_t word = ((k % 16) / 4 == 0) ? v.x : ((k % 16) / 4 == 1) ? v.y : ((k % 16) / 4 == 2) ? v.z : v.w;
+            f = ((word >> (8 * (k % 4))) & 0xffu) != 0u;
+          } else {
+            const int j = k - centre - 1;
+            f = ((pw[j >> 5] >> (j & 31)) & 1u) != 0u;
+          }
+          const unsigned long long bal = __ballot(valid && f);
+          if (lane == jj) mine[s] = bal;
         }
       }
     }
@@ -315,73 +426,83 @@ __global__ __launch_bounds__(1024) void k_count(const uint32_t* __restrict__ mas
     for (int s = 0; s < NS; ++s) {
       const int k = s * 64 + lane;
       if (k < KV) tile_mask[static_cast<int64_t>(k) * tiles + t] = mine[s];
+      cnt[s] += __popcll(mine[s]);
     }
   }
-  __shared__ int part[kChunkTiles][NS * 64];
+  __shared__ int part[kGroupTiles][NS * 64];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) part[wave][s * 64 + lane] = __popcll(mine[s]);
+  for (int s = 0; s < NS; ++s) part[wave][s * 64 + lane] = cnt[s];
   __syncthreads();
   for (int k = threadIdx.x; k < KV; k += 1024) {
     int sum = 0;
 #pragma unroll
-    for (int w = 0; w < kChunkTiles; ++w) sum += part[w][k];
+    for (int w = 0; w < kGroupTiles; ++w) sum += part[w][k];
     chunk_sum[static_cast<int64_t>(k) * chunks + chunk] = sum;
+    if (sum != 0) {
+      atomicAdd(reinterpret_cast<unsigned long long*>(&summary[kSummaryHead + k]),
+                static_cast<unsigned long long>(sum));
+    }
   }
 }
 
-// One workgroup of 1024 threads scans the chunk counts (a kernel boundary
-// orders it after k_count, which is far cheaper than a device-wide fence on a
-// GPU whose L2 caches are per XCD).
-__global__ __launch_bounds__(1024) void k_scan(int64_t* chunk_sum, int KV, int64_t chunks,
-                                               long long* summary, int32_t* tile_off_end) {
-  __shared__ int64_t scan_part[1024];
-  scan_chunk_sums(chunk_sum, KV, chunks, summary, tile_off_end, scan_part);
-}
-
 // Grid: x = chunk, y = offset k; 256 threads, wave w places the entries of
-// tiles chunk * 16 + 4 w + [0, 4) from their tile masks.  tile_off[k * tiles
-// + t] = first entry of tile t in list k (tile_off[KV * tiles] = E is written
-// by the scan).
+// the quarter w of the chunk's tiles, in tile order.  The workgroup's first
+// list position is the sum of the totals of offsets before k and of the
+// counts of chunks of offset k before this one (k_count has completed: a
+// kernel boundary).  tile_off[k * tiles + t] = first entry of tile t in list
+// k; the last workgroup also writes tile_off[KV * tiles] = E.
 __global__ __launch_bounds__(256) void k_compact(const unsigned long long* __restrict__ tile_mask,
                                                  const int32_t* __restrict__ nbr, int64_t n,
-                                                 int64_t tiles, int centre, int64_t chunks,
-                                                 const int64_t* __restrict__ chunk_base,
+                                                 int64_t tiles, int centre, int KV, int64_t group_tiles,
+                                                 int64_t chunks, const int64_t* __restrict__ chunk_sum,
+                                                 const long long* __restrict__ summary,
                                                  int32_t* __restrict__ in_idx,
                                                  int32_t* __restrict__ out_idx,
                                                  int32_t* __restrict__ tile_off) {
-  constexpr int kTilesPerWave = kChunkTiles / 4;
   const int k = blockIdx.y;
   const int64_t chunk = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool is_centre = (k == centre);
-  // lane i < kTilesPerWave holds the mask of the wave's tile i
-  const int64_t tl = chunk * kChunkTiles + wave * kTilesPerWave + lane;
-  const unsigned long long my_mask =
-      (lane < kTilesPerWave && tl < tiles) ? tile_mask[static_cast<int64_t>(k) * tiles + tl] : 0ull;
-  int wsum = __popcll(my_mask);
+  const int64_t per = group_tiles / 4;  // tiles of this wave
+  const int64_t t0 = chunk * group_tiles + wave * per;
+  __shared__ long long s_base;
+  __shared__ long long s_wave[4];
+  if (wave == 0) {
+    long long s = 0;
+    for (int i = lane; i < k; i += 64) s += summary[kSummaryHead + i];
+    for (int64_t cc = lane; cc < chunk; cc += 64) s += chunk_sum[static_cast<int64_t>(k) * chunks + cc];
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) wsum += __shfl_xor(wsum, d);  // the wave's total
-  __shared__ int part[4];
-  if (lane == 0) part[wave] = wsum;
+    for (int d = 1; d < 64; d <<= 1) s += __shfl_xor(s, d);
+    if (lane == 0) s_base = s;
+  }
+  long long wsum = 0;
+  for (int64_t i = lane; i < per; i += 64) {
+    const int64_t t = t0 + i;
+    if (t < tiles) wsum += __popcll(tile_mask[static_cast<int64_t>(k) * tiles + t]);
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) wsum += __shfl_xor(wsum, d);
+  if (lane == 0) s_wave[wave] = wsum;
   __syncthreads();
-  int64_t base = chunk_base[static_cast<int64_t>(k) * chunks + chunk];
-  for (int w = 0; w < wave; ++w) base += part[w];
+  long long base = s_base;
+  for (int w = 0; w < wave; ++w) base += s_wave[w];
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int32_t* nk = nbr + static_cast<int64_t>(k) * n;
-#pragma unroll
-  for (int i = 0; i < kTilesPerWave; ++i) {
-    const int64_t t = chunk * kChunkTiles + wave * kTilesPerWave + i;
-    if (t < tiles) {
-      const unsigned long long m = __shfl(my_mask, i);
-      if (lane == 0) tile_off[static_cast<int64_t>(k) * tiles + t] = static_cast<int32_t>(base);
-      if ((m >> lane) & 1ull) {
-        const int64_t q = t * kTileRows + lane;
-        const int64_t pos = base + __popcll(m & below);
-        in_idx[pos] = is_centre ? static_cast<int32_t>(q) : nk[q];
-        out_idx[pos] = static_cast<int32_t>(q);
-      }
-      base += __popcll(m);
+  for (int64_t i = 0; i < per; ++i) {
+    const int64_t t = t0 + i;
+    if (t >= tiles) break;
+    const unsigned long long m = tile_mask[static_cast<int64_t>(k) * tiles + t];
+    if (lane == 0) tile_off[static_cast<int64_t>(k) * tiles + t] = static_cast<int32_t>(base);
+    if ((m >> lane) & 1ull) {
+      const int64_t q = t * kTileRows + lane;
+      const int64_t pos = base + __popcll(m & below);
+      in_idx[pos] = is_centre ? static_cast<int32_t>(q) : nk[q];
+      out_idx[pos] = static_cast<int32_t>(q);
     }
+    base += __popcll(m);
+  }
+  if (k == KV - 1 && chunk == chunks - 1 && wave == 3 && lane == 0) {
+    tile_off[static_cast<int64_t>(KV) * tiles] = static_cast<int32_t>(base);
   }
 }
 
@@ -394,13 +515,49 @@ int grid_for(int64_t work, int per_block, int cap) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// The negative-half flag records are cleared (as 32-bit words); the probe
+// writes every row's positive-half bits, and the centre is implicit.
+int64_t negative_flag_words(const BuildPlan& p) {
+  return static_cast<int64_t>(neg_bytes(p.K)) / 4 * p.n;
+}
+
+template <int K>
+void launch_probe_count(const BuildPlan& p, const int4* c4, const BuildScratch& s, const MapBuffers& m,
+                        unsigned long long window_mask, hipStream_t stream) {
+  const unsigned gx = static_cast<unsigned>((p.n + 255) / 256);
+  if (K > 1) {
+    hipLaunchKernelGGL((k_probe<K>), dim3(gx), dim3(256), 0, stream, c4, p.n, s.table, window_mask,
+                       s.nbr, s.pos_bits, s.neg_flags, s.summary);
+  }
+  hipLaunchKernelGGL((k_count<K>), dim3(static_cast<unsigned>(p.chunks)), dim3(1024), 0, stream,
+                     s.pos_bits, s.neg_flags, p.n, p.tiles, p.group_tiles, p.chunks, m.tile_mask,
+                     s.chunk_sum, s.summary);
+}
+
 }  // namespace
+
+BuildPlan make_plan(int64_t n, int32_t K) {
+  BuildPlan p;
+  p.n = n;
+  p.K = K;
+  p.KV = K * K * K;
+  p.centre = (p.KV - 1) / 2;
+  p.tiles = (n + kTileRows - 1) / kTileRows;
+  const int64_t groups = (p.tiles + kGroupTiles - 1) / kGroupTiles;
+  const int64_t groups_per_chunk = (groups + kMaxChunks - 1) / kMaxChunks;
+  p.group_tiles = groups_per_chunk * kGroupTiles;
+  p.chunks = (p.tiles + p.group_tiles - 1) / p.group_tiles;
+  int64_t slots = 64;
+  while (slots < kTableSlotsPerVoxel * n) slots <<= 1;
+  p.table_slots = slots;
+  return p;
+}
 
 size_t build_scratch_bytes(const BuildPlan& p) {
   size_t b = 0;
-  b += align_up(static_cast<size_t>(p.table_slots) * sizeof(unsigned long long), 256);
-  b += align_up(static_cast<size_t>(p.table_slots) * sizeof(int32_t), 256);
-  b += align_up(static_cast<size_t>(p.mask_words) * p.n * sizeof(uint32_t), 256);
+  b += align_up(static_cast<size_t>(p.table_slots) * sizeof(ulonglong2), 256);
+  b += align_up(static_cast<size_t>(pos_words(p.K)) * p.n * sizeof(uint32_t), 256);
+  b += align_up(static_cast<size_t>(neg_bytes(p.K)) * p.n, 256);
   b += align_up(static_cast<size_t>(p.KV) * p.n * sizeof(int32_t), 256);
   b += align_up(static_cast<size_t>(p.KV) * p.chunks * sizeof(int64_t), 256);
   b += align_up(static_cast<size_t>(kSummaryHead + p.KV) * sizeof(long long), 256);
@@ -409,12 +566,12 @@ size_t build_scratch_bytes(const BuildPlan& p) {
 
 void carve_build_scratch(const BuildPlan& p, void* base, BuildScratch* s) {
   char* c = static_cast<char*>(base);
-  s->keys = reinterpret_cast<unsigned long long*>(c);
-  c += align_up(static_cast<size_t>(p.table_slots) * sizeof(unsigned long long), 256);
-  s->rows = reinterpret_cast<int32_t*>(c);
-  c += align_up(static_cast<size_t>(p.table_slots) * sizeof(int32_t), 256);
-  s->masks = reinterpret_cast<uint32_t*>(c);
-  c += align_up(static_cast<size_t>(p.mask_words) * p.n * sizeof(uint32_t), 256);
+  s->table = reinterpret_cast<ulonglong2*>(c);
+  c += align_up(static_cast<size_t>(p.table_slots) * sizeof(ulonglong2), 256);
+  s->pos_bits = reinterpret_cast<uint32_t*>(c);
+  c += align_up(static_cast<size_t>(pos_words(p.K)) * p.n * sizeof(uint32_t), 256);
+  s->neg_flags = reinterpret_cast<uint8_t*>(c);
+  c += align_up(static_cast<size_t>(neg_bytes(p.K)) * p.n, 256);
   s->nbr = reinterpret_cast<int32_t*>(c);
   c += align_up(static_cast<size_t>(p.KV) * p.n * sizeof(int32_t), 256);
   s->chunk_sum = reinterpret_cast<int64_t*>(c);
@@ -444,50 +601,28 @@ void carve_map_buffers(const BuildPlan& p, void* base, MapBuffers* m) {
 
 hipError_t launch_build(const BuildPlan& p, const int32_t* coords, const BuildScratch& s,
                         const MapBuffers& m, hipStream_t stream) {
-  const int64_t mask_elems = static_cast<int64_t>(p.mask_words) * p.n;
-  const int64_t key_pairs = p.table_slots / 2;
-  const int64_t init_work = key_pairs > mask_elems ? key_pairs : mask_elems;
-  hipLaunchKernelGGL(k_init, dim3(grid_for(init_work, 256, 4096)), dim3(256), 0, stream,
-                     reinterpret_cast<ulonglong2*>(s.keys), key_pairs, s.masks, mask_elems,
-                     s.summary, kSummaryHead + p.KV);
+  const int64_t nwords = negative_flag_words(p);
+  const int64_t init_work = p.table_slots > nwords ? p.table_slots : nwords;
+  hipLaunchKernelGGL(k_init, dim3(grid_for(init_work, 256, 4096)), dim3(256), 0, stream, s.table,
+                     p.table_slots, reinterpret_cast<uint32_t*>(s.neg_flags), nwords, s.summary,
+                     kSummaryHead + p.KV);
   const unsigned long long window_mask =
       static_cast<unsigned long long>(p.table_slots / kWindowSlots) - 1ull;
   const int4* c4 = reinterpret_cast<const int4*>(coords);
   const unsigned gx = static_cast<unsigned>((p.n + 255) / 256);
-  hipLaunchKernelGGL(k_insert, dim3(gx), dim3(256), 0, stream, c4, p.n, s.keys, s.rows,
-                     window_mask, s.summary);
-  if (p.K > 1) {
-    const int r = (p.K - 1) / 2;
-    const unsigned rows = static_cast<unsigned>(1 + r + r * p.K);  // (dz, dy) rows with d > 0
-    hipLaunchKernelGGL(k_probe, dim3(gx, rows), dim3(256), 0, stream, c4, p.n, p.K, p.KV, s.keys,
-                       s.rows, window_mask, s.nbr, s.masks, s.summary);
-  }
-  const dim3 gc(static_cast<unsigned>(p.chunks));
+  hipLaunchKernelGGL(k_claim, dim3(gx), dim3(256), 0, stream, c4, p.n, s.table, window_mask);
+  hipLaunchKernelGGL(k_insert, dim3(gx), dim3(256), 0, stream, c4, p.n, s.table, window_mask, s.summary);
   switch (p.K) {
-    case 1:
-      hipLaunchKernelGGL(k_count<1>, gc, dim3(1024), 0, stream, s.masks, p.n, p.tiles, p.chunks,
-                         m.tile_mask, s.chunk_sum);
-      break;
-    case 3:
-      hipLaunchKernelGGL(k_count<3>, gc, dim3(1024), 0, stream, s.masks, p.n, p.tiles, p.chunks,
-                         m.tile_mask, s.chunk_sum);
-      break;
-    case 5:
-      hipLaunchKernelGGL(k_count<5>, gc, dim3(1024), 0, stream, s.masks, p.n, p.tiles, p.chunks,
-                         m.tile_mask, s.chunk_sum);
-      break;
-    case 7:
-      hipLaunchKernelGGL(k_count<7>, gc, dim3(1024), 0, stream, s.masks, p.n, p.tiles, p.chunks,
-                         m.tile_mask, s.chunk_sum);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 1: launch_probe_count<1>(p, c4, s, m, window_mask, stream); break;
+    case 3: launch_probe_count<3>(p, c4, s, m, window_mask, stream); break;
+    case 5: launch_probe_count<5>(p, c4, s, m, window_mask, stream); break;
+    case 7: launch_probe_count<7>(p, c4, s, m, window_mask, stream); break;
+    default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, s.chunk_sum, p.KV, p.chunks,
-                     s.summary, m.tile_off + static_cast<int64_t>(p.KV) * p.tiles);
   hipLaunchKernelGGL(k_compact, dim3(static_cast<unsigned>(p.chunks), static_cast<unsigned>(p.KV)),
-                     dim3(256), 0, stream, m.tile_mask, s.nbr, p.n, p.tiles, p.centre, p.chunks,
-                     s.chunk_sum, m.in_idx, m.out_idx, m.tile_off);
+                     dim3(256), 0, stream, m.tile_mask, s.nbr, p.n, p.tiles, p.centre, p.KV,
+                     p.group_tiles, p.chunks, s.chunk_sum, s.summary, m.in_idx, m.out_idx,
+                     m.tile_off);
   return hipGetLastError();
 }
 
