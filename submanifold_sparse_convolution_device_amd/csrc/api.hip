@@ -366,14 +366,23 @@ spconv_status spconv_forward(const void* d_feats, const void* d_weights, const s
   a.cout = c_out;
   a.dtype = static_cast<int32_t>(dtype);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  if (!spconv::small_supported(a) && spconv::tiled_supported(a)) {
+  const bool wide = !spconv::small_supported(a) && spconv::wide_supported(a);
+  if (wide || (!spconv::small_supported(a) && spconv::tiled_supported(a))) {
     hipMemPool_t pool = nullptr;
     const spconv_status st = pool_for(map->device, &pool);
     if (st != SPCONV_OK) return st;
     void* ws = nullptr;
     hipError_t e = hipMallocFromPoolAsync(&ws, spconv::tiled_workspace_bytes(a), pool, stream);
     if (e != hipSuccess) return hip_fail(e, "forward workspace allocation");
-    e = spconv::launch_forward_tiled(a, ws, stream);
+    if (wide) {
+      e = spconv::launch_prep_weights(a, ws, stream);
+      if (e == hipSuccess) {
+        e = spconv::launch_forward_wide(a, static_cast<const uint4*>(ws), spconv::workspace_zero_row(a, ws),
+                                        stream);
+      }
+    } else {
+      e = spconv::launch_forward_tiled(a, ws, stream);
+    }
     const hipError_t ef = hipFreeAsync(ws, stream);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     if (ef != hipSuccess) return hip_fail(ef, "forward workspace release");

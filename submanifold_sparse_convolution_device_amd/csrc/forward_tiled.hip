@@ -61,8 +61,9 @@ __device__ __forceinline__ floatx4 mfma(uint4 a, uint4 b, floatx4 c) {
 // One thread per (block, lane).
 template <typename T>
 __global__ __launch_bounds__(256) void k_prep_weights(const T* __restrict__ w, uint4* __restrict__ wop,
-                                                      int KV, int cin, int cout) {
+                                                      uint4* __restrict__ zero, int KV, int cin, int cout) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx < 4) zero[idx] = make_uint4(0u, 0u, 0u, 0u);
   const int nch = cin / 32, ncbg = cout / 16;
   const int64_t total = static_cast<int64_t>(KV) * ncbg * nch * 64;
   if (idx >= total) return;
@@ -373,21 +374,36 @@ bool tiled_supported(const ForwardArgs& a) {
   return a.cout % 16 == 0;
 }
 
+// Operand-order weights, then a 64-byte zero row (aligned to 256 bytes).
 size_t tiled_workspace_bytes(const ForwardArgs& a) {
-  return static_cast<size_t>(a.KV) * a.cin * a.cout * 2;
+  return (static_cast<size_t>(a.KV) * a.cin * a.cout * 2 + 255) / 256 * 256 + 256;
 }
 
-hipError_t launch_forward_tiled(const ForwardArgs& a, void* workspace, hipStream_t stream) {
+const uint4* workspace_zero_row(const ForwardArgs& a, const void* workspace) {
+  return reinterpret_cast<const uint4*>(static_cast<const char*>(workspace) +
+                                        (static_cast<size_t>(a.KV) * a.cin * a.cout * 2 + 255) / 256 * 256);
+}
+
+hipError_t launch_prep_weights(const ForwardArgs& a, void* workspace, hipStream_t stream) {
   uint4* wop = static_cast<uint4*>(workspace);
+  uint4* zero = const_cast<uint4*>(workspace_zero_row(a, workspace));
   const int64_t total = static_cast<int64_t>(a.KV) * (a.cout / 16) * (a.cin / 32) * 64;
   const unsigned grid = static_cast<unsigned>((total + 255) / 256);
   if (a.dtype == 1) {
     hipLaunchKernelGGL(k_prep_weights<_Float16>, dim3(grid), dim3(256), 0, stream,
-                       static_cast<const _Float16*>(a.weights), wop, a.KV, a.cin, a.cout);
-    return launch_tiled_typed<_Float16>(a, wop, stream);
+                       static_cast<const _Float16*>(a.weights), wop, zero, a.KV, a.cin, a.cout);
+  } else {
+    hipLaunchKernelGGL(k_prep_weights<__bf16>, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const __bf16*>(a.weights), wop, zero, a.KV, a.cin, a.cout);
   }
-  hipLaunchKernelGGL(k_prep_weights<__bf16>, dim3(grid), dim3(256), 0, stream,
-                     static_cast<const __bf16*>(a.weights), wop, a.KV, a.cin, a.cout);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward_tiled(const ForwardArgs& a, void* workspace, hipStream_t stream) {
+  const hipError_t e = launch_prep_weights(a, workspace, stream);
+  if (e != hipSuccess) return e;
+  const uint4* wop = static_cast<const uint4*>(workspace);
+  if (a.dtype == 1) return launch_tiled_typed<_Float16>(a, wop, stream);
   return launch_tiled_typed<__bf16>(a, wop, stream);
 }
 

@@ -105,6 +105,15 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream);
 bool tiled_supported(const ForwardArgs& a);
 size_t tiled_workspace_bytes(const ForwardArgs& a);
 hipError_t launch_forward_tiled(const ForwardArgs& a, void* workspace, hipStream_t stream);
+// Writes the weights in MFMA operand order and a 64-byte zero row into the
+// workspace (tiled_workspace_bytes(a) bytes).
+hipError_t launch_prep_weights(const ForwardArgs& a, void* workspace, hipStream_t stream);
+const uint4* workspace_zero_row(const ForwardArgs& a, const void* workspace);
+// Wide path (forward_wide.hip): gathered rows staged in LDS, shared by the
+// waves of a 128-row task; uses the prepared workspace.
+bool wide_supported(const ForwardArgs& a);
+hipError_t launch_forward_wide(const ForwardArgs& a, const uint4* wop, const uint4* zero_row,
+                               hipStream_t stream);
 // True when the small-channel kernel (every W_d resident in LDS) serves `a`.
 bool small_supported(const ForwardArgs& a);
 
