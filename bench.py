@@ -39,13 +39,64 @@ ELEM = {"f32": 4, "f16": 2, "bf16": 2}
 
 def algorithmic_forward_bytes(n, e, kv, cin, cout, dtype):
     """Minimum HBM bytes of one forward: each input row read once, each output
-    row written once, the weights once, and the (in, out) int32 index pair of
-    every non-centre entry once."""
+    row written once, the weights once, and the int32 input row index of every
+    non-centre entry once (the output row of an entry is implied by its
+    position in the output-ordered lists)."""
     s = ELEM[dtype]
-    return n * cin * s + n * cout * s + kv * cin * cout * s + 8 * (e - n)
+    return n * cin * s + n * cout * s + kv * cin * cout * s + 4 * (e - n)
 
 
-def cpu_baseline(layer, feats, w, budget_s=10.0, max_passes=5):
+FORWARD_SOURCES = ("forward.hip", "internal.h")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_forward_small_indoor_c32_f16_hbm_traffic.md")
+
+
+def forward_source_digest():
+    """sha256 over the sources of the small-channel forward kernel."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "submanifold_sparse_convolution_device_amd", "csrc")
+    for name in FORWARD_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per forward launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or
+    None when there is none or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            key, _, val = line[2:].partition(": ")
+            fields[key.strip("` ")] = val.strip("` ")
+    try:
+        if fields["forward_source_sha256"] != forward_source_digest():
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, dev, mib=256, reps=5):
+    """A plain device-to-device copy of known size, for scaling the HBM
+    counters: FETCH_SIZE and WRITE_SIZE of this copy should each read `mib`
+    MiB per dispatch."""
+    src = torch.ones(mib * 2**20 // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def cpu_baseline(layer, feats, w, budget_s=12.0, max_passes=200):
     """The oracle, as it stands, on the same workload: map build (ordered-tree
     lookups) plus fp64 forward, single-threaded, repeated until ~budget_s."""
     import oracle
@@ -79,11 +130,14 @@ def main(argv=None):
                     help="workload index 0..4 (default: the indoor scene)")
     ap.add_argument("--layer", type=int, default=0, help="layer of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a 256 MiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
-              "multi-GPU path; see the sharding notes in DESIGN.md", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library has no "
+              "multi-GPU path; the workload would shard by frame, one frame set per GPU",
+              file=sys.stderr)
         return 2
 
     import numpy as np
@@ -94,6 +148,8 @@ def main(argv=None):
 
     sp.lib()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     wl = workloads.make_workload(args.workload)
     layer = wl.layers[args.layer]
     feats_h, w_h = workloads.layer_inputs(layer)
@@ -177,13 +233,14 @@ def main(argv=None):
         "forward_ms": round(fwd_ms, 4),
         "forward_tflops": round(flops / (fwd_ms * 1e-3) / 1e12, 4),
         "roofline": {
-            "kernel": "k_forward (fused gather-MFMA-accumulate)",
+            "kernel": "k_forward_small (fused gather-MFMA-accumulate)" if layer.cin <= 32
+                      else "k_forward_wide / k_forward_tiled (fused gather-MFMA-accumulate)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic() if (args.workload, args.layer) == (DEFAULT_WORKLOAD, 0) else None,
             "algorithmic_bytes_per_launch": int(fwd_bytes),
         },
     }
