@@ -16,11 +16,13 @@
 
 namespace {
 
-// Pinned host slot that receives one build's summary, with the event that
-// marks its arrival.  Slots are reused; a slot released while its copy may
-// still be in flight is reclaimed only once its event has completed.
+// Pinned host slot that receives one build's summary (written by the build's
+// last kernel), with the event that marks its arrival.  Slots are reused; a
+// slot released while its build may still be running is reclaimed only once
+// its event has completed.
 struct SummarySlot {
   long long* host = nullptr;
+  long long* device = nullptr;  // the same memory, as the device addresses it
   hipEvent_t done = nullptr;
 };
 
@@ -104,7 +106,7 @@ constexpr int kSlotsPerBatch = 16;
 
 struct SlotPool {
   std::vector<SummarySlot*> free;
-  std::vector<SummarySlot*> pending;  // released while their copy may be in flight
+  std::vector<SummarySlot*> pending;  // released while their build may still write them
 };
 std::mutex g_slot_mu;
 std::vector<SlotPool> g_slots;
@@ -124,11 +126,16 @@ spconv_status acquire_slot(int device, SummarySlot** out) {
   }
   if (pool.free.empty()) {
     void* p = nullptr;
-    SPCONV_HIP(hipHostMalloc(&p, kSlotBytes * kSlotsPerBatch, hipHostMallocPortable), "hipHostMalloc");
+    SPCONV_HIP(hipHostMalloc(&p, kSlotBytes * kSlotsPerBatch,
+                             hipHostMallocPortable | hipHostMallocMapped | hipHostMallocCoherent),
+               "hipHostMalloc");
     for (int i = 0; i < kSlotsPerBatch; ++i) {
       SummarySlot* slot = new (std::nothrow) SummarySlot;
       if (slot == nullptr) return fail(SPCONV_ERR_OUT_OF_MEMORY, "host allocation");
       slot->host = reinterpret_cast<long long*>(static_cast<char*>(p) + kSlotBytes * i);
+      void* dp = nullptr;
+      SPCONV_HIP(hipHostGetDevicePointer(&dp, slot->host, 0), "hipHostGetDevicePointer");
+      slot->device = static_cast<long long*>(dp);
       SPCONV_HIP(hipEventCreateWithFlags(&slot->done, hipEventDisableTiming), "hipEventCreateWithFlags");
       pool.free.push_back(slot);
     }
@@ -262,11 +269,8 @@ spconv_status spconv_build_map_async(const int32_t* d_coords, int64_t n, int32_t
     return st;
   };
 
-  e = spconv::launch_build(p, d_coords, s, m->buf, stream);
+  e = spconv::launch_build(p, d_coords, s, m->buf, m->slot->device, stream);
   if (e != hipSuccess) return discard(hip_fail(e, "map build launch"));
-  e = hipMemcpyAsync(m->slot->host, s.summary, sizeof(long long) * (spconv::kSummaryHead + KV),
-                     hipMemcpyDeviceToHost, stream);
-  if (e != hipSuccess) return discard(hip_fail(e, "summary read-back"));
   e = hipEventRecord(m->slot->done, stream);
   if (e != hipSuccess) return discard(hip_fail(e, "hipEventRecord"));
   (void)hipFreeAsync(ws, stream);

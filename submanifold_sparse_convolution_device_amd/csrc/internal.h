@@ -77,10 +77,11 @@ struct MapBuffers {
 size_t map_buffer_bytes(const BuildPlan& p);
 void carve_map_buffers(const BuildPlan& p, void* base, MapBuffers* m);
 
-// The whole map build (all asynchronous on `stream`); the summary in the
-// scratch holds the flags, E and the per-offset counts when it completes.
+// The whole map build (all asynchronous on `stream`).  When it completes,
+// host_summary (pinned host memory, kSummaryHead + KV values) holds the flags
+// and the per-offset counts.
 hipError_t launch_build(const BuildPlan& p, const int32_t* coords, const BuildScratch& s,
-                        const MapBuffers& m, hipStream_t stream);
+                        const MapBuffers& m, long long* host_summary, hipStream_t stream);
 
 // Forward launch.  dtype: 0 f32, 1 f16, 2 bf16.
 struct ForwardArgs {

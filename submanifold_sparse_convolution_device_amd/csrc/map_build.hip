@@ -19,7 +19,8 @@
 // (the key, EMPTY, or another key in an unmarked slot: absent) except in the
 // few marked slots, where the window is scanned.
 //
-// Pipeline (one stream, six launches, then one read-back of a small summary):
+// Pipeline (one stream, six launches; the last one also writes the small
+// summary into the host's pinned memory):
 //   k_init     clear the table, the negative-half neighbour flags and the
 //              summary
 //   k_claim    one lane per voxel: a plain store of its row claims its
@@ -79,6 +80,12 @@ __device__ __forceinline__ unsigned long long preferred_slot(unsigned long long 
                                                              unsigned long long window_mask) {
   const unsigned long long h = key_hash(key);
   return (h & window_mask) * kWindowSlots + ((h >> 60) & 4ull) + (key & 3ull);
+}
+
+__device__ __forceinline__ unsigned long long lane_u64(unsigned long long v, int src) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), src));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), src));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
 }
 
 __device__ __forceinline__ bool coord_in_range(int v) { return v >= 0 && v < 65536; }
@@ -458,9 +465,15 @@ __global__ __launch_bounds__(256) void k_compact(const unsigned long long* __res
                                                  const long long* __restrict__ summary,
                                                  int32_t* __restrict__ in_idx,
                                                  int32_t* __restrict__ out_idx,
-                                                 int32_t* __restrict__ tile_off) {
+                                                 int32_t* __restrict__ tile_off,
+                                                 long long* __restrict__ host_summary) {
   const int k = blockIdx.y;
   const int64_t chunk = blockIdx.x;
+  // The summary is final (its writers ran in earlier kernels): the first
+  // workgroup hands it to the host's pinned slot, which saves a copy launch.
+  if (chunk == 0 && k == 0) {
+    for (int i = threadIdx.x; i < kSummaryHead + KV; i += blockDim.x) host_summary[i] = summary[i];
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool is_centre = (k == centre);
   const int64_t per = group_tiles / 4;  // tiles of this wave
@@ -475,10 +488,14 @@ __global__ __launch_bounds__(256) void k_compact(const unsigned long long* __res
     for (int d = 1; d < 64; d <<= 1) s += __shfl_xor(s, d);
     if (lane == 0) s_base = s;
   }
+  // The wave's tiles in rounds of 64, one tile mask per lane: the round's
+  // entry count, then (after the workgroup base is known) each tile's first
+  // position by a wave prefix sum.
+  const int64_t rounds = (per + 63) / 64;
   long long wsum = 0;
-  for (int64_t i = lane; i < per; i += 64) {
-    const int64_t t = t0 + i;
-    if (t < tiles) wsum += __popcll(tile_mask[static_cast<int64_t>(k) * tiles + t]);
+  for (int64_t rd = 0; rd < rounds; ++rd) {
+    const int64_t t = t0 + rd * 64 + lane;
+    if (rd * 64 + lane < per && t < tiles) wsum += __popcll(tile_mask[static_cast<int64_t>(k) * tiles + t]);
   }
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) wsum += __shfl_xor(wsum, d);
@@ -488,18 +505,46 @@ __global__ __launch_bounds__(256) void k_compact(const unsigned long long* __res
   for (int w = 0; w < wave; ++w) base += s_wave[w];
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int32_t* nk = nbr + static_cast<int64_t>(k) * n;
-  for (int64_t i = 0; i < per; ++i) {
-    const int64_t t = t0 + i;
-    if (t >= tiles) break;
-    const unsigned long long m = tile_mask[static_cast<int64_t>(k) * tiles + t];
-    if (lane == 0) tile_off[static_cast<int64_t>(k) * tiles + t] = static_cast<int32_t>(base);
-    if ((m >> lane) & 1ull) {
-      const int64_t q = t * kTileRows + lane;
-      const int64_t pos = base + __popcll(m & below);
-      in_idx[pos] = is_centre ? static_cast<int32_t>(q) : nk[q];
-      out_idx[pos] = static_cast<int32_t>(q);
+  constexpr int kBatch = 8;  // tiles whose neighbour rows are loaded together
+  for (int64_t rd = 0; rd < rounds; ++rd) {
+    const int64_t tr = t0 + rd * 64;
+    const bool have = rd * 64 + lane < per && tr + lane < tiles;
+    const unsigned long long mt = have ? tile_mask[static_cast<int64_t>(k) * tiles + tr + lane] : 0ull;
+    const int ct = __popcll(mt);
+    int incl = ct;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int up = __shfl_up(incl, d);
+      if (lane >= d) incl += up;
     }
-    base += __popcll(m);
+    if (have) tile_off[static_cast<int64_t>(k) * tiles + tr + lane] = static_cast<int32_t>(base + incl - ct);
+    const int nt = static_cast<int>(per - rd * 64 < 64 ? per - rd * 64 : 64);
+    for (int b0 = 0; b0 < nt; b0 += kBatch) {
+      int32_t src[kBatch];
+      if (is_centre) {
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) src[i] = static_cast<int32_t>((tr + b0 + i) * kTileRows + lane);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {  // all loads before any store (clamped rows)
+          const int64_t q = (tr + b0 + i) * kTileRows + lane;
+          src[i] = nk[q < n ? q : n - 1];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (b0 + i < nt) {
+          const unsigned long long m = lane_u64(mt, b0 + i);
+          const long long tb = base + __builtin_amdgcn_readlane(incl - ct, b0 + i);
+          if ((m >> lane) & 1ull) {
+            const int64_t pos = tb + __popcll(m & below);
+            in_idx[pos] = src[i];
+            out_idx[pos] = static_cast<int32_t>((tr + b0 + i) * kTileRows + lane);
+          }
+        }
+      }
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
   }
   if (k == KV - 1 && chunk == chunks - 1 && wave == 3 && lane == 0) {
     tile_off[static_cast<int64_t>(KV) * tiles] = static_cast<int32_t>(base);
@@ -600,7 +645,7 @@ void carve_map_buffers(const BuildPlan& p, void* base, MapBuffers* m) {
 }
 
 hipError_t launch_build(const BuildPlan& p, const int32_t* coords, const BuildScratch& s,
-                        const MapBuffers& m, hipStream_t stream) {
+                        const MapBuffers& m, long long* host_summary, hipStream_t stream) {
   const int64_t nwords = negative_flag_words(p);
   const int64_t init_work = p.table_slots > nwords ? p.table_slots : nwords;
   hipLaunchKernelGGL(k_init, dim3(grid_for(init_work, 256, 4096)), dim3(256), 0, stream, s.table,
@@ -622,7 +667,7 @@ hipError_t launch_build(const BuildPlan& p, const int32_t* coords, const BuildSc
   hipLaunchKernelGGL(k_compact, dim3(static_cast<unsigned>(p.chunks), static_cast<unsigned>(p.KV)),
                      dim3(256), 0, stream, m.tile_mask, s.nbr, p.n, p.tiles, p.centre, p.KV,
                      p.group_tiles, p.chunks, s.chunk_sum, s.summary, m.in_idx, m.out_idx,
-                     m.tile_off);
+                     m.tile_off, host_summary);
   return hipGetLastError();
 }
 
