@@ -63,7 +63,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_prep_weights(const T* __restrict__ w, uint4* __restrict__ wop,
                                                       uint4* __restrict__ zero, int KV, int cin, int cout) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx < 4) zero[idx] = make_uint4(0u, 0u, 0u, 0u);
+  if (idx < 32) zero[idx] = make_uint4(0u, 0u, 0u, 0u);
   const int nch = cin / 32, ncbg = cout / 16;
   const int64_t total = static_cast<int64_t>(KV) * ncbg * nch * 64;
   if (idx >= total) return;
@@ -374,9 +374,9 @@ bool tiled_supported(const ForwardArgs& a) {
   return a.cout % 16 == 0;
 }
 
-// Operand-order weights, then a 64-byte zero row (aligned to 256 bytes).
+// Operand-order weights, then a 512-byte zero row (aligned to 256 bytes).
 size_t tiled_workspace_bytes(const ForwardArgs& a) {
-  return (static_cast<size_t>(a.KV) * a.cin * a.cout * 2 + 255) / 256 * 256 + 256;
+  return (static_cast<size_t>(a.KV) * a.cin * a.cout * 2 + 255) / 256 * 256 + 512;
 }
 
 const uint4* workspace_zero_row(const ForwardArgs& a, const void* workspace) {

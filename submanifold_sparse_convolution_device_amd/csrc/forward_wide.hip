@@ -20,10 +20,10 @@
 //   * each wave keeps its slice of W_d (A operands, from a copy of the weights
 //     in operand order) in registers and applies it to every block present;
 // and the work is software-pipelined: while offset i runs on MFMA, the
-// weights and gathered rows of offset i + 1 are in flight and the row indices
-// of offset i + 2 too.  Every stage issues the same number of loads (unused
-// stages load harmless addresses), so the waits on the asynchronous LDS
-// copies are exact counts.
+// weights and gathered rows of offset i + 1 and the row indices of offset
+// i + 2 are loaded, their load instructions spread between the MFMA groups
+// so that they issue in the matrix core's shadow.  A step begins by waiting
+// for all of them (and, by a barrier, for the other waves' row copies).
 #include "internal.h"
 
 namespace spconv {
@@ -86,13 +86,13 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // The B operands of the eight blocks of one 32-wide ci chunk: eight 16-byte
-// LDS reads at `addr` + j * STRIDE bytes, complete when the asm ends.  Written
-// as asm because the compiler, unable to tell the two stage buffers apart,
-// would otherwise wait for every copy into LDS still in flight before each
-// read, the next offset's included.
+// LDS reads at `addr` + j * STRIDE bytes, left in flight.  Written as asm
+// because the compiler, unable to tell the two stage buffers apart, would
+// otherwise wait for every copy into LDS still in flight before each read,
+// the next offset's included; the asm also keeps it from waiting for the
+// reads themselves before their registers are needed.
 template <int STRIDE>
-__device__ __forceinline__ void read_stage8(uint32_t addr, u32x4& v0, u32x4& v1, u32x4& v2, u32x4& v3,
-                                            u32x4& v4, u32x4& v5, u32x4& v6, u32x4& v7) {
+__device__ __forceinline__ void read_stage8(uint32_t addr, u32x4 (&v)[8]) {
   static_assert(7 * STRIDE < 65536, "ds_read offset range");
   asm volatile(
       "ds_read_b128 %0, %8\n\t"
@@ -102,12 +102,23 @@ __device__ __forceinline__ void read_stage8(uint32_t addr, u32x4& v0, u32x4& v1,
       "ds_read_b128 %4, %8 offset:%12\n\t"
       "ds_read_b128 %5, %8 offset:%13\n\t"
       "ds_read_b128 %6, %8 offset:%14\n\t"
-      "ds_read_b128 %7, %8 offset:%15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(v4), "=&v"(v5), "=&v"(v6), "=&v"(v7)
+      "ds_read_b128 %7, %8 offset:%15"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
       : "v"(addr), "i"(STRIDE), "i"(2 * STRIDE), "i"(3 * STRIDE), "i"(4 * STRIDE), "i"(5 * STRIDE),
         "i"(6 * STRIDE), "i"(7 * STRIDE)
       : "memory");
+}
+
+// Waits until at most N LDS (or scalar-memory) operations are in flight and
+// only then releases v: the registers pass through the asm, so nothing that
+// reads them can be scheduled before the wait.
+template <int N>
+__device__ __forceinline__ void wait_lgkm(u32x4 (&v)[8]) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+               : "i"(N)
+               : "memory");
 }
 
 // s_waitcnt with only a vector-memory count (the other counters unconstrained).
@@ -125,12 +136,30 @@ struct WideShape {
   static constexpr int NCH = CIN / 32;            // 32-wide ci chunks
   static constexpr int NCB = 4;                   // 16-wide column blocks per wave
   static constexpr int BPW = kTaskBlocks / NW;    // blocks staged by each wave
+  // A staged row is SEG 16-byte segments; one copy instruction moves RPI
+  // whole rows (64 lanes x 16 bytes), so a block takes IPB of them.  Whole
+  // rows per instruction matter: the gather's cost follows the number of
+  // distinct rows an instruction touches, not its bytes.
+  static constexpr int SEG = CIN / 8;
+  static constexpr int RPI = 64 / SEG;
+  static constexpr int IPB = 16 / RPI;
+  // Rows sharing one 256-byte LDS bank period.
+  static constexpr int RP = SEG * 16 >= 256 ? 1 : 256 / (SEG * 16);
   static constexpr int LOADS_A = NCB * NCH;       // weight loads per wave and offset
-  static constexpr int LOADS_B = BPW * NCH;       // LDS copies per wave and offset
+  static constexpr int LOADS_B = BPW * IPB;       // LDS copies per wave and offset
   static constexpr int LOADS_I = BPW;             // index loads per wave and offset
-  static constexpr int STAGE = kTaskBlocks * NCH * 64;  // uint4 per B stage
+  static constexpr int BLOCK_BYTES = 16 * SEG * 16;     // one staged 16-row block
+  static constexpr int STAGE = kTaskBlocks * BLOCK_BYTES / 16;  // uint4 per B stage
   static size_t lds_bytes() { return static_cast<size_t>(2) * STAGE * sizeof(uint4); }
 };
+
+// Segment swizzle of staged row i: its 16-byte segment c sits at position
+// c ^ seg_swizzle(i), so that the 16 rows a B-operand read touches at one
+// segment fall on distinct LDS banks.
+template <int SEG, int RP>
+__device__ __forceinline__ int seg_swizzle(int i) {
+  return (i / RP) & ((SEG < 16 ? SEG : 16) - 1);
+}
 
 // Per-offset state the pipeline carries: the offset, and for each of the two
 // tiles its row mask and first list position (wave-uniform).
@@ -148,6 +177,8 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
     int64_t tiles, int64_t tasks, int KV, int cout) {
   using Sh = WideShape<CIN, NW>;
   constexpr int NCH = Sh::NCH, NCB = Sh::NCB, BPW = Sh::BPW, STAGE = Sh::STAGE;
+  constexpr int SEG = Sh::SEG, RPI = Sh::RPI, IPB = Sh::IPB, RP = Sh::RP, BLOCK_BYTES = Sh::BLOCK_BYTES;
+  static_assert(STAGE * 2 * 16 == 2 * kTaskBlocks * BLOCK_BYTES, "stage size");
   extern __shared__ uint4 bstage[];  // [2][kTaskBlocks][NCH][64]
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
@@ -203,51 +234,64 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
     return o;
   };
 
-  // Row indices of this wave's staged blocks (block wave + NW j) at offset o,
-  // lane (g, r) -> row 16 b + r of the task; -1 where there is no entry.  Always
-  // exactly BPW loads (an unused offset or row loads in_idx[0]).
-  auto load_idx = [&](const OffsetRef& o, int32_t (&idx)[BPW]) {
-#pragma unroll
-    for (int j = 0; j < BPW; ++j) {
-      const int b = wave + NW * j;
-      const unsigned long long m = (b < 4) ? o.m0 : o.m1;
-      const int bit = 16 * (b & 3) + r;
-      const bool has = o.k >= 0 && ((m >> bit) & 1ull);
-      const int rank = __popcll(m & ((1ull << bit) - 1ull));
-      const int lo = (b < 4) ? o.lo0 : o.lo1;
-      const int32_t v = in_idx[has ? lo + rank : 0];  // the centre's list holds the row itself
-      // An OR with the "no entry" mask rather than a select on the loaded
-      // value: a select would let the compiler move the load under a branch
-      // and wait for it there.
-      idx[j] = v | (has ? 0 : -1);
-    }
+  // The loads that prepare an offset, one at a time so that they can be
+  // spread through the MFMAs of the offset before (see run).
+  //   Index load j (< BPW): the input row of lane (g, r)'s row 16 b + r of the
+  //     wave's staged block b = wave + NW j at offset o; -1 where there is no
+  //     entry (the load itself is unconditional: in_idx[0] stands in).
+  auto load_idx_one = [&](const OffsetRef& o, int32_t (&idx)[BPW], int j) {
+    const int b = wave + NW * j;
+    const unsigned long long m = (b < 4) ? o.m0 : o.m1;
+    const int bit = 16 * (b & 3) + r;
+    const bool has = o.k >= 0 && ((m >> bit) & 1ull);
+    const int rank = __popcll(m & ((1ull << bit) - 1ull));
+    const int lo = (b < 4) ? o.lo0 : o.lo1;
+    const int32_t v = in_idx[has ? lo + rank : 0];  // the centre's list holds the row itself
+    // An OR with the "no entry" mask rather than a select on the loaded
+    // value: a select would let the compiler move the load under a branch
+    // and wait for it there.
+    idx[j] = v | (has ? 0 : -1);
   };
-  // Copies this wave's blocks of offset o into B stage `buf` (rows without an
-  // entry copy the zero row).  Always exactly BPW x NCH copies.
-  auto stage_b = [&](int buf, const int32_t (&idx)[BPW]) {
+  //   Row copy j (< BPW x IPB): rows [RPI q, RPI q + RPI) of staged block
+  //     jj (q = j % IPB, jj = j / IPB), whole rows, from global memory
+  //     straight into B stage `buf`: lane l copies segment (l % SEG) ^ swizzle
+  //     of row RPI q + l / SEG, whose input row is srow[j] (-1: a zero row).
+  //     A block with no entry at the offset is skipped (its MFMAs are too).
+  //     srow comes from copy_rows, which moves the index of row i from lane
+  //     i of idx (a cross-lane read, done before the MFMAs start, where its
+  //     wait costs nothing).
+  auto copy_rows = [&](const int32_t (&idx)[BPW], int32_t (&srow)[Sh::LOADS_B]) {
 #pragma unroll
-    for (int j = 0; j < BPW; ++j) {
-      const int b = wave + NW * j;
+    for (int j = 0; j < Sh::LOADS_B; ++j) srow[j] = __shfl(idx[j / IPB], RPI * (j % IPB) + lane / SEG);
+    // Settle the cross-lane reads here: their results pass through an asm,
+    // so the wait for them lands before the stage reads start instead of
+    // between them (where it would also wait for those).
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) {
-        const void* src = (idx[j] >= 0)
-                              ? static_cast<const void*>(feats_raw + static_cast<int64_t>(idx[j]) * CIN + ch * 32 + g * 8)
-                              : static_cast<const void*>(zero_row + g);
-        uint4* dst = bstage + ((buf * kTaskBlocks + b) * NCH + ch) * 64;
-        __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
-      }
-    }
+    for (int j = 0; j < Sh::LOADS_B; ++j) asm volatile("" : "+v"(srow[j]));
   };
-  // This wave's slice of W_k in operand order.  Always exactly NCB x NCH loads.
+  auto stage_b_one = [&](const OffsetRef& o, int buf, const int32_t (&srow)[Sh::LOADS_B], int j) {
+    const int jj = j / IPB, q = j % IPB;
+    const int b = wave + NW * jj;
+    const unsigned long long m = (b < 4) ? o.m0 : o.m1;
+    if (((m >> (16 * (b & 3))) & 0xffffull) == 0ull) return;  // wave-uniform
+    const int i = RPI * q + lane / SEG;
+    const int c = (lane % SEG) ^ seg_swizzle<SEG, RP>(i);
+    const int32_t src_row = srow[j];
+    const void* src = (src_row >= 0)
+                          ? static_cast<const void*>(feats_raw + static_cast<int64_t>(src_row) * CIN + c * 8)
+                          : static_cast<const void*>(zero_row + c);
+    uint4* dst = bstage + ((buf * kTaskBlocks + b) * BLOCK_BYTES + q * RPI * SEG * 16) / 16;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+  };
+  //   Weight load j (< NCB x NCH): this wave's slice of W_k in operand order.
   const int ncbg = cout / 16;
-  auto load_a = [&](const OffsetRef& o, uint4 (&a)[NCB][NCH]) {
+  auto load_a_one = [&](const OffsetRef& o, uint4 (&a)[NCB][NCH], int j) {
     const int k = o.k < 0 ? 0 : o.k;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int ch = 0; ch < NCH; ++ch)
-        a[cb][ch] = wop[((static_cast<int64_t>(k) * ncbg + NCB * wave + cb) * NCH + ch) * 64 + lane];
+    const int cb = j / NCH, ch = j % NCH;
+    a[cb][ch] = wop[((static_cast<int64_t>(k) * ncbg + NCB * wave + cb) * NCH + ch) * 64 + lane];
   };
+  constexpr int A = Sh::LOADS_A, B = Sh::LOADS_B, I = Sh::LOADS_I;
+  constexpr int kLoads = A + B + I;
 
   floatx4 acc[kTaskBlocks][NCB];
 #pragma unroll
@@ -256,9 +300,13 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
     for (int cb = 0; cb < NCB; ++cb) acc[b][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   typedef __attribute__((address_space(3))) uint4 lds_uint4;
-  const uint32_t stage_addr =
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_uint4*)bstage)) + 16u * static_cast<uint32_t>(lane);
-  auto run = [&](const OffsetRef& o, int buf, const uint4 (&a)[NCB][NCH]) {
+  const uint32_t stage_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_uint4*)bstage));
+  // MFMAs of offset o from stage `buf` and weights a.  The loads of the next
+  // offset (load(item), items 0 .. kLoads - 1: rows, weights, then the
+  // indices of the offset after) are issued a few at a time between the
+  // MFMA groups of the blocks, where they issue while the matrix core is
+  // busy instead of stalling the wave before the offset starts.
+  auto run = [&](const OffsetRef& o, int buf, const uint4 (&a)[NCB][NCH], auto&& load) {
     uint32_t pm = 0u;  // blocks with at least one entry
 #pragma unroll
     for (int b = 0; b < kTaskBlocks; ++b) {
@@ -266,17 +314,33 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
       if (((m >> (16 * (b & 3))) & 0xffffull) != 0ull) pm |= 1u << b;
     }
     pm = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(pm)));
+    constexpr int kSlots = NCH * kTaskBlocks;
+    // Chunk ch + 1's reads are in flight while chunk ch runs on MFMA; the
+    // wait before a chunk's MFMAs leaves only the newer chunk's eight reads.
+    // Lane (g, r) reads row r, segment 4 ch + g (swizzled) of each block.
+    u32x4 bv[2][kTaskBlocks];
+    const uint32_t base = stage_addr + static_cast<uint32_t>(buf * kTaskBlocks * BLOCK_BYTES + r * SEG * 16);
+    const int swz = seg_swizzle<SEG, RP>(r);
+    auto chunk_addr = [&](int ch) { return base + static_cast<uint32_t>(((4 * ch + g) ^ swz) * 16); };
+    read_stage8<BLOCK_BYTES>(chunk_addr(0), bv[0]);
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-      u32x4 bv[kTaskBlocks];
-      read_stage8<NCH * 1024>(stage_addr + static_cast<uint32_t>((buf * kTaskBlocks * NCH + ch) * 1024), bv[0],
-                              bv[1], bv[2], bv[3], bv[4], bv[5], bv[6], bv[7]);
+      if (ch + 1 < NCH) {
+        read_stage8<BLOCK_BYTES>(chunk_addr(ch + 1), bv[(ch + 1) & 1]);
+        wait_lgkm<kTaskBlocks>(bv[ch & 1]);
+      } else {
+        wait_lgkm<0>(bv[ch & 1]);
+      }
 #pragma unroll
       for (int b = 0; b < kTaskBlocks; ++b) {
         if (pm & (1u << b)) {
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) acc[b][cb] = mfma<T>(a[cb][ch], __builtin_bit_cast(uint4, bv[b]), acc[b][cb]);
+          for (int cb = 0; cb < NCB; ++cb)
+            acc[b][cb] = mfma<T>(a[cb][ch], __builtin_bit_cast(uint4, bv[ch & 1][b]), acc[b][cb]);
         }
+        const int slot = ch * kTaskBlocks + b;
+#pragma unroll
+        for (int it = slot * kLoads / kSlots; it < (slot + 1) * kLoads / kSlots; ++it) load(it);
       }
     }
   };
@@ -287,42 +351,45 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
   OffsetRef o1 = next_ref();
   OffsetRef o2 = next_ref();
   int32_t ix0[BPW], ix1[BPW];
-  load_idx(o0, ix0);
-  load_idx(o1, ix1);
   uint4 ax[NCB][NCH], ay[NCB][NCH];
-  load_a(o0, ax);
-  stage_b(0, ix0);
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) load_idx_one(o0, ix0, j);
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) load_idx_one(o1, ix1, j);
+#pragma unroll
+  for (int j = 0; j < A; ++j) load_a_one(o0, ax, j);
+  int32_t srow[Sh::LOADS_B];
+  copy_rows(ix0, srow);
+#pragma unroll
+  for (int j = 0; j < B; ++j) stage_b_one(o0, 0, srow, j);
 
   // Steady state, two offsets per trip so that the register sets alternate
-  // without copies.  One step: (1) indices of the offset after next (issued
-  // first: the counter retires loads in order, so the next step can wait for
-  // them without waiting for this step's rows), (2) weights and rows of the
-  // next offset, (3) wait for this offset's rows (own copies by count, the
-  // other waves' by barrier), (4) MFMAs, (5) barrier before the next step
-  // overwrites the stage just read.
-  constexpr int A = Sh::LOADS_A, B = Sh::LOADS_B, I = Sh::LOADS_I;
+  // without copies.  One step: wait for every load of the step before (this
+  // offset's rows, weights and the next offset's indices) and for the other
+  // waves' row copies (barrier; it also ends every wave's reads of the stage
+  // the step refills), then run this offset while loading the next.
   while (true) {
-    // ---- offset o0 (weights ax, stage 0; rows of o1 from ix1)
-    // (With copies into LDS in flight the compiler treats the counter as
-    // unordered, so using ix1 here waits for all of the last step's loads:
-    // the rows and weights of o0, needed below anyway.)
-    load_idx(o2, ix0);
-    load_a(o1, ay);
-    stage_b(1, ix1);
-    wait_vm<I + A + B>();
+    // ---- offset o0: weights ax, stage 0; loads rows of o1 (from ix1) into
+    // stage 1, its weights into ay, the indices of o2 into ix0
+    wait_vm<0>();
     lds_barrier();
-    run(o0, 0, ax);
-    lds_barrier();
+    copy_rows(ix1, srow);
+    run(o0, 0, ax, [&](int it) {
+      if (it < B) stage_b_one(o1, 1, srow, it);
+      else if (it < B + A) load_a_one(o1, ay, it - B);
+      else load_idx_one(o2, ix0, it - B - A);
+    });
     if (o1.k < 0) break;
     OffsetRef o3 = next_ref();
-    // ---- offset o1 (weights ay, stage 1; rows of o2 from ix0)
-    load_idx(o3, ix1);
-    load_a(o2, ax);
-    stage_b(0, ix0);
-    wait_vm<I + A + B>();
+    // ---- offset o1: weights ay, stage 1; loads for o2 and the indices of o3
+    wait_vm<0>();
     lds_barrier();
-    run(o1, 1, ay);
-    lds_barrier();
+    copy_rows(ix0, srow);
+    run(o1, 1, ay, [&](int it) {
+      if (it < B) stage_b_one(o2, 0, srow, it);
+      else if (it < B + A) load_a_one(o2, ax, it - B);
+      else load_idx_one(o3, ix1, it - B - A);
+    });
     if (o2.k < 0) break;
     o0 = o2;
     o1 = o3;

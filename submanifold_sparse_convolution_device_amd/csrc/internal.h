@@ -106,7 +106,7 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream);
 bool tiled_supported(const ForwardArgs& a);
 size_t tiled_workspace_bytes(const ForwardArgs& a);
 hipError_t launch_forward_tiled(const ForwardArgs& a, void* workspace, hipStream_t stream);
-// Writes the weights in MFMA operand order and a 64-byte zero row into the
+// Writes the weights in MFMA operand order and a 512-byte zero row into the
 // workspace (tiled_workspace_bytes(a) bytes).
 hipError_t launch_prep_weights(const ForwardArgs& a, void* workspace, hipStream_t stream);
 const uint4* workspace_zero_row(const ForwardArgs& a, const void* workspace);
