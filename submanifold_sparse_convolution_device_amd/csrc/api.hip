@@ -376,14 +376,12 @@ spconv_status spconv_forward(const void* d_feats, const void* d_weights, const s
     const spconv_status st = pool_for(map->device, &pool);
     if (st != SPCONV_OK) return st;
     void* ws = nullptr;
-    hipError_t e = hipMallocFromPoolAsync(&ws, spconv::tiled_workspace_bytes(a), pool, stream);
+    const size_t ws_bytes = wide ? spconv::wide_workspace_bytes(a) : spconv::tiled_workspace_bytes(a);
+    hipError_t e = hipMallocFromPoolAsync(&ws, ws_bytes, pool, stream);
     if (e != hipSuccess) return hip_fail(e, "forward workspace allocation");
     if (wide) {
       e = spconv::launch_prep_weights(a, ws, stream);
-      if (e == hipSuccess) {
-        e = spconv::launch_forward_wide(a, static_cast<const uint4*>(ws), spconv::workspace_zero_row(a, ws),
-                                        stream);
-      }
+      if (e == hipSuccess) e = spconv::launch_forward_wide(a, ws, stream);
     } else {
       e = spconv::launch_forward_tiled(a, ws, stream);
     }

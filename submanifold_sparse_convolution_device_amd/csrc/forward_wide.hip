@@ -1,5 +1,5 @@
 // Forward of a submanifold sparse convolution for wide channel counts
-// (C_in 64 with C_out 64, 128 or 256; C_in 128 with C_out 128 or 256) on
+// (C_in 64, 128 or 256; C_out a multiple of 64, of 32 at C_in = 256) on
 // gfx950.
 //
 // Same computation as the other forward kernels: for every output row Q,
@@ -7,16 +7,17 @@
 // convolution for point clouds", section "The map and the update rule"),
 // accumulated on chip per output row and written once.
 //
-// Work unit: a task of 128 output rows (two 64-row tiles, eight 16-row blocks)
-// and all C_out columns.  The workgroup has C_out / 64 waves; wave w owns
-// columns [64 w, 64 w + 64) of all 128 rows, so its accumulators are
-// 8 blocks x 4 column blocks of MFMA tiles.  The task walks the offsets that
-// occur in its rows.  Per offset d:
-//   * the gathered input rows of the eight blocks (B operands, zero for rows
-//     without a neighbour at d) are copied from global memory straight into
-//     LDS in MFMA operand order (global_load_lds: lane l of a load writes
-//     16 bytes at l x 16), shared by all waves of the task, so each entry's
-//     input row leaves memory once;
+// Work unit: a task of TB 16-row blocks (one or two 64-row tiles) and a
+// group of NW x NCB x 16 output columns.  Wave w of the workgroup owns NCB
+// 16-column blocks of all TB blocks, so its accumulators are TB x NCB MFMA
+// tiles.  Large layers use one column group (every column of a task in one
+// workgroup, so a gathered row is shared by all of them); small ones split
+// the columns and shorten the tasks so that the grid still fills the chip.
+// The task walks the offsets that occur in its rows.  Per offset d:
+//   * the gathered input rows of the task's blocks (B operands, zero for
+//     rows without a neighbour at d) are copied from global memory straight
+//     into LDS (global_load_lds: lane l of a load writes 16 bytes at l x 16),
+//     whole rows per copy, shared by all waves of the workgroup;
 //   * each wave keeps its slice of W_d (A operands, from a copy of the weights
 //     in operand order) in registers and applies it to every block present;
 // and the work is software-pipelined: while offset i runs on MFMA, the
@@ -85,40 +86,56 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// The B operands of the eight blocks of one 32-wide ci chunk: eight 16-byte
-// LDS reads at `addr` + j * STRIDE bytes, left in flight.  Written as asm
+// The B operands of the TB blocks of one 32-wide ci chunk: TB 16-byte LDS
+// reads at `addr` + j * STRIDE bytes, left in flight.  Written as asm
 // because the compiler, unable to tell the two stage buffers apart, would
 // otherwise wait for every copy into LDS still in flight before each read,
 // the next offset's included; the asm also keeps it from waiting for the
 // reads themselves before their registers are needed.
-template <int STRIDE>
-__device__ __forceinline__ void read_stage8(uint32_t addr, u32x4 (&v)[8]) {
-  static_assert(7 * STRIDE < 65536, "ds_read offset range");
-  asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %8 offset:%9\n\t"
-      "ds_read_b128 %2, %8 offset:%10\n\t"
-      "ds_read_b128 %3, %8 offset:%11\n\t"
-      "ds_read_b128 %4, %8 offset:%12\n\t"
-      "ds_read_b128 %5, %8 offset:%13\n\t"
-      "ds_read_b128 %6, %8 offset:%14\n\t"
-      "ds_read_b128 %7, %8 offset:%15"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
-      : "v"(addr), "i"(STRIDE), "i"(2 * STRIDE), "i"(3 * STRIDE), "i"(4 * STRIDE), "i"(5 * STRIDE),
-        "i"(6 * STRIDE), "i"(7 * STRIDE)
-      : "memory");
+template <int TB, int STRIDE>
+__device__ __forceinline__ void read_stage(uint32_t addr, u32x4 (&v)[TB]) {
+  static_assert((TB - 1) * STRIDE < 65536, "ds_read offset range");
+  if constexpr (TB == 8) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:%9\n\t"
+        "ds_read_b128 %2, %8 offset:%10\n\t"
+        "ds_read_b128 %3, %8 offset:%11\n\t"
+        "ds_read_b128 %4, %8 offset:%12\n\t"
+        "ds_read_b128 %5, %8 offset:%13\n\t"
+        "ds_read_b128 %6, %8 offset:%14\n\t"
+        "ds_read_b128 %7, %8 offset:%15"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(addr), "i"(STRIDE), "i"(2 * STRIDE), "i"(3 * STRIDE), "i"(4 * STRIDE), "i"(5 * STRIDE),
+          "i"(6 * STRIDE), "i"(7 * STRIDE)
+        : "memory");
+  } else {
+    static_assert(TB == 4, "tasks of 4 or 8 blocks");
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:%5\n\t"
+        "ds_read_b128 %2, %4 offset:%6\n\t"
+        "ds_read_b128 %3, %4 offset:%7"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(addr), "i"(STRIDE), "i"(2 * STRIDE), "i"(3 * STRIDE)
+        : "memory");
+  }
 }
 
 // Waits until at most N LDS (or scalar-memory) operations are in flight and
 // only then releases v: the registers pass through the asm, so nothing that
 // reads them can be scheduled before the wait.
-template <int N>
-__device__ __forceinline__ void wait_lgkm(u32x4 (&v)[8]) {
+template <int N, int TB>
+__device__ __forceinline__ void wait_lgkm(u32x4 (&v)[TB]) {
   static_assert(N >= 0 && N < 16, "lgkmcnt range");
-  asm volatile("s_waitcnt lgkmcnt(%8)"
-               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
-               : "i"(N)
-               : "memory");
+  if constexpr (TB == 8) {
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+                 : "i"(N)
+                 : "memory");
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]) : "i"(N) : "memory");
+  }
 }
 
 // s_waitcnt with only a vector-memory count (the other counters unconstrained).
@@ -128,14 +145,12 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-constexpr int kTaskBlocks = 8;  // 16-row blocks per task (two tiles)
-constexpr int kTaskRows = 16 * kTaskBlocks;
-
-template <int CIN, int NW>
+template <int CIN, int TB, int NCB, int NW>
 struct WideShape {
   static constexpr int NCH = CIN / 32;            // 32-wide ci chunks
-  static constexpr int NCB = 4;                   // 16-wide column blocks per wave
-  static constexpr int BPW = kTaskBlocks / NW;    // blocks staged by each wave
+  static constexpr int TPT = TB / 4;              // 64-row tiles per task
+  static constexpr int BPW = TB / NW;             // blocks staged by each wave
+  static constexpr int COLS = NW * NCB * 16;      // output columns of a workgroup
   // A staged row is SEG 16-byte segments; one copy instruction moves RPI
   // whole rows (64 lanes x 16 bytes), so a block takes IPB of them.  Whole
   // rows per instruction matter: the gather's cost follows the number of
@@ -148,9 +163,11 @@ struct WideShape {
   static constexpr int LOADS_A = NCB * NCH;       // weight loads per wave and offset
   static constexpr int LOADS_B = BPW * IPB;       // LDS copies per wave and offset
   static constexpr int LOADS_I = BPW;             // index loads per wave and offset
-  static constexpr int BLOCK_BYTES = 16 * SEG * 16;     // one staged 16-row block
-  static constexpr int STAGE = kTaskBlocks * BLOCK_BYTES / 16;  // uint4 per B stage
-  static size_t lds_bytes() { return static_cast<size_t>(2) * STAGE * sizeof(uint4); }
+  static constexpr int BLOCK_BYTES = 16 * SEG * 16;  // one staged 16-row block
+  static constexpr int STAGE_BYTES = TB * BLOCK_BYTES;
+  static size_t lds_bytes() { return static_cast<size_t>(2) * STAGE_BYTES; }
+  static_assert(TB == 4 || TB == 8, "tasks of one or two tiles");
+  static_assert(BPW >= 1 && BPW * NW == TB, "blocks split evenly over the waves");
 };
 
 // Segment swizzle of staged row i: its 16-byte segment c sits at position
@@ -161,37 +178,43 @@ __device__ __forceinline__ int seg_swizzle(int i) {
   return (i / RP) & ((SEG < 16 ? SEG : 16) - 1);
 }
 
-// Per-offset state the pipeline carries: the offset, and for each of the two
-// tiles its row mask and first list position (wave-uniform).
+// Per-offset state the pipeline carries: the offset, and for each of the
+// (up to) two tiles its row mask and first list position (wave-uniform).
 struct OffsetRef {
   int k;
   unsigned long long m0, m1;
   int lo0, lo1;
 };
 
-template <typename T, int CIN, int NW>
+template <typename T, int CIN, int TB, int NCB, int NW>
 __global__ __launch_bounds__(64 * NW) void k_forward_wide(
     const uint16_t* __restrict__ feats_raw, const uint4* __restrict__ wop, T* __restrict__ out,
     const int32_t* __restrict__ in_idx, const int32_t* __restrict__ tile_off,
     const unsigned long long* __restrict__ tile_mask, const uint4* __restrict__ zero_row, int64_t n,
-    int64_t tiles, int64_t tasks, int KV, int cout) {
-  using Sh = WideShape<CIN, NW>;
-  constexpr int NCH = Sh::NCH, NCB = Sh::NCB, BPW = Sh::BPW, STAGE = Sh::STAGE;
+    int64_t tiles, int64_t tasks, int groups, int splits, float* __restrict__ part, int KV, int cout) {
+  using Sh = WideShape<CIN, TB, NCB, NW>;
+  constexpr int NCH = Sh::NCH, BPW = Sh::BPW, TPT = Sh::TPT;
   constexpr int SEG = Sh::SEG, RPI = Sh::RPI, IPB = Sh::IPB, RP = Sh::RP, BLOCK_BYTES = Sh::BLOCK_BYTES;
-  static_assert(STAGE * 2 * 16 == 2 * kTaskBlocks * BLOCK_BYTES, "stage size");
-  extern __shared__ uint4 bstage[];  // [2][kTaskBlocks][NCH][64]
+  extern __shared__ uint4 bstage[];  // [2][TB] staged blocks of 16 rows
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
-  // Consecutive tasks on one XCD (workgroups are dealt to the 8 XCDs in turn),
-  // so that tasks sharing neighbour rows share an L2.  The grid is a multiple
-  // of 8 workgroups, which makes the remapping a permutation of [0, grid).
+  // Consecutive work units on one XCD (workgroups are dealt to the 8 XCDs in
+  // turn), so that units sharing rows share an L2: a task's column groups
+  // are adjacent, and so are neighbouring tasks.  The grid is a multiple of
+  // 8 workgroups, which makes the remapping a permutation of [0, grid).
   const int64_t per_xcd = gridDim.x / 8;
   const int64_t bid = blockIdx.x;
-  const int64_t task = (bid % 8) * per_xcd + bid / 8;
-  if (task >= tasks) return;  // uniform over the workgroup
-  const int64_t t0 = 2 * task, t1 = t0 + 1;
+  const int64_t unit = (bid % 8) * per_xcd + bid / 8;
+  if (unit >= tasks * groups * splits) return;  // uniform over the workgroup
+  // unit = (task x groups + column group) x splits + offset share
+  const int share = static_cast<int>(unit % splits);
+  const int64_t tg = unit / splits;
+  const int64_t task = tg / groups;
+  const int cg = static_cast<int>(tg - task * groups);
+  const int64_t t0 = TPT * task, t1 = t0 + 1;
   const int64_t q0 = t0 * kTileRows;
+  const int col0 = cg * Sh::COLS + wave * NCB * 16;  // this wave's first output column
 
   // Task metadata: lane k (and k - 64) holds offset k's masks and list starts.
   unsigned long long mA0 = 0ull, mA1 = 0ull, mB0 = 0ull, mB1 = 0ull;
@@ -199,7 +222,7 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
   if (lane < KV) {
     mA0 = tile_mask[static_cast<int64_t>(lane) * tiles + t0];
     lA0 = tile_off[static_cast<int64_t>(lane) * tiles + t0];
-    if (t1 < tiles) {
+    if (TPT == 2 && t1 < tiles) {
       mA1 = tile_mask[static_cast<int64_t>(lane) * tiles + t1];
       lA1 = tile_off[static_cast<int64_t>(lane) * tiles + t1];
     }
@@ -207,22 +230,31 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
   if (lane + 64 < KV) {
     mB0 = tile_mask[static_cast<int64_t>(lane + 64) * tiles + t0];
     lB0 = tile_off[static_cast<int64_t>(lane + 64) * tiles + t0];
-    if (t1 < tiles) {
+    if (TPT == 2 && t1 < tiles) {
       mB1 = tile_mask[static_cast<int64_t>(lane + 64) * tiles + t1];
       lB1 = tile_off[static_cast<int64_t>(lane + 64) * tiles + t1];
     }
   }
   unsigned long long todo0 = __ballot((mA0 | mA1) != 0ull), todo1 = __ballot((mB0 | mB1) != 0ull);
+  // With splits > 1 the task's offsets are dealt round-robin over the
+  // splits workgroups of the unit, each summing its share into its own fp32
+  // partial output; offsets of other shares are skipped here.
+  // (splits is a power of two.)
+  int seen = 0;
+  const int share_u = __builtin_amdgcn_readfirstlane(share);
+  const int smask = __builtin_amdgcn_readfirstlane(splits - 1);
+  auto pick = [&](unsigned long long& todo, int base) -> int {
+    while (todo != 0ull) {
+      const int kk = base + __ffsll(static_cast<long long>(todo)) - 1;
+      todo &= todo - 1ull;
+      if ((seen++ & smask) == share_u) return kk;
+    }
+    return -1;
+  };
   auto next_ref = [&]() -> OffsetRef {
     OffsetRef o{-1, 0ull, 0ull, 0, 0};
-    int k = -1;
-    if (todo0) {
-      k = __ffsll(static_cast<long long>(todo0)) - 1;
-      todo0 &= todo0 - 1ull;
-    } else if (todo1) {
-      k = 64 + __ffsll(static_cast<long long>(todo1)) - 1;
-      todo1 &= todo1 - 1ull;
-    }
+    int k = pick(todo0, 0);
+    if (k < 0) k = pick(todo1, 64);
     if (k >= 0) {
       const int s = k & 63;
       o.k = k;
@@ -232,6 +264,11 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
       o.lo1 = lane_i32(k < 64 ? lA1 : lB1, s);
     }
     return o;
+  };
+  // Row mask of block b (16 bits) at offset o.
+  auto block_bits = [&](const OffsetRef& o, int b) -> unsigned long long {
+    const unsigned long long m = (b < 4) ? o.m0 : o.m1;
+    return (m >> (16 * (b & 3))) & 0xffffull;
   };
 
   // The loads that prepare an offset, one at a time so that they can be
@@ -272,30 +309,30 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
   auto stage_b_one = [&](const OffsetRef& o, int buf, const int32_t (&srow)[Sh::LOADS_B], int j) {
     const int jj = j / IPB, q = j % IPB;
     const int b = wave + NW * jj;
-    const unsigned long long m = (b < 4) ? o.m0 : o.m1;
-    if (((m >> (16 * (b & 3))) & 0xffffull) == 0ull) return;  // wave-uniform
+    if (block_bits(o, b) == 0ull) return;  // wave-uniform
     const int i = RPI * q + lane / SEG;
     const int c = (lane % SEG) ^ seg_swizzle<SEG, RP>(i);
     const int32_t src_row = srow[j];
     const void* src = (src_row >= 0)
                           ? static_cast<const void*>(feats_raw + static_cast<int64_t>(src_row) * CIN + c * 8)
                           : static_cast<const void*>(zero_row + c);
-    uint4* dst = bstage + ((buf * kTaskBlocks + b) * BLOCK_BYTES + q * RPI * SEG * 16) / 16;
+    uint4* dst = bstage + ((buf * TB + b) * BLOCK_BYTES + q * RPI * SEG * 16) / 16;
     __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
   };
   //   Weight load j (< NCB x NCH): this wave's slice of W_k in operand order.
   const int ncbg = cout / 16;
+  const int cb0 = col0 / 16;
   auto load_a_one = [&](const OffsetRef& o, uint4 (&a)[NCB][NCH], int j) {
     const int k = o.k < 0 ? 0 : o.k;
     const int cb = j / NCH, ch = j % NCH;
-    a[cb][ch] = wop[((static_cast<int64_t>(k) * ncbg + NCB * wave + cb) * NCH + ch) * 64 + lane];
+    a[cb][ch] = wop[((static_cast<int64_t>(k) * ncbg + cb0 + cb) * NCH + ch) * 64 + lane];
   };
   constexpr int A = Sh::LOADS_A, B = Sh::LOADS_B, I = Sh::LOADS_I;
   constexpr int kLoads = A + B + I;
 
-  floatx4 acc[kTaskBlocks][NCB];
+  floatx4 acc[TB][NCB];
 #pragma unroll
-  for (int b = 0; b < kTaskBlocks; ++b)
+  for (int b = 0; b < TB; ++b)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[b][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
@@ -309,36 +346,34 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
   auto run = [&](const OffsetRef& o, int buf, const uint4 (&a)[NCB][NCH], auto&& load) {
     uint32_t pm = 0u;  // blocks with at least one entry
 #pragma unroll
-    for (int b = 0; b < kTaskBlocks; ++b) {
-      const unsigned long long m = (b < 4) ? o.m0 : o.m1;
-      if (((m >> (16 * (b & 3))) & 0xffffull) != 0ull) pm |= 1u << b;
-    }
+    for (int b = 0; b < TB; ++b)
+      if (block_bits(o, b) != 0ull) pm |= 1u << b;
     pm = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(pm)));
-    constexpr int kSlots = NCH * kTaskBlocks;
-    // Chunk ch + 1's reads are in flight while chunk ch runs on MFMA; the
-    // wait before a chunk's MFMAs leaves only the newer chunk's eight reads.
-    // Lane (g, r) reads row r, segment 4 ch + g (swizzled) of each block.
-    u32x4 bv[2][kTaskBlocks];
-    const uint32_t base = stage_addr + static_cast<uint32_t>(buf * kTaskBlocks * BLOCK_BYTES + r * SEG * 16);
+    constexpr int kSlots = NCH * TB;
+    // Lane (g, r) reads row r, segment 4 ch + g (swizzled) of each block;
+    // chunk ch + 1's reads are in flight while chunk ch runs on MFMA, the
+    // wait before a chunk's MFMAs leaving only the newer chunk's reads.
+    u32x4 bv[2][TB];
+    const uint32_t base = stage_addr + static_cast<uint32_t>(buf * TB * BLOCK_BYTES + r * SEG * 16);
     const int swz = seg_swizzle<SEG, RP>(r);
     auto chunk_addr = [&](int ch) { return base + static_cast<uint32_t>(((4 * ch + g) ^ swz) * 16); };
-    read_stage8<BLOCK_BYTES>(chunk_addr(0), bv[0]);
+    read_stage<TB, BLOCK_BYTES>(chunk_addr(0), bv[0]);
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       if (ch + 1 < NCH) {
-        read_stage8<BLOCK_BYTES>(chunk_addr(ch + 1), bv[(ch + 1) & 1]);
-        wait_lgkm<kTaskBlocks>(bv[ch & 1]);
+        read_stage<TB, BLOCK_BYTES>(chunk_addr(ch + 1), bv[(ch + 1) & 1]);
+        wait_lgkm<TB, TB>(bv[ch & 1]);
       } else {
-        wait_lgkm<0>(bv[ch & 1]);
+        wait_lgkm<0, TB>(bv[ch & 1]);
       }
 #pragma unroll
-      for (int b = 0; b < kTaskBlocks; ++b) {
+      for (int b = 0; b < TB; ++b) {
         if (pm & (1u << b)) {
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb)
             acc[b][cb] = mfma<T>(a[cb][ch], __builtin_bit_cast(uint4, bv[ch & 1][b]), acc[b][cb]);
         }
-        const int slot = ch * kTaskBlocks + b;
+        const int slot = ch * TB + b;
 #pragma unroll
         for (int it = slot * kLoads / kSlots; it < (slot + 1) * kLoads / kSlots; ++it) load(it);
       }
@@ -398,64 +433,163 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
   wait_vm<0>();  // no copy into LDS may be left in flight at exit
 
   // Epilogue: D element (row 4 g + i, column r) of block (b, cb) is output
-  // column 64 wave + 16 cb + 4 g + i of row q0 + 16 b + r.
+  // column col0 + 16 cb + 4 g + i of row q0 + 16 b + r; a share of split
+  // offsets writes its fp32 partial sums instead (k_reduce_splits rounds).
+  float* pout = part + static_cast<int64_t>(share) * n * cout;
 #pragma unroll
-  for (int b = 0; b < kTaskBlocks; ++b) {
+  for (int b = 0; b < TB; ++b) {
     const int64_t q = q0 + 16 * b + r;
     if (q < n) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) store4<T>(out + q * cout + 64 * wave + 16 * cb + 4 * g, acc[b][cb]);
+      for (int cb = 0; cb < NCB; ++cb) {
+        if (splits == 1) {
+          store4<T>(out + q * cout + col0 + 16 * cb + 4 * g, acc[b][cb]);
+        } else {
+          *reinterpret_cast<floatx4*>(pout + q * cout + col0 + 16 * cb + 4 * g) = acc[b][cb];
+        }
+      }
     }
   }
 }
 
-template <typename T, int CIN, int NW>
-hipError_t launch_wide_shape(const ForwardArgs& a, const uint4* wop, const uint4* zero_row, hipStream_t stream) {
-  using Sh = WideShape<CIN, NW>;
-  const int64_t tasks = (a.tiles + 1) / 2;
+// Sum of the splits fp32 partial outputs, rounded to the output type (each
+// thread four consecutive values).
+template <typename T>
+__global__ __launch_bounds__(256) void k_reduce_splits(const float* __restrict__ part, T* __restrict__ out,
+                                                       int64_t count4, int64_t stride, int splits) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= count4) return;
+  floatx4 s = reinterpret_cast<const floatx4*>(part)[i];
+  for (int p = 1; p < splits; ++p) s += reinterpret_cast<const floatx4*>(part + p * stride)[i];
+  store4<T>(out + 4 * i, s);
+}
+
+template <typename T, int CIN, int TB, int NCB, int NW>
+hipError_t launch_wide_shape(const ForwardArgs& a, int splits, const uint4* wop, const uint4* zero_row,
+                             float* part, hipStream_t stream) {
+  using Sh = WideShape<CIN, TB, NCB, NW>;
+  const int64_t tasks = (a.tiles + Sh::TPT - 1) / Sh::TPT;
+  const int groups = a.cout / Sh::COLS;
   static bool raised = false;
   if (!raised) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_forward_wide<T, CIN, NW>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_forward_wide<T, CIN, TB, NCB, NW>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              static_cast<int>(Sh::lds_bytes()));
     if (e != hipSuccess) return e;
     raised = true;
   }
-  const int64_t grid = (tasks + 7) / 8 * 8;
-  hipLaunchKernelGGL((k_forward_wide<T, CIN, NW>), dim3(static_cast<unsigned>(grid)), dim3(64 * NW),
+  const int64_t grid = (tasks * groups * splits + 7) / 8 * 8;
+  hipLaunchKernelGGL((k_forward_wide<T, CIN, TB, NCB, NW>), dim3(static_cast<unsigned>(grid)), dim3(64 * NW),
                      Sh::lds_bytes(), stream, static_cast<const uint16_t*>(a.feats), wop, static_cast<T*>(a.out),
-                     a.in_idx, a.tile_off, a.tile_mask, zero_row, a.n, a.tiles, tasks, a.KV, a.cout);
+                     a.in_idx, a.tile_off, a.tile_mask, zero_row, a.n, a.tiles, tasks, groups, splits, part, a.KV,
+                     a.cout);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t count4 = a.n * a.cout / 4;
+  hipLaunchKernelGGL(k_reduce_splits<T>, dim3(static_cast<unsigned>((count4 + 255) / 256)), dim3(256), 0, stream,
+                     part, static_cast<T*>(a.out), count4, a.n * a.cout, splits);
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_wide_typed(const ForwardArgs& a, const uint4* wop, const uint4* zero_row, hipStream_t stream) {
-  const int nw = a.cout / 64;
-  if (a.cin == 64) {
-    if (nw == 1) return launch_wide_shape<T, 64, 1>(a, wop, zero_row, stream);
-    if (nw == 2) return launch_wide_shape<T, 64, 2>(a, wop, zero_row, stream);
-    return launch_wide_shape<T, 64, 4>(a, wop, zero_row, stream);
+// The compiled shapes: (C_in, task blocks, column blocks per wave, waves).
+// Tasks are one tile (TB = 4): measured against two-tile tasks, which halve
+// the weight traffic per row, the smaller register and LDS footprint (two
+// waves per SIMD) wins on every workload here.  Column blocks per wave are 4
+// (64 columns) up to C_in = 128 and 2 at 256, where a wave's
+// double-buffered weight slice would not fit otherwise.
+struct WideChoice {
+  int tb, ncb, nw, splits;
+};
+
+int wide_ncb(int cin) { return cin <= 128 ? 4 : 2; }
+constexpr int kMaxSplits = 8;
+
+bool wide_compiled(int cin, int tb, int nw) {
+  if (nw != 1 && nw != 2 && nw != 4) return false;
+  return tb == 4 && (cin == 64 || cin == 128 || cin == 256);
+}
+
+int wide_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    cus = (hipGetDevice(&dev) == hipSuccess &&
+           hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+              ? v
+              : 256;
   }
-  if (nw == 2) return launch_wide_shape<T, 128, 2>(a, wop, zero_row, stream);
-  return launch_wide_shape<T, 128, 4>(a, wop, zero_row, stream);
+  return cus;
+}
+
+// Largest workgroups (every column of a task in one, up to 4 waves), unless
+// the grid would leave CUs idle: then the offsets of a task split over up to
+// kMaxSplits workgroups (fp32 partials, one reduction; no input row is read
+// twice), and only then narrower workgroups (more column groups, each
+// gathering the task's rows again).
+bool choose_wide(const ForwardArgs& a, WideChoice* out) {
+  const int ncb = wide_ncb(a.cin);
+  const int per_wave = 16 * ncb;
+  if (a.cout % per_wave != 0) return false;
+  const int waves_total = a.cout / per_wave;
+  int nw = 4;
+  while (nw > 1 && waves_total % nw != 0) nw /= 2;
+  const int64_t want = 2 * static_cast<int64_t>(wide_cus());
+  auto units = [&](int tb, int w) { return (a.tiles + tb / 4 - 1) / (tb / 4) * (a.cout / (per_wave * w)); };
+  const int tb = 4;
+  if (!wide_compiled(a.cin, tb, nw)) return false;
+  // Splits cost a pass over fp32 partials: only for grids under one
+  // workgroup per CU.
+  int splits = 1;
+  if (units(tb, nw) < want / 2) {
+    while (splits < kMaxSplits && units(tb, nw) * splits < want && 2 * splits <= a.KV) splits *= 2;
+  }
+  while (nw > 1 && units(tb, nw) * splits < want && wide_compiled(a.cin, tb, nw / 2)) nw /= 2;
+  *out = WideChoice{tb, ncb, nw, splits};
+  return true;
+}
+
+template <typename T, int CIN, int NCB>
+hipError_t launch_wide_cin(const ForwardArgs& a, const WideChoice& c, const uint4* wop, const uint4* zero_row,
+                           float* part, hipStream_t stream) {
+  if (c.tb != 4) return hipErrorNotSupported;
+  if (c.nw == 4) return launch_wide_shape<T, CIN, 4, NCB, 4>(a, c.splits, wop, zero_row, part, stream);
+  if (c.nw == 2) return launch_wide_shape<T, CIN, 4, NCB, 2>(a, c.splits, wop, zero_row, part, stream);
+  return launch_wide_shape<T, CIN, 4, NCB, 1>(a, c.splits, wop, zero_row, part, stream);
+}
+
+template <typename T>
+hipError_t launch_wide_typed(const ForwardArgs& a, const WideChoice& c, const uint4* wop, const uint4* zero_row,
+                             float* part, hipStream_t stream) {
+  if (a.cin == 64) return launch_wide_cin<T, 64, 4>(a, c, wop, zero_row, part, stream);
+  if (a.cin == 128) return launch_wide_cin<T, 128, 4>(a, c, wop, zero_row, part, stream);
+  return launch_wide_cin<T, 256, 2>(a, c, wop, zero_row, part, stream);
 }
 
 }  // namespace
 
-// Shapes whose per-offset load counts fit the 6-bit vector-memory counter
-// and whose double-buffered weights fit the registers.
 bool wide_supported(const ForwardArgs& a) {
   if (a.dtype != 1 && a.dtype != 2) return false;
   if (a.KV > 128) return false;
-  if (a.cin == 64) return a.cout == 64 || a.cout == 128 || a.cout == 256;
-  if (a.cin == 128) return a.cout == 128 || a.cout == 256;
-  return false;
+  if (a.cin != 64 && a.cin != 128 && a.cin != 256) return false;
+  WideChoice c;
+  return choose_wide(a, &c);
 }
 
-hipError_t launch_forward_wide(const ForwardArgs& a, const uint4* wop, const uint4* zero_row,
-                               hipStream_t stream) {
-  if (a.dtype == 1) return launch_wide_typed<_Float16>(a, wop, zero_row, stream);
-  return launch_wide_typed<__bf16>(a, wop, zero_row, stream);
+size_t wide_workspace_bytes(const ForwardArgs& a) {
+  WideChoice c;
+  const size_t base = tiled_workspace_bytes(a);
+  if (!choose_wide(a, &c) || c.splits == 1) return base;
+  return base + static_cast<size_t>(c.splits) * a.n * a.cout * sizeof(float);
+}
+
+hipError_t launch_forward_wide(const ForwardArgs& a, void* workspace, hipStream_t stream) {
+  WideChoice c;
+  if (!choose_wide(a, &c)) return hipErrorNotSupported;
+  const uint4* wop = static_cast<const uint4*>(workspace);
+  const uint4* zero_row = workspace_zero_row(a, workspace);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + tiled_workspace_bytes(a));
+  if (a.dtype == 1) return launch_wide_typed<_Float16>(a, c, wop, zero_row, part, stream);
+  return launch_wide_typed<__bf16>(a, c, wop, zero_row, part, stream);
 }
 
 }  // namespace spconv

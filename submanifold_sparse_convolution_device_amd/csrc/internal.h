@@ -111,10 +111,12 @@ hipError_t launch_forward_tiled(const ForwardArgs& a, void* workspace, hipStream
 hipError_t launch_prep_weights(const ForwardArgs& a, void* workspace, hipStream_t stream);
 const uint4* workspace_zero_row(const ForwardArgs& a, const void* workspace);
 // Wide path (forward_wide.hip): gathered rows staged in LDS, shared by the
-// waves of a 128-row task; uses the prepared workspace.
+// waves of a workgroup.  Its workspace (wide_workspace_bytes(a) bytes) starts
+// with the prepared weights and zero row (launch_prep_weights), followed by
+// fp32 partial outputs when a small layer splits its offsets.
 bool wide_supported(const ForwardArgs& a);
-hipError_t launch_forward_wide(const ForwardArgs& a, const uint4* wop, const uint4* zero_row,
-                               hipStream_t stream);
+size_t wide_workspace_bytes(const ForwardArgs& a);
+hipError_t launch_forward_wide(const ForwardArgs& a, void* workspace, hipStream_t stream);
 // True when the small-channel kernel (every W_d resident in LDS) serves `a`.
 bool small_supported(const ForwardArgs& a);
 
