@@ -221,6 +221,18 @@ def test_forward_mid_large_channels(sp, dtype, K, cin, cout):
     _forward_check(sp, kmap, c, K, cin, cout, dtype, seed=cin * 5 + cout + K)
 
 
+@pytest.mark.parametrize("dtype,cin,cout", [("bf16", 256, 256), ("f16", 128, 256), ("bf16", 64, 128)])
+def test_forward_wide_large_grid_sampled(sp, dtype, cin, cout):
+    """A grid of ~40k voxels: enough 64-row tiles that the wide path runs
+    without splitting offsets, with every column group of a tile in one
+    workgroup (C_in 256: two groups of 128 columns).  Sampled rows against
+    the oracle."""
+    c = workloads.random_grid(cin + cout, 48, 0.35, 1)
+    kmap = _gpu_map(sp, c, 3)
+    rows = np.sort(np.random.default_rng(cin).choice(c.shape[0], 600, replace=False))
+    _forward_check(sp, kmap, c, 3, cin, cout, dtype, seed=cin + 3 * cout, rows=rows)
+
+
 @pytest.mark.parametrize("dtype,ch", [("f16", 32), ("bf16", 32), ("f32", 16), ("f16", 128),
                                       ("bf16", 256)])
 @pytest.mark.parametrize("extent", [12, 20])
