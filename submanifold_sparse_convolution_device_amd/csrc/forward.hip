@@ -265,6 +265,7 @@ __global__ __launch_bounds__(kThreads) void k_forward(
 // the next range are in flight while the current one runs on MFMA.
 // ---------------------------------------------------------------------------
 constexpr int kSmallWaves = 12;    // most waves per workgroup
+constexpr int kSpares = 2;         // spare waves that take halves of heavy tiles
 constexpr int kStageRounds = 2;    // 64-slot rounds per stage
 constexpr int kStageEntries = 64 * kStageRounds;  // plus one zero row per wave
 constexpr size_t kSmallLdsCap = 160 * 1024;  // one workgroup per CU
@@ -279,7 +280,10 @@ struct SmallShape {
   static_assert(CIN % CHUNK == 0 && COUT % 16 == 0, "shape");
   static size_t wbytes(int KV) { return static_cast<size_t>(KV) * NCB * NCH * 64 * 16; }
   static size_t stage_bytes() { return static_cast<size_t>(ROWV) * (kStageEntries + 1) * 16; }
-  static size_t lds_bytes(int KV, int waves) { return wbytes(KV) + static_cast<size_t>(waves) * stage_bytes(); }
+  // Weights, one stage per wave, then the heavy-tile flags (one int per wave).
+  static size_t lds_bytes(int KV, int waves) {
+    return wbytes(KV) + static_cast<size_t>(waves) * stage_bytes() + 16 * ((kSmallWaves * 4 + 15) / 16);
+  }
 };
 
 template <typename T, int NCB>
@@ -390,17 +394,15 @@ struct TileMeta {
   int total;
 };
 
-template <typename T, int CIN>
-__device__ __forceinline__ TileMeta tile_meta(const unsigned long long* __restrict__ tile_mask,
-                                              const int32_t* __restrict__ tile_off, int64_t t,
-                                              int64_t tiles, int KV, int centre, int lane) {
+// The rows [row_lo, row_hi) of a tile's metadata (whole = [0, 64)): the
+// masks keep those rows' bits and list starts move past the rows before.
+__device__ __forceinline__ TileMeta window_meta(unsigned long long mk, int lok, int row_lo, int row_hi, int KV,
+                                                int centre, int lane) {
   TileMeta tm;
-  tm.mk = 0ull;
-  tm.lok = 0;
-  if (lane < KV) {
-    tm.mk = tile_mask[static_cast<int64_t>(lane) * tiles + t];
-    tm.lok = tile_off[static_cast<int64_t>(lane) * tiles + t];
-  }
+  const unsigned long long below = row_lo == 0 ? 0ull : (~0ull >> (64 - row_lo));
+  const unsigned long long upto = row_hi == 64 ? ~0ull : (~0ull >> (64 - row_hi));
+  tm.mk = mk & upto & ~below;
+  tm.lok = lok + static_cast<int>(__popcll(mk & below));
   const int cnt = (lane < KV && lane != centre) ? __popcll(tm.mk) : 0;
   int incl = cnt;
 #pragma unroll
@@ -411,6 +413,28 @@ __device__ __forceinline__ TileMeta tile_meta(const unsigned long long* __restri
   tm.basek = incl - cnt;
   tm.total = lane_i32(incl, 63);
   return tm;
+}
+
+// Lane k < KV loads offset k's row mask and list start of tile t.
+__device__ __forceinline__ void load_meta(const unsigned long long* __restrict__ tile_mask,
+                                          const int32_t* __restrict__ tile_off, int64_t t, int64_t tiles, int KV,
+                                          int lane, unsigned long long& mk, int& lok) {
+  mk = 0ull;
+  lok = 0;
+  if (lane < KV) {
+    mk = tile_mask[static_cast<int64_t>(lane) * tiles + t];
+    lok = tile_off[static_cast<int64_t>(lane) * tiles + t];
+  }
+}
+
+template <typename T, int CIN>
+__device__ __forceinline__ TileMeta tile_meta(const unsigned long long* __restrict__ tile_mask,
+                                              const int32_t* __restrict__ tile_off, int64_t t,
+                                              int64_t tiles, int KV, int centre, int lane) {
+  unsigned long long mk;
+  int lok;
+  load_meta(tile_mask, tile_off, t, tiles, KV, lane, mk, lok);
+  return window_meta(mk, lok, 0, kTileRows, KV, centre, lane);
 }
 
 // Stage layout of a wave: chunk-major, stage[v * kStageStride + slot] is the
@@ -534,7 +558,7 @@ template <typename T, int CIN, int COUT>
 __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
     const T* __restrict__ feats, const T* __restrict__ weights, T* __restrict__ out,
     const int32_t* __restrict__ in_idx, const int32_t* __restrict__ tile_off,
-    const unsigned long long* __restrict__ tile_mask, int64_t n, int64_t tiles, int KV) {
+    const unsigned long long* __restrict__ tile_mask, int64_t n, int64_t tiles, int KV, int tw) {
   using Sh = SmallShape<T, CIN, COUT>;
   constexpr int CHUNK = Sh::CHUNK, VEC = Sh::VEC, NCH = Sh::NCH, NCB = Sh::NCB, ROWV = Sh::ROWV;
   extern __shared__ uint4 smem4[];
@@ -556,8 +580,18 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
   const int nblk = KV * kRB * kCBK;
   WeightBlock<T, CIN, COUT> wb;
   weight_block_load<T, CIN, COUT>(wb, weights, tid, nblk);
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * nw;
-  int64_t t = static_cast<int64_t>(blockIdx.x) * nw + wave;
+  // Waves [0, tw) own tiles; the others are spares.  A tile of the first
+  // round with more entries than one stage holds gives its rows [32, 64) to
+  // a spare, when there is one, instead of taking a second gather round.
+  int* s_heavy = reinterpret_cast<int*>(wl + static_cast<size_t>(KV) * NCB * NCH * 64 +
+                                        static_cast<size_t>(nw) * ROWV * kStageStride);
+  const bool spare = wave >= tw;
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * tw;
+  int64_t t = spare ? tiles : static_cast<int64_t>(blockIdx.x) * tw + wave;
+  int row_lo = 0, row_hi = kTileRows;  // rows of the tile this wave computes
+  unsigned long long mk_full = 0ull;
+  int lok_full = 0;
+  bool deferred = false;  // first-round loads wait for the split decision
   TileMeta tm{0ull, 0, 0, 0};
   int cntk = 0;
   StageRows<ROWV> rows;
@@ -575,27 +609,63 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
       }
     }
   };
-  if (t < tiles) {
-    load_centre(t * kTileRows);
-    tm = tile_meta<T, CIN>(tile_mask, tile_off, t, tiles, KV, centre, lane);
+  auto issue_first = [&]() {
     cntk = (lane < KV && lane != centre) ? __popcll(tm.mk) : 0;
     if (tm.total > 0) {
       int pos[kStageRounds];
       stage_positions(tm, cntk, 0, lane, pos);
       load_stage_rows<T, CIN>(feats, in_idx, pos, rows);
     }
+  };
+  if (t < tiles) {
+    load_centre(t * kTileRows);
+    load_meta(tile_mask, tile_off, t, tiles, KV, lane, mk_full, lok_full);
+    tm = window_meta(mk_full, lok_full, 0, kTileRows, KV, centre, lane);
+    deferred = tm.total > kStageEntries && tw < nw;
+    if (!deferred) issue_first();
   }
+  if (!spare && lane == 0) s_heavy[wave] = deferred ? static_cast<int>(t) : -1;
   weight_block_store<T, CIN, COUT>(wb, wl, nblk);
   for (int b = tid + blockDim.x; b < nblk; b += blockDim.x) {
     weight_block_load<T, CIN, COUT>(wb, weights, b, nblk);
     weight_block_store<T, CIN, COUT>(wb, wl, nblk);
   }
   __syncthreads();
+  if (tw < nw) {
+    // Heavy tiles in wave order: the i-th goes to spare i (if any).
+    int nheavy = 0, my_rank = -1;
+    int64_t helped = tiles;
+    for (int w = 0; w < tw; ++w) {
+      const int ht = s_heavy[w];
+      if (ht >= 0) {
+        if (w == wave) my_rank = nheavy;
+        if (spare && nheavy == wave - tw) helped = ht;
+        ++nheavy;
+      }
+    }
+    if (spare && helped < tiles) {
+      t = helped;
+      row_lo = kTileRows / 2;
+      load_centre(t * kTileRows);
+      load_meta(tile_mask, tile_off, t, tiles, KV, lane, mk_full, lok_full);
+      tm = window_meta(mk_full, lok_full, row_lo, row_hi, KV, centre, lane);
+      issue_first();
+    } else if (deferred) {
+      if (my_rank < nw - tw) {
+        row_hi = kTileRows / 2;
+        tm = window_meta(mk_full, lok_full, row_lo, row_hi, KV, centre, lane);
+      }
+      issue_first();
+    }
+  }
 
   bool first = true;
   for (; t < tiles; t += nwaves) {
     const int64_t q0 = t * kTileRows;
     if (!first) {
+      if (spare) break;  // a spare computes one half tile
+      row_lo = 0;
+      row_hi = kTileRows;
       load_centre(q0);
       tm = tile_meta<T, CIN>(tile_mask, tile_off, t, tiles, KV, centre, lane);
       cntk = (lane < KV && lane != centre) ? __popcll(tm.mk) : 0;
@@ -664,11 +734,13 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
       }
     }
     first = false;
-    // epilogue: round to the output dtype, each row written once
+    // epilogue: round to the output dtype, each row written once (only the
+    // rows of this wave's window: a split tile's other half is another
+    // wave's)
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       const int64_t q = q0 + qb * 16 + r;
-      if (q < n) {
+      if (q < n && qb * 16 >= row_lo && qb * 16 < row_hi) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) Elem<T>::store4(out + q * COUT + cb * 16 + 4 * g, acc[qb][cb]);
       }
@@ -697,12 +769,16 @@ hipError_t launch_small(const ForwardArgs& a, hipStream_t stream) {
   // have its own wave when the CUs allow it; a workgroup takes consecutive
   // tiles, so the rows its waves gather overlap in the CU's and the XCD's
   // caches.
+  // Up to kSpares more waves per workgroup take the upper halves of tiles
+  // with more entries than one stage holds, when the workgroup has room.
   const int64_t cus = device_cu_count();
-  int64_t waves = (a.tiles + cus - 1) / cus;
-  if (waves < 1) waves = 1;
+  int64_t tw = (a.tiles + cus - 1) / cus;
+  if (tw < 1) tw = 1;
+  if (tw > kSmallWaves) tw = kSmallWaves;
+  int64_t waves = tw + kSpares;
   if (waves > kSmallWaves) waves = kSmallWaves;
   const size_t lds = Sh::lds_bytes(a.KV, static_cast<int>(waves));
-  const int64_t want = (a.tiles + waves - 1) / waves;
+  const int64_t want = (a.tiles + tw - 1) / tw;
   const unsigned grid = static_cast<unsigned>(want < cus ? want : cus);
   static bool lds_raised = false;  // raise the dynamic-LDS limit once per instantiation
   if (!lds_raised) {
@@ -714,7 +790,8 @@ hipError_t launch_small(const ForwardArgs& a, hipStream_t stream) {
   }
   hipLaunchKernelGGL((k_forward_small<T, CIN, COUT>), dim3(grid), dim3(static_cast<unsigned>(waves) * 64), lds, stream,
                      static_cast<const T*>(a.feats), static_cast<const T*>(a.weights),
-                     static_cast<T*>(a.out), a.in_idx, a.tile_off, a.tile_mask, a.n, a.tiles, a.KV);
+                     static_cast<T*>(a.out), a.in_idx, a.tile_off, a.tile_mask, a.n, a.tiles, a.KV,
+                     static_cast<int>(tw));
   return hipGetLastError();
 }
 
