@@ -587,7 +587,10 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
                                         static_cast<size_t>(nw) * ROWV * kStageStride);
   const bool spare = wave >= tw;
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * tw;
-  int64_t t = spare ? tiles : static_cast<int64_t>(blockIdx.x) * tw + wave;
+  // Tile w G + b for wave w of workgroup b (G workgroups): dense regions,
+  // whose tiles are heavy, are spread over many workgroups (measured: 10%
+  // faster on the indoor scene than consecutive tiles per workgroup).
+  int64_t t = spare ? tiles : static_cast<int64_t>(wave) * gridDim.x + blockIdx.x;
   int row_lo = 0, row_hi = kTileRows;  // rows of the tile this wave computes
   unsigned long long mk_full = 0ull;
   int lok_full = 0;
@@ -766,9 +769,7 @@ template <typename T, int CIN, int COUT>
 hipError_t launch_small(const ForwardArgs& a, hipStream_t stream) {
   using Sh = SmallShape<T, CIN, COUT>;
   // One workgroup per CU (LDS-bound), with just enough waves for every tile to
-  // have its own wave when the CUs allow it; a workgroup takes consecutive
-  // tiles, so the rows its waves gather overlap in the CU's and the XCD's
-  // caches.
+  // have its own wave when the CUs allow it.
   // Up to kSpares more waves per workgroup take the upper halves of tiles
   // with more entries than one stage holds, when the workgroup has room.
   const int64_t cus = device_cu_count();
