@@ -42,7 +42,12 @@
  * spconv_build_map_async only enqueues, and the counts and device errors are
  * read by the first call that needs them.  spconv_forward is asynchronous on
  * its stream.  The map's device buffers come from a library-owned
- * stream-ordered memory pool on the current device.
+ * stream-ordered memory pool on the current device.  The library also keeps,
+ * per (device, stream), a build workspace, a forward workspace and up to four
+ * released map blocks, and reuses them for later calls on the same stream
+ * (stream order makes the reuse safe); they are held until the process ends.
+ * A stream that the library has used must not be destroyed while library
+ * work on it is still pending.
  *
  * Errors: functions return a status; nothing throws across the ABI.  Host-
  * checkable errors are reported before any device work.  On error, output
@@ -145,8 +150,8 @@ spconv_status spconv_map_lists(const spconv_map* map, const int32_t** d_in_idx,
  * (identity-indexed) GEMM and every other offset gathers its input rows by
  * index; each output row is accumulated on chip and written once.  For
  * F16/BF16 with c_in in {32, 64, 128, 256} outside the small-channel shapes,
- * a short kernel first copies W into MFMA operand order in a workspace from
- * the library's stream-ordered pool.
+ * a short kernel first copies W into MFMA operand order in the stream's
+ * forward workspace.
  *
  * Requirements: c_in, c_out multiples of 8 in [8, 1024] (F16/BF16), or
  * multiples of 4 in [4, 512] (F32).  Errors: INVALID_ARG (NULL or misaligned
@@ -157,9 +162,9 @@ spconv_status spconv_forward(const void* d_feats, const void* d_weights, const s
                              int32_t c_in, int32_t c_out, spconv_dtype dtype, void* d_out,
                              void* hip_stream);
 
-/* Releases a map.  Its buffers return to the pool in the order of the build's
- * stream; the caller must not free a map while work on another stream still
- * reads it.  NULL is ignored. */
+/* Releases a map.  Its buffers go back, in the order of the build's stream,
+ * to that stream's cache of map blocks (or to the pool); the caller must not
+ * free a map while work on another stream still reads it.  NULL is ignored. */
 void spconv_map_free(spconv_map* map);
 
 /* Static name of a status ("SPCONV_OK", ...). */

@@ -9,6 +9,7 @@
 #include <mutex>
 #include <new>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/spconv.h"
@@ -36,6 +37,7 @@ struct spconv_map {
   int64_t n = 0;
   int64_t tiles = 0;
   void* block = nullptr;  // one pool allocation holding the MapBuffers
+  size_t block_bytes = 0;
   spconv::MapBuffers buf;
   // Filled when the build's summary has been read (see finish_build).
   SummarySlot* slot = nullptr;   // non-null while the summary is not yet read
@@ -97,6 +99,77 @@ spconv_status pool_for(int device, hipMemPool_t* out) {
   }
   *out = g_pools[device];
   return SPCONV_OK;
+}
+
+// Device buffers kept per (device, stream) between calls.  Work on one stream
+// runs in order, so a buffer that earlier work on a stream has released can
+// be handed to later work on the same stream with no allocator call (the
+// pool's asynchronous malloc and free cost several microseconds of host time
+// each, on every build and forward otherwise).  Buffers leave a stream only
+// through the pool's stream-ordered free.
+struct StreamCache {
+  int device = 0;
+  hipStream_t stream = nullptr;
+  void* scratch = nullptr;  // map build workspace
+  size_t scratch_bytes = 0;
+  void* fwd = nullptr;  // forward workspace
+  size_t fwd_bytes = 0;
+  std::vector<std::pair<void*, size_t>> blocks;  // map blocks released on this stream
+};
+constexpr size_t kCachedBlocks = 4;
+std::mutex g_cache_mu;
+std::vector<StreamCache*> g_caches;
+
+StreamCache* cache_for(int device, hipStream_t stream) {
+  for (StreamCache* c : g_caches)
+    if (c->device == device && c->stream == stream) return c;
+  StreamCache* c = new StreamCache;
+  c->device = device;
+  c->stream = stream;
+  g_caches.push_back(c);
+  return c;
+}
+
+// Makes `buf` hold at least `need` bytes (grown with 25% headroom).
+spconv_status grow_buffer(void*& buf, size_t& have, size_t need, hipMemPool_t pool, hipStream_t stream,
+                          const char* what) {
+  if (have >= need && buf != nullptr) return SPCONV_OK;
+  if (buf != nullptr) (void)hipFreeAsync(buf, stream);
+  buf = nullptr;
+  have = 0;
+  const size_t want = need + need / 4;
+  SPCONV_HIP(hipMallocFromPoolAsync(&buf, want, pool, stream), what);
+  have = want;
+  return SPCONV_OK;
+}
+
+// A released map block of at least `need` bytes (and at most twice that),
+// else a new one.
+spconv_status take_block(StreamCache* c, size_t need, hipMemPool_t pool, void** out, size_t* bytes) {
+  size_t best = c->blocks.size();
+  for (size_t i = 0; i < c->blocks.size(); ++i) {
+    const size_t b = c->blocks[i].second;
+    if (b >= need && b <= 2 * need && (best == c->blocks.size() || b < c->blocks[best].second)) best = i;
+  }
+  if (best < c->blocks.size()) {
+    *out = c->blocks[best].first;
+    *bytes = c->blocks[best].second;
+    c->blocks.erase(c->blocks.begin() + static_cast<std::ptrdiff_t>(best));
+    return SPCONV_OK;
+  }
+  SPCONV_HIP(hipMallocFromPoolAsync(out, need, pool, c->stream), "map allocation");
+  *bytes = need;
+  return SPCONV_OK;
+}
+
+void release_block(int device, hipStream_t stream, void* block, size_t bytes) {
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  StreamCache* c = cache_for(device, stream);
+  if (c->blocks.size() < kCachedBlocks) {
+    c->blocks.emplace_back(block, bytes);
+  } else {
+    (void)hipFreeAsync(block, stream);
+  }
 }
 
 // Summary slots, one free list per device.  A slot holds enough for the
@@ -244,36 +317,32 @@ spconv_status spconv_build_map_async(const int32_t* d_coords, int64_t n, int32_t
     delete m;
     return st;
   }
-  void* ws = nullptr;
-  hipError_t e = hipMallocFromPoolAsync(&ws, spconv::build_scratch_bytes(p), pool, stream);
-  if (e != hipSuccess) {
+  // The stream's build workspace and a map block (both reused across builds
+  // on this stream); the cache lock also serialises enqueueing on a stream.
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  StreamCache* c = cache_for(device, stream);
+  st = grow_buffer(c->scratch, c->scratch_bytes, spconv::build_scratch_bytes(p), pool, stream,
+                   "workspace allocation");
+  if (st == SPCONV_OK) st = take_block(c, spconv::map_buffer_bytes(p), pool, &m->block, &m->block_bytes);
+  if (st != SPCONV_OK) {
     release_slot(device, m->slot);
     delete m;
-    return hip_fail(e, "workspace allocation");
-  }
-  e = hipMallocFromPoolAsync(&m->block, spconv::map_buffer_bytes(p), pool, stream);
-  if (e != hipSuccess) {
-    (void)hipFreeAsync(ws, stream);
-    release_slot(device, m->slot);
-    delete m;
-    return hip_fail(e, "map allocation");
+    return st;
   }
   spconv::BuildScratch s;
-  spconv::carve_build_scratch(p, ws, &s);
+  spconv::carve_build_scratch(p, c->scratch, &s);
   spconv::carve_map_buffers(p, m->block, &m->buf);
   auto discard = [&](spconv_status st) {
-    (void)hipFreeAsync(ws, stream);
     (void)hipFreeAsync(m->block, stream);
     release_slot(device, m->slot);
     delete m;
     return st;
   };
 
-  e = spconv::launch_build(p, d_coords, s, m->buf, m->slot->device, stream);
+  hipError_t e = spconv::launch_build(p, d_coords, s, m->buf, m->slot->device, stream);
   if (e != hipSuccess) return discard(hip_fail(e, "map build launch"));
   e = hipEventRecord(m->slot->done, stream);
   if (e != hipSuccess) return discard(hip_fail(e, "hipEventRecord"));
-  (void)hipFreeAsync(ws, stream);
 
   m->device = device;
   m->stream = stream;
@@ -375,19 +444,22 @@ spconv_status spconv_forward(const void* d_feats, const void* d_weights, const s
     hipMemPool_t pool = nullptr;
     const spconv_status st = pool_for(map->device, &pool);
     if (st != SPCONV_OK) return st;
-    void* ws = nullptr;
+    // The stream's forward workspace (prepared weights, zero row, partials),
+    // reused by later forwards on the stream.
     const size_t ws_bytes = wide ? spconv::wide_workspace_bytes(a) : spconv::tiled_workspace_bytes(a);
-    hipError_t e = hipMallocFromPoolAsync(&ws, ws_bytes, pool, stream);
-    if (e != hipSuccess) return hip_fail(e, "forward workspace allocation");
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    StreamCache* c = cache_for(map->device, stream);
+    const spconv_status sg = grow_buffer(c->fwd, c->fwd_bytes, ws_bytes, pool, stream, "forward workspace allocation");
+    if (sg != SPCONV_OK) return sg;
+    void* ws = c->fwd;
+    hipError_t e;
     if (wide) {
       e = spconv::launch_prep_weights(a, ws, stream);
       if (e == hipSuccess) e = spconv::launch_forward_wide(a, ws, stream);
     } else {
       e = spconv::launch_forward_tiled(a, ws, stream);
     }
-    const hipError_t ef = hipFreeAsync(ws, stream);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
-    if (ef != hipSuccess) return hip_fail(ef, "forward workspace release");
     return SPCONV_OK;
   }
   const hipError_t e = spconv::launch_forward(a, stream);
@@ -397,7 +469,7 @@ spconv_status spconv_forward(const void* d_feats, const void* d_weights, const s
 
 void spconv_map_free(spconv_map* map) {
   if (map == nullptr) return;
-  if (map->block != nullptr) (void)hipFreeAsync(map->block, map->stream);
+  if (map->block != nullptr) release_block(map->device, map->stream, map->block, map->block_bytes);
   if (map->slot != nullptr) release_slot(map->device, map->slot);
   delete map;
 }
