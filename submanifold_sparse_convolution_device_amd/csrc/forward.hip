@@ -266,6 +266,8 @@ __global__ __launch_bounds__(kThreads) void k_forward(
 // ---------------------------------------------------------------------------
 constexpr int kSmallWaves = 12;    // most waves per workgroup
 constexpr int kSpares = 2;         // spare waves that take halves of heavy tiles
+constexpr int kSplitMin = 64;      // fewest entries of a tile whose upper half a spare takes
+static_assert(kSplitMin > 0, "a shared tile's owner must fill its stage");
 constexpr int kStageRounds = 2;    // 64-slot rounds per stage
 constexpr int kStageEntries = 64 * kStageRounds;  // plus one zero row per wave
 constexpr size_t kSmallLdsCap = 160 * 1024;  // one workgroup per CU
@@ -280,9 +282,10 @@ struct SmallShape {
   static_assert(CIN % CHUNK == 0 && COUT % 16 == 0, "shape");
   static size_t wbytes(int KV) { return static_cast<size_t>(KV) * NCB * NCH * 64 * 16; }
   static size_t stage_bytes() { return static_cast<size_t>(ROWV) * (kStageEntries + 1) * 16; }
-  // Weights, one stage per wave, then the heavy-tile flags (one int per wave).
+  // Weights, one stage per wave, then three ints per wave for splitting
+  // tiles (tile, weight, stage-ready flag).
   static size_t lds_bytes(int KV, int waves) {
-    return wbytes(KV) + static_cast<size_t>(waves) * stage_bytes() + 16 * ((kSmallWaves * 4 + 15) / 16);
+    return wbytes(KV) + static_cast<size_t>(waves) * stage_bytes() + 16 * ((kSmallWaves * 12 + 15) / 16);
   }
 };
 
@@ -570,7 +573,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
   const int aslot = operand_slot(lane);
   const uint32_t below_r = (1u << r) - 1u;
   uint4* stage = wl + static_cast<size_t>(KV) * NCB * NCH * 64 + static_cast<size_t>(wave) * ROWV * kStageStride;
-  const uint4* stage_g = stage + g * kStageStride;  // this lane's chunk (of ci-chunk 0)
+  const uint4* stage_g = stage + g * kStageStride;  // this lane's chunk (of ci-chunk 0) of the stage it reads
   const int centre = (KV - 1) / 2;
   if (lane < ROWV) stage[lane * kStageStride + kStageEntries] = make_uint4(0u, 0u, 0u, 0u);  // zero row
 
@@ -580,11 +583,17 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
   const int nblk = KV * kRB * kCBK;
   WeightBlock<T, CIN, COUT> wb;
   weight_block_load<T, CIN, COUT>(wb, weights, tid, nblk);
-  // Waves [0, tw) own tiles; the others are spares.  A tile of the first
-  // round with more entries than one stage holds gives its rows [32, 64) to
-  // a spare, when there is one, instead of taking a second gather round.
-  int* s_heavy = reinterpret_cast<int*>(wl + static_cast<size_t>(KV) * NCB * NCH * 64 +
-                                        static_cast<size_t>(nw) * ROWV * kStageStride);
+  // Waves [0, tw) own tiles; the others are spares, which take the rows
+  // [32, 64) of the workgroup's heaviest tiles, so that those end with the
+  // rest.  A tile with more entries than one stage holds splits first (each
+  // half then gathers its own entries instead of the tile taking a second
+  // gather round); a lighter one (at least kSplitMin entries, and only when
+  // its owner has no later tile) is shared: the spare computes its upper
+  // half from the owner's stage once the owner flags it filled.
+  int* s_tile = reinterpret_cast<int*>(wl + static_cast<size_t>(KV) * NCB * NCH * 64 +
+                                       static_cast<size_t>(nw) * ROWV * kStageStride);
+  int* s_weight = s_tile + kSmallWaves;
+  int* s_ready = s_weight + kSmallWaves;
   const bool spare = wave >= tw;
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * tw;
   // Workgroups are dealt to the 8 XCDs in turn (b mod 8); each XCD takes a
@@ -601,6 +610,8 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
   unsigned long long mk_full = 0ull;
   int lok_full = 0;
   bool deferred = false;  // first-round loads wait for the split decision
+  bool publish = false;   // an owner whose stage a spare also reads
+  int shared_from = -1;   // a spare: the owner wave whose stage it reads
   TileMeta tm{0ull, 0, 0, 0};
   int cntk = 0;
   StageRows<ROWV> rows;
@@ -633,7 +644,13 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
     deferred = tm.total > kStageEntries && tw < nw;
     if (!deferred) issue_first();
   }
-  if (!spare && lane == 0) s_heavy[wave] = deferred ? static_cast<int>(t) : -1;
+  if (!spare && lane == 0) {
+    int weight = -1;
+    if (t < tiles && (deferred || (tm.total >= kSplitMin && t + nwaves >= tiles))) weight = tm.total;
+    s_tile[wave] = static_cast<int>(t);
+    s_weight[wave] = weight;
+    s_ready[wave] = -1;
+  }
   weight_block_store<T, CIN, COUT>(wb, wl, nblk);
   for (int b = tid + blockDim.x; b < nblk; b += blockDim.x) {
     weight_block_load<T, CIN, COUT>(wb, weights, b, nblk);
@@ -641,29 +658,49 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
   }
   __syncthreads();
   if (tw < nw) {
-    // Heavy tiles in wave order: the i-th goes to spare i (if any).
-    int nheavy = 0, my_rank = -1;
-    int64_t helped = tiles;
-    for (int w = 0; w < tw; ++w) {
-      const int ht = s_heavy[w];
-      if (ht >= 0) {
-        if (w == wave) my_rank = nheavy;
-        if (spare && nheavy == wave - tw) helped = ht;
-        ++nheavy;
-      }
+    // Split candidates by weight (ties by wave): the i-th goes to spare i.
+    const int wv = lane < tw ? s_weight[lane] : -1;
+    int rank = 0;
+    for (int u = 0; u < tw; ++u) {
+      const int wu = lane_i32(wv, u);
+      rank += (wu > wv || (wu == wv && u < lane)) ? 1 : 0;
     }
-    if (spare && helped < tiles) {
-      t = helped;
-      row_lo = kTileRows / 2;
-      load_centre(t * kTileRows);
-      load_meta(tile_mask, tile_off, t, tiles, KV, lane, mk_full, lok_full);
-      tm = window_meta(mk_full, lok_full, row_lo, row_hi, KV, centre, lane);
-      issue_first();
-    } else if (deferred) {
-      if (my_rank < nw - tw) {
-        row_hi = kTileRows / 2;
-        tm = window_meta(mk_full, lok_full, row_lo, row_hi, KV, centre, lane);
+    const bool split = wv >= 0 && rank < nw - tw;
+    const unsigned long long splits = __ballot(split);
+    if (spare) {
+      const unsigned long long mine = __ballot(split && rank == wave - tw);
+      if (mine != 0ull) {
+        const int w = __ffsll(static_cast<long long>(mine)) - 1;
+        t = s_tile[w];
+        row_lo = kTileRows / 2;
+        load_centre(t * kTileRows);
+        load_meta(tile_mask, tile_off, t, tiles, KV, lane, mk_full, lok_full);
+        if (s_weight[w] > kStageEntries) {
+          tm = window_meta(mk_full, lok_full, row_lo, row_hi, KV, centre, lane);
+          issue_first();
+        } else {
+          // the owner's slot numbering, restricted to rows [32, 64): offset
+          // k's first slot moves past its entries in rows [0, 32)
+          tm = window_meta(mk_full, lok_full, 0, kTileRows, KV, centre, lane);
+          tm.basek += static_cast<int>(__popcll(tm.mk & (~0ull >> (kTileRows / 2))));
+          tm.mk &= ~0ull << (kTileRows / 2);
+          shared_from = w;
+          stage_g = wl + static_cast<size_t>(KV) * NCB * NCH * 64 + static_cast<size_t>(w) * ROWV * kStageStride +
+                    g * kStageStride;
+        }
+      } else {
+        t = tiles;
       }
+    } else if ((splits >> wave) & 1ull) {
+      row_hi = kTileRows / 2;
+      if (deferred) {
+        tm = window_meta(mk_full, lok_full, row_lo, row_hi, KV, centre, lane);
+        issue_first();
+      } else {
+        tm.mk &= ~0ull >> (kTileRows / 2);  // rows [0, 32), same slots
+        publish = true;
+      }
+    } else if (deferred) {
       issue_first();
     }
   }
@@ -702,9 +739,20 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
     }
     for (int s0 = 0; s0 < tm.total; s0 += kStageEntries) {
       const int s1 = (tm.total - s0 < kStageEntries) ? tm.total : s0 + kStageEntries;
-      wave_lds_sync();  // earlier reads of the stage are done
-      commit_stage<ROWV>(stage, rows, lane);
-      wave_lds_sync();
+      if (shared_from >= 0) {
+        // the owner's stage: wait until its owner has filled it
+        while (__hip_atomic_load(&s_ready[shared_from], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) !=
+               static_cast<int>(t)) {
+          __builtin_amdgcn_s_sleep(1);
+        }
+      } else {
+        wave_lds_sync();  // earlier reads of the stage are done
+        commit_stage<ROWV>(stage, rows, lane);
+        wave_lds_sync();
+        if (publish && lane == 0) {
+          __hip_atomic_store(&s_ready[wave], static_cast<int>(t), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
       // the next range's rows are loaded while this one runs
       if (s1 < tm.total) {
         stage_positions(tm, cntk, s1, lane, pos_next);
