@@ -432,6 +432,7 @@ spconv_status spconv_forward(const void* d_feats, const void* d_weights, const s
   a.out_idx = map->buf.out_idx;
   a.tile_off = map->buf.tile_off;
   a.tile_mask = map->buf.tile_mask;
+  a.tile_rows = map->buf.tile_rows;
   a.n = map->n;
   a.tiles = map->tiles;
   a.KV = map->KV;

@@ -270,6 +270,7 @@ constexpr int kSplitMin = 64;      // fewest entries of a tile whose upper half 
 static_assert(kSplitMin > 0, "a shared tile's owner must fill its stage");
 constexpr int kStageRounds = 2;    // 64-slot rounds per stage
 constexpr int kStageEntries = 64 * kStageRounds;  // plus one zero row per wave
+static_assert(kStageEntries == kTileSlots, "a whole-tile stage is the tile's slot table");
 constexpr size_t kSmallLdsCap = 160 * 1024;  // one workgroup per CU
 
 template <typename T, int CIN, int COUT>
@@ -407,14 +408,8 @@ __device__ __forceinline__ TileMeta window_meta(unsigned long long mk, int lok, 
   tm.mk = mk & upto & ~below;
   tm.lok = lok + static_cast<int>(__popcll(mk & below));
   const int cnt = (lane < KV && lane != centre) ? __popcll(tm.mk) : 0;
-  int incl = cnt;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int up = __shfl_up(incl, d);
-    if (lane >= d) incl += up;
-  }
-  tm.basek = incl - cnt;
-  tm.total = lane_i32(incl, 63);
+  tm.basek = wave_prefix_small<7>(cnt);
+  tm.total = lane_i32(tm.basek + cnt, 63);
   return tm;
 }
 
@@ -495,6 +490,23 @@ __device__ __forceinline__ void load_stage_rows(const T* __restrict__ feats, con
   }
 }
 
+// Input rows of stage slots lane + 64 rd, read from the tile's slot table
+// (srow, loaded with the tile's masks); slots at or past `total` load row 0,
+// a valid row that nothing reads.
+template <typename T, int CIN>
+__device__ __forceinline__ void load_slot_rows(const T* __restrict__ feats, const int32_t (&srow)[kStageRounds],
+                                               int total, int lane,
+                                               StageRows<CIN * static_cast<int>(sizeof(T)) / 16>& rows) {
+  constexpr int ROWV = CIN * static_cast<int>(sizeof(T)) / 16;
+#pragma unroll
+  for (int rd = 0; rd < kStageRounds; ++rd) {
+    const int32_t src = lane + 64 * rd < total ? srow[rd] : 0;
+    const u32x4* rowp = reinterpret_cast<const u32x4*>(feats + static_cast<int64_t>(src) * CIN);
+#pragma unroll
+    for (int v = 0; v < ROWV; ++v) rows.v[rd][v] = rowp[v];
+  }
+}
+
 template <int ROWV>
 __device__ __forceinline__ void commit_stage(uint4* stage, const StageRows<ROWV>& rows, int lane) {
 #pragma unroll
@@ -561,7 +573,8 @@ template <typename T, int CIN, int COUT>
 __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
     const T* __restrict__ feats, const T* __restrict__ weights, T* __restrict__ out,
     const int32_t* __restrict__ in_idx, const int32_t* __restrict__ tile_off,
-    const unsigned long long* __restrict__ tile_mask, int64_t n, int64_t tiles, int KV, int tw) {
+    const unsigned long long* __restrict__ tile_mask, const int32_t* __restrict__ tile_rows, int64_t n,
+    int64_t tiles, int KV, int tw) {
   using Sh = SmallShape<T, CIN, COUT>;
   constexpr int CHUNK = Sh::CHUNK, VEC = Sh::VEC, NCH = Sh::NCH, NCB = Sh::NCB, ROWV = Sh::ROWV;
   extern __shared__ uint4 smem4[];
@@ -629,6 +642,17 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
       }
     }
   };
+  // A whole tile's first stage comes from its slot table, loaded with its
+  // masks (the list positions of its entries are not needed).
+  int32_t srow[kStageRounds];
+  auto load_slots = [&](int64_t tt) {
+#pragma unroll
+    for (int rd = 0; rd < kStageRounds; ++rd) srow[rd] = tile_rows[tt * kTileSlots + lane + 64 * rd];
+  };
+  auto issue_slots = [&]() {
+    cntk = (lane < KV && lane != centre) ? __popcll(tm.mk) : 0;
+    if (tm.total > 0) load_slot_rows<T, CIN>(feats, srow, tm.total, lane, rows);
+  };
   auto issue_first = [&]() {
     cntk = (lane < KV && lane != centre) ? __popcll(tm.mk) : 0;
     if (tm.total > 0) {
@@ -640,9 +664,10 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
   if (t < tiles) {
     load_centre(t * kTileRows);
     load_meta(tile_mask, tile_off, t, tiles, KV, lane, mk_full, lok_full);
+    load_slots(t);
     tm = window_meta(mk_full, lok_full, 0, kTileRows, KV, centre, lane);
     deferred = tm.total > kStageEntries && tw < nw;
-    if (!deferred) issue_first();
+    if (!deferred) issue_slots();
   }
   if (!spare && lane == 0) {
     int weight = -1;
@@ -701,7 +726,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
         publish = true;
       }
     } else if (deferred) {
-      issue_first();
+      issue_slots();
     }
   }
 
@@ -713,13 +738,9 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
       row_lo = 0;
       row_hi = kTileRows;
       load_centre(q0);
+      load_slots(t);
       tm = tile_meta<T, CIN>(tile_mask, tile_off, t, tiles, KV, centre, lane);
-      cntk = (lane < KV && lane != centre) ? __popcll(tm.mk) : 0;
-      if (tm.total > 0) {
-        int pos[kStageRounds];
-        stage_positions(tm, cntk, 0, lane, pos);
-        load_stage_rows<T, CIN>(feats, in_idx, pos, rows);
-      }
+      issue_slots();
     }
     floatx4 acc[4][NCB];
 #pragma unroll
@@ -845,8 +866,8 @@ hipError_t launch_small(const ForwardArgs& a, hipStream_t stream) {
   }
   hipLaunchKernelGGL((k_forward_small<T, CIN, COUT>), dim3(grid), dim3(static_cast<unsigned>(waves) * 64), lds, stream,
                      static_cast<const T*>(a.feats), static_cast<const T*>(a.weights),
-                     static_cast<T*>(a.out), a.in_idx, a.tile_off, a.tile_mask, a.n, a.tiles, a.KV,
-                     static_cast<int>(tw));
+                     static_cast<T*>(a.out), a.in_idx, a.tile_off, a.tile_mask, a.tile_rows, a.n, a.tiles,
+                     a.KV, static_cast<int>(tw));
   return hipGetLastError();
 }
 

@@ -19,6 +19,13 @@ constexpr int kTileRows = 64;
 constexpr int kGroupTiles = 16;
 constexpr int kMaxChunks = 128;
 
+// Per tile, the input rows of its first kTileSlots non-centre entries in the
+// order the small-channel forward stages them: by offset, then by output row
+// (slot s of tile t at tile_rows[t * kTileSlots + s]).  With it the forward
+// loads a tile's gather indices together with the tile's masks instead of
+// after them.
+constexpr int kTileSlots = 128;
+
 // Coordinate table: open addressing over 16-byte slots (64-bit key, int32 row,
 // flags), probed in aligned windows of 8 slots (128 bytes, one L2 line).  A
 // key first claims its preferred slot (x & 3 in a hash-chosen half of its home
@@ -36,6 +43,22 @@ constexpr unsigned long long kFlagTableFull = 4ull;
 // Layout of the small device summary the host reads once per build:
 //   [0] error flags, [1] unused, [2 + k] entries of offset k.
 constexpr int kSummaryHead = 2;
+
+// Exclusive prefix sum over the lanes of a wavefront of values in [0, 2^BITS),
+// bit plane by bit plane: a ballot of bit b, counted below the lane (mbcnt),
+// weighs 2^b.  No cross-lane data movement, so no LDS round trips.
+template <int BITS>
+__device__ __forceinline__ int wave_prefix_small(int v) {
+  int excl = 0;
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) {
+    const unsigned long long m = __ballot((v >> b) & 1);
+    const int below = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+        static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+    excl += below << b;
+  }
+  return excl;
+}
 
 struct BuildPlan {
   int64_t n = 0;
@@ -61,6 +84,7 @@ struct BuildScratch {
   uint8_t* neg_flags = nullptr;  // n x neg_bytes(K)
   int32_t* nbr = nullptr;        // KV x n, offset-major; valid where the flag is set
   int64_t* chunk_sum = nullptr;  // KV x chunks entry counts
+  int32_t* tile_base = nullptr;  // KV x tiles: slot of offset k's first entry in tile t
   long long* summary = nullptr;  // kSummaryHead + KV
 };
 
@@ -73,6 +97,7 @@ struct MapBuffers {
   int32_t* out_idx = nullptr;               // capacity KV * n
   int32_t* tile_off = nullptr;              // KV * tiles + 1
   unsigned long long* tile_mask = nullptr;  // KV * tiles
+  int32_t* tile_rows = nullptr;             // tiles * kTileSlots (slots past a tile's entries unset)
 };
 size_t map_buffer_bytes(const BuildPlan& p);
 void carve_map_buffers(const BuildPlan& p, void* base, MapBuffers* m);
@@ -92,6 +117,7 @@ struct ForwardArgs {
   const int32_t* out_idx;
   const int32_t* tile_off;                  // KV * tiles + 1
   const unsigned long long* tile_mask;      // KV * tiles
+  const int32_t* tile_rows;                 // tiles * kTileSlots
   int64_t n;
   int64_t tiles;
   int32_t KV;

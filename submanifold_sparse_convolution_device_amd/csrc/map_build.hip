@@ -375,13 +375,15 @@ __global__ __launch_bounds__(256) void k_probe(const int4* __restrict__ coords, 
 // One workgroup of 1024 threads (16 waves) per chunk of group_tiles tiles,
 // one tile per wave at a time.  Per tile and offset k, a ballot of the row
 // flags is the tile's row mask; lane k mod 64 keeps it (slot k / 64) and
-// stores it to tile_mask[k][t].  Per-chunk counts go to chunk_sum[k][chunk]
-// and are added to the per-offset totals in the summary.
+// stores it to tile_mask[k][t], with tile_base[k][t], the number of the
+// tile's non-centre entries at offsets before k.  Per-chunk counts go to
+// chunk_sum[k][chunk] and are added to the per-offset totals in the summary.
 template <int K>
 __global__ __launch_bounds__(1024) void k_count(const uint32_t* __restrict__ pos_bits,
                                                 const uint8_t* __restrict__ neg_flags, int64_t n,
                                                 int64_t tiles, int64_t group_tiles, int64_t chunks,
                                                 unsigned long long* __restrict__ tile_mask,
+                                                int32_t* __restrict__ tile_base,
                                                 int64_t* __restrict__ chunk_sum, long long* summary) {
   constexpr int KV = K * K * K;
   constexpr int centre = (KV - 1) / 2;
@@ -429,10 +431,17 @@ __global__ __launch_bounds__(1024) void k_count(const uint32_t* __restrict__ pos
         }
       }
     }
+    int before = 0;  // non-centre entries of the tile at offsets of earlier slots
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int k = s * 64 + lane;
-      if (k < KV) tile_mask[static_cast<int64_t>(k) * tiles + t] = mine[s];
+      const int c = (k < KV && k != centre) ? static_cast<int>(__popcll(mine[s])) : 0;
+      const int excl = wave_prefix_small<7>(c);
+      if (k < KV) {
+        tile_mask[static_cast<int64_t>(k) * tiles + t] = mine[s];
+        tile_base[static_cast<int64_t>(k) * tiles + t] = before + excl;
+      }
+      before += __builtin_amdgcn_readlane(excl + c, 63);
       cnt[s] += __popcll(mine[s]);
     }
   }
@@ -457,8 +466,12 @@ __global__ __launch_bounds__(1024) void k_count(const uint32_t* __restrict__ pos
 // list position is the sum of the totals of offsets before k and of the
 // counts of chunks of offset k before this one (k_count has completed: a
 // kernel boundary).  tile_off[k * tiles + t] = first entry of tile t in list
-// k; the last workgroup also writes tile_off[KV * tiles] = E.
+// k; the last workgroup also writes tile_off[KV * tiles] = E.  A non-centre
+// entry also goes to its tile's slot table (tile_rows), at slot
+// tile_base[k][t] + its rank in the tile's mask, when that is below
+// kTileSlots.
 __global__ __launch_bounds__(256) void k_compact(const unsigned long long* __restrict__ tile_mask,
+                                                 const int32_t* __restrict__ tile_base,
                                                  const int32_t* __restrict__ nbr, int64_t n,
                                                  int64_t tiles, int centre, int KV, int64_t group_tiles,
                                                  int64_t chunks, const int64_t* __restrict__ chunk_sum,
@@ -466,6 +479,7 @@ __global__ __launch_bounds__(256) void k_compact(const unsigned long long* __res
                                                  int32_t* __restrict__ in_idx,
                                                  int32_t* __restrict__ out_idx,
                                                  int32_t* __restrict__ tile_off,
+                                                 int32_t* __restrict__ tile_rows,
                                                  long long* __restrict__ host_summary) {
   const int k = blockIdx.y;
   const int64_t chunk = blockIdx.x;
@@ -510,13 +524,9 @@ __global__ __launch_bounds__(256) void k_compact(const unsigned long long* __res
     const int64_t tr = t0 + rd * 64;
     const bool have = rd * 64 + lane < per && tr + lane < tiles;
     const unsigned long long mt = have ? tile_mask[static_cast<int64_t>(k) * tiles + tr + lane] : 0ull;
+    const int sb = have && !is_centre ? tile_base[static_cast<int64_t>(k) * tiles + tr + lane] : 0;
     const int ct = __popcll(mt);
-    int incl = ct;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int up = __shfl_up(incl, d);
-      if (lane >= d) incl += up;
-    }
+    const int incl = wave_prefix_small<7>(ct) + ct;
     if (have) tile_off[static_cast<int64_t>(k) * tiles + tr + lane] = static_cast<int32_t>(base + incl - ct);
     const int nt = static_cast<int>(per - rd * 64 < 64 ? per - rd * 64 : 64);
     for (int b0 = 0; b0 < nt; b0 += kBatch) {
@@ -536,10 +546,15 @@ __global__ __launch_bounds__(256) void k_compact(const unsigned long long* __res
         if (b0 + i < nt) {
           const unsigned long long m = lane_u64(mt, b0 + i);
           const long long tb = base + __builtin_amdgcn_readlane(incl - ct, b0 + i);
+          const int sbi = __builtin_amdgcn_readlane(sb, b0 + i);
           if ((m >> lane) & 1ull) {
-            const int64_t pos = tb + __popcll(m & below);
+            const int rank = __popcll(m & below);
+            const int64_t pos = tb + rank;
             in_idx[pos] = src[i];
             out_idx[pos] = static_cast<int32_t>((tr + b0 + i) * kTileRows + lane);
+            if (!is_centre && sbi + rank < kTileSlots) {
+              tile_rows[(tr + b0 + i) * kTileSlots + sbi + rank] = src[i];
+            }
           }
         }
       }
@@ -576,7 +591,7 @@ void launch_probe_count(const BuildPlan& p, const int4* c4, const BuildScratch& 
   }
   hipLaunchKernelGGL((k_count<K>), dim3(static_cast<unsigned>(p.chunks)), dim3(1024), 0, stream,
                      s.pos_bits, s.neg_flags, p.n, p.tiles, p.group_tiles, p.chunks, m.tile_mask,
-                     s.chunk_sum, s.summary);
+                     s.tile_base, s.chunk_sum, s.summary);
 }
 
 }  // namespace
@@ -605,6 +620,7 @@ size_t build_scratch_bytes(const BuildPlan& p) {
   b += align_up(static_cast<size_t>(neg_bytes(p.K)) * p.n, 256);
   b += align_up(static_cast<size_t>(p.KV) * p.n * sizeof(int32_t), 256);
   b += align_up(static_cast<size_t>(p.KV) * p.chunks * sizeof(int64_t), 256);
+  b += align_up(static_cast<size_t>(p.KV) * p.tiles * sizeof(int32_t), 256);
   b += align_up(static_cast<size_t>(kSummaryHead + p.KV) * sizeof(long long), 256);
   return b;
 }
@@ -621,6 +637,8 @@ void carve_build_scratch(const BuildPlan& p, void* base, BuildScratch* s) {
   c += align_up(static_cast<size_t>(p.KV) * p.n * sizeof(int32_t), 256);
   s->chunk_sum = reinterpret_cast<int64_t*>(c);
   c += align_up(static_cast<size_t>(p.KV) * p.chunks * sizeof(int64_t), 256);
+  s->tile_base = reinterpret_cast<int32_t*>(c);
+  c += align_up(static_cast<size_t>(p.KV) * p.tiles * sizeof(int32_t), 256);
   s->summary = reinterpret_cast<long long*>(c);
 }
 
@@ -628,7 +646,8 @@ size_t map_buffer_bytes(const BuildPlan& p) {
   const size_t cap = static_cast<size_t>(p.KV) * p.n;
   const size_t tiles = static_cast<size_t>(p.KV) * p.tiles;
   return 2 * align_up(cap * sizeof(int32_t), 256) + align_up((tiles + 1) * sizeof(int32_t), 256) +
-         align_up(tiles * sizeof(unsigned long long), 256);
+         align_up(tiles * sizeof(unsigned long long), 256) +
+         align_up(static_cast<size_t>(p.tiles) * kTileSlots * sizeof(int32_t), 256);
 }
 
 void carve_map_buffers(const BuildPlan& p, void* base, MapBuffers* m) {
@@ -642,6 +661,8 @@ void carve_map_buffers(const BuildPlan& p, void* base, MapBuffers* m) {
   m->tile_off = reinterpret_cast<int32_t*>(c);
   c += align_up((tiles + 1) * sizeof(int32_t), 256);
   m->tile_mask = reinterpret_cast<unsigned long long*>(c);
+  c += align_up(tiles * sizeof(unsigned long long), 256);
+  m->tile_rows = reinterpret_cast<int32_t*>(c);
 }
 
 hipError_t launch_build(const BuildPlan& p, const int32_t* coords, const BuildScratch& s,
@@ -665,9 +686,9 @@ hipError_t launch_build(const BuildPlan& p, const int32_t* coords, const BuildSc
     default: return hipErrorInvalidValue;
   }
   hipLaunchKernelGGL(k_compact, dim3(static_cast<unsigned>(p.chunks), static_cast<unsigned>(p.KV)),
-                     dim3(256), 0, stream, m.tile_mask, s.nbr, p.n, p.tiles, p.centre, p.KV,
+                     dim3(256), 0, stream, m.tile_mask, s.tile_base, s.nbr, p.n, p.tiles, p.centre, p.KV,
                      p.group_tiles, p.chunks, s.chunk_sum, s.summary, m.in_idx, m.out_idx,
-                     m.tile_off, host_summary);
+                     m.tile_off, m.tile_rows, host_summary);
   return hipGetLastError();
 }
 
