@@ -80,6 +80,7 @@ __host__ __device__ constexpr int neg_bytes(int K) { return ((K * K * K - 1) / 2
 
 struct BuildScratch {
   ulonglong2* table = nullptr;   // table_slots 16-byte slots: .x key, .y row
+  uint4* occ = nullptr;          // occupancy map: table_slots / 4 buckets of 16 bytes
   uint32_t* pos_bits = nullptr;  // n x pos_words(K)
   uint8_t* neg_flags = nullptr;  // n x neg_bytes(K)
   int32_t* nbr = nullptr;        // KV x n, offset-major; valid where the flag is set

@@ -82,6 +82,18 @@ __device__ __forceinline__ unsigned long long preferred_slot(unsigned long long 
   return (h & window_mask) * kWindowSlots + ((h >> 60) & 4ull) + (key & 3ull);
 }
 
+// Occupancy map: buckets of 16 bytes, one per run of 16 x values of a
+// (b, z, y) line, at a hash of (b, z, y, x >> 4); byte x & 15 is set when
+// that voxel is present.  A probe reads a whole bucket per line of
+// neighbours (K = 3: 5 lines cover the 13 offsets), so most absent
+// neighbours are settled without touching the table.  Buckets of different
+// runs may coincide: a set byte is a candidate, confirmed in the table; a
+// clear byte is a certain miss.
+__device__ __forceinline__ unsigned long long occ_bucket(int b, int z, int y, int xr,
+                                                         unsigned long long bucket_mask) {
+  return mix64(pack_key(b, z, y, xr) + 0x9e3779b97f4a7c15ull) & bucket_mask;
+}
+
 __device__ __forceinline__ unsigned long long lane_u64(unsigned long long v, int src) {
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), src));
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), src));
@@ -109,26 +121,31 @@ __device__ __forceinline__ void raise_flag(long long* summary, unsigned long lon
   atomicOr(reinterpret_cast<unsigned long long*>(summary), bit);
 }
 
-__global__ __launch_bounds__(256) void k_init(ulonglong2* table, int64_t slots, uint32_t* flag_words,
-                                              int64_t nwords, long long* summary, int summary_len) {
+__global__ __launch_bounds__(256) void k_init(ulonglong2* table, int64_t slots, uint4* occ, int64_t buckets,
+                                              uint32_t* flag_words, int64_t nwords, long long* summary,
+                                              int summary_len) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const ulonglong2 empty = make_ulonglong2(kEmptyKey, 0x00000000ffffffffull);  // row -1, no flags
   for (int64_t i = t0; i < slots; i += stride) table[i] = empty;
+  for (int64_t i = t0; i < buckets; i += stride) occ[i] = make_uint4(0u, 0u, 0u, 0u);
   for (int64_t i = t0; i < nwords; i += stride) flag_words[i] = 0u;
   for (int64_t i = t0; i < summary_len; i += stride) summary[i] = 0;
 }
 
 // Insert, phase 1 (one lane per voxel): claim the preferred slot of the home
-// window with a plain store of the row; the last writer wins.
+// window with a plain store of the row; the last writer wins.  The voxel's
+// byte of the occupancy map is set too (every writer stores 1).
 __global__ __launch_bounds__(256) void k_claim(const int4* __restrict__ coords, int64_t n, ulonglong2* table,
-                                               unsigned long long window_mask) {
+                                               uint8_t* occ, unsigned long long window_mask,
+                                               unsigned long long bucket_mask) {
   const int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (v >= n) return;
   const int4 c = coords[v];
   if (!voxel_in_range(c)) return;  // reported by phase 2
   const unsigned long long key = pack_key(c.x, c.y, c.z, c.w);
   *slot_row(&table[preferred_slot(key, window_mask)]) = static_cast<uint32_t>(v);
+  occ[occ_bucket(c.x, c.y, c.z, c.w >> 4, bucket_mask) * 16 + (c.w & 15)] = 1;
 }
 
 __device__ __forceinline__ bool same_voxel(int4 a, int4 b) {
@@ -246,6 +263,21 @@ __device__ __forceinline__ void positive_offset(int j, int& dz, int& dy, int& dx
   dx = k % K - R;
 }
 
+// Lines of the positive half: line 0 is (dz, dy) = (0, 0) with dx in [1, R];
+// lines 1..R are (0, dy) and the rest (dz > 0, dy) with dx in [-R, R], in
+// the same lexicographic order as the offsets, so a line's offsets are a
+// contiguous range of positive indices starting at its first.
+template <int K>
+struct PosLine {
+  static constexpr int R = (K - 1) / 2, W = 2 * R + 1;
+  static constexpr int kLines = 1 + R + R * W;
+  static constexpr int dz(int l) { return l <= R ? 0 : 1 + (l - R - 1) / W; }
+  static constexpr int dy(int l) { return l <= R ? l : -R + (l - R - 1) % W; }
+  static constexpr int dx_lo(int l) { return l == 0 ? 1 : -R; }
+  static constexpr int count(int l) { return l == 0 ? R : W; }
+  static constexpr int first(int l) { return l == 0 ? 0 : R + (l - 1) * W; }
+};
+
 // Records the entry (P = p, Q = q, offset k) and its mirror (Q, P, -d).
 template <int K>
 __device__ __forceinline__ void emit_pair(int j, int64_t q, int32_t p, int64_t n, int32_t* __restrict__ nbr,
@@ -258,20 +290,33 @@ __device__ __forceinline__ void emit_pair(int j, int64_t q, int32_t p, int64_t n
   neg_flags[static_cast<int64_t>(p) * NB + kneg] = 1;
 }
 
-// One lane per voxel Q: the (K^3 - 1) / 2 offsets after the centre, in
-// groups of up to 32.  For a group, every preferred-slot load is issued (in
-// batches of 16) and resolved before any store: vector-memory counters retire
-// in order, so a store issued between loads would make the later loads' waits
-// wait for its write acknowledgement too.  The few lookups that land on a
-// displaced slot are finished afterwards from their whole home windows.
+// One lane per voxel Q: the (K^3 - 1) / 2 offsets after the centre, a few
+// lines of neighbours at a time, each in rounds of loads:
+//   1. the occupancy bucket(s) of every line (two when its x range crosses a
+//      run boundary): a clear byte settles a lookup as a miss;
+//   2. the preferred slot of each candidate: the key is a hit; EMPTY, or
+//      another key in a slot not marked displaced, a miss;
+//   3. the whole home window of each candidate on a displaced slot (a second
+//      pass scans further windows when it is full).
+// Within a round every load is issued before any is used, and all stores
+// come after the last round: vector-memory counters retire in order, so a
+// store issued between loads would make the later loads' waits wait for its
+// write acknowledgement too.  A hit on P = Q + d stores the bit of (Q, d) in
+// Q's positive-half flag word, the neighbour row at [k][Q], and the mirror
+// entry (P, Q, -d).
 template <int K>
 __global__ __launch_bounds__(256) void k_probe(const int4* __restrict__ coords, int64_t n,
                                                const ulonglong2* __restrict__ table,
-                                               unsigned long long window_mask, int32_t* __restrict__ nbr,
+                                               const uint4* __restrict__ occ, unsigned long long window_mask,
+                                               unsigned long long bucket_mask, int32_t* __restrict__ nbr,
                                                uint32_t* __restrict__ pos_bits,
                                                uint8_t* __restrict__ neg_flags, long long* summary) {
-  constexpr int KV = K * K * K, centre = (KV - 1) / 2, NPOS = (KV - 1) / 2;
-  constexpr int GROUP = 32, BATCH = 16, PW = pos_words(K);
+  using L = PosLine<K>;
+  constexpr int PW = pos_words(K);
+  constexpr int kLinesPerStep = 32 / L::W;         // lines whose buckets are in flight together
+  constexpr int kMaxLook = kLinesPerStep * L::W;   // lookups of a step (<= 32)
+  constexpr int kCand = 4, kPend = 2;              // loads per lane per round of steps 2 and 3
+  static_assert(kMaxLook <= 32, "a step's lookups fit a 32-bit mask");
   const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (q >= n) return;
   const int4 c = coords[q];
@@ -280,47 +325,93 @@ __global__ __launch_bounds__(256) void k_probe(const int4* __restrict__ coords, 
   uint32_t bits[PW > 0 ? PW : 1];
 #pragma unroll
   for (int w = 0; w < PW; ++w) bits[w] = 0u;
+  auto key_of = [&](int j) {
+    int dz, dy, dx;
+    positive_offset<K>(j, dz, dy, dx);
+    return pack_key(c.x, c.y + dz, c.z + dy, c.w + dx);
+  };
 #pragma unroll
-  for (int g0 = 0; g0 < NPOS; g0 += GROUP) {
-    int32_t row[GROUP];
-    uint32_t pend = 0u;  // bit i: offset g0 + i needs the window scan
+  for (int l0 = 0; l0 < L::kLines; l0 += kLinesPerStep) {
+    const int j0 = L::first(l0);
+    // 1. occupancy buckets of the step's lines
+    uint4 v0[kLinesPerStep], v1[kLinesPerStep];
+    int xr0[kLinesPerStep];
 #pragma unroll
-    for (int b0 = g0; b0 < g0 + GROUP && b0 < NPOS; b0 += BATCH) {
-      unsigned long long key[BATCH];
-      bool valid[BATCH];
-      ulonglong2 slot[BATCH];
-#pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        if (b0 + i < NPOS && b0 + i < g0 + GROUP) {
-          int dz, dy, dx;
-          positive_offset<K>(b0 + i, dz, dy, dx);
-          const int z = c.y + dz, y = c.z + dy, x = c.w + dx;
-          valid[i] = ok && coord_in_range(z) && coord_in_range(y) && coord_in_range(x);
-          key[i] = pack_key(c.x, z, y, x);
-          const unsigned long long s = valid[i] ? preferred_slot(key[i], window_mask) : 0ull;
-          slot[i] = table[s];  // unconditional (slot 0 exists), so the loads batch
-        }
+    for (int i = 0; i < kLinesPerStep; ++i) {
+      const int l = l0 + i;
+      if (l < L::kLines) {
+        const int zz = c.y + L::dz(l), yy = c.z + L::dy(l);
+        const bool line_ok = ok && coord_in_range(zz) && coord_in_range(yy);
+        const int xlo = max(c.w + L::dx_lo(l), 0), xhi = min(c.w + L::dx_lo(l) + L::count(l) - 1, 65535);
+        xr0[i] = xlo >> 4;
+        const int xr1 = xhi >> 4;
+        const unsigned long long b0 = line_ok ? occ_bucket(c.x, zz, yy, xlo >> 4, bucket_mask) : 0ull;
+        v0[i] = occ[b0];  // unconditional (bucket 0 exists), so the loads batch
+        v1[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (line_ok && xr1 != xr0[i]) v1[i] = occ[occ_bucket(c.x, zz, yy, xr1, bucket_mask)];
       }
+    }
+    uint32_t cand = 0u;  // bit i: lookup j0 + i has its occupancy byte set
 #pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        if (b0 + i < NPOS && b0 + i < g0 + GROUP) {
-          int32_t p = -1;
-          if (valid[i]) {
-            if (slot[i].x == key[i]) {
-              p = static_cast<int32_t>(static_cast<uint32_t>(slot[i].y));
-            } else if (slot[i].x != kEmptyKey &&
-                       ((static_cast<uint32_t>(slot[i].y >> 32) & kSlotDisplaced) != 0u)) {
-              pend |= 1u << (b0 + i - g0);
-            }
+    for (int i = 0; i < kLinesPerStep; ++i) {
+      const int l = l0 + i;
+      if (l < L::kLines) {
+        const int zz = c.y + L::dz(l), yy = c.z + L::dy(l);
+        const bool line_ok = ok && coord_in_range(zz) && coord_in_range(yy);
+#pragma unroll
+        for (int e = 0; e < L::W; ++e) {
+          if (e < L::count(l)) {
+            const int x = c.w + L::dx_lo(l) + e;
+            const uint4 v = ((x >> 4) == xr0[i]) ? v0[i] : v1[i];
+            const int by = x & 15;
+            const uint32_t word = (by < 4) ? v.x : (by < 8) ? v.y : (by < 12) ? v.z : v.w;
+            const bool set = line_ok && coord_in_range(x) && ((word >> (8 * (by & 3))) & 0xffu) != 0u;
+            cand |= set ? (1u << (L::first(l) - j0 + e)) : 0u;
           }
-          row[b0 + i - g0] = (p >= 0 && p < n) ? p : -1;  // a claimed slot holds a row in range
         }
       }
     }
-    // Lookups on displaced slots: up to kPend per lane per round, every home
-    // window loaded before any is scanned (one round covers nearly every wave).
+    int32_t row[kMaxLook];
+#pragma unroll
+    for (int i = 0; i < kMaxLook; ++i) row[i] = -1;
+    uint32_t pend = 0u;
+    // 2. preferred slots of the candidates
+    while (cand != 0u) {
+      int js[kCand];
+      unsigned long long ks[kCand];
+      ulonglong2 sv[kCand];
+#pragma unroll
+      for (int u = 0; u < kCand; ++u) {
+        js[u] = -1;
+        ks[u] = 0ull;
+        if (cand != 0u) {
+          js[u] = __ffs(cand) - 1;
+          cand &= cand - 1u;
+          ks[u] = key_of(j0 + js[u]);
+          sv[u] = table[preferred_slot(ks[u], window_mask)];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kCand; ++u) {
+        if (js[u] >= 0) {
+          if (sv[u].x == ks[u]) {
+            const int64_t p = static_cast<int64_t>(static_cast<uint32_t>(sv[u].y));
+            if (p < n) {
+#pragma unroll
+              for (int i = 0; i < kMaxLook; ++i) {
+                if (i == js[u]) row[i] = static_cast<int32_t>(p);
+              }
+            }
+          } else if (sv[u].x != kEmptyKey &&
+                     (static_cast<uint32_t>(sv[u].y >> 32) & kSlotDisplaced) != 0u) {
+            pend |= 1u << js[u];
+          }
+        }
+      }
+    }
+    // 3. candidates on displaced slots: whole home windows, every one loaded
+    // before any is scanned
     while (pend != 0u) {
-      constexpr int kPend = 2;
       int js[kPend];
       unsigned long long ks[kPend];
       ulonglong2 wv[kPend][kWindowSlots];
@@ -329,11 +420,9 @@ __global__ __launch_bounds__(256) void k_probe(const int4* __restrict__ coords, 
         js[u] = -1;
         ks[u] = 0ull;
         if (pend != 0u) {
-          js[u] = g0 + __ffs(pend) - 1;
+          js[u] = __ffs(pend) - 1;
           pend &= pend - 1u;
-          int dz, dy, dx;
-          positive_offset<K>(js[u], dz, dy, dx);
-          ks[u] = pack_key(c.x, c.y + dz, c.z + dy, c.w + dx);
+          ks[u] = key_of(j0 + js[u]);
           const ulonglong2* win = table + home_window(ks[u], window_mask) * kWindowSlots;
 #pragma unroll
           for (int s2 = 0; s2 < kWindowSlots; ++s2) wv[u][s2] = win[s2];
@@ -351,17 +440,20 @@ __global__ __launch_bounds__(256) void k_probe(const int4* __restrict__ coords, 
           }
           if (p < 0 && !empty) p = find_row_scan(ks[u], table, window_mask, overflow);  // full window
           if (p >= 0 && p < n) {
-            const int j = js[u];
-            bits[j >> 5] |= 1u << (j & 31);
-            emit_pair<K>(j, q, static_cast<int32_t>(p), n, nbr, neg_flags);
+#pragma unroll
+            for (int i = 0; i < kMaxLook; ++i) {
+              if (i == js[u]) row[i] = static_cast<int32_t>(p);
+            }
           }
         }
       }
     }
+    const int lend = (l0 + kLinesPerStep < L::kLines) ? l0 + kLinesPerStep : L::kLines;
+    const int jn = L::first(lend - 1) + L::count(lend - 1) - j0;  // lookups of the step
 #pragma unroll
-    for (int i = 0; i < GROUP; ++i) {
-      if (g0 + i < NPOS && row[i] >= 0) {
-        const int j = g0 + i;
+    for (int i = 0; i < kMaxLook; ++i) {
+      if (i < jn && row[i] >= 0) {
+        const int j = j0 + i;
         bits[j >> 5] |= 1u << (j & 31);
         emit_pair<K>(j, q, row[i], n, nbr, neg_flags);
       }
@@ -581,13 +673,18 @@ int64_t negative_flag_words(const BuildPlan& p) {
   return static_cast<int64_t>(neg_bytes(p.K)) / 4 * p.n;
 }
 
+// Occupancy buckets: a power of two, one per 4 table slots (at least one
+// per voxel), so that about a quarter to a half are in use.
+int64_t occ_buckets(const BuildPlan& p) { return p.table_slots / 4; }
+
 template <int K>
 void launch_probe_count(const BuildPlan& p, const int4* c4, const BuildScratch& s, const MapBuffers& m,
                         unsigned long long window_mask, hipStream_t stream) {
   const unsigned gx = static_cast<unsigned>((p.n + 255) / 256);
   if (K > 1) {
-    hipLaunchKernelGGL((k_probe<K>), dim3(gx), dim3(256), 0, stream, c4, p.n, s.table, window_mask,
-                       s.nbr, s.pos_bits, s.neg_flags, s.summary);
+    hipLaunchKernelGGL((k_probe<K>), dim3(gx), dim3(256), 0, stream, c4, p.n, s.table, s.occ, window_mask,
+                       static_cast<unsigned long long>(occ_buckets(p) - 1), s.nbr, s.pos_bits, s.neg_flags,
+                       s.summary);
   }
   hipLaunchKernelGGL((k_count<K>), dim3(static_cast<unsigned>(p.chunks)), dim3(1024), 0, stream,
                      s.pos_bits, s.neg_flags, p.n, p.tiles, p.group_tiles, p.chunks, m.tile_mask,
@@ -616,6 +713,7 @@ BuildPlan make_plan(int64_t n, int32_t K) {
 size_t build_scratch_bytes(const BuildPlan& p) {
   size_t b = 0;
   b += align_up(static_cast<size_t>(p.table_slots) * sizeof(ulonglong2), 256);
+  b += align_up(static_cast<size_t>(occ_buckets(p)) * sizeof(uint4), 256);
   b += align_up(static_cast<size_t>(pos_words(p.K)) * p.n * sizeof(uint32_t), 256);
   b += align_up(static_cast<size_t>(neg_bytes(p.K)) * p.n, 256);
   b += align_up(static_cast<size_t>(p.KV) * p.n * sizeof(int32_t), 256);
@@ -629,6 +727,8 @@ void carve_build_scratch(const BuildPlan& p, void* base, BuildScratch* s) {
   char* c = static_cast<char*>(base);
   s->table = reinterpret_cast<ulonglong2*>(c);
   c += align_up(static_cast<size_t>(p.table_slots) * sizeof(ulonglong2), 256);
+  s->occ = reinterpret_cast<uint4*>(c);
+  c += align_up(static_cast<size_t>(occ_buckets(p)) * sizeof(uint4), 256);
   s->pos_bits = reinterpret_cast<uint32_t*>(c);
   c += align_up(static_cast<size_t>(pos_words(p.K)) * p.n * sizeof(uint32_t), 256);
   s->neg_flags = reinterpret_cast<uint8_t*>(c);
@@ -670,13 +770,15 @@ hipError_t launch_build(const BuildPlan& p, const int32_t* coords, const BuildSc
   const int64_t nwords = negative_flag_words(p);
   const int64_t init_work = p.table_slots > nwords ? p.table_slots : nwords;
   hipLaunchKernelGGL(k_init, dim3(grid_for(init_work, 256, 4096)), dim3(256), 0, stream, s.table,
-                     p.table_slots, reinterpret_cast<uint32_t*>(s.neg_flags), nwords, s.summary,
-                     kSummaryHead + p.KV);
+                     p.table_slots, s.occ, occ_buckets(p), reinterpret_cast<uint32_t*>(s.neg_flags), nwords,
+                     s.summary, kSummaryHead + p.KV);
   const unsigned long long window_mask =
       static_cast<unsigned long long>(p.table_slots / kWindowSlots) - 1ull;
   const int4* c4 = reinterpret_cast<const int4*>(coords);
   const unsigned gx = static_cast<unsigned>((p.n + 255) / 256);
-  hipLaunchKernelGGL(k_claim, dim3(gx), dim3(256), 0, stream, c4, p.n, s.table, window_mask);
+  hipLaunchKernelGGL(k_claim, dim3(gx), dim3(256), 0, stream, c4, p.n, s.table,
+                     reinterpret_cast<uint8_t*>(s.occ), window_mask,
+                     static_cast<unsigned long long>(occ_buckets(p) - 1));
   hipLaunchKernelGGL(k_insert, dim3(gx), dim3(256), 0, stream, c4, p.n, s.table, window_mask, s.summary);
   switch (p.K) {
     case 1: launch_probe_count<1>(p, c4, s, m, window_mask, stream); break;
