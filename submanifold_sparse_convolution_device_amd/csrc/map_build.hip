@@ -181,12 +181,18 @@ __global__ __launch_bounds__(256) void k_insert(const int4* __restrict__ coords,
     pslot->x = key;
     return;
   }
-  // claim is another voxel's row (phase 1 wrote one for every voxel in range)
-  if (claim < static_cast<uint64_t>(n) && same_voxel(coords[claim], c)) {
+  // claim is another voxel's row (phase 1 wrote one for every voxel in range).
+  // The winner's coordinates (the duplicate check) and the home window are
+  // loaded together; the displaced mark is stored after the search, so that
+  // no store sits between these loads and the CAS.
+  const int4 cw = coords[claim < static_cast<uint64_t>(n) ? claim : 0];
+  ulonglong2 e0[kWindowSlots];
+#pragma unroll
+  for (int j = 0; j < kWindowSlots; ++j) e0[j] = table[w * kWindowSlots + j];
+  if (claim < static_cast<uint64_t>(n) && same_voxel(cw, c)) {
     raise_flag(summary, kFlagDuplicate);
     return;
   }
-  *slot_flags(pslot) = kSlotDisplaced;  // every writer stores the same value
   const unsigned long long max_steps = window_mask + 1;
   for (unsigned long long step = 0; step < max_steps; ++step) {
     ulonglong2* win = table + w * kWindowSlots;
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(256) void k_insert(const int4* __restrict__ coords,
     // and our own slot's winner was compared above.
 #pragma unroll
     for (int j = 0; j < kWindowSlots; ++j) {
-      const ulonglong2 e = win[j];
+      const ulonglong2 e = (step == 0) ? e0[j] : win[j];
       view[j] = e.x;
       reserved[j] = (static_cast<uint32_t>(e.y) != 0xffffffffu);
     }
@@ -211,6 +217,7 @@ __global__ __launch_bounds__(256) void k_insert(const int4* __restrict__ coords,
         if (view[j] == kEmptyKey && !reserved[j]) target = j;
       }
       if (dup) {
+        *slot_flags(pslot) = kSlotDisplaced;
         raise_flag(summary, kFlagDuplicate);
         return;
       }
@@ -222,12 +229,14 @@ __global__ __launch_bounds__(256) void k_insert(const int4* __restrict__ coords,
           atomicCAS(reinterpret_cast<unsigned long long*>(&win[target]), kEmptyKey, key);
       if (old == kEmptyKey) {
         *slot_row(&win[target]) = static_cast<uint32_t>(v);
+        *slot_flags(pslot) = kSlotDisplaced;  // every writer stores the same value
         return;
       }
       view[target] = old;  // learn the true key and try again
     }
     if (moved) w = (w + 1) & window_mask;
   }
+  *slot_flags(pslot) = kSlotDisplaced;
   raise_flag(summary, kFlagTableFull);
 }
 
