@@ -121,16 +121,34 @@ __device__ __forceinline__ void raise_flag(long long* summary, unsigned long lon
   atomicOr(reinterpret_cast<unsigned long long*>(summary), bit);
 }
 
-__global__ __launch_bounds__(256) void k_init(ulonglong2* table, int64_t slots, uint4* occ, int64_t buckets,
-                                              uint32_t* flag_words, int64_t nwords, long long* summary,
+// Clears the table slots to (EMPTY, row -1, no flags), the occupancy map and
+// the negative-half flags (all in 16-byte units: kInitUnits per thread, a
+// workgroup's stores contiguous) and the summary.
+constexpr int kInitUnits = 4;
+__global__ __launch_bounds__(256) void k_init(uint4* table, int64_t slots, uint4* occ, int64_t buckets,
+                                              uint4* flags, int64_t nflags, long long* summary,
                                               int summary_len) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const ulonglong2 empty = make_ulonglong2(kEmptyKey, 0x00000000ffffffffull);  // row -1, no flags
-  for (int64_t i = t0; i < slots; i += stride) table[i] = empty;
-  for (int64_t i = t0; i < buckets; i += stride) occ[i] = make_uint4(0u, 0u, 0u, 0u);
-  for (int64_t i = t0; i < nwords; i += stride) flag_words[i] = 0u;
-  for (int64_t i = t0; i < summary_len; i += stride) summary[i] = 0;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * blockDim.x * kInitUnits + threadIdx.x;
+  const uint4 empty = make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0u);  // key ~0, row -1, no flags
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int u = 0; u < kInitUnits; ++u) {
+    int64_t i = base + static_cast<int64_t>(u) * blockDim.x;
+    if (i < slots) {
+      table[i] = empty;
+      continue;
+    }
+    i -= slots;
+    if (i < buckets) {
+      occ[i] = zero;
+      continue;
+    }
+    i -= buckets;
+    if (i < nflags) flags[i] = zero;
+  }
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < summary_len; i += blockDim.x) summary[i] = 0;
+  }
 }
 
 // Insert, phase 1 (one lane per voxel): claim the preferred slot of the home
@@ -676,10 +694,10 @@ int grid_for(int64_t work, int per_block, int cap) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// The negative-half flag records are cleared (as 32-bit words); the probe
+// The negative-half flag records are cleared (in 16-byte units); the probe
 // writes every row's positive-half bits, and the centre is implicit.
-int64_t negative_flag_words(const BuildPlan& p) {
-  return static_cast<int64_t>(neg_bytes(p.K)) / 4 * p.n;
+int64_t negative_flag_units(const BuildPlan& p) {
+  return static_cast<int64_t>(neg_bytes(p.K)) / 16 * p.n;
 }
 
 // Occupancy buckets: a power of two, one per 4 table slots (at least one
@@ -776,11 +794,12 @@ void carve_map_buffers(const BuildPlan& p, void* base, MapBuffers* m) {
 
 hipError_t launch_build(const BuildPlan& p, const int32_t* coords, const BuildScratch& s,
                         const MapBuffers& m, long long* host_summary, hipStream_t stream) {
-  const int64_t nwords = negative_flag_words(p);
-  const int64_t init_work = p.table_slots > nwords ? p.table_slots : nwords;
-  hipLaunchKernelGGL(k_init, dim3(grid_for(init_work, 256, 4096)), dim3(256), 0, stream, s.table,
-                     p.table_slots, s.occ, occ_buckets(p), reinterpret_cast<uint32_t*>(s.neg_flags), nwords,
-                     s.summary, kSummaryHead + p.KV);
+  const int64_t nflags = negative_flag_units(p);
+  const int64_t units = p.table_slots + occ_buckets(p) + nflags;
+  const int64_t init_blocks = (units + 256 * kInitUnits - 1) / (256 * kInitUnits);
+  hipLaunchKernelGGL(k_init, dim3(static_cast<unsigned>(init_blocks)), dim3(256), 0, stream,
+                     reinterpret_cast<uint4*>(s.table), p.table_slots, s.occ, occ_buckets(p),
+                     reinterpret_cast<uint4*>(s.neg_flags), nflags, s.summary, kSummaryHead + p.KV);
   const unsigned long long window_mask =
       static_cast<unsigned long long>(p.table_slots / kWindowSlots) - 1ull;
   const int4* c4 = reinterpret_cast<const int4*>(coords);
