@@ -559,13 +559,14 @@ __device__ __forceinline__ void run_item(floatx4 (&acc)[NCB], const ItemOps<NCH,
   for (int ch = 0; ch < NCH; ++ch) mfma_block<T, NCB>(acc, op.a[ch], op.b[ch]);
 }
 
-// Next item of block qb: the lowest offset left in todo.  lov and subv hold,
-// in lane k, offset k's first slot for this block (relative to the range
-// start) and the block's 16-bit row mask.
-__device__ __forceinline__ Item next_item(unsigned long long& todo, int lov, int subv) {
-  if (todo == 0ull) return Item{-1, 0, 0u};
-  const int k = __ffsll(static_cast<long long>(todo)) - 1;
-  todo &= todo - 1ull;
+// Next item of block qb: the lowest offset left in todo (K^3 <= 32 here, so
+// one 32-bit word holds the offsets).  lov and subv hold, in lane k, offset
+// k's first slot for this block (relative to the range start) and the
+// block's 16-bit row mask.
+__device__ __forceinline__ Item next_item(uint32_t& todo, int lov, int subv) {
+  if (todo == 0u) return Item{-1, 0, 0u};
+  const int k = __builtin_ctz(todo);
+  todo &= todo - 1u;
   return Item{k, lane_i32(lov, k), static_cast<uint32_t>(lane_i32(subv, k))};
 }
 
@@ -791,12 +792,12 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
         const unsigned long long below = (qb == 0) ? 0ull : (tm.mk & ((1ull << (16 * qb)) - 1ull));
         const int lov = tm.basek + static_cast<int>(__popcll(below)) - s0;
         const int c = __popc(static_cast<uint32_t>(subv));
-        unsigned long long todo = __ballot(c > 0 && lov + c > 0 && lov < lim);
-        if (todo == 0ull) continue;
+        uint32_t todo = static_cast<uint32_t>(__ballot(c > 0 && lov + c > 0 && lov < lim));
+        if (todo == 0u) continue;
         // Items go in pairs; an odd count is padded with an end item, whose
         // B operand is the zero row (it adds nothing).  One loop exit keeps
         // the LDS wait counts the same on every path.
-        const int items = __popcll(todo);
+        const int items = __popc(todo);
         ItemOps<NCH, NCB> x, y;
         load_item<T, CIN, COUT>(x, wl, stage_g, next_item(todo, lov, subv), lim, r, below_r, aslot);
         for (int i = 0; i < items; i += 2) {
@@ -874,7 +875,7 @@ hipError_t launch_small(const ForwardArgs& a, hipStream_t stream) {
 // Small kernel shapes; returns hipErrorNotSupported when the shape has none.
 template <typename T>
 hipError_t try_small(const ForwardArgs& a, hipStream_t stream) {
-  if (a.KV > 64) return hipErrorNotSupported;
+  if (a.KV > 32) return hipErrorNotSupported;  // one 32-bit word of offsets
   constexpr size_t kBudget = kSmallLdsCap;
   if constexpr (sizeof(T) == 2) {
     if (a.cin == 32 && a.cout == 32 && SmallShape<T, 32, 32>::lds_bytes(a.KV, kSmallWaves) <= kBudget) return launch_small<T, 32, 32>(a, stream);
@@ -919,7 +920,7 @@ hipError_t dispatch(const ForwardArgs& a, hipStream_t stream) {
 }
 
 bool small_supported(const ForwardArgs& a) {
-  if (a.KV > 64) return false;
+  if (a.KV > 32) return false;
   if (a.dtype == 0) {
     return a.cin == 16 && (a.cout == 16 || a.cout == 32);
   }
