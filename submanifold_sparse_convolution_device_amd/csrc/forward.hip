@@ -515,25 +515,27 @@ __device__ __forceinline__ void commit_stage(uint4* stage, const StageRows<ROWV>
     for (int v = 0; v < ROWV; ++v) *reinterpret_cast<u32x4*>(stage + v * kStageStride + lane + 64 * rd) = rows.v[rd][v];
 }
 
-// One unit of MFMA work: the rows of one 16-row block that have a neighbour
-// at offset k, with at least one of them in the current stage range.  All
-// fields are wave-uniform.  lo is the stage slot of the block's first entry at
-// k relative to the range start; sub has bit i set when row i of the block has
-// that neighbour.  k < 0 marks the end of a walk.
+// One unit of MFMA work: the rows of a pair of 16-row blocks (32 rows) that
+// have a neighbour at offset k, with at least one of them in the current
+// stage range.  All fields are wave-uniform.  lo is the stage slot of the
+// pair's first entry at k relative to the range start; sub has bit i set when
+// row i of the pair has that neighbour.  k < 0 marks the end of a walk.  One
+// read of W_k serves both blocks: a pair of blocks has 40% fewer items than
+// its blocks one by one on the indoor scene.
 struct Item {
   int k;
   int lo;
   uint32_t sub;
 };
 
-// A operands (W_k for every co-block) and the B operand of one item.  A lane
-// whose row has no entry in range reads the stage's zero row.  An item with
-// k < 0 reads offset 0 and the zero row (a harmless read that keeps the LDS
-// wait counts the same on every path).
+// A operands (W_k for every co-block) and the B operands of one item's two
+// blocks.  A lane whose row has no entry in range reads the stage's zero row.
+// An item with k < 0 reads offset 0 and the zero row (a harmless read that
+// keeps the LDS wait counts the same on every path).
 template <int NCH, int NCB>
 struct ItemOps {
   uint4 a[NCH][NCB];
-  uint4 b[NCH];
+  uint4 b[2][NCH];
 };
 
 template <typename T, int CIN, int COUT>
@@ -546,23 +548,31 @@ __device__ __forceinline__ void load_item(ItemOps<CIN / Elem<T>::kChunk, COUT / 
   for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) op.a[ch][cb] = wl[((static_cast<size_t>(k) * NCB + cb) * NCH + ch) * 64 + aslot];
-  const int ls0 = it.lo + __popc(it.sub & below_r);
-  const bool has = ((it.sub >> r) & 1u) && static_cast<unsigned>(ls0) < static_cast<unsigned>(lim);
-  const int ls = has ? ls0 : kStageEntries;  // the zero row
 #pragma unroll
-  for (int ch = 0; ch < NCH; ++ch) op.b[ch] = stage_g[ch * 4 * kStageStride + ls];
+  for (int h = 0; h < 2; ++h) {
+    // row r of block h: its slot follows the pair's entries at k in the rows before it
+    const uint32_t before = h == 0 ? below_r : (0xffffu | (below_r << 16));
+    const int ls0 = it.lo + __popc(it.sub & before);
+    const bool has = ((it.sub >> (16 * h + r)) & 1u) && static_cast<unsigned>(ls0) < static_cast<unsigned>(lim);
+    const int ls = has ? ls0 : kStageEntries;  // the zero row
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) op.b[h][ch] = stage_g[ch * 4 * kStageStride + ls];
+  }
 }
 
 template <typename T, int NCH, int NCB>
-__device__ __forceinline__ void run_item(floatx4 (&acc)[NCB], const ItemOps<NCH, NCB>& op) {
+__device__ __forceinline__ void run_item(floatx4 (&acc0)[NCB], floatx4 (&acc1)[NCB], const ItemOps<NCH, NCB>& op) {
 #pragma unroll
-  for (int ch = 0; ch < NCH; ++ch) mfma_block<T, NCB>(acc, op.a[ch], op.b[ch]);
+  for (int ch = 0; ch < NCH; ++ch) {
+    mfma_block<T, NCB>(acc0, op.a[ch], op.b[0][ch]);
+    mfma_block<T, NCB>(acc1, op.a[ch], op.b[1][ch]);
+  }
 }
 
-// Next item of block qb: the lowest offset left in todo (K^3 <= 32 here, so
-// one 32-bit word holds the offsets).  lov and subv hold, in lane k, offset
-// k's first slot for this block (relative to the range start) and the
-// block's 16-bit row mask.
+// Next item of a block pair: the lowest offset left in todo (K^3 <= 32 here,
+// so one 32-bit word holds the offsets).  lov and subv hold, in lane k, offset
+// k's first slot for the pair (relative to the range start) and the pair's
+// 32-bit row mask.
 __device__ __forceinline__ Item next_item(uint32_t& todo, int lov, int subv) {
   if (todo == 0u) return Item{-1, 0, 0u};
   const int k = __builtin_ctz(todo);
@@ -780,35 +790,37 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
         stage_positions(tm, cntk, s1, lane, pos_next);
         load_stage_rows<T, CIN>(feats, in_idx, pos_next, rows);
       }
-      // Per 16-row block, the offsets with entries in [s0, s1), ping-ponging
-      // between two operand sets: the next item's LDS reads are in flight
-      // while the current one runs on MFMA.  The block index is static, so
-      // each block's accumulators stay in place.
+      // Per pair of 16-row blocks, the offsets with entries in [s0, s1),
+      // ping-ponging between two operand sets: the next item's LDS reads are
+      // in flight while the current one runs on MFMA.  The pair index is
+      // static, so each block's accumulators stay in place.
       const int lim = s1 - s0;
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
+      for (int qp = 0; qp < 2; ++qp) {
         const bool mine = lane < KV && lane != centre;
-        const int subv = mine ? static_cast<int>((tm.mk >> (16 * qb)) & 0xffffull) : 0;
-        const unsigned long long below = (qb == 0) ? 0ull : (tm.mk & ((1ull << (16 * qb)) - 1ull));
+        const uint32_t subv = mine ? static_cast<uint32_t>(tm.mk >> (32 * qp)) : 0u;
+        const unsigned long long below = (qp == 0) ? 0ull : (tm.mk & 0xffffffffull);
         const int lov = tm.basek + static_cast<int>(__popcll(below)) - s0;
-        const int c = __popc(static_cast<uint32_t>(subv));
+        const int c = __popc(subv);
         uint32_t todo = static_cast<uint32_t>(__ballot(c > 0 && lov + c > 0 && lov < lim));
         if (todo == 0u) continue;
         // Items go in pairs; an odd count is padded with an end item, whose
-        // B operand is the zero row (it adds nothing).  One loop exit keeps
+        // B operands are the zero row (it adds nothing).  One loop exit keeps
         // the LDS wait counts the same on every path.
         const int items = __popc(todo);
         ItemOps<NCH, NCB> x, y;
-        load_item<T, CIN, COUT>(x, wl, stage_g, next_item(todo, lov, subv), lim, r, below_r, aslot);
+        load_item<T, CIN, COUT>(x, wl, stage_g, next_item(todo, lov, static_cast<int>(subv)), lim, r, below_r, aslot);
         for (int i = 0; i < items; i += 2) {
-          load_item<T, CIN, COUT>(y, wl, stage_g, next_item(todo, lov, subv), lim, r, below_r, aslot);
+          load_item<T, CIN, COUT>(y, wl, stage_g, next_item(todo, lov, static_cast<int>(subv)), lim, r, below_r,
+                                  aslot);
           // keep the scheduler from sinking these reads below the MFMAs
           // (which would reuse one operand set and wait on every item)
           __builtin_amdgcn_sched_barrier(0);
-          run_item<T, NCH, NCB>(acc[qb], x);
-          load_item<T, CIN, COUT>(x, wl, stage_g, next_item(todo, lov, subv), lim, r, below_r, aslot);
+          run_item<T, NCH, NCB>(acc[2 * qp], acc[2 * qp + 1], x);
+          load_item<T, CIN, COUT>(x, wl, stage_g, next_item(todo, lov, static_cast<int>(subv)), lim, r, below_r,
+                                  aslot);
           __builtin_amdgcn_sched_barrier(0);
-          run_item<T, NCH, NCB>(acc[qb], y);
+          run_item<T, NCH, NCB>(acc[2 * qp], acc[2 * qp + 1], y);
         }
       }
     }
