@@ -233,6 +233,23 @@ def test_forward_wide_large_grid_sampled(sp, dtype, cin, cout):
     _forward_check(sp, kmap, c, 3, cin, cout, dtype, seed=cin + 3 * cout, rows=rows)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_forward_small_many_tiles_sampled(sp, dtype):
+    """About 205k voxels at C = 32 (a box at 40% occupancy, about 10
+    neighbours per row): more 64-row tiles than 11 per CU, so the
+    small-channel kernel runs 12 tile waves per workgroup with no spare
+    waves, some waves take a second tile, and tiles hold several stages of
+    entries (the later ones gathered through the lists).  Sampled rows,
+    including the last tile's, against the oracle."""
+    c = workloads.random_grid(77, 80, 0.4, 1)
+    n = c.shape[0]
+    assert (n + 63) // 64 > 11 * 256
+    kmap = _gpu_map(sp, c, 3)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([rng.choice(n, 600, replace=False), np.arange(n - 64, n)]))
+    _forward_check(sp, kmap, c, 3, 32, 32, dtype, seed=77 if dtype == "f16" else 78, rows=rows)
+
+
 @pytest.mark.parametrize("dtype,ch", [("f16", 32), ("bf16", 32), ("f32", 16), ("f16", 128),
                                       ("bf16", 256)])
 @pytest.mark.parametrize("extent", [12, 20])
