@@ -186,6 +186,30 @@ def test_async_build_matches_sync_and_defers_errors(sp):
     assert sp.build_map(dc, 3).total_entries == ref.total_entries
 
 
+def test_map_sequence_on_one_stream(sp):
+    """Builds enqueued back to back on one stream without host waits,
+    growing, shrinking and changing K (so the stream's reused workspace is
+    regrown and reused in prefixes of changing size), then each map against
+    the oracle; one build fails (duplicates) in the middle of the sequence."""
+    specs = [(21, 24, 0.3, 3), (22, 10, 0.5, 5), (23, 40, 0.25, 3), (24, 8, 0.6, 7), (25, 16, 0.4, 1),
+             (26, 48, 0.3, 3), (27, 12, 0.5, 5), (28, 32, 0.2, 3)]
+    grids = [workloads.permuted(workloads.random_grid(seed, ext, occ, 2), seed) for seed, ext, occ, _ in specs]
+    dup = torch.from_numpy(np.array([[0, 1, 2, 3], [0, 5, 5, 5], [0, 1, 2, 3]], np.int32)).to(DEV)
+    maps = []
+    for i, (c, (_, _, _, K)) in enumerate(zip(grids, specs)):
+        maps.append(sp.build_map(torch.from_numpy(c).to(DEV), K, wait=False))
+        if i == 3:
+            bad = sp.build_map(dup, 3, wait=False)
+    with pytest.raises(sp.SpconvError) as e:
+        bad.wait()
+    assert e.value.name == "SPCONV_ERR_DUPLICATE_COORD"
+    bad.free()
+    for m, c, (_, _, _, K) in zip(maps, grids, specs):
+        m.wait()
+        assert_map_equal(m, oracle.build_map(c, K))
+        m.free()
+
+
 def test_map_deterministic(sp):
     c = workloads.permuted(workloads.random_grid(99, 30, 0.1, 2), 99)
     a1, b1 = _gpu_lists(_gpu_map(sp, c, 3))
