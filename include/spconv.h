@@ -153,6 +153,10 @@ spconv_status spconv_map_lists(const spconv_map* map, const int32_t** d_in_idx,
  * a short kernel first copies W into MFMA operand order in the stream's
  * forward workspace.
  *
+ * The forward is ordered after the map's build: by stream order on the
+ * build's stream; on another stream the library makes that stream wait for
+ * the build first.
+ *
  * Requirements: c_in, c_out multiples of 8 in [8, 1024] (F16/BF16), or
  * multiples of 4 in [4, 512] (F32).  Errors: INVALID_ARG (NULL or misaligned
  * pointers, channel counts out of range), UNSUPPORTED (dtype, channel

@@ -440,6 +440,12 @@ spconv_status spconv_forward(const void* d_feats, const void* d_weights, const s
   a.cout = c_out;
   a.dtype = static_cast<int32_t>(dtype);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (stream != map->stream && map->slot != nullptr) {
+    // another stream than the build's, before the build is known complete:
+    // order this stream after it (stream order covers the build's own stream)
+    const hipError_t ew = hipStreamWaitEvent(stream, map->slot->done, 0);
+    if (ew != hipSuccess) return hip_fail(ew, "hipStreamWaitEvent");
+  }
   const bool wide = !spconv::small_supported(a) && spconv::wide_supported(a);
   if (wide || (!spconv::small_supported(a) && spconv::tiled_supported(a))) {
     hipMemPool_t pool = nullptr;

@@ -210,6 +210,26 @@ def test_map_sequence_on_one_stream(sp):
         m.free()
 
 
+def test_forward_on_another_stream_follows_the_build(sp):
+    """A build enqueued without a host wait on one stream and a forward
+    enqueued at once on another: the forward still sees the finished map."""
+    c = workloads.random_grid(91, 40, 0.3, 1)
+    dc = torch.from_numpy(c).to(DEV)
+    f = workloads.features(c.shape[0], 32, "f16", 91).to(DEV)
+    w = workloads.weights(3, 32, 32, "f16", 92).to(DEV)
+    ref = sp.forward(f, w, sp.build_map(dc, 3))
+    other = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        m = sp.build_map(dc, 3, wait=False)
+        with torch.cuda.stream(other):
+            out = sp.forward(f, w, m)
+        other.synchronize()
+        assert torch.equal(out, ref)
+        m.wait()
+        m.free()
+
+
 def test_map_deterministic(sp):
     c = workloads.permuted(workloads.random_grid(99, 30, 0.1, 2), 99)
     a1, b1 = _gpu_lists(_gpu_map(sp, c, 3))
