@@ -501,7 +501,7 @@ struct WideChoice {
   int tb, ncb, nw, splits;
 };
 
-int wide_ncb(int cin) { return cin <= 128 ? 4 : 2; }
+int wide_ncb(int cin) { return cin == 128 ? 4 : 2; }
 constexpr int kMaxSplits = 8;
 
 bool wide_compiled(int cin, int tb, int nw) {
@@ -560,7 +560,7 @@ hipError_t launch_wide_cin(const ForwardArgs& a, const WideChoice& c, const uint
 template <typename T>
 hipError_t launch_wide_typed(const ForwardArgs& a, const WideChoice& c, const uint4* wop, const uint4* zero_row,
                              float* part, hipStream_t stream) {
-  if (a.cin == 64) return launch_wide_cin<T, 64, 4>(a, c, wop, zero_row, part, stream);
+  if (a.cin == 64) return launch_wide_cin<T, 64, 2>(a, c, wop, zero_row, part, stream);
   if (a.cin == 128) return launch_wide_cin<T, 128, 4>(a, c, wop, zero_row, part, stream);
   return launch_wide_cin<T, 256, 2>(a, c, wop, zero_row, part, stream);
 }
