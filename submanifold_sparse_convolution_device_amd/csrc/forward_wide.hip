@@ -495,7 +495,10 @@ hipError_t launch_wide_shape(const ForwardArgs& a, int splits, const uint4* wop,
 // Tasks are one tile (TB = 4): measured against two-tile tasks, which halve
 // the weight traffic per row, the smaller register and LDS footprint (two
 // waves per SIMD) wins on every workload here.  Column blocks per wave are 4
-// (64 columns) up to C_in = 128 and 2 at 256, where a wave's
+// (64 columns) at C_in = 128 and 2 at 64 and 256.  At 64, two waves per
+// workgroup sharing the staged rows hide more latency than one (LiDAR frame
+// step 84.0 -> 79.4 us, 8 frames at K = 5 770 -> 738 us); one block per wave
+// lost 50 us on the latter, two lost 6 us at 128.  At 256 a wave's
 // double-buffered weight slice would not fit otherwise.
 struct WideChoice {
   int tb, ncb, nw, splits;
