@@ -84,7 +84,7 @@ struct BuildScratch {
   uint32_t* pos_bits = nullptr;  // n x pos_words(K)
   uint8_t* neg_flags = nullptr;  // n x neg_bytes(K)
   int32_t* nbr = nullptr;        // KV x n, offset-major; valid where the flag is set
-  int64_t* chunk_sum = nullptr;  // KV x chunks entry counts
+  int64_t* chunk_sum = nullptr;  // KV x groups entry counts (per kGroupTiles tiles)
   int32_t* tile_base = nullptr;  // KV x tiles: slot of offset k's first entry in tile t
   long long* summary = nullptr;  // kSummaryHead + KV
 };

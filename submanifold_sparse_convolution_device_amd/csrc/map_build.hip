@@ -492,7 +492,8 @@ __global__ __launch_bounds__(256) void k_probe(const int4* __restrict__ coords, 
 }
 
 // One workgroup of 1024 threads (16 waves) per chunk of group_tiles tiles,
-// one tile per wave at a time.  Per tile and offset k, a ballot of the row
+// one tile per wave at a time (launched with chunks of one group, so each
+// wave counts one tile).  Per tile and offset k, a ballot of the row
 // flags is the tile's row mask; lane k mod 64 keeps it (slot k / 64) and
 // stores it to tile_mask[k][t], with tile_base[k][t], the number of the
 // tile's non-centre entries at offsets before k.  Per-chunk counts go to
@@ -616,7 +617,10 @@ __global__ __launch_bounds__(256) void k_compact(const unsigned long long* __res
   if (wave == 0) {
     long long s = 0;
     for (int i = lane; i < k; i += 64) s += summary[kSummaryHead + i];
-    for (int64_t cc = lane; cc < chunk; cc += 64) s += chunk_sum[static_cast<int64_t>(k) * chunks + cc];
+    // the counts were taken per group of kGroupTiles tiles
+    const int64_t groups = (tiles + kGroupTiles - 1) / kGroupTiles;
+    const int64_t before = chunk * (group_tiles / kGroupTiles);
+    for (int64_t cc = lane; cc < before; cc += 64) s += chunk_sum[static_cast<int64_t>(k) * groups + cc];
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) s += __shfl_xor(s, d);
     if (lane == 0) s_base = s;
@@ -713,8 +717,9 @@ void launch_probe_count(const BuildPlan& p, const int4* c4, const BuildScratch& 
                        static_cast<unsigned long long>(occ_buckets(p) - 1), s.nbr, s.pos_bits, s.neg_flags,
                        s.summary);
   }
-  hipLaunchKernelGGL((k_count<K>), dim3(static_cast<unsigned>(p.chunks)), dim3(1024), 0, stream,
-                     s.pos_bits, s.neg_flags, p.n, p.tiles, p.group_tiles, p.chunks, m.tile_mask,
+  const int64_t groups = (p.tiles + kGroupTiles - 1) / kGroupTiles;
+  hipLaunchKernelGGL((k_count<K>), dim3(static_cast<unsigned>(groups)), dim3(1024), 0, stream,
+                     s.pos_bits, s.neg_flags, p.n, p.tiles, static_cast<int64_t>(kGroupTiles), groups, m.tile_mask,
                      s.tile_base, s.chunk_sum, s.summary);
 }
 
@@ -744,7 +749,7 @@ size_t build_scratch_bytes(const BuildPlan& p) {
   b += align_up(static_cast<size_t>(pos_words(p.K)) * p.n * sizeof(uint32_t), 256);
   b += align_up(static_cast<size_t>(neg_bytes(p.K)) * p.n, 256);
   b += align_up(static_cast<size_t>(p.KV) * p.n * sizeof(int32_t), 256);
-  b += align_up(static_cast<size_t>(p.KV) * p.chunks * sizeof(int64_t), 256);
+  b += align_up(static_cast<size_t>(p.KV) * ((p.tiles + kGroupTiles - 1) / kGroupTiles) * sizeof(int64_t), 256);
   b += align_up(static_cast<size_t>(p.KV) * p.tiles * sizeof(int32_t), 256);
   b += align_up(static_cast<size_t>(kSummaryHead + p.KV) * sizeof(long long), 256);
   return b;
@@ -763,7 +768,7 @@ void carve_build_scratch(const BuildPlan& p, void* base, BuildScratch* s) {
   s->nbr = reinterpret_cast<int32_t*>(c);
   c += align_up(static_cast<size_t>(p.KV) * p.n * sizeof(int32_t), 256);
   s->chunk_sum = reinterpret_cast<int64_t*>(c);
-  c += align_up(static_cast<size_t>(p.KV) * p.chunks * sizeof(int64_t), 256);
+  c += align_up(static_cast<size_t>(p.KV) * ((p.tiles + kGroupTiles - 1) / kGroupTiles) * sizeof(int64_t), 256);
   s->tile_base = reinterpret_cast<int32_t*>(c);
   c += align_up(static_cast<size_t>(p.KV) * p.tiles * sizeof(int32_t), 256);
   s->summary = reinterpret_cast<long long*>(c);
