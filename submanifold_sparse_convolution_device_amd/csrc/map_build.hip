@@ -174,10 +174,10 @@ __device__ __forceinline__ bool same_voxel(int4 a, int4 b) {
 // boundary).  The winner of a preferred slot writes its key there with a
 // plain store.  A loser whose winner has the same coordinates is a duplicate;
 // otherwise it marks the slot displaced and takes, by CAS, the first slot
-// that no phase-1 winner reserved and no other loser took, in a fixed order
-// (increasing slot index, window after window).  Two losers with one key thus
-// always meet on the slot the first one took, so duplicates are always
-// detected.  Views are read with plain loads; a stale view can only show a
+// that no phase-1 winner reserved and no other loser took, in an order fixed
+// by the key (increasing or decreasing slot index, by a hash bit, window
+// after window).  Two losers with one key thus always meet on the slot the
+// first one took, so duplicates are always detected.  Views are read with plain loads; a stale view can only show a
 // slot free that has since been taken (slots are never released), and a
 // failed CAS returns the slot's true key.  Every window is left as soon as it
 // is seen full, so the search visits each window at most once.
@@ -211,6 +211,7 @@ __global__ __launch_bounds__(256) void k_insert(const int4* __restrict__ coords,
     raise_flag(summary, kFlagDuplicate);
     return;
   }
+  const bool descending = ((key_hash(key) >> 40) & 1ull) != 0ull;
   const unsigned long long max_steps = window_mask + 1;
   for (unsigned long long step = 0; step < max_steps; ++step) {
     ulonglong2* win = table + w * kWindowSlots;
@@ -227,13 +228,21 @@ __global__ __launch_bounds__(256) void k_insert(const int4* __restrict__ coords,
     }
     bool moved = false;
     for (int attempt = 0; attempt <= kWindowSlots; ++attempt) {
+      // the first free slot in ascending or, for half the keys (a hash bit),
+      // descending order, so that losers sharing a window race for one slot
+      // less often; equal keys take the same order
       bool dup = false;
-      int target = -1;
+      int first = -1, last = -1;
 #pragma unroll
       for (int j = kWindowSlots - 1; j >= 0; --j) {
         dup |= (view[j] == key);
-        if (view[j] == kEmptyKey && !reserved[j]) target = j;
+        if (view[j] == kEmptyKey && !reserved[j]) first = j;
       }
+#pragma unroll
+      for (int j = 0; j < kWindowSlots; ++j) {
+        if (view[j] == kEmptyKey && !reserved[j]) last = j;
+      }
+      const int target = descending ? last : first;
       if (dup) {
         *slot_flags(pslot) = kSlotDisplaced;
         raise_flag(summary, kFlagDuplicate);
