@@ -164,6 +164,8 @@ def main(argv=None):
                     help="workload index 0..4 (default: the indoor scene)")
     ap.add_argument("--layer", type=int, default=0, help="layer of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-two-streams", action="store_true",
+                    help="skip the two-stream throughput pass (e.g. when tracing kernel durations)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 256 MiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args(argv)
@@ -290,8 +292,9 @@ def main(argv=None):
     # the other's.  Reported beside the single-stream figures, which `value`
     # and the roofline keep (a kernel timed while another stream runs would
     # not describe the kernel).
-    result["two_streams"] = two_stream_throughput(torch, sp, coords, feats, w, layer, args.steps, args.warmup,
-                                                  e_total, flops)
+    if not args.no_two_streams:
+        result["two_streams"] = two_stream_throughput(torch, sp, coords, feats, w, layer, args.steps,
+                                                      args.warmup, e_total, flops)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(layer, feats_h, w_h)
