@@ -210,6 +210,31 @@ def test_map_sequence_on_one_stream(sp):
         m.free()
 
 
+def test_map_same_plan_repeated_on_one_stream(sp):
+    """Builds of different voxel sets with the same n and K, back to back on
+    one stream without host waits, so each reuses the workspace of the one
+    before with the same layout: nothing of an earlier build leaks into a
+    later one (a stale key would show up as a false neighbour), also after a
+    build that failed on duplicates and around a build with another K."""
+    grids = [workloads.permuted(workloads.random_grid(seed, 40, 0.3, 2), seed) for seed in (61, 62, 63, 64)]
+    n0 = min(g.shape[0] for g in grids)
+    n0 -= n0 % 64 - 37 if n0 % 64 >= 37 else n0 % 64 + 27  # a ragged last tile
+    sets = [np.ascontiguousarray(g[:n0]) for g in grids]
+    dup = sets[0].copy()
+    dup[-1] = dup[0]
+    plan = [(sets[0], 3), (sets[1], 3), (dup, 3), (sets[2], 3), (sets[3], 5), (sets[0], 3), (sets[3], 3)]
+    maps = [sp.build_map(torch.from_numpy(c).to(DEV), K, wait=False) for c, K in plan]
+    for i, (m, (c, K)) in enumerate(zip(maps, plan)):
+        if i == 2:
+            with pytest.raises(sp.SpconvError) as e:
+                m.wait()
+            assert e.value.name == "SPCONV_ERR_DUPLICATE_COORD"
+        else:
+            m.wait()
+            assert_map_equal(m, oracle.build_map(c, K))
+        m.free()
+
+
 def test_forward_on_another_stream_follows_the_build(sp):
     """A build enqueued without a host wait on one stream and a forward
     enqueued at once on another: the forward still sees the finished map."""
