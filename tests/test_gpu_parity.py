@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import box_map
 import oracle
 import workloads
 
@@ -131,6 +132,37 @@ def test_map_dense_cube_closed_form(sp):
     for k in range(27):
         dz, dy, dx = oracle.offset_of(k, 3)
         assert kmap.counts[k] == (n - abs(dz)) * (n - abs(dy)) * (n - abs(dx))
+
+
+@pytest.mark.parametrize("K,boxes,cin", [
+    (3, [(0, (431, 431, 428)), (1, (1, 2, 15361))], 32),
+    (7, [(0, (184, 184, 184)), (1, (2, 2, 7845))], 16)])
+def test_map_and_forward_at_the_size_limit(sp, K, boxes, cin):
+    """The largest n the ABI takes (n x K^3 just below 2^31: 79,536,430
+    voxels at K = 3, 6,260,884 at K = 7), as two fully active boxes in
+    separate batches.  Every entry of every list is checked against its
+    closed form (box_map.py, itself checked against the oracle on small
+    boxes): the entries of offset d are the rows q of each box whose q + d
+    stays inside it, in increasing q.  The forward with all-ones features and
+    weights gives C_in x deg(q), exact in fp16."""
+    kv = K ** 3
+    n = sum(lz * ly * lx for _, (lz, ly, lx) in boxes)
+    assert n * kv < 2 ** 31 and n == (1 << 31) // kv - 1, "the largest accepted n"
+    c = box_map.box_rows(boxes, DEV)
+    kmap = sp.build_map(c, K)
+    a, b = kmap.lists()
+    for k in range(kv):
+        p, q = box_map.box_list(boxes, K, k, DEV)
+        lo, hi = int(kmap.offsets[k]), int(kmap.offsets[k + 1])
+        assert kmap.counts[k] == q.numel(), f"offset {k} count"
+        assert torch.equal(b[lo:hi].long(), q) and torch.equal(a[lo:hi].long(), p), f"offset {k} entries"
+    del a, b
+    f = torch.ones((n, cin), dtype=torch.float16, device=DEV)
+    w = torch.ones((kv, cin, cin), dtype=torch.float16, device=DEV)
+    out = sp.forward(f, w, kmap)
+    deg = box_map.box_degree(boxes, K, DEV)
+    assert torch.equal(out, (cin * deg).to(torch.float16)[:, None].expand(n, cin))
+    kmap.free()
 
 
 def test_map_device_errors(sp):
