@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 DEFAULT_WORKLOAD = 1  # the indoor scene: 150k voxels, K=3, C=32, fp16
+PERMUTATION_SEED = 7  # the random row order of the permuted pass
 
 ELEM = {"f32": 4, "f16": 2, "bf16": 2}
 
@@ -155,6 +156,43 @@ def two_stream_throughput(torch, sp, coords, feats, w, layer, steps, warmup, e_t
             "note": "the same steps, two frames in flight on two streams (steady-state throughput)"}
 
 
+def permuted_throughput(torch, sp, layer, feats_h, w, steps, warmup, e_total, flops):
+    """The same single-stream steps with the workload's rows in a seeded
+    random order (coordinates and features permuted together): the map and
+    the output are the same up to that relabelling, but neighbouring rows no
+    longer sit in neighbouring lanes, so loads and stores stop coalescing."""
+    import numpy as np
+
+    perm = np.random.default_rng(PERMUTATION_SEED).permutation(layer.n)
+    dev = w.device
+    coords = torch.from_numpy(np.ascontiguousarray(layer.coords[perm])).to(dev)
+    feats = feats_h[torch.from_numpy(perm)].contiguous().to(dev)
+    out = torch.empty((layer.n, layer.cout), dtype=feats.dtype, device=dev)
+
+    def run(count):
+        prev = None
+        for _ in range(count):
+            kmap = sp.build_map(coords, layer.k, wait=False)
+            sp.forward(feats, w, kmap, out=out)
+            if prev is not None:
+                prev.wait()
+                assert prev.total_entries == e_total
+                prev.free()
+            prev = kmap
+        prev.wait()
+        assert prev.total_entries == e_total
+        prev.free()
+
+    run(max(1, warmup))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    return {"ms_per_step": round(ms, 4), "value": round(flops / (ms * 1e-3) / 1e12, 4), "unit": "TFLOP/s",
+            "note": f"the same steps with the rows in a seeded random order (seed {PERMUTATION_SEED})"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,6 +202,8 @@ def main(argv=None):
                     help="workload index 0..4 (default: the indoor scene)")
     ap.add_argument("--layer", type=int, default=0, help="layer of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-permuted", action="store_true",
+                    help="skip the pass over the rows in a random order")
     ap.add_argument("--no-two-streams", action="store_true",
                     help="skip the two-stream throughput pass (e.g. when tracing kernel durations)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -295,6 +335,9 @@ def main(argv=None):
     if not args.no_two_streams:
         result["two_streams"] = two_stream_throughput(torch, sp, coords, feats, w, layer, args.steps,
                                                       args.warmup, e_total, flops)
+    if not args.no_permuted:
+        result["permuted_rows"] = permuted_throughput(torch, sp, layer, feats_h, w, args.steps, args.warmup,
+                                                      e_total, flops)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(layer, feats_h, w_h)
