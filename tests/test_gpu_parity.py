@@ -351,6 +351,17 @@ def test_forward_small_many_tiles_sampled(sp, dtype):
     _forward_check(sp, kmap, c, 3, 32, 32, dtype, seed=77 if dtype == "f16" else 78, rows=rows)
 
 
+@pytest.mark.parametrize("dtype,cin,cout", [("f16", 1024, 1024), ("bf16", 1024, 8), ("bf16", 8, 1024),
+                                            ("f32", 512, 512), ("f32", 4, 512), ("f32", 512, 4)])
+def test_forward_channel_limits(sp, dtype, cin, cout):
+    """The largest channel counts the ABI takes (1024 in fp16/bf16, 512 in
+    fp32) and the smallest (8 and 4), on a grid of a few ragged tiles."""
+    c = workloads.permuted(workloads.random_grid(cin + cout, 7, 0.45, 1), 3)
+    assert 64 < c.shape[0] < 256
+    kmap = _gpu_map(sp, c, 3)
+    _forward_check(sp, kmap, c, 3, cin, cout, dtype, seed=cin + 2 * cout)
+
+
 @pytest.mark.parametrize("dtype,ch", [("f16", 32), ("bf16", 32), ("f32", 16), ("f16", 128),
                                       ("bf16", 256)])
 @pytest.mark.parametrize("extent", [12, 20])
