@@ -158,9 +158,10 @@ spconv_status spconv_map_lists(const spconv_map* map, const int32_t** d_in_idx,
  * the build first.
  *
  * Requirements: c_in, c_out multiples of 8 in [8, 1024] (F16/BF16), or
- * multiples of 4 in [4, 512] (F32).  Errors: INVALID_ARG (NULL or misaligned
- * pointers, channel counts out of range), UNSUPPORTED (dtype, channel
- * multiple), OUT_OF_MEMORY (workspace), DEVICE.
+ * multiples of 4 in [4, 512] (F32); d_out shares no byte with d_feats or
+ * d_weights (no in-place forward).  Errors: INVALID_ARG (NULL or misaligned
+ * pointers, channel counts out of range, d_out overlapping an input),
+ * UNSUPPORTED (dtype, channel multiple), OUT_OF_MEMORY (workspace), DEVICE.
  */
 spconv_status spconv_forward(const void* d_feats, const void* d_weights, const spconv_map* map,
                              int32_t c_in, int32_t c_out, spconv_dtype dtype, void* d_out,

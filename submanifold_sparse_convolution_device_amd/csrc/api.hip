@@ -424,6 +424,21 @@ spconv_status spconv_forward(const void* d_feats, const void* d_weights, const s
     return fail(SPCONV_ERR_UNSUPPORTED, "c_in = %d and c_out = %d must be multiples of %d", c_in,
                 c_out, mult);
   }
+  {
+    // The output is written while other workgroups still read input rows and
+    // weights: it must not share a byte with either.
+    const uint64_t es = (dtype == SPCONV_F32) ? 4u : 2u;
+    const uint64_t out_b = static_cast<uint64_t>(map->n) * c_out * es;
+    const uint64_t in_b = static_cast<uint64_t>(map->n) * c_in * es;
+    const uint64_t w_b = static_cast<uint64_t>(map->KV) * c_in * c_out * es;
+    auto overlap = [](const void* p, uint64_t np, const void* q, uint64_t nq) {
+      const uint64_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
+      return a0 < b0 + nq && b0 < a0 + np;
+    };
+    if (overlap(d_out, out_b, d_feats, in_b) || overlap(d_out, out_b, d_weights, w_b)) {
+      return fail(SPCONV_ERR_INVALID_ARG, "d_out overlaps the features or the weights");
+    }
+  }
   spconv::ForwardArgs a;
   a.feats = d_feats;
   a.weights = d_weights;

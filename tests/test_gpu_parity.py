@@ -394,6 +394,37 @@ def test_forward_routing_is_exact(sp, dtype):
             assert torch.equal(out, exp), f"offset {k}, {ch} channels"
 
 
+def test_forward_rejects_overlapping_output(sp):
+    """The output may share no byte with the features or the weights (other
+    workgroups still read those while it is written): an in-place or
+    overlapping output is INVALID_ARG and leaves the buffers untouched; an
+    output right after the features in one allocation is fine."""
+    c = workloads.random_grid(23, 9, 0.4, 1)
+    n, ch = c.shape[0], 32
+    kmap = _gpu_map(sp, c, 3)
+    buf = torch.zeros((2 * n + 8, ch), dtype=torch.float16, device=DEV)
+    feats = buf[:n]
+    feats.copy_(workloads.features(n, ch, "f16", 23).to(DEV))
+    w = workloads.weights(3, ch, ch, "f16", 24).to(DEV)
+    before = buf.clone()
+    for out in (feats, buf[n // 2:n // 2 + n], buf[1:n + 1]):
+        with pytest.raises(sp.SpconvError) as e:
+            sp.forward(feats, w, kmap, out=out)
+        assert e.value.name == "SPCONV_ERR_INVALID_ARG"
+    wout = torch.empty((n, ch), dtype=torch.float16, device=DEV)
+    wbuf = torch.zeros(27 * ch * ch + n * ch, dtype=torch.float16, device=DEV)
+    wv = wbuf[:27 * ch * ch].view(27, ch, ch)
+    wv.copy_(w)
+    with pytest.raises(sp.SpconvError) as e:
+        sp.forward(feats, wv, kmap, out=wbuf[27 * ch * ch - 8:27 * ch * ch - 8 + n * ch].view(n, ch))
+    assert e.value.name == "SPCONV_ERR_INVALID_ARG"
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before)
+    ref = sp.forward(feats, w, kmap, out=wout)
+    got = sp.forward(feats, w, kmap, out=buf[n:2 * n])
+    assert torch.equal(got, ref) and torch.equal(buf[:n], before[:n])
+
+
 def test_forward_all_ones_degree(sp):
     """All-ones features and weights: f_out[q][c] = Cin x deg(q), exact in fp16."""
     c = workloads.random_grid(17, 10, 0.5, 1)
