@@ -287,6 +287,56 @@ def test_forward_on_another_stream_follows_the_build(sp):
         m.free()
 
 
+def test_concurrent_host_threads(sp):
+    """Four host threads, each with its own stream, build maps of different
+    sizes and run forwards at once through the library's shared caches and
+    summary-slot pools (ctypes releases the interpreter lock during each
+    call); every map and output equals the single-threaded result."""
+    import threading
+
+    grids = [workloads.random_grid(80 + i, 10 + 2 * i, 0.3, 1) for i in range(4)]
+    inputs, refs = [], []
+    for i, c in enumerate(grids):
+        dc = torch.from_numpy(c).to(DEV)
+        f = workloads.features(c.shape[0], 32, "f16", 90 + i).to(DEV)
+        w = workloads.weights(3, 32, 32, "f16", 95 + i).to(DEV)
+        m = sp.build_map(dc, 3)
+        refs.append((m.counts.copy(), [x.cpu() for x in m.lists()], sp.forward(f, w, m).cpu()))
+        m.free()
+        inputs.append((dc, f, w))
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(i):
+        try:
+            stream = torch.cuda.Stream()
+            dc, f, w = inputs[i]
+            with torch.cuda.stream(stream):
+                for it in range(15):
+                    m = sp.build_map(dc, 3, wait=(it % 2 == 0))
+                    out = sp.forward(f, w, m)
+                    m.wait()
+                    lists = m.lists()
+                    stream.synchronize()
+                    counts, rl, ro = refs[i]
+                    ok = (np.array_equal(m.counts, counts) and torch.equal(lists[0].cpu(), rl[0])
+                          and torch.equal(lists[1].cpu(), rl[1]) and torch.equal(out.cpu(), ro))
+                    m.free()
+                    if not ok:
+                        errors.append(f"thread {i} iteration {it}: result differs")
+                        return
+        except Exception as exc:  # reported below
+            errors.append(f"thread {i}: {exc!r}")
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a thread did not finish"
+    assert not errors, errors
+
+
 def test_map_deterministic(sp):
     c = workloads.permuted(workloads.random_grid(99, 30, 0.1, 2), 99)
     a1, b1 = _gpu_lists(_gpu_map(sp, c, 3))
