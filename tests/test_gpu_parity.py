@@ -475,6 +475,41 @@ def test_forward_rejects_overlapping_output(sp):
     assert torch.equal(got, ref) and torch.equal(buf[:n], before[:n])
 
 
+@pytest.mark.parametrize("dtype,cin,cout", [("f16", 32, 32), ("bf16", 32, 16), ("f16", 64, 64),
+                                            ("bf16", 128, 128), ("bf16", 256, 256), ("f16", 32, 48),
+                                            ("bf16", 8, 24), ("f16", 40, 16)])
+def test_forward_rounds_ties_to_even(sp, dtype, cin, cout):
+    """Sums that fall exactly halfway between two values of the output type
+    (1 + odd x half an ulp, with several signs and binades) come out rounded
+    to the even neighbour in every kernel (small, wide with and without
+    split offsets, tiled, generic); the epilogue's rule, checked exactly.
+    Row 0 gets a + b from the centre and the +x offset (channel 0 only),
+    row 1 gets a alone."""
+    c = np.array([[0, 0, 0, 0], [0, 0, 0, 1]], np.int32)
+    kmap = _gpu_map(sp, c, 3)
+    tdt = TORCH_DT[dtype]
+    half_ulp = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11  # of values in [1, 2): 7 and 10 mantissa bits
+    co = np.arange(cout)
+    scale = np.array([1.0, -1.0, 2.0, -4.0])[co % 4]
+    a = scale
+    b = scale * half_ulp * (2 * ((co // 4) % 4) + 1)  # odd multiples: exact ties
+    f = torch.zeros((2, cin), dtype=tdt)
+    f[:, 0] = 1.0
+    w = torch.zeros((27, cin, cout), dtype=tdt)
+    w[13, 0] = torch.from_numpy(a).to(tdt)
+    w[14, 0] = torch.from_numpy(b).to(tdt)  # offset (0, 0, +1): row 0 reads row 1
+    assert torch.equal(w[13, 0].double(), torch.from_numpy(a)) and torch.equal(w[14, 0].double(), torch.from_numpy(b))
+    out = sp.forward(f.to(DEV), w.to(DEV), kmap).cpu()
+    exp0 = torch.from_numpy(a + b).to(torch.float32).to(tdt)  # exact in fp32, then nearest-even
+    # every sum is a tie: in units of the type's ulp at its binade it ends in exactly one half
+    mbits = 7 if dtype == "bf16" else 10
+    v = np.abs(a + b)
+    units = v / 2.0 ** (np.floor(np.log2(v)) - mbits)
+    assert np.all(units - np.floor(units) == 0.5)
+    assert torch.equal(out[0], exp0), f"row 0: {out[0][:8]} vs {exp0[:8]}"
+    assert torch.equal(out[1], torch.from_numpy(a).to(tdt))
+
+
 def test_forward_all_ones_degree(sp):
     """All-ones features and weights: f_out[q][c] = Cin x deg(q), exact in fp16."""
     c = workloads.random_grid(17, 10, 0.5, 1)
