@@ -510,6 +510,59 @@ def test_forward_rounds_ties_to_even(sp, dtype, cin, cout):
     assert torch.equal(out[1], torch.from_numpy(a).to(tdt))
 
 
+@pytest.mark.parametrize("dtype,cin,cout", [("f16", 32, 32), ("bf16", 64, 64), ("bf16", 128, 48),
+                                            ("f32", 16, 16), ("f32", 48, 24)])
+def test_forward_nonfinite_rows_stay_local(sp, dtype, cin, cout):
+    """A NaN or an infinity in a few input rows reaches exactly the output
+    rows whose neighbourhood holds those rows (lanes of other rows, padding
+    and zero rows never pick it up); every other row matches the oracle."""
+    c = workloads.permuted(workloads.random_grid(61, 11, 0.3, 1), 61)
+    n = c.shape[0]
+    kmap = _gpu_map(sp, c, 3)
+    f = workloads.features(n, cin, dtype, 62)
+    w = workloads.weights(3, cin, cout, dtype, 63)
+    bad = np.array([3, n // 2, n - 1])
+    f[bad[0], 5] = float("nan")
+    f[bad[1], 0] = float("inf")
+    f[bad[2], cin - 1] = float("-inf")
+    out = sp.forward(f.to(DEV), w.to(DEV), kmap).double().cpu().numpy()
+    ref_map = oracle.build_map(c, 3)
+    hit = np.zeros(n, bool)
+    for k in range(27):
+        j, q = ref_map.lists[k]
+        hit[q[np.isin(j, bad)]] = True
+    assert np.array_equal(~np.isfinite(out).all(axis=1), hit)
+    clean = f.double().numpy()
+    clean[bad] = 0.0
+    ref = ref_map.forward(clean, w.double().numpy())
+    rms = float(np.sqrt(np.mean(ref[~hit] ** 2)))
+    assert np.max(np.abs(out[~hit] - ref[~hit])) <= TOL[dtype] * rms
+
+
+@pytest.mark.parametrize("dtype,cin", [("f16", 32), ("f16", 64), ("bf16", 32), ("bf16", 128), ("f32", 16),
+                                       ("f32", 48)])
+def test_forward_subnormal_inputs(sp, dtype, cin):
+    """Features in the subnormal range of their type (scaled by 2^-16 in
+    fp16, 2^-128 in bf16 and fp32) against weights scaled up by 2^10 (2^20),
+    so that the outputs are normal numbers: the products are formed, not
+    flushed to zero, and the output matches the oracle on the same stored
+    values within the usual tolerance."""
+    c = workloads.random_grid(71, 10, 0.3, 1)
+    n = c.shape[0]
+    kmap = _gpu_map(sp, c, 3)
+    fs, ws = (2.0 ** -16, 2.0 ** 10) if dtype == "f16" else (2.0 ** -128, 2.0 ** 20)
+    tdt = TORCH_DT[dtype]
+    f = (workloads.features(n, cin, "f32", 72).double() * fs).to(tdt)
+    tiny = torch.finfo(tdt).tiny
+    assert (f.double().abs() < tiny).double().mean() > 0.9 and (f != 0).double().mean() > 0.9
+    w = (workloads.weights(3, cin, cin, "f32", 73).double() * ws).to(tdt)
+    out = sp.forward(f.to(DEV), w.to(DEV), kmap).double().cpu().numpy()
+    ref = oracle.build_map(c, 3).forward(f.double().numpy(), w.double().numpy())
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    assert rms > 100 * tiny, "the outputs are normal numbers"
+    assert np.max(np.abs(out - ref)) <= TOL[dtype] * rms
+
+
 def test_forward_all_ones_degree(sp):
     """All-ones features and weights: f_out[q][c] = Cin x deg(q), exact in fp16."""
     c = workloads.random_grid(17, 10, 0.5, 1)
