@@ -122,6 +122,31 @@ def test_map_extreme_coordinates(sp):
     assert_map_equal(_gpu_map(sp, c, 5), oracle.build_map(c, 5))
 
 
+@pytest.mark.parametrize("layout", ["x_line", "z_column", "many_batches", "plane_stripes"])
+def test_map_degenerate_layouts(sp, layout):
+    """Layouts that load the hash and the occupancy map unevenly: a whole
+    x line (65,536 voxels on one (b, z, y), so every occupancy run and home
+    window of the line is full), a z column, 4,096 batches of 8 voxels at
+    the same coordinates (keys that differ only in b), and alternate rows of
+    a plane; each against the oracle, with K = 3 and 5, rows permuted."""
+    if layout == "x_line":
+        x = np.arange(65536)
+        c = np.stack([np.zeros_like(x), np.full_like(x, 7), np.full_like(x, 9), x], 1)
+    elif layout == "z_column":
+        z = np.arange(0, 65536, 3)
+        c = np.stack([np.zeros_like(z), z, np.full_like(z, 65535), np.zeros_like(z)], 1)
+    elif layout == "many_batches":
+        b = np.repeat(np.arange(4096), 8)
+        i = np.tile(np.arange(8), 4096)
+        c = np.stack([b, i // 4, (i // 2) % 2, i % 2], 1)
+    else:
+        y, x = np.meshgrid(np.arange(0, 400, 2), np.arange(300), indexing="ij")
+        c = np.stack([np.zeros(y.size), np.full(y.size, 5), y.ravel(), x.ravel()], 1)
+    c = workloads.permuted(np.ascontiguousarray(c, dtype=np.int32), 17)
+    for K in (3, 5):
+        assert_map_equal(_gpu_map(sp, c, K), oracle.build_map(c, K))
+
+
 def test_map_dense_cube_closed_form(sp):
     """Fully active 100^3 cube (1M voxels): count(d) = prod (100 - |d_i|)."""
     n = 100
