@@ -635,6 +635,19 @@ def test_workload_map_and_forward(sp, index):
                    seed=layer.feat_seed, ref_map=ref)
 
 
+def test_workload_permuted_rows(sp):
+    """The bench workload (indoor scene) with its rows in the seeded random
+    order of bench.py's permuted pass: whole map and whole forward against
+    the oracle."""
+    layer = _workload(1).layers[0]
+    perm = np.random.default_rng(7).permutation(layer.n)
+    c = np.ascontiguousarray(layer.coords[perm])
+    ref = oracle.build_map(c, layer.k)
+    kmap = _gpu_map(sp, c, layer.k)
+    assert_map_equal(kmap, ref)
+    _forward_check(sp, kmap, c, layer.k, layer.cin, layer.cout, layer.dtype, seed=layer.feat_seed, ref_map=ref)
+
+
 def test_workload_unet_stack(sp):
     """Four levels x two chained convs; conv 2 takes conv 1's GPU output as
     stored (bf16), and the oracle takes that same tensor, so parity is per
