@@ -58,29 +58,44 @@ __device__ __forceinline__ floatx4 mfma(uint4 a, uint4 b, floatx4 c) {
 
 // Weights in MFMA operand order: block (k, cbg, ch) holds, for lane
 // (g, r) = (l / 16, l mod 16), the 8 values W[k][ch * 32 + 8 g + i][16 cbg + r].
-// One thread per (block, lane).
+// One workgroup per (k, ch, group of 64 output channels): its 32 x 64 slice
+// of W_k is read in 16-byte pieces along the output channels (one per
+// thread, whole rows coalesced), transposed through LDS, and written as up
+// to four whole operand blocks (1 KB each, one per wave).  The first
+// workgroup also clears the 512-byte zero row.
 template <typename T>
 __global__ __launch_bounds__(256) void k_prep_weights(const T* __restrict__ w, uint4* __restrict__ wop,
                                                       uint4* __restrict__ zero, int KV, int cin, int cout) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx < 32) zero[idx] = make_uint4(0u, 0u, 0u, 0u);
-  const int nch = cin / 32, ncbg = cout / 16;
-  const int64_t total = static_cast<int64_t>(KV) * ncbg * nch * 64;
-  if (idx >= total) return;
-  const int lane = static_cast<int>(idx & 63);
-  const int64_t blk = idx >> 6;
-  const int ch = static_cast<int>(blk % nch);
-  const int cbg = static_cast<int>((blk / nch) % ncbg);
-  const int k = static_cast<int>(blk / (static_cast<int64_t>(nch) * ncbg));
-  const int r = lane & 15, g = lane >> 4;
-  const int co = cbg * 16 + r;
-  const int ci0 = ch * 32 + g * 8;
-  T v[8];
+  constexpr int kCols = 64, kStride = kCols + 8;  // row stride of 144 bytes: 16-byte aligned rows
+  __shared__ __align__(16) uint16_t tile[32 * kStride];
+  const int t = threadIdx.x;
+  if (blockIdx.x == 0 && t < 32) zero[t] = make_uint4(0u, 0u, 0u, 0u);
+  const int nch = cin / 32, ncbg = cout / 16, ngrp = (cout + kCols - 1) / kCols;
+  const int64_t b = blockIdx.x;
+  const int grp = static_cast<int>(b % ngrp);
+  const int ch = static_cast<int>((b / ngrp) % nch);
+  const int k = static_cast<int>(b / (static_cast<int64_t>(ngrp) * nch));
+  if (k >= KV) return;  // uniform over the workgroup
+  const int co0 = grp * kCols;
+  {
+    const int row = t >> 3, c8 = (t & 7) * 8;  // C_out is a multiple of 16: a piece is all in or all out
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (co0 + c8 < cout) {
+      v = *reinterpret_cast<const uint4*>(w + (static_cast<int64_t>(k) * cin + ch * 32 + row) * cout + co0 + c8);
+    }
+    *reinterpret_cast<uint4*>(&tile[row * kStride + c8]) = v;
+  }
+  __syncthreads();
+  const int cb = t >> 6, lane = t & 63, r = lane & 15, g = lane >> 4;
+  const int cbg = grp * (kCols / 16) + cb;
+  if (cbg < ncbg) {
+    uint16_t o[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = w[(static_cast<int64_t>(k) * cin + ci0 + i) * cout + co];
-  uint4 o;
-  __builtin_memcpy(&o, v, sizeof(o));
-  wop[idx] = o;
+    for (int i = 0; i < 8; ++i) o[i] = tile[(8 * g + i) * kStride + 16 * cb + r];
+    uint4 out;
+    __builtin_memcpy(&out, o, sizeof(out));
+    wop[((static_cast<int64_t>(k) * ncbg + cbg) * nch + ch) * 64 + lane] = out;
+  }
 }
 
 template <int CIN, int CB, int QB>
@@ -387,8 +402,8 @@ const uint4* workspace_zero_row(const ForwardArgs& a, const void* workspace) {
 hipError_t launch_prep_weights(const ForwardArgs& a, void* workspace, hipStream_t stream) {
   uint4* wop = static_cast<uint4*>(workspace);
   uint4* zero = const_cast<uint4*>(workspace_zero_row(a, workspace));
-  const int64_t total = static_cast<int64_t>(a.KV) * (a.cout / 16) * (a.cin / 32) * 64;
-  const unsigned grid = static_cast<unsigned>((total + 255) / 256);
+  const int64_t groups = static_cast<int64_t>(a.KV) * (a.cin / 32) * ((a.cout + 63) / 64);
+  const unsigned grid = static_cast<unsigned>(groups);
   if (a.dtype == 1) {
     hipLaunchKernelGGL(k_prep_weights<_Float16>, dim3(grid), dim3(256), 0, stream,
                        static_cast<const _Float16*>(a.weights), wop, zero, a.KV, a.cin, a.cout);
