@@ -437,6 +437,40 @@ def test_forward_channel_limits(sp, dtype, cin, cout):
     _forward_check(sp, kmap, c, 3, cin, cout, dtype, seed=cin + 2 * cout)
 
 
+@pytest.mark.parametrize("tiles", [3, 250, 700, 1300, 2600, 3100, 4000])
+def test_forward_small_tile_counts(sp, tiles):
+    """The small-channel kernel across tile counts that give 1 to 12 tile
+    waves per workgroup, spare waves or none, and more tiles than waves
+    (several rounds): a sparse field with dense 8^3 clusters, so some tiles
+    are far heavier than the rest (split or shared with spares, several
+    stages).  Sampled rows, including every row of the heaviest tiles and
+    of the last tile, against the oracle."""
+    rng = np.random.default_rng(tiles)
+    n_target = tiles * 64 - 17
+    n_clusters = max(1, n_target // 20000)
+    ax = np.arange(8)
+    z, y, x = np.meshgrid(ax, ax, ax, indexing="ij")
+    cube = np.stack([z.ravel(), y.ravel(), x.ravel()], 1)
+    parts = [cube + rng.integers(0, 400, size=3) for _ in range(n_clusters)]
+    field = rng.integers(0, 2000, size=(2 * n_target, 3))
+    zyx = np.unique(np.concatenate(parts + [field]), axis=0)
+    zyx = zyx[rng.permutation(zyx.shape[0])[:n_target]]
+    zyx = zyx[np.lexsort((zyx[:, 2], zyx[:, 1], zyx[:, 0]))]
+    c = np.concatenate([np.zeros((zyx.shape[0], 1), np.int64), zyx], 1).astype(np.int32)
+    n = c.shape[0]
+    assert (n + 63) // 64 == tiles
+    kmap = _gpu_map(sp, c, 3)
+    ref = oracle.build_map(c, 3)
+    deg = np.zeros(n, np.int64)
+    for k in range(27):
+        np.add.at(deg, ref.lists[k][1], 1)
+    per_tile = np.add.reduceat(deg, np.arange(0, n, 64))
+    heavy = np.argsort(per_tile)[-3:]
+    rows = np.unique(np.concatenate([rng.choice(n, min(n, 500), replace=False), np.arange(max(0, n - 64), n)]
+                                    + [np.arange(t * 64, min(n, t * 64 + 64)) for t in heavy]))
+    _forward_check(sp, kmap, c, 3, 32, 32, "f16", seed=tiles, ref_map=ref, rows=rows)
+
+
 @pytest.mark.parametrize("dtype,ch", [("f16", 32), ("bf16", 32), ("f32", 16), ("f16", 128),
                                       ("bf16", 256)])
 @pytest.mark.parametrize("extent", [12, 20])
