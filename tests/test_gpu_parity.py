@@ -445,13 +445,15 @@ def test_forward_channel_limits(sp, dtype, cin, cout):
     _forward_check(sp, kmap, c, 3, cin, cout, dtype, seed=cin + 2 * cout)
 
 
-@pytest.mark.parametrize("cin,cout", [(64, 64), (128, 128), (256, 256), (256, 32)])
+@pytest.mark.parametrize("cin,cout", [(64, 64), (128, 128), (256, 256), (256, 32),
+                                      (32, 64), (64, 48), (128, 80), (256, 48)])
 @pytest.mark.parametrize("tiles", [2, 40, 130, 400])
 def test_forward_wide_tile_counts(sp, cin, cout, tiles):
     """The wide kernel's launch choices across grid sizes: offsets split over
     up to 8 workgroups with a reduction (few tiles), narrower workgroups, and
-    one workgroup per tile and column group (many tiles).  A clustered grid
-    in bf16; sampled rows, including the last tile's, against the oracle."""
+    one workgroup per tile and column group (many tiles); the last four
+    shapes go to the tiled kernel instead.  A clustered grid in bf16;
+    sampled rows, including the last tile's, against the oracle."""
     rng = np.random.default_rng(tiles * 7 + cin)
     n_target = tiles * 64 - 5
     zyx = np.unique(np.concatenate([rng.integers(0, 24, size=(n_target, 3)),
