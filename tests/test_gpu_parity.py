@@ -468,6 +468,25 @@ def test_forward_wide_tile_counts(sp, cin, cout, tiles):
     _forward_check(sp, kmap, c, 3, cin, cout, "bf16", seed=tiles + cin, rows=rows)
 
 
+@pytest.mark.parametrize("K,dtype,cin,cout", [(7, "f16", 16, 16), (5, "bf16", 40, 24), (3, "f32", 48, 24),
+                                              (5, "f32", 512, 64), (7, "bf16", 64, 32)])
+@pytest.mark.parametrize("tiles", [2, 130, 400])
+def test_forward_generic_tile_counts(sp, K, dtype, cin, cout, tiles):
+    """The generic kernel (K = 5 and 7, channel counts that are not multiples
+    of 16, fp32 beyond the small shapes) across grid sizes, on a clustered
+    grid; sampled rows against the oracle."""
+    rng = np.random.default_rng(tiles * 11 + K + cin)
+    n_target = tiles * 64 - 9
+    zyx = np.unique(np.concatenate([rng.integers(0, 20, size=(n_target, 3)),
+                                    rng.integers(0, 200, size=(2 * n_target, 3))]), axis=0)
+    zyx = zyx[rng.permutation(zyx.shape[0])[:n_target]]
+    c = np.concatenate([np.zeros((n_target, 1), np.int64), zyx], 1).astype(np.int32)
+    n = c.shape[0]
+    kmap = _gpu_map(sp, c, K)
+    rows = np.unique(np.concatenate([rng.choice(n, min(n, 200), replace=False), np.arange(max(0, n - 64), n)]))
+    _forward_check(sp, kmap, c, K, cin, cout, dtype, seed=tiles + cin + K, rows=rows)
+
+
 @pytest.mark.parametrize("tiles", [3, 250, 700, 1300, 2600, 3100, 4000])
 def test_forward_small_tile_counts(sp, tiles):
     """The small-channel kernel across tile counts that give 1 to 12 tile
