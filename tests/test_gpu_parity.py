@@ -370,6 +370,28 @@ def test_concurrent_host_threads(sp):
     assert not errors, errors
 
 
+def test_forward_workspace_reuse_across_shapes(sp):
+    """Forwards of different shapes on one stream with no host wait between
+    them: the stream's forward workspace (operand-order weights, zero row,
+    split partials) is regrown and reused while earlier forwards may still
+    be running; every output equals the same forward run alone."""
+    c = workloads.random_grid(55, 12, 0.35, 1)
+    n = c.shape[0]
+    kmap = _gpu_map(sp, c, 3)
+    shapes = [(32, 32, "f16"), (64, 64, "bf16"), (256, 256, "bf16"), (32, 48, "f16"), (128, 128, "f16"),
+              (64, 64, "bf16"), (256, 32, "bf16"), (16, 16, "f32")]
+    inputs = [(workloads.features(n, ci, dt, 100 + i).to(DEV), workloads.weights(3, ci, co, dt, 200 + i).to(DEV))
+              for i, (ci, co, dt) in enumerate(shapes)]
+    alone = []
+    for f, w in inputs:
+        alone.append(sp.forward(f, w, kmap).cpu())
+        torch.cuda.synchronize()
+    outs = [sp.forward(f, w, kmap) for f, w in inputs for _ in range(2)]
+    torch.cuda.synchronize()
+    for i, ref in enumerate(alone):
+        assert torch.equal(outs[2 * i].cpu(), ref) and torch.equal(outs[2 * i + 1].cpu(), ref), shapes[i]
+
+
 def test_map_deterministic(sp):
     c = workloads.permuted(workloads.random_grid(99, 30, 0.1, 2), 99)
     a1, b1 = _gpu_lists(_gpu_map(sp, c, 3))
