@@ -32,7 +32,13 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
-DEFAULT_WORKLOAD = 1  # the indoor scene: 150k voxels, K=3, C=32, fp16
+# The largest configuration that fits one GPU: 8 batched LiDAR frames
+# (640,812 voxels), K=3, C=128, bf16.  Its K=5 C=64 layer and the indoor
+# scene (150k voxels, K=3, C=32, fp16) are timed the same way and reported
+# beside it in the same line.
+DEFAULT_WORKLOAD = 4
+DEFAULT_LAYER = 0
+EXTRA_LAYERS = ((4, 1), (1, 0))
 PERMUTATION_SEED = 7  # the random row order of the permuted pass
 
 ELEM = {"f32": 4, "f16": 2, "bf16": 2}
@@ -40,35 +46,75 @@ ELEM = {"f32": 4, "f16": 2, "bf16": 2}
 
 def algorithmic_forward_bytes(n, e, kv, cin, cout, dtype):
     """Minimum HBM bytes of one forward: each input row read once, each output
-    row written once, the weights once, and the int32 input row index of every
-    non-centre entry once (the output row of an entry is implied by its
-    position in the output-ordered lists)."""
+    row written once, the weights once, and 8 bytes (an int32 input and output
+    row index) per non-centre entry of the map."""
     s = ELEM[dtype]
-    return n * cin * s + n * cout * s + kv * cin * cout * s + 4 * (e - n)
+    return n * cin * s + n * cout * s + kv * cin * cout * s + 8 * (e - n)
 
 
-FORWARD_SOURCES = ("forward.hip",)
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_forward_small_indoor_c32_f16_hbm_traffic.md")
+def roofline(layer, e, fwd_ms, traffic=None):
+    """Roofline of one forward: the ceiling is min(MFMA peak, AI x HBM peak)
+    with AI = 2 E C_in C_out / algorithmic bytes; `bound` names the side that
+    sets it, and `achieved`/`peak`/`frac` are in that side's unit.  Both
+    fractions are reported beside it."""
+    kv = layer.k ** 3
+    flops = 2.0 * e * layer.cin * layer.cout
+    nbytes = algorithmic_forward_bytes(layer.n, e, kv, layer.cin, layer.cout, layer.dtype)
+    ai = flops / nbytes
+    t = fwd_ms * 1e-3
+    gbs = nbytes / t / 1e9
+    tflops = flops / t / 1e12
+    mfma_peak = MFMA_PEAK_TFLOPS[layer.dtype]
+    hbm_frac = gbs / HBM_PEAK_GBS
+    mfma_frac = tflops / mfma_peak
+    mfma_bound = mfma_peak * 1e12 < ai * HBM_PEAK_GBS * 1e9
+    r = {
+        "bound": "mfma" if mfma_bound else "hbm",
+        "achieved": round(tflops if mfma_bound else gbs, 2),
+        "peak": mfma_peak if mfma_bound else HBM_PEAK_GBS,
+        "unit": "TFLOP/s" if mfma_bound else "GB/s",
+        "frac": round(mfma_frac if mfma_bound else hbm_frac, 4),
+        "traffic": traffic,
+        "algorithmic_bytes_per_launch": int(nbytes),
+        "flops_per_launch": int(flops),
+        "arithmetic_intensity": round(ai, 1),
+        "hbm_frac": round(hbm_frac, 4),
+        "mfma_frac": round(mfma_frac, 4),
+        "time_at_roofline_us": round(max(flops / (mfma_peak * 1e12), nbytes / (HBM_PEAK_GBS * 1e9)) * 1e6, 2),
+    }
+    return r
 
 
-def forward_source_digest():
-    """sha256 of the source file of the small-channel forward kernel."""
+# Counter summaries of HBM traffic per forward launch, by (workload, layer):
+# the profile and the kernel sources whose sha256 it was taken on.
+TRAFFIC_PROFILES = {
+    (4, 0): ("k_forward_wide_batch8_k3_c128_bf16_hbm_traffic.md", ("forward_wide.hip", "forward_tiled.hip")),
+    (1, 0): ("k_forward_small_indoor_c32_f16_hbm_traffic.md", ("forward.hip",)),
+}
+
+
+def source_digest(names):
+    """sha256 over the named kernel source files, in order."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "submanifold_sparse_convolution_device_amd", "csrc")
-    for name in FORWARD_SOURCES:
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def recorded_traffic():
+def recorded_traffic(workload, layer):
     """HBM bytes per forward launch from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or
-    None when there is none or the kernel source changed since it was taken."""
+    None when there is none or the kernel sources changed since it was taken."""
+    entry = TRAFFIC_PROFILES.get((workload, layer))
+    if entry is None:
+        return None
+    name, sources = entry
     try:
-        with open(TRAFFIC_PROFILE) as f:
+        with open(os.path.join(ROOT, "profiles", name)) as f:
             text = f.read()
     except OSError:
         return None
@@ -78,7 +124,7 @@ def recorded_traffic():
             key, _, val = line[2:].partition(": ")
             fields[key.strip("` ")] = val.strip("` ")
     try:
-        if fields["forward_source_sha256"] != forward_source_digest():
+        if fields["forward_source_sha256"] != source_digest(sources):
             return None
         return int(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
@@ -97,28 +143,88 @@ def copy_calibration(torch, dev, mib=256, reps=5):
     del src, dst
 
 
-def cpu_baseline(layer, feats, w, budget_s=12.0, max_passes=200):
-    """The oracle, as it stands, on the same workload: map build (ordered-tree
-    lookups) plus fp64 forward, single-threaded, repeated until ~budget_s."""
+def host_cpu():
+    """(logical CPUs, model name) of the host."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count() or 0, model
+
+
+def cpu_baseline(layer, feats, w, leg_s=8.0):
+    """The oracle, as it stands, timed on the host on a bounded sample of the
+    same workload, in two legs:
+      * all cores: the map build (single-threaded ordered-tree lookups) plus
+        the fp64 forward split over output rows on every host thread, over
+        the whole voxel set;
+      * one core: the map build plus the serial fp64 forward, over the first
+        frame of the batch (batch index 0) when there are several, else the
+        whole set.
+    Each leg's value is 2 |map| C_in C_out / t over what it ran, t being the
+    mean of passes repeated for about leg_s seconds."""
+    import numpy as np
     import oracle
 
+    nproc, model = host_cpu()
+    threads = oracle.max_threads()
     fd, wd = feats.double().numpy(), w.double().numpy()
-    times = []
-    e = 0
-    while len(times) < max_passes and sum(times) < budget_s:
+
+    # Each leg repeats its pass until it has run about `leg_s` seconds.
+    t_all, passes_all = 0.0, 0
+    t_build = 0.0
+    while passes_all == 0 or t_all < leg_s:
         t0 = time.perf_counter()
         m = oracle.build_map(layer.coords, layer.k)
-        m.forward(fd, wd)
-        times.append(time.perf_counter() - t0)
-        e = m.total_entries
-    t = sum(times) / len(times)
+        t1 = time.perf_counter()
+        m.forward_parallel(fd, wd, threads)
+        t2 = time.perf_counter()
+        t_build += t1 - t0
+        t_all += t2 - t0
+        passes_all += 1
+        e_all = m.total_entries
+        del m
+    t_build /= passes_all
+    t_all /= passes_all
+
+    c = layer.coords
+    sel = c[:, 0] == c[0, 0]
+    one_frame = bool(sel.sum() < c.shape[0])
+    idx = np.nonzero(sel)[0]
+    t_one, passes_one = 0.0, 0
+    while passes_one == 0 or t_one < leg_s:
+        t0 = time.perf_counter()
+        m1 = oracle.build_map(c[idx], layer.k)
+        m1.forward(fd[idx], wd)
+        t_one += time.perf_counter() - t0
+        passes_one += 1
+        e_one = m1.total_entries
+        del m1
+    t_one /= passes_one
+    flop = 2.0 * layer.cin * layer.cout
     return {
-        "value": 2.0 * e * layer.cin * layer.cout / t / 1e12,
+        "value": round(flop * e_all / t_all / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"whole workload (map build + fp64 forward), {len(times)} pass(es), "
-                  f"{t:.2f} s per pass",
+        "sample": f"whole workload ({layer.n} voxels, {e_all} entries): map build {t_build:.2f} s "
+                  f"single-threaded + fp64 forward on {threads} threads, {t_all:.2f} s per pass, "
+                  f"{passes_all} pass(es)",
+        "nproc": nproc,
+        "cpu_model": model,
+        "single_core": {
+            "value": round(flop * e_one / t_one / 1e12, 6),
+            "unit": "TFLOP/s",
+            "cores": 1,
+            "sample": (f"first frame of the batch ({idx.shape[0]} voxels, {e_one} entries)" if one_frame
+                       else f"whole workload ({e_one} entries)")
+            + f": map build + serial fp64 forward, {t_one:.2f} s per pass, {passes_one} pass(es)",
+        },
     }
 
 
@@ -193,48 +299,17 @@ def permuted_throughput(torch, sp, layer, feats_h, w, steps, warmup, e_total, fl
             "note": f"the same steps with the rows in a seeded random order (seed {PERMUTATION_SEED})"}
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD,
-                    help="workload index 0..4 (default: the indoor scene)")
-    ap.add_argument("--layer", type=int, default=0, help="layer of the workload")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-permuted", action="store_true",
-                    help="skip the pass over the rows in a random order")
-    ap.add_argument("--no-two-streams", action="store_true",
-                    help="skip the two-stream throughput pass (e.g. when tracing kernel durations)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="first run a 256 MiB device copy (reference for the HBM byte counters)")
-    args = ap.parse_args(argv)
-
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library has no "
-              "multi-GPU path; the workload would shard by frame, one frame set per GPU",
-              file=sys.stderr)
-        return 2
-
+def measure(torch, sp, layer, steps, warmup, events_wanted=10):
+    """Single-stream steps over `layer`; returns the step time and the mean
+    build and forward times from HIP events on the launch stream."""
     import numpy as np
-    import torch
 
-    import submanifold_sparse_convolution_device_amd as sp
-    import workloads
-
-    sp.lib()
     dev = torch.device("cuda:0")
-    if args.copy_calibration:
-        copy_calibration(torch, dev)
-    wl = workloads.make_workload(args.workload)
-    layer = wl.layers[args.layer]
-    feats_h, w_h = workloads.layer_inputs(layer)
+    feats_h, w_h = _inputs(layer)
     coords = torch.from_numpy(layer.coords).to(dev)
     feats = feats_h.to(dev)
     w = w_h.to(dev)
     out = torch.empty((layer.n, layer.cout), dtype=feats.dtype, device=dev)
-    print(f"[bench] workload={wl.name} layer={args.layer} N={layer.n} K={layer.k} "
-          f"C={layer.cin}->{layer.cout} {layer.dtype}", file=sys.stderr, flush=True)
 
     # One step: the map build, enqueued without a host wait, then the forward
     # on the same stream.  The previous step's map is waited on (its device
@@ -257,21 +332,21 @@ def main(argv=None):
         kmap.free()  # stream-ordered release, as a network layer would do
         return e
 
-    for _ in range(args.warmup):
+    e_total = None
+    for _ in range(max(1, warmup)):
         e_total = retire(step())
     torch.cuda.synchronize()
-    kv = layer.k ** 3
 
     # HIP events on a sample of the timed steps (about ten, evenly spread):
     # an event record costs host and device time of its own, so timing every
     # step would slow the steps it measures.
-    stride = max(1, args.steps // 10)
-    sampled = list(range(0, args.steps, stride))
+    stride = max(1, steps // events_wanted)
+    sampled = list(range(0, steps, stride))
     events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     prev = None
-    for i in range(args.steps):
+    for i in range(steps):
         kmap = step(events.get(i))
         if prev is not None:
             assert retire(prev) == e_total
@@ -279,22 +354,96 @@ def main(argv=None):
     assert retire(prev) == e_total
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    build_ms = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in events.values()]))
-    fwd_ms = float(np.mean([ev[1].elapsed_time(ev[2]) for ev in events.values()]))
+    return {
+        "ms_step": (t1 - t0) * 1e3 / steps,
+        "build_ms": float(np.mean([ev[0].elapsed_time(ev[1]) for ev in events.values()])),
+        "fwd_ms": float(np.mean([ev[1].elapsed_time(ev[2]) for ev in events.values()])),
+        "e_total": e_total,
+        "coords": coords, "feats": feats, "w": w, "feats_h": feats_h, "w_h": w_h,
+    }
 
+
+def _inputs(layer):
+    import workloads
+
+    return workloads.layer_inputs(layer)
+
+
+def layer_summary(wl, layer, li, r, traffic):
+    flops = 2.0 * r["e_total"] * layer.cin * layer.cout
+    return {
+        "workload": wl.name,
+        "layer": li,
+        "n_voxels": layer.n,
+        "map_entries": r["e_total"],
+        "kernel": layer.k,
+        "c_in": layer.cin,
+        "c_out": layer.cout,
+        "dtype": layer.dtype,
+        "ms_per_step": round(r["ms_step"], 4),
+        "value": round(flops / (r["ms_step"] * 1e-3) / 1e12, 4),
+        "map_build_ms": round(r["build_ms"], 4),
+        "map_build_mvoxel_per_s": round(layer.n / (r["build_ms"] * 1e-3) / 1e6, 2),
+        "forward_ms": round(r["fwd_ms"], 4),
+        "forward_tflops": round(flops / (r["fwd_ms"] * 1e-3) / 1e12, 4),
+        "roofline": roofline(layer, r["e_total"], r["fwd_ms"], traffic),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD,
+                    help="workload index 0..4 (default: the 8 batched LiDAR frames)")
+    ap.add_argument("--layer", type=int, default=DEFAULT_LAYER, help="layer of the workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the extra layers reported beside the default one")
+    ap.add_argument("--no-permuted", action="store_true",
+                    help="skip the pass over the rows in a random order")
+    ap.add_argument("--no-two-streams", action="store_true",
+                    help="skip the two-stream throughput pass (e.g. when tracing kernel durations)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a 256 MiB device copy (reference for the HBM byte counters)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library has no "
+              "multi-GPU path; the workload would shard by frame, one frame set per GPU",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import submanifold_sparse_convolution_device_amd as sp
+    import workloads
+
+    sp.lib()
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+    wl = workloads.make_workload(args.workload)
+    layer = wl.layers[args.layer]
+    print(f"[bench] workload={wl.name} layer={args.layer} N={layer.n} K={layer.k} "
+          f"C={layer.cin}->{layer.cout} {layer.dtype}", file=sys.stderr, flush=True)
+    r = measure(torch, sp, layer, args.steps, args.warmup)
+    e_total = r["e_total"]
+    summary = layer_summary(wl, layer, args.layer, r, recorded_traffic(args.workload, args.layer))
     flops = 2.0 * e_total * layer.cin * layer.cout
-    value = flops / (ms_step * 1e-3) / 1e12
-    fwd_bytes = algorithmic_forward_bytes(layer.n, e_total, kv, layer.cin, layer.cout, layer.dtype)
-    achieved = fwd_bytes / (fwd_ms * 1e-3) / 1e9
+    rl = dict(summary["roofline"])
+    rl["kernel"] = ("k_forward_small (fused gather-MFMA-accumulate)" if layer.cin <= 32
+                    else "k_forward_wide / k_forward_tiled (fused gather-MFMA-accumulate; the forward "
+                         "call, whose weight re-layout kernel is included)")
     result = {
         "metric": "sparse-conv effective TFLOP/s (2*|map|*Cin*Cout/t) + map build Mvoxel/s",
-        "value": round(value, 4),
+        "value": summary["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": summary["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -303,27 +452,18 @@ def main(argv=None):
         "config": {
             "workload": wl.name,
             "description": wl.description,
+            "layer": args.layer,
             "n_voxels": layer.n,
             "map_entries": e_total,
             "kernel": layer.k,
             "c_in": layer.cin,
             "c_out": layer.cout,
         },
-        "map_build_mvoxel_per_s": round(layer.n / (build_ms * 1e-3) / 1e6, 2),
-        "map_build_ms": round(build_ms, 4),
-        "forward_ms": round(fwd_ms, 4),
-        "forward_tflops": round(flops / (fwd_ms * 1e-3) / 1e12, 4),
-        "roofline": {
-            "kernel": "k_forward_small (fused gather-MFMA-accumulate)" if layer.cin <= 32
-                      else "k_forward_wide / k_forward_tiled (fused gather-MFMA-accumulate)",
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic() if (args.workload, args.layer) == (DEFAULT_WORKLOAD, 0) else None,
-            "algorithmic_bytes_per_launch": int(fwd_bytes),
-        },
+        "map_build_mvoxel_per_s": summary["map_build_mvoxel_per_s"],
+        "map_build_ms": summary["map_build_ms"],
+        "forward_ms": summary["forward_ms"],
+        "forward_tflops": summary["forward_tflops"],
+        "roofline": rl,
     }
     # The same steps with two frames in flight: step i on stream i mod 2, each
     # stream retiring its own previous map, no waits between the streams.
@@ -333,14 +473,27 @@ def main(argv=None):
     # and the roofline keep (a kernel timed while another stream runs would
     # not describe the kernel).
     if not args.no_two_streams:
-        result["two_streams"] = two_stream_throughput(torch, sp, coords, feats, w, layer, args.steps,
-                                                      args.warmup, e_total, flops)
+        result["two_streams"] = two_stream_throughput(torch, sp, r["coords"], r["feats"], r["w"], layer,
+                                                      args.steps, args.warmup, e_total, flops)
     if not args.no_permuted:
-        result["permuted_rows"] = permuted_throughput(torch, sp, layer, feats_h, w, args.steps, args.warmup,
-                                                      e_total, flops)
+        result["permuted_rows"] = permuted_throughput(torch, sp, layer, r["feats_h"], r["w"], args.steps,
+                                                      args.warmup, e_total, flops)
+    main_inputs = (r["feats_h"], r["w_h"])
+    del r
+    if not args.no_extra and (args.workload, args.layer) == (DEFAULT_WORKLOAD, DEFAULT_LAYER):
+        extra = []
+        for wi, li in EXTRA_LAYERS:
+            xwl = wl if wi == args.workload else workloads.make_workload(wi)
+            xl = xwl.layers[li]
+            print(f"[bench] extra: workload={xwl.name} layer={li} N={xl.n} K={xl.k} "
+                  f"C={xl.cin}->{xl.cout} {xl.dtype}", file=sys.stderr, flush=True)
+            xr = measure(torch, sp, xl, args.steps, args.warmup)
+            extra.append(layer_summary(xwl, xl, li, xr, recorded_traffic(wi, li)))
+            del xr
+        result["other_layers"] = extra
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(layer, feats_h, w_h)
+        result["cpu_baseline"] = cpu_baseline(layer, *main_inputs)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -74,6 +74,10 @@ def _lib() -> ctypes.CDLL:
         lib.oracle_map_list.restype = ctypes.c_int
         lib.oracle_forward.argtypes = [ctypes.c_void_p, _f64p, _f64p, ctypes.c_int32, ctypes.c_int32, _f64p]
         lib.oracle_forward.restype = ctypes.c_int
+        lib.oracle_forward_parallel.argtypes = lib.oracle_forward.argtypes + [ctypes.c_int32]
+        lib.oracle_forward_parallel.restype = ctypes.c_int
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ctypes.c_int32
         lib.oracle_forward_rows.argtypes = [ctypes.c_void_p, _f64p, _f64p, ctypes.c_int32, ctypes.c_int32,
                                             _i64p, ctypes.c_int64, _f64p]
         lib.oracle_forward_rows.restype = ctypes.c_int
@@ -142,6 +146,23 @@ class OracleMap:
             raise OracleError(st)
         return out
 
+    def forward_parallel(self, feats: np.ndarray, weights: np.ndarray, threads: int = 0) -> np.ndarray:
+        """The same fp64 forward split over output rows on ``threads`` OpenMP
+        threads (0: all the runtime offers).  Same terms in the same order per
+        output value as ``forward``, hence bit-identical to it."""
+        if not self.has_lists:
+            raise ValueError("built with lists=False: use forward_rows")
+        f = np.ascontiguousarray(np.asarray(feats, dtype=np.float64))
+        w = np.ascontiguousarray(np.asarray(weights, dtype=np.float64))
+        cin, cout = w.shape[1], w.shape[2]
+        assert f.shape == (self.N, cin) and w.shape[0] == self.K ** 3
+        out = np.empty((self.N, cout), np.float64)
+        st = _lib().oracle_forward_parallel(self._h, _ptr(f, _f64p), _ptr(w, _f64p), cin, cout,
+                                            _ptr(out, _f64p), int(threads))
+        if st != 0:
+            raise OracleError(st)
+        return out
+
     def forward_rows(self, feats: np.ndarray, weights: np.ndarray, rows: Sequence[int]) -> np.ndarray:
         """fp64 forward for selected output rows, evaluated from the coordinate
         table one row at a time."""
@@ -173,6 +194,11 @@ def build_map(coords: np.ndarray, K: int) -> OracleMap:
 def build_table(coords: np.ndarray, K: int) -> OracleMap:
     """Coordinate table only, for row-at-a-time evaluation."""
     return OracleMap(coords, K, lists=False)
+
+
+def max_threads() -> int:
+    """Threads the oracle's parallel forward uses by default."""
+    return int(_lib().oracle_max_threads())
 
 
 def offset_index(dz: int, dy: int, dx: int, K: int) -> int:

@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libspconv_oracle.so")
 def build(verbose: bool = False) -> str:
     """Compile the oracle with g++ (no fast-math) and return the library path."""
     tmp = LIB + ".tmp"
-    cmd = ["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-Wall", "-Wextra", "-o", tmp, SRC]
+    cmd = ["g++", "-O2", "-std=c++17", "-fopenmp", "-shared", "-fPIC", "-Wall", "-Wextra", "-o", tmp, SRC]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

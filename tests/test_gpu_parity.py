@@ -779,39 +779,22 @@ def test_workload_unet_stack(sp):
 
 
 @pytest.mark.parametrize("li", [0, 1])
-def test_workload_batched_frames_sampled(sp, li):
-    """640k voxels: map invariants at full size, oracle rows sampled (neighbour
-    sets and features computed one row at a time)."""
-    wl = _workload(4)
-    layer = wl.layers[li]
-    c = layer.coords
-    kv = layer.k ** 3
-    kmap = _gpu_map(sp, c, layer.k)
-    a, b = _gpu_lists(kmap)
-    counts = kmap.counts
-    assert counts[kv // 2] == layer.n
-    assert np.array_equal(counts, counts[::-1])  # count(d) = count(-d)
-    # every entry at full size: coords[in] - coords[out] is its offset, same batch
-    ci = c.astype(np.int64)
-    r = (layer.k - 1) // 2
-    for k in range(kv):
-        lo, hi = kmap.offsets[k], kmap.offsets[k + 1]
-        d = ci[a[lo:hi]] - ci[b[lo:hi]]
-        dz, dy, dx = oracle.offset_of(k, layer.k)
-        assert np.all(d == np.array([0, dz, dy, dx]))
-        assert np.all(np.diff(b[lo:hi]) > 0)
-    # sampled rows against the oracle's lookups
-    rng = np.random.default_rng(li)
-    rows = np.sort(rng.choice(layer.n, 2000, replace=False))
-    ref = oracle.build_table(c, layer.k)
-    nbr = ref.neighbours(rows)
-    gnbr = np.full((rows.shape[0], kv), -1, np.int64)
-    pos = {int(q): i for i, q in enumerate(rows)}
-    for k in range(kv):
-        lo, hi = kmap.offsets[k], kmap.offsets[k + 1]
-        sel = np.isin(b[lo:hi], rows)
-        for j, q in zip(a[lo:hi][sel], b[lo:hi][sel]):
-            gnbr[pos[int(q)], k] = j
-    assert np.array_equal(gnbr, nbr)
-    _forward_check(sp, kmap, c, layer.k, layer.cin, layer.cout, layer.dtype, seed=layer.feat_seed,
-                   ref_map=ref, rows=rows)
+def test_workload_batched_frames(sp, li):
+    """8 batched LiDAR frames (640,812 voxels), K = 3 at C = 128 and K = 5 at
+    C = 64, bf16: the whole map against the oracle's as per-offset sets
+    (every list element, counts and offsets), and the whole forward against
+    the oracle's fp64 forward on every output row (its row-parallel variant,
+    pinned bit-identical to the serial one on the CPU)."""
+    layer = _workload(4).layers[li]
+    ref = oracle.build_map(layer.coords, layer.k)
+    kmap = _gpu_map(sp, layer.coords, layer.k)
+    assert_map_equal(kmap, ref)
+    f = workloads.features(layer.n, layer.cin, layer.dtype, layer.feat_seed)
+    w = workloads.weights(layer.k, layer.cin, layer.cout, layer.dtype, layer.weight_seed)
+    out = sp.forward(f.to(DEV), w.to(DEV), kmap).double().cpu().numpy()
+    r = ref.forward_parallel(f.double().numpy(), w.double().numpy())
+    rms = float(np.sqrt(np.mean(r ** 2)))
+    diff = np.abs(out - r)
+    assert np.all(np.isfinite(out))
+    bound = TOL[layer.dtype] * rms + HALF_ULP[layer.dtype] * np.abs(r)
+    assert np.all(diff <= bound), f"max |err| {float(diff.max()):.3e} vs RMS {rms:.3e}"

@@ -154,6 +154,28 @@ def test_forward_rows_matches_full_forward():
             assert (hit.tolist() or [-1]) == [nbr[i, k]]
 
 
+@pytest.mark.parametrize("threads", [0, 1, 2, 3, 7])
+def test_forward_parallel_is_bit_identical(threads):
+    """The row-parallel timing variant sums the same terms in the same order
+    per output value as the serial forward (thread counts that do not divide
+    the rows, more threads than needed, the runtime's default), and both agree
+    with the dense conv3d reference."""
+    c = workloads.permuted(workloads.random_grid(33, 11, 0.25, 2), 33)
+    rng = np.random.default_rng(33)
+    f = rng.standard_normal((c.shape[0], 12))
+    w = rng.standard_normal((27, 12, 20))
+    m = oracle.build_map(c, 3)
+    serial = m.forward(f, w)
+    par = m.forward_parallel(f, w, threads)
+    assert np.array_equal(serial, par)
+    tiny = np.array([[0, 1, 1, 1], [0, 1, 1, 2]], np.int32)
+    mt = oracle.build_map(tiny, 3)
+    ft, wt = rng.standard_normal((2, 4)), rng.standard_normal((27, 4, 4))
+    assert np.array_equal(mt.forward(ft, wt), mt.forward_parallel(ft, wt, 5))
+    ref = _dense_conv3d_reference(c, f, w, 3)
+    assert np.max(np.abs(par - ref)) <= 1e-12 * np.sqrt(np.mean(ref ** 2))
+
+
 def test_forward_routing_special_cases():
     c = workloads.random_grid(41, 8, 0.3, 1)
     n = c.shape[0]
