@@ -167,6 +167,32 @@ spconv_status spconv_forward(const void* d_feats, const void* d_weights, const s
                              int32_t c_in, int32_t c_out, spconv_dtype dtype, void* d_out,
                              void* hip_stream);
 
+/*
+ * The same forward as spconv_forward, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  It calls no device allocator.  Where spconv_forward
+ * would take its workspace from the stream's cache (F16/BF16 shapes with
+ * c_in in {32, 64, 128, 256} outside the small-channel ones: the weights in
+ * MFMA operand order, a zero row and any fp32 partial outputs), this variant
+ * uses a fixed scratch array of 32 MiB per device instead, held by the
+ * library from its first use on a device until the process ends.  The
+ * caller still passes the inputs and the output.
+ *
+ * Every call on one device shares that device's scratch: calls whose work
+ * overlaps on one device (on different streams, or on one stream while an
+ * earlier call of this variant is still using it from another) race and may
+ * return wrong results.  Calls ordered one after another are safe: each
+ * overwrites everything it reads of the scratch.
+ *
+ * Arguments, ordering after the map's build, outputs and errors as for
+ * spconv_forward, plus UNSUPPORTED when the forward needs more workspace
+ * than the scratch holds (the message states both sizes) and INVALID_ARG
+ * when the current device is not the map's.
+ */
+spconv_status spconv_forward_noalloc(const void* d_feats, const void* d_weights, const spconv_map* map,
+                                     int32_t c_in, int32_t c_out, spconv_dtype dtype, void* d_out,
+                                     void* hip_stream);
+
 /* Releases a map.  Its buffers go back, in the order of the build's stream,
  * to that stream's cache of map blocks (or to the pool); the caller must not
  * free a map while work on another stream still reads it.  NULL is ignored. */

@@ -36,7 +36,7 @@ DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 EXPORTED = (
     "spconv_abi_version", "spconv_build_map", "spconv_build_map_async", "spconv_map_wait",
     "spconv_map_info", "spconv_map_counts", "spconv_map_lists", "spconv_forward",
-    "spconv_map_free", "spconv_status_string", "spconv_last_error",
+    "spconv_forward_noalloc", "spconv_map_free", "spconv_status_string", "spconv_last_error",
 )
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
     L.spconv_map_lists.restype = ctypes.c_int
     L.spconv_forward.argtypes = [vp, vp, vp, i32, i32, ctypes.c_int, vp, vp]
     L.spconv_forward.restype = ctypes.c_int
+    L.spconv_forward_noalloc.argtypes = L.spconv_forward.argtypes
+    L.spconv_forward_noalloc.restype = ctypes.c_int
     L.spconv_map_free.argtypes, L.spconv_map_free.restype = [vp], None
     L.spconv_status_string.argtypes, L.spconv_status_string.restype = [ctypes.c_int], ctypes.c_char_p
     L.spconv_last_error.argtypes, L.spconv_last_error.restype = [], ctypes.c_char_p
@@ -153,6 +155,11 @@ def spconv_map_lists(handle: int) -> Tuple[int, int]:
 def spconv_forward(d_feats: int, d_weights: int, handle: int, c_in: int, c_out: int, dtype: int,
                    d_out: int, hip_stream: int) -> None:
     _check(lib().spconv_forward(d_feats, d_weights, handle, c_in, c_out, dtype, d_out, hip_stream))
+
+
+def spconv_forward_noalloc(d_feats: int, d_weights: int, handle: int, c_in: int, c_out: int, dtype: int,
+                           d_out: int, hip_stream: int) -> None:
+    _check(lib().spconv_forward_noalloc(d_feats, d_weights, handle, c_in, c_out, dtype, d_out, hip_stream))
 
 
 def spconv_map_free(handle: int) -> None:
@@ -283,9 +290,12 @@ def build_map(coords, kernel_size: int, wait: bool = True) -> SpconvMap:
 _DT = None
 
 
-def forward(feats, weights, kmap: SpconvMap, out=None):
+def forward(feats, weights, kmap: SpconvMap, out=None, noalloc=False):
     """f_out = submanifold convolution of feats [N, C_in] with weights
-    [K^3, C_in, C_out] over ``kmap``; returns out [N, C_out] (same dtype)."""
+    [K^3, C_in, C_out] over ``kmap``; returns out [N, C_out] (same dtype).
+    With ``noalloc`` the call goes to ``spconv_forward_noalloc`` (the
+    library's fixed per-device scratch instead of an allocated workspace;
+    ``out`` must then be given, so that nothing is allocated here either)."""
     global _DT
     torch = _torch()
     if _DT is None:
@@ -306,10 +316,12 @@ def forward(feats, weights, kmap: SpconvMap, out=None):
     if code is None:
         raise SpconvError(4, f"dtype {dt} not supported")
     if out is None:
+        if noalloc:
+            raise SpconvError(1, "noalloc needs a caller-allocated out")
         out = torch.empty((n, cout), dtype=dt, device=feats.device)
     elif not (out.is_cuda and out.is_contiguous() and out.dtype == dt and tuple(out.shape) == (n, cout)):
         raise SpconvError(1, "out must be a contiguous [N, C_out] tensor of the feature dtype")
     with _OnDevice(feats.device):
-        spconv_forward(feats.data_ptr(), weights.data_ptr(), kmap.handle, cin, cout, code,
-                       out.data_ptr(), _stream())
+        fn = spconv_forward_noalloc if noalloc else spconv_forward
+        fn(feats.data_ptr(), weights.data_ptr(), kmap.handle, cin, cout, code, out.data_ptr(), _stream())
     return out

@@ -263,6 +263,132 @@ spconv_status finish_build(spconv_map* m) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Fixed scratch of spconv_forward_noalloc: one array per device, held until
+// the process ends, for the forward workspace (weights in MFMA operand order,
+// the zero row and any fp32 partial outputs).  Host code never uses the
+// array's name as an address: each device's address comes from
+// hipGetSymbolAddress, taken once with that device current.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+spconv_status noalloc_scratch(int device, void** out) {
+  if (device < 0 || device >= kMaxDevices) {
+    return fail(SPCONV_ERR_UNSUPPORTED, "device %d beyond the %d the fixed scratch covers", device, kMaxDevices);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device] == nullptr) {
+    void* ptr = nullptr;
+    SPCONV_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(SPCONV_ERR_DEVICE, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = g_scratch_ptr[device];
+  return SPCONV_OK;
+}
+
+// Validates a forward call and fills its launch arguments.
+spconv_status forward_args(const void* d_feats, const void* d_weights, const spconv_map* map, int32_t c_in,
+                           int32_t c_out, spconv_dtype dtype, void* d_out, spconv::ForwardArgs* out) {
+  if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
+  if (d_feats == nullptr || d_weights == nullptr || d_out == nullptr) {
+    return fail(SPCONV_ERR_INVALID_ARG, "NULL feature, weight or output pointer");
+  }
+  if (!aligned16(d_feats) || !aligned16(d_weights) || !aligned16(d_out)) {
+    return fail(SPCONV_ERR_INVALID_ARG, "feature, weight and output buffers must be 16-byte aligned");
+  }
+  if (dtype != SPCONV_F32 && dtype != SPCONV_F16 && dtype != SPCONV_BF16) {
+    return fail(SPCONV_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(dtype));
+  }
+  const int32_t cmax = (dtype == SPCONV_F32) ? 512 : 1024;
+  if (c_in < 1 || c_out < 1 || c_in > cmax || c_out > cmax) {
+    return fail(SPCONV_ERR_INVALID_ARG, "c_in = %d, c_out = %d must lie in [1, %d]", c_in, c_out, cmax);
+  }
+  const int32_t mult = (dtype == SPCONV_F32) ? 4 : 8;
+  if (c_in % mult != 0 || c_out % mult != 0) {
+    return fail(SPCONV_ERR_UNSUPPORTED, "c_in = %d and c_out = %d must be multiples of %d", c_in,
+                c_out, mult);
+  }
+  {
+    // The output is written while other workgroups still read input rows and
+    // weights: it must not share a byte with either.
+    const uint64_t es = (dtype == SPCONV_F32) ? 4u : 2u;
+    const uint64_t out_b = static_cast<uint64_t>(map->n) * c_out * es;
+    const uint64_t in_b = static_cast<uint64_t>(map->n) * c_in * es;
+    const uint64_t w_b = static_cast<uint64_t>(map->KV) * c_in * c_out * es;
+    auto overlap = [](const void* p, uint64_t np, const void* q, uint64_t nq) {
+      const uint64_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
+      return a0 < b0 + nq && b0 < a0 + np;
+    };
+    if (overlap(d_out, out_b, d_feats, in_b) || overlap(d_out, out_b, d_weights, w_b)) {
+      return fail(SPCONV_ERR_INVALID_ARG, "d_out overlaps the features or the weights");
+    }
+  }
+  spconv::ForwardArgs& a = *out;
+  a.feats = d_feats;
+  a.weights = d_weights;
+  a.out = d_out;
+  a.in_idx = map->buf.in_idx;
+  a.out_idx = map->buf.out_idx;
+  a.tile_off = map->buf.tile_off;
+  a.tile_mask = map->buf.tile_mask;
+  a.tile_rows = map->buf.tile_rows;
+  a.n = map->n;
+  a.tiles = map->tiles;
+  a.KV = map->KV;
+  a.cin = c_in;
+  a.cout = c_out;
+  a.dtype = static_cast<int32_t>(dtype);
+  return SPCONV_OK;
+}
+
+// Orders `stream` after the map's build when it is another stream than the
+// build's and the build is not yet known complete.
+spconv_status order_after_build(const spconv_map* map, hipStream_t stream) {
+  if (stream != map->stream && map->slot != nullptr) {
+    const hipError_t ew = hipStreamWaitEvent(stream, map->slot->done, 0);
+    if (ew != hipSuccess) return hip_fail(ew, "hipStreamWaitEvent");
+  }
+  return SPCONV_OK;
+}
+
+enum class ForwardPath { kSmall, kWide, kTiled, kGeneric };
+
+ForwardPath forward_path(const spconv::ForwardArgs& a) {
+  if (spconv::small_supported(a)) return ForwardPath::kSmall;
+  if (spconv::wide_supported(a)) return ForwardPath::kWide;
+  if (spconv::tiled_supported(a)) return ForwardPath::kTiled;
+  return ForwardPath::kGeneric;
+}
+
+size_t forward_workspace_bytes(ForwardPath path, const spconv::ForwardArgs& a) {
+  if (path == ForwardPath::kWide) return spconv::wide_workspace_bytes(a);
+  if (path == ForwardPath::kTiled) return spconv::tiled_workspace_bytes(a);
+  return 0;
+}
+
+// Launches the forward's kernels; `ws` holds forward_workspace_bytes(path, a)
+// bytes (unused by the small and generic paths).
+spconv_status launch_forward_path(ForwardPath path, const spconv::ForwardArgs& a, void* ws, hipStream_t stream) {
+  hipError_t e;
+  switch (path) {
+    case ForwardPath::kWide:
+      e = spconv::launch_prep_weights(a, ws, stream);
+      if (e == hipSuccess) e = spconv::launch_forward_wide(a, ws, stream);
+      break;
+    case ForwardPath::kTiled:
+      e = spconv::launch_forward_tiled(a, ws, stream);
+      break;
+    default:
+      e = spconv::launch_forward(a, stream);
+      break;
+  }
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  return SPCONV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -405,88 +531,55 @@ spconv_status spconv_forward(const void* d_feats, const void* d_weights, const s
                              int32_t c_in, int32_t c_out, spconv_dtype dtype, void* d_out,
                              void* hip_stream) {
   g_last_error.clear();
-  if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
-  if (d_feats == nullptr || d_weights == nullptr || d_out == nullptr) {
-    return fail(SPCONV_ERR_INVALID_ARG, "NULL feature, weight or output pointer");
-  }
-  if (!aligned16(d_feats) || !aligned16(d_weights) || !aligned16(d_out)) {
-    return fail(SPCONV_ERR_INVALID_ARG, "feature, weight and output buffers must be 16-byte aligned");
-  }
-  if (dtype != SPCONV_F32 && dtype != SPCONV_F16 && dtype != SPCONV_BF16) {
-    return fail(SPCONV_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(dtype));
-  }
-  const int32_t cmax = (dtype == SPCONV_F32) ? 512 : 1024;
-  if (c_in < 1 || c_out < 1 || c_in > cmax || c_out > cmax) {
-    return fail(SPCONV_ERR_INVALID_ARG, "c_in = %d, c_out = %d must lie in [1, %d]", c_in, c_out, cmax);
-  }
-  const int32_t mult = (dtype == SPCONV_F32) ? 4 : 8;
-  if (c_in % mult != 0 || c_out % mult != 0) {
-    return fail(SPCONV_ERR_UNSUPPORTED, "c_in = %d and c_out = %d must be multiples of %d", c_in,
-                c_out, mult);
-  }
-  {
-    // The output is written while other workgroups still read input rows and
-    // weights: it must not share a byte with either.
-    const uint64_t es = (dtype == SPCONV_F32) ? 4u : 2u;
-    const uint64_t out_b = static_cast<uint64_t>(map->n) * c_out * es;
-    const uint64_t in_b = static_cast<uint64_t>(map->n) * c_in * es;
-    const uint64_t w_b = static_cast<uint64_t>(map->KV) * c_in * c_out * es;
-    auto overlap = [](const void* p, uint64_t np, const void* q, uint64_t nq) {
-      const uint64_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
-      return a0 < b0 + nq && b0 < a0 + np;
-    };
-    if (overlap(d_out, out_b, d_feats, in_b) || overlap(d_out, out_b, d_weights, w_b)) {
-      return fail(SPCONV_ERR_INVALID_ARG, "d_out overlaps the features or the weights");
-    }
-  }
   spconv::ForwardArgs a;
-  a.feats = d_feats;
-  a.weights = d_weights;
-  a.out = d_out;
-  a.in_idx = map->buf.in_idx;
-  a.out_idx = map->buf.out_idx;
-  a.tile_off = map->buf.tile_off;
-  a.tile_mask = map->buf.tile_mask;
-  a.tile_rows = map->buf.tile_rows;
-  a.n = map->n;
-  a.tiles = map->tiles;
-  a.KV = map->KV;
-  a.cin = c_in;
-  a.cout = c_out;
-  a.dtype = static_cast<int32_t>(dtype);
+  spconv_status st = forward_args(d_feats, d_weights, map, c_in, c_out, dtype, d_out, &a);
+  if (st != SPCONV_OK) return st;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  if (stream != map->stream && map->slot != nullptr) {
-    // another stream than the build's, before the build is known complete:
-    // order this stream after it (stream order covers the build's own stream)
-    const hipError_t ew = hipStreamWaitEvent(stream, map->slot->done, 0);
-    if (ew != hipSuccess) return hip_fail(ew, "hipStreamWaitEvent");
+  st = order_after_build(map, stream);
+  if (st != SPCONV_OK) return st;
+  const ForwardPath path = forward_path(a);
+  const size_t ws_bytes = forward_workspace_bytes(path, a);
+  if (ws_bytes == 0) return launch_forward_path(path, a, nullptr, stream);
+  hipMemPool_t pool = nullptr;
+  st = pool_for(map->device, &pool);
+  if (st != SPCONV_OK) return st;
+  // The stream's forward workspace (prepared weights, zero row, partials),
+  // reused by later forwards on the stream.
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  StreamCache* c = cache_for(map->device, stream);
+  st = grow_buffer(c->fwd, c->fwd_bytes, ws_bytes, pool, stream, "forward workspace allocation");
+  if (st != SPCONV_OK) return st;
+  return launch_forward_path(path, a, c->fwd, stream);
+}
+
+spconv_status spconv_forward_noalloc(const void* d_feats, const void* d_weights, const spconv_map* map,
+                                     int32_t c_in, int32_t c_out, spconv_dtype dtype, void* d_out,
+                                     void* hip_stream) {
+  g_last_error.clear();
+  spconv::ForwardArgs a;
+  spconv_status st = forward_args(d_feats, d_weights, map, c_in, c_out, dtype, d_out, &a);
+  if (st != SPCONV_OK) return st;
+  const ForwardPath path = forward_path(a);
+  const size_t ws_bytes = forward_workspace_bytes(path, a);
+  if (ws_bytes > kNoAllocScratchBytes) {
+    return fail(SPCONV_ERR_UNSUPPORTED,
+                "this forward needs %zu bytes of workspace; the fixed scratch of spconv_forward_noalloc holds %zu",
+                ws_bytes, kNoAllocScratchBytes);
   }
-  const bool wide = !spconv::small_supported(a) && spconv::wide_supported(a);
-  if (wide || (!spconv::small_supported(a) && spconv::tiled_supported(a))) {
-    hipMemPool_t pool = nullptr;
-    const spconv_status st = pool_for(map->device, &pool);
+  int device = 0;
+  SPCONV_HIP(hipGetDevice(&device), "hipGetDevice");
+  if (device != map->device) {
+    return fail(SPCONV_ERR_INVALID_ARG, "the current device (%d) is not the map's (%d)", device, map->device);
+  }
+  void* ws = nullptr;
+  if (ws_bytes > 0) {
+    st = noalloc_scratch(device, &ws);
     if (st != SPCONV_OK) return st;
-    // The stream's forward workspace (prepared weights, zero row, partials),
-    // reused by later forwards on the stream.
-    const size_t ws_bytes = wide ? spconv::wide_workspace_bytes(a) : spconv::tiled_workspace_bytes(a);
-    std::lock_guard<std::mutex> lock(g_cache_mu);
-    StreamCache* c = cache_for(map->device, stream);
-    const spconv_status sg = grow_buffer(c->fwd, c->fwd_bytes, ws_bytes, pool, stream, "forward workspace allocation");
-    if (sg != SPCONV_OK) return sg;
-    void* ws = c->fwd;
-    hipError_t e;
-    if (wide) {
-      e = spconv::launch_prep_weights(a, ws, stream);
-      if (e == hipSuccess) e = spconv::launch_forward_wide(a, ws, stream);
-    } else {
-      e = spconv::launch_forward_tiled(a, ws, stream);
-    }
-    if (e != hipSuccess) return hip_fail(e, "forward launch");
-    return SPCONV_OK;
   }
-  const hipError_t e = spconv::launch_forward(a, stream);
-  if (e != hipSuccess) return hip_fail(e, "forward launch");
-  return SPCONV_OK;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  st = order_after_build(map, stream);
+  if (st != SPCONV_OK) return st;
+  return launch_forward_path(path, a, ws, stream);
 }
 
 void spconv_map_free(spconv_map* map) {
