@@ -82,7 +82,8 @@ typedef enum spconv_dtype {
 /* Opaque kernel map.  Owns its device buffers until spconv_map_free. */
 typedef struct spconv_map spconv_map;
 
-/* Version of this ABI (incremented on any incompatible change). */
+/* Version of this ABI (incremented on any incompatible change; 2: lists in
+ * the map's row order instead of increasing out_idx). */
 int32_t spconv_abi_version(void);
 
 /*
@@ -91,11 +92,20 @@ int32_t spconv_abi_version(void);
  *
  * The map holds, for every offset k, the list of entries (in_idx, out_idx)
  * with coords[in_idx] = coords[out_idx] + d(k) (same b).  The centre list is
- * the identity (q, q) for every row.  Within one offset the entries are in
- * increasing out_idx.  Work: a device hash insert of all N keys, a probe of
- * the (K^3 - 1) / 2 offsets with k > centre for every voxel, each hit also
- * emitting its mirror entry (P, Q, d) <-> (Q, P, -d) ("Sparse inputs and
- * sparse convolution", section "A symmetry you can check on the slide"), and
+ * the identity (q, q) for every row.  Within one offset the entries follow
+ * the map's row order, the order in which the forward computes its rows: for
+ * K > 1 and N >= 262144, the rows of each window of 4096 consecutive input
+ * rows sorted stably by a 16-bit key of their neighbour set (bit 15 - i set
+ * when the row has a neighbour at the i-th of: the offsets with every
+ * coordinate within one step of the centre, in index order, then the others
+ * in index order), so that rows computed together need the same weights
+ * ("TorchSparse: regular computation from irregular sparsity", section
+ * "TorchSparse++: overlap memory with computation"); otherwise the input
+ * order.  The centre list therefore lists every row once, in that order.
+ * Work: a device hash insert of all N keys, a probe of the (K^3 - 1) / 2
+ * offsets with k > centre for every voxel, each hit also emitting its mirror
+ * entry (P, Q, d) <-> (Q, P, -d) ("Sparse inputs and sparse convolution",
+ * section "A symmetry you can check on the slide"), the per-window sort, and
  * a prefix-scan compaction per offset.
  *
  * Errors: INVALID_ARG (d_coords or out_map NULL, N <= 0, N x K^3 >= 2^31),

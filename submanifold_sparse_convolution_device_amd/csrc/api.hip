@@ -335,6 +335,7 @@ spconv_status forward_args(const void* d_feats, const void* d_weights, const spc
   a.tile_off = map->buf.tile_off;
   a.tile_mask = map->buf.tile_mask;
   a.tile_rows = map->buf.tile_rows;
+  a.perm = map->buf.perm;
   a.n = map->n;
   a.tiles = map->tiles;
   a.KV = map->KV;
@@ -393,7 +394,7 @@ spconv_status launch_forward_path(ForwardPath path, const spconv::ForwardArgs& a
 
 extern "C" {
 
-int32_t spconv_abi_version(void) { return 1; }
+int32_t spconv_abi_version(void) { return 2; }
 
 const char* spconv_status_string(spconv_status s) {
   switch (s) {

@@ -148,8 +148,9 @@ struct Step<float, NCB> {
 template <typename T, int CB>
 __global__ __launch_bounds__(kThreads) void k_forward(
     const T* __restrict__ feats, const T* __restrict__ weights, T* __restrict__ out,
-    const int32_t* __restrict__ in_idx, const int32_t* __restrict__ out_idx,
-    const int32_t* __restrict__ tile_off, int64_t n, int64_t tiles, int KV, int cin, int cout) {
+    const int32_t* __restrict__ in_idx, const unsigned long long* __restrict__ tile_mask,
+    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ perm, int64_t n, int64_t tiles, int KV,
+    int cin, int cout) {
   constexpr int NCB = CB / 16;
   constexpr int VEC = Elem<T>::kVec;
   constexpr int CHUNK = Elem<T>::kChunk;
@@ -168,7 +169,8 @@ __global__ __launch_bounds__(kThreads) void k_forward(
   const int r = lane & 15, g = lane >> 4;
   const int centre = (KV - 1) / 2;
   const int row_in_tile = wave * 16 + r;
-  const int64_t q = q0 + row_in_tile;
+  const int64_t q = q0 + row_in_tile;  // position in the map's row order
+  const int32_t qrow = q < n ? (perm != nullptr ? perm[q] : static_cast<int32_t>(q)) : -1;  // its row
 
   floatx4 acc[NCB];
 #pragma unroll
@@ -184,12 +186,18 @@ __global__ __launch_bounds__(kThreads) void k_forward(
     }
     for (int i = tid; i < kn * kTileRows; i += kThreads) nbr_lds[i] = -1;
     __syncthreads();
-    // row -> input-row table of this tile for the stage's offsets
+    // position -> input-row table of this tile for the stage's offsets: the
+    // tile's entries at offset k follow its row mask, one per set bit
     for (int i = 0; i < kn; ++i) {
       if (kb + i == centre) continue;
-      const int lo = lo_lds[i], hi = hi_lds[i];
-      for (int e = lo + tid; e < hi; e += kThreads) {
-        nbr_lds[i * kTileRows + static_cast<int>(out_idx[e] - q0)] = in_idx[e];
+      const int lo = lo_lds[i];
+      if (lo == hi_lds[i]) continue;
+      const unsigned long long m = tile_mask[static_cast<int64_t>(kb + i) * tiles + tile];
+      for (int row = tid; row < kTileRows; row += kThreads) {
+        if ((m >> row) & 1ull) {
+          const unsigned long long lower = row == 0 ? 0ull : (m & (~0ull >> (64 - row)));
+          nbr_lds[i * kTileRows + row] = in_idx[lo + __popcll(lower)];
+        }
       }
     }
     for (int i = 0; i < kn; ++i) {
@@ -215,8 +223,7 @@ __global__ __launch_bounds__(kThreads) void k_forward(
         for (int j = 0; j < VEC; ++j) wt[(cv + j) * ldw + ci] = vals[j];
       }
       __syncthreads();
-      const int32_t src = (k == centre) ? (q < n ? static_cast<int32_t>(q) : -1)
-                                        : nbr_lds[i * kTileRows + row_in_tile];
+      const int32_t src = (k == centre) ? qrow : nbr_lds[i * kTileRows + row_in_tile];
       if (__ballot(src >= 0) == 0ull) continue;  // none of this wave's 16 rows uses offset k
       const T* frow = feats + static_cast<int64_t>(src < 0 ? 0 : src) * cin;
       const T* wrow = wt + r * ldw;
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void k_forward(
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const int co = co0 + cb * 16 + 4 * g;
-      if (co < cout) Elem<T>::store4(out + q * cout + co, acc[cb]);
+      if (co < cout) Elem<T>::store4(out + static_cast<int64_t>(qrow) * cout + co, acc[cb]);
     }
   }
 }
@@ -593,8 +600,8 @@ template <typename T, int CIN, int COUT>
 __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
     const T* __restrict__ feats, const T* __restrict__ weights, T* __restrict__ out,
     const int32_t* __restrict__ in_idx, const int32_t* __restrict__ tile_off,
-    const unsigned long long* __restrict__ tile_mask, const int32_t* __restrict__ tile_rows, int64_t n,
-    int64_t tiles, int KV, int tw) {
+    const unsigned long long* __restrict__ tile_mask, const int32_t* __restrict__ tile_rows,
+    const int32_t* __restrict__ perm, int64_t n, int64_t tiles, int KV, int tw) {
   using Sh = SmallShape<T, CIN, COUT>;
   constexpr int CHUNK = Sh::CHUNK, VEC = Sh::VEC, NCH = Sh::NCH, NCB = Sh::NCB, ROWV = Sh::ROWV;
   extern __shared__ uint4 smem4[];
@@ -653,8 +660,9 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
   auto load_centre = [&](int64_t q0) {
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      const int64_t q = q0 + qb * 16 + r;
-      const int64_t qs = q < n ? q : n - 1;
+      const int64_t q = q0 + qb * 16 + r;  // position; its row through perm
+      const int64_t qp = q < n ? q : n - 1;
+      const int64_t qs = perm != nullptr ? static_cast<int64_t>(perm[qp]) : qp;
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
         bc[qb][ch] = *reinterpret_cast<const uint4*>(feats + qs * CIN + ch * CHUNK + g * VEC);
@@ -841,8 +849,9 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
     for (int qb = 0; qb < 4; ++qb) {
       const int64_t q = q0 + qb * 16 + r;
       if (q < n && qb * 16 >= row_lo && qb * 16 < row_hi) {
+        const int64_t row = perm != nullptr ? static_cast<int64_t>(perm[q]) : q;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) Elem<T>::store4(out + q * COUT + cb * 16 + 4 * g, acc[qb][cb]);
+        for (int cb = 0; cb < NCB; ++cb) Elem<T>::store4(out + row * COUT + cb * 16 + 4 * g, acc[qb][cb]);
       }
     }
   }
@@ -888,8 +897,8 @@ hipError_t launch_small(const ForwardArgs& a, hipStream_t stream) {
   }
   hipLaunchKernelGGL((k_forward_small<T, CIN, COUT>), dim3(grid), dim3(static_cast<unsigned>(waves) * 64), lds, stream,
                      static_cast<const T*>(a.feats), static_cast<const T*>(a.weights),
-                     static_cast<T*>(a.out), a.in_idx, a.tile_off, a.tile_mask, a.tile_rows, a.n, a.tiles,
-                     a.KV, static_cast<int>(tw));
+                     static_cast<T*>(a.out), a.in_idx, a.tile_off, a.tile_mask, a.tile_rows, a.perm, a.n,
+                     a.tiles, a.KV, static_cast<int>(tw));
   return hipGetLastError();
 }
 
@@ -915,7 +924,7 @@ hipError_t launch_typed(const ForwardArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.tiles), static_cast<unsigned>((a.cout + CB - 1) / CB));
   hipLaunchKernelGGL((k_forward<T, CB>), grid, dim3(kThreads), lds, stream,
                      static_cast<const T*>(a.feats), static_cast<const T*>(a.weights),
-                     static_cast<T*>(a.out), a.in_idx, a.out_idx, a.tile_off, a.n, a.tiles, a.KV,
+                     static_cast<T*>(a.out), a.in_idx, a.tile_mask, a.tile_off, a.perm, a.n, a.tiles, a.KV,
                      a.cin, a.cout);
   return hipGetLastError();
 }

@@ -115,7 +115,8 @@ template <typename T, int CIN, int CB, int QB>
 __global__ __launch_bounds__(512) void k_forward_tiled(
     const T* __restrict__ feats, const uint4* __restrict__ wop, T* __restrict__ out,
     const int32_t* __restrict__ in_idx, const int32_t* __restrict__ tile_off,
-    const unsigned long long* __restrict__ tile_mask, int64_t n, int64_t tiles, int KV, int cout) {
+    const unsigned long long* __restrict__ tile_mask, const int32_t* __restrict__ perm, int64_t n, int64_t tiles,
+    int KV, int cout) {
   using Sh = TiledShape<CIN, CB, QB>;
   constexpr int NCH = Sh::NCH, NCB = Sh::NCB, WSLICE = Sh::WSLICE;
   constexpr int UNITS_PER_TILE = 4 / QB;  // waves per 64-row tile
@@ -201,8 +202,9 @@ __global__ __launch_bounds__(512) void k_forward_tiled(
     for (int b = 0; b < QB; ++b) {
       const int row = (qb0 + b) * 16 + r;
       const bool has = (m >> row) & 1ull;
-      if (k == centre) {
-        s.v[b] = has ? static_cast<int>(t * kTileRows + row) : -1;
+      if (k == centre) {  // the row at this position (the list of the centre is the identity)
+        const int64_t q = t * kTileRows + row;
+        s.v[b] = has ? (perm != nullptr ? perm[q] : static_cast<int>(q)) : -1;
       } else {
         const int rank = __popcll(m & ((1ull << row) - 1ull));
         s.v[b] = has ? in_idx[static_cast<int64_t>(lk) + rank] : -1;
@@ -305,9 +307,10 @@ __global__ __launch_bounds__(512) void k_forward_tiled(
     for (int b = 0; b < QB; ++b) {
       const int64_t q = q_first + b * 16 + r;
       if (q < n) {
+        const int64_t row = perm != nullptr ? static_cast<int64_t>(perm[q]) : q;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          store4<T>(out + q * cout + (cbg0 + cb) * 16 + 4 * g, acc[b][cb]);
+          store4<T>(out + row * cout + (cbg0 + cb) * 16 + 4 * g, acc[b][cb]);
         }
       }
     }
@@ -343,7 +346,7 @@ hipError_t launch_tiled_shape(const ForwardArgs& a, const uint4* wop, int nw, hi
   }
   hipLaunchKernelGGL((k_forward_tiled<T, CIN, CB, QB>), grid, dim3(64 * nw), lds, stream,
                      static_cast<const T*>(a.feats), wop, static_cast<T*>(a.out), a.in_idx, a.tile_off,
-                     a.tile_mask, a.n, a.tiles, a.KV, a.cout);
+                     a.tile_mask, a.perm, a.n, a.tiles, a.KV, a.cout);
   return hipGetLastError();
 }
 

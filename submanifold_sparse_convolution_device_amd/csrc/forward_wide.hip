@@ -190,8 +190,9 @@ template <typename T, int CIN, int TB, int NCB, int NW>
 __global__ __launch_bounds__(64 * NW) void k_forward_wide(
     const uint16_t* __restrict__ feats_raw, const uint4* __restrict__ wop, T* __restrict__ out,
     const int32_t* __restrict__ in_idx, const int32_t* __restrict__ tile_off,
-    const unsigned long long* __restrict__ tile_mask, const uint4* __restrict__ zero_row, int64_t n,
-    int64_t tiles, int64_t tasks, int groups, int splits, float* __restrict__ part, int KV, int cout) {
+    const unsigned long long* __restrict__ tile_mask, const uint4* __restrict__ zero_row,
+    const int32_t* __restrict__ perm, int64_t n, int64_t tiles, int64_t tasks, int groups, int splits,
+    float* __restrict__ part, int KV, int cout) {
   using Sh = WideShape<CIN, TB, NCB, NW>;
   constexpr int NCH = Sh::NCH, BPW = Sh::BPW, TPT = Sh::TPT;
   constexpr int SEG = Sh::SEG, RPI = Sh::RPI, IPB = Sh::IPB, RP = Sh::RP, BLOCK_BYTES = Sh::BLOCK_BYTES;
@@ -433,13 +434,15 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
   wait_vm<0>();  // no copy into LDS may be left in flight at exit
 
   // Epilogue: D element (row 4 g + i, column r) of block (b, cb) is output
-  // column col0 + 16 cb + 4 g + i of row q0 + 16 b + r; a share of split
-  // offsets writes its fp32 partial sums instead (k_reduce_splits rounds).
+  // column col0 + 16 cb + 4 g + i of the row at position q0 + 16 b + r; a
+  // share of split offsets writes its fp32 partial sums instead
+  // (k_reduce_splits rounds).
   float* pout = part + static_cast<int64_t>(share) * n * cout;
 #pragma unroll
   for (int b = 0; b < TB; ++b) {
-    const int64_t q = q0 + 16 * b + r;
-    if (q < n) {
+    const int64_t qpos = q0 + 16 * b + r;
+    if (qpos < n) {
+      const int64_t q = perm != nullptr ? static_cast<int64_t>(perm[qpos]) : qpos;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         if (splits == 1) {
@@ -481,8 +484,8 @@ hipError_t launch_wide_shape(const ForwardArgs& a, int splits, const uint4* wop,
   const int64_t grid = (tasks * groups * splits + 7) / 8 * 8;
   hipLaunchKernelGGL((k_forward_wide<T, CIN, TB, NCB, NW>), dim3(static_cast<unsigned>(grid)), dim3(64 * NW),
                      Sh::lds_bytes(), stream, static_cast<const uint16_t*>(a.feats), wop, static_cast<T*>(a.out),
-                     a.in_idx, a.tile_off, a.tile_mask, zero_row, a.n, a.tiles, tasks, groups, splits, part, a.KV,
-                     a.cout);
+                     a.in_idx, a.tile_off, a.tile_mask, zero_row, a.perm, a.n, a.tiles, tasks, groups, splits, part,
+                     a.KV, a.cout);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const int64_t count4 = a.n * a.cout / 4;

@@ -26,6 +26,17 @@ constexpr int kMaxChunks = 128;
 // after them.
 constexpr int kTileSlots = 128;
 
+// The map's row order (the order the forward computes rows in): for K > 1
+// and at least kOrderMinRows rows, the rows of each window of kOrderWindow
+// consecutive input rows sorted stably by a kOrderKeyBits-bit key of their
+// neighbour set; otherwise the input order.  A window is a multiple of
+// kTileRows, so a tile never straddles two.  Below kOrderMinRows the forward
+// is bound by per-tile latency rather than by the weights and rows it
+// fetches, and the order does not repay its build time.
+constexpr int kOrderWindow = 4096;
+constexpr int kOrderKeyBits = 16;
+constexpr int64_t kOrderMinRows = 262144;
+
 // Coordinate table: open addressing over 16-byte slots (64-bit key, int32 row,
 // flags), probed in aligned windows of 8 slots (128 bytes, one L2 line).  A
 // key first claims its preferred slot (x & 3 in a hash-chosen half of its home
@@ -67,6 +78,7 @@ struct BuildPlan {
   int64_t group_tiles = 0;  // tiles per chunk (a multiple of kGroupTiles)
   int64_t chunks = 0;       // ceil(tiles / group_tiles) <= kMaxChunks
   int64_t table_slots = 0;  // power of two >= kTableSlotsPerVoxel n, >= 64
+  bool ordered = false;     // rows reordered by neighbour set (see kOrderWindow)
 };
 BuildPlan make_plan(int64_t n, int32_t K);
 
@@ -87,6 +99,7 @@ struct BuildScratch {
   int64_t* chunk_sum = nullptr;  // KV x groups entry counts (per kGroupTiles tiles)
   int32_t* tile_base = nullptr;  // KV x tiles: slot of offset k's first entry in tile t
   long long* summary = nullptr;  // kSummaryHead + KV
+  int32_t* group_base = nullptr;  // KV x groups: first list position of each group (ordered maps)
 };
 
 size_t build_scratch_bytes(const BuildPlan& p);
@@ -99,6 +112,7 @@ struct MapBuffers {
   int32_t* tile_off = nullptr;              // KV * tiles + 1
   unsigned long long* tile_mask = nullptr;  // KV * tiles
   int32_t* tile_rows = nullptr;             // tiles * kTileSlots (slots past a tile's entries unset)
+  int32_t* perm = nullptr;                  // n: row at each position of the forward's order (NULL: identity)
 };
 size_t map_buffer_bytes(const BuildPlan& p);
 void carve_map_buffers(const BuildPlan& p, void* base, MapBuffers* m);
@@ -119,6 +133,7 @@ struct ForwardArgs {
   const int32_t* tile_off;                  // KV * tiles + 1
   const unsigned long long* tile_mask;      // KV * tiles
   const int32_t* tile_rows;                 // tiles * kTileSlots
+  const int32_t* perm;                      // n, or NULL (identity): output row of each position
   int64_t n;
   int64_t tiles;
   int32_t KV;

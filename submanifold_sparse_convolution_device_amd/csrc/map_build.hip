@@ -19,8 +19,8 @@
 // (the key, EMPTY, or another key in an unmarked slot: absent) except in the
 // few marked slots, where the window is scanned.
 //
-// Pipeline (one stream, six launches; the last one also writes the small
-// summary into the host's pinned memory):
+// Pipeline (one stream, six launches, seven or eight for an ordered map; the last one
+// also writes the small summary into the host's pinned memory):
 //   k_init     clear the table, the negative-half neighbour flags and the
 //              summary
 //   k_claim    one lane per voxel: a plain store of its row claims its
@@ -36,13 +36,22 @@
 //              check on the slide"), so half of the offsets are probed.  Each
 //              (row, offset) cell has one writer, so flags and neighbour rows
 //              are plain stores.
-//   k_count    per 64-row tile and offset, a ballot of the flags is the tile's
-//              row mask; per-chunk counts and per-offset totals
+//   k_order    (ordered maps) per window of kOrderWindow rows, the rows sorted
+//              by a 16-bit key of their neighbour flags: the map's row order
+//              (perm)
+//   k_count    per 64-row tile (of positions of the row order) and offset, a
+//              ballot of the flags is the tile's row mask; per-group counts
+//              and per-offset totals
+//   k_scan     (ordered maps of more than kScanGroups groups) per offset:
+//              each group's first list position
 //   k_compact  per (offset, chunk): the list start from the totals and the
 //              counts of earlier chunks, then each entry's place from the tile
 //              masks; lists come out grouped by offset ("sorted by weight
-//              offset", section "Nine entries become two") and ordered by
-//              output row within an offset.
+//              offset", section "Nine entries become two") and in the row
+//              order within an offset.  An ordered map uses k_compact_window:
+//              per (offset, window), the probe's neighbour column of the
+//              window's rows staged in LDS with coalesced loads, then read
+//              through the permutation.
 // The lists are sized for the bound of K^3 entries per voxel, so nothing on
 // the device waits for the host; the host reads the summary once at the end.
 #include "internal.h"
@@ -500,16 +509,187 @@ __global__ __launch_bounds__(256) void k_probe(const int4* __restrict__ coords, 
   if (overflow) raise_flag(summary, kFlagTableFull);
 }
 
+// Offsets whose neighbour flags form a row's order key, most significant
+// first: the offsets next to the centre (every coordinate within one step)
+// in index order, then the others in index order, kOrderKeyBits of them.
+template <int K>
+struct KeyOffsets {
+  int k[kOrderKeyBits];
+  int count;
+  constexpr KeyOffsets() : k{}, count(0) {
+    constexpr int R = (K - 1) / 2, KV = K * K * K, C = (KV - 1) / 2;
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int kk = 0; kk < KV && count < kOrderKeyBits; ++kk) {
+        if (kk == C) continue;
+        const int dz = kk / (K * K) - R, dy = (kk / K) % K - R, dx = kk % K - R;
+        const bool inner = dz >= -1 && dz <= 1 && dy >= -1 && dy <= 1 && dx >= -1 && dx <= 1;
+        if ((pass == 0) == inner) k[count++] = kk;
+      }
+    }
+  }
+};
+
+// Order key of row q: bit kOrderKeyBits - 1 - i set when the row has a
+// neighbour at the i-th key offset (the probe's flags).
+template <int K>
+__device__ __forceinline__ uint32_t order_key(const uint32_t* __restrict__ pos_bits,
+                                              const uint8_t* __restrict__ neg_flags, int64_t q) {
+  constexpr int KV = K * K * K, centre = (KV - 1) / 2;
+  constexpr int PW = pos_words(K), NB = neg_bytes(K), NV = NB / 16;
+  constexpr KeyOffsets<K> ko{};
+  uint32_t pw[PW];
+  uint4 nv[NV];
+#pragma unroll
+  for (int w = 0; w < PW; ++w) pw[w] = pos_bits[q * PW + w];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) nv[v] = *reinterpret_cast<const uint4*>(neg_flags + q * NB + 16 * v);
+  uint32_t key = 0u;
+#pragma unroll
+  for (int i = 0; i < ko.count; ++i) {
+    const int k = ko.k[i];
+    bool f;
+    if (k < centre) {
+      const uint4 v = nv[k / 16];
+      const uint32_t word = ((k % 16) / 4 == 0) ? v.x : ((k % 16) / 4 == 1) ? v.y : ((k % 16) / 4 == 2) ? v.z : v.w;
+      f = ((word >> (8 * (k % 4))) & 0xffu) != 0u;
+    } else {
+      const int j = k - centre - 1;
+      f = ((pw[j >> 5] >> (j & 31)) & 1u) != 0u;
+    }
+    key |= static_cast<uint32_t>(f) << (kOrderKeyBits - 1 - i);
+  }
+  return key;
+}
+
+// The map's row order ("TorchSparse: regular computation from irregular
+// sparsity", section "TorchSparse++: overlap memory with computation": rows
+// reordered by their neighbour bitmask, so that rows computed together need
+// the same weights).  One workgroup of 1024 threads per window of
+// kOrderWindow consecutive rows sorts the window's rows stably by key and
+// writes perm[w0 + i] = the row at sorted position i (each row's key is
+// order_key of its flags); windows keep rows near
+// their neighbours in space, and tiles never straddle two.  An LSD radix sort
+// over 8-bit digits in LDS: element e of the window sits with wave
+// e / (E x 64), round (e / 64) mod E, lane e mod 64, and within a pass a
+// wave ranks its own elements round by round (lanes with equal digits found
+// by eight ballots, counts kept in the wave's row of the histogram), so that
+// the only workgroup barriers are those around the per-digit scan and the
+// scatter.  Rows past n sort last (key ~0 and the largest positions).
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderPerThread = kOrderWindow / kOrderThreads;
+constexpr int kOrderWaves = kOrderThreads / 64;
+constexpr int kOrderPasses = (kOrderKeyBits + 7) / 8;
+template <int K>
+__global__ __launch_bounds__(kOrderThreads) void k_order(const uint32_t* __restrict__ pos_bits,
+                                                          const uint8_t* __restrict__ neg_flags, int64_t n,
+                                                          int32_t* __restrict__ perm) {
+  constexpr int E = kOrderPerThread;
+  __shared__ unsigned long long buf[kOrderWindow];
+  __shared__ uint32_t hist[kOrderWaves * 256];
+  __shared__ uint32_t wtot[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w0 = static_cast<int64_t>(blockIdx.x) * kOrderWindow;
+  const int64_t wn = (n - w0 < kOrderWindow) ? n - w0 : kOrderWindow;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  uint32_t key[E], idx[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int e = (wave * E + j) * 64 + lane;
+    idx[j] = static_cast<uint32_t>(e);
+    const uint32_t kv = order_key<K>(pos_bits, neg_flags, w0 + (e < wn ? e : wn - 1));  // unconditional loads batch
+    key[j] = (e < wn) ? kv : ~0u;
+  }
+#pragma unroll 1
+  for (int pass = 0; pass < kOrderPasses; ++pass) {
+    const int shift = 8 * pass;
+    uint32_t* row = hist + wave * 256;
+    for (int d = lane; d < 256; d += 64) row[d] = 0u;
+    // Lanes with the digit of each round (independent of one another, so
+    // computed for all rounds first), then the rounds' counts in order: each
+    // lane reads its digit's count so far and every lane of the digit writes
+    // the same new count (LDS operations of a wave run in order, so a round
+    // sees the rounds before it).
+    uint32_t rank[E], cnt[E], dig[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const uint32_t d = (key[j] >> shift) & 255u;
+      unsigned long long peers = ~0ull;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const unsigned long long bb = __ballot((d >> b) & 1u);
+        peers &= ((d >> b) & 1u) ? bb : ~bb;
+      }
+      dig[j] = d;
+      rank[j] = static_cast<uint32_t>(__popcll(peers & below));
+      cnt[j] = static_cast<uint32_t>(__popcll(peers));
+    }
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const uint32_t base = row[dig[j]];
+      rank[j] += base;
+      row[dig[j]] = base + cnt[j];
+    }
+    __syncthreads();
+    // Per digit (thread d < 256): the counts of earlier waves become each
+    // wave's base, and an exclusive scan over digits gives the digit starts.
+    uint32_t tot = 0u, incl = 0u;
+    if (threadIdx.x < 256) {
+      const int d = threadIdx.x;
+#pragma unroll
+      for (int w = 0; w < kOrderWaves; ++w) {
+        const uint32_t c = hist[w * 256 + d];
+        hist[w * 256 + d] = tot;
+        tot += c;
+      }
+      incl = tot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t u = __shfl_up(incl, o);
+        if (lane >= o) incl += u;
+      }
+      if (lane == 63) wtot[wave] = incl;
+    }
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      const int d = threadIdx.x;
+      uint32_t start = incl - tot;
+      for (int w = 0; w < wave; ++w) start += wtot[w];
+#pragma unroll
+      for (int w = 0; w < kOrderWaves; ++w) hist[w * 256 + d] += start;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      buf[hist[wave * 256 + dig[j]] + rank[j]] = (static_cast<unsigned long long>(key[j]) << 32) | idx[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const unsigned long long u = buf[(wave * E + j) * 64 + lane];
+      key[j] = static_cast<uint32_t>(u >> 32);
+      idx[j] = static_cast<uint32_t>(u);
+    }
+    __syncthreads();  // every read of buf and of the histogram done before the next pass
+  }
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int e = (wave * E + j) * 64 + lane;
+    if (e < wn) perm[w0 + e] = static_cast<int32_t>(w0 + idx[j]);
+  }
+}
+
 // One workgroup of 1024 threads (16 waves) per chunk of group_tiles tiles,
 // one tile per wave at a time (launched with chunks of one group, so each
-// wave counts one tile).  Per tile and offset k, a ballot of the row
+// wave counts one tile; tiles are over positions of the row order, whose
+// rows' flags come through perm).  Per tile and offset k, a ballot of the row
 // flags is the tile's row mask; lane k mod 64 keeps it (slot k / 64) and
 // stores it to tile_mask[k][t], with tile_base[k][t], the number of the
 // tile's non-centre entries at offsets before k.  Per-chunk counts go to
 // chunk_sum[k][chunk] and are added to the per-offset totals in the summary.
 template <int K>
 __global__ __launch_bounds__(1024) void k_count(const uint32_t* __restrict__ pos_bits,
-                                                const uint8_t* __restrict__ neg_flags, int64_t n,
+                                                const uint8_t* __restrict__ neg_flags,
+                                                const int32_t* __restrict__ perm, int64_t n,
                                                 int64_t tiles, int64_t group_tiles, int64_t chunks,
                                                 unsigned long long* __restrict__ tile_mask,
                                                 int32_t* __restrict__ tile_base,
@@ -526,9 +706,10 @@ __global__ __launch_bounds__(1024) void k_count(const uint32_t* __restrict__ pos
   for (int64_t g = 0; g < group_tiles; g += kGroupTiles) {
     const int64_t t = chunk * group_tiles + g + wave;
     if (t >= tiles) break;  // tiles of later groups are past the end too
-    const int64_t q = t * kTileRows + lane;
+    const int64_t q = t * kTileRows + lane;  // position in the row order
     const bool valid = q < n;
-    const int64_t qs = valid ? q : n - 1;
+    const int64_t qp = valid ? q : n - 1;
+    const int64_t qs = perm != nullptr ? static_cast<int64_t>(perm[qp]) : qp;  // its row
     uint32_t pw[PW > 0 ? PW : 1];
     uint4 nv[NV > 0 ? NV : 1];
 #pragma unroll
@@ -698,6 +879,158 @@ __global__ __launch_bounds__(256) void k_compact(const unsigned long long* __res
   }
 }
 
+// Ordered maps, one workgroup per offset k (1024 threads): list positions.
+// The first entry of offset k is the sum of the totals of the offsets before
+// it (the summary, final since k_count), and each group of kGroupTiles tiles
+// starts after the groups before it: group_base[k][g] = that sum plus an
+// exclusive scan of the per-group counts.
+__global__ __launch_bounds__(1024) void k_scan(const int64_t* __restrict__ chunk_sum, int64_t groups,
+                                               const long long* __restrict__ summary,
+                                               int32_t* __restrict__ group_base) {
+  const int k = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ long long s_wave[16];
+  __shared__ long long s_base;
+  if (wave == 0) {
+    long long b = 0;
+    for (int i = lane; i < k; i += 64) b += summary[kSummaryHead + i];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) b += __shfl_xor(b, d);
+    if (lane == 0) s_base = b;
+  }
+  __syncthreads();
+  long long running = s_base;
+  for (int64_t c0 = 0; c0 < groups; c0 += 1024) {
+    const int64_t g = c0 + tid;
+    const long long v = g < groups ? chunk_sum[static_cast<int64_t>(k) * groups + g] : 0;
+    long long incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const long long u = __shfl_up(incl, d);
+      if (lane >= d) incl += u;
+    }
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    long long before = running, total = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const long long t = s_wave[w];
+      if (w < wave) before += t;
+      total += t;
+    }
+    if (g < groups) group_base[static_cast<int64_t>(k) * groups + g] = static_cast<int32_t>(before + incl - v);
+    running += total;
+    __syncthreads();  // s_wave is rewritten by the next round
+  }
+}
+
+// Ordered maps.  Grid: x = window of kOrderWindow positions (kWindowGroups
+// groups of kGroupTiles tiles), y = offset k; one wave per group.  The
+// positions of a window hold a permutation of the window's rows, so the
+// probe's neighbour column of those rows at offset k (nbr[k][w0 .. w0 +
+// window)) is first copied into LDS with coalesced loads and then read
+// through perm.  A group's first list position comes from k_scan when there
+// are more than kScanGroups groups, else each wave sums the counts before it.
+// Wave w places the entries of group w of the window: each
+// tile's first list position (group_base plus the earlier tiles' counts, a
+// wave prefix sum) goes to tile_off[k][t], and each entry, at its rank in the
+// tile's mask, gets the row at its position (out_idx) and that row's
+// neighbour (in_idx; the row itself at the centre).  A non-centre entry also
+// goes to its tile's slot table (tile_rows), at slot tile_base[k][t] + rank,
+// when that is below kTileSlots.  The workgroup of the last offset and window
+// also writes tile_off[KV * tiles] = E, and the first one hands the summary
+// to the host's pinned slot.
+constexpr int kWindowGroups = kOrderWindow / (kTileRows * kGroupTiles);
+constexpr int64_t kScanGroups = 4096;
+static_assert(kWindowGroups * kTileRows * kGroupTiles == kOrderWindow, "whole groups per window");
+__global__ __launch_bounds__(64 * kWindowGroups) void k_compact_window(
+    const unsigned long long* __restrict__ tile_mask, const int32_t* __restrict__ tile_base,
+    const int32_t* __restrict__ nbr, const int32_t* __restrict__ perm, int64_t n, int64_t tiles, int centre,
+    int KV, const int64_t* __restrict__ chunk_sum, const int32_t* __restrict__ group_base,
+    const long long* __restrict__ summary, int32_t* __restrict__ in_idx, int32_t* __restrict__ out_idx,
+    int32_t* __restrict__ tile_off, int32_t* __restrict__ tile_rows, long long* __restrict__ host_summary) {
+  __shared__ int32_t col[kOrderWindow];
+  const int k = blockIdx.y;
+  const int64_t win = blockIdx.x;
+  const int64_t w0 = win * kOrderWindow;
+  const int64_t wn = (n - w0 < kOrderWindow) ? n - w0 : kOrderWindow;
+  if (win == 0 && k == 0) {
+    for (int i = threadIdx.x; i < kSummaryHead + KV; i += blockDim.x) host_summary[i] = summary[i];
+  }
+  const bool is_centre = (k == centre);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t groups = (tiles + kGroupTiles - 1) / kGroupTiles;
+  const int64_t g = win * kWindowGroups + wave;
+  const bool active = g < groups;
+  // Issued together: the column of the window's rows, the wave's tile
+  // masks and (once the masks are in) the rows at the present positions.
+  constexpr int kPerThread = kOrderWindow / (64 * kWindowGroups);
+  int32_t cv[kPerThread];
+  if (!is_centre) {
+    const int32_t* nk = nbr + static_cast<int64_t>(k) * n + w0;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int e = i * 64 * kWindowGroups + static_cast<int>(threadIdx.x);
+      cv[i] = nk[e < wn ? e : wn - 1];
+    }
+  }
+  const int64_t t0 = g * kGroupTiles;
+  const int64_t tl = t0 + lane;
+  const bool have = active && lane < kGroupTiles && tl < tiles;
+  const unsigned long long mt = have ? tile_mask[static_cast<int64_t>(k) * tiles + tl] : 0ull;
+  const int sb = (have && !is_centre) ? tile_base[static_cast<int64_t>(k) * tiles + tl] : 0;
+  const int nt = active ? static_cast<int>(tiles - t0 < kGroupTiles ? tiles - t0 : kGroupTiles) : 0;
+  int32_t row[kGroupTiles];
+#pragma unroll
+  for (int i = 0; i < kGroupTiles; ++i) {
+    const unsigned long long m = (i < nt) ? lane_u64(mt, i) : 0ull;
+    const int64_t q = (t0 + i) * kTileRows + lane;
+    row[i] = ((m >> lane) & 1ull) ? perm[q] : static_cast<int32_t>(w0);
+  }
+  // This group's first list position: from k_scan for many groups, else the
+  // totals of earlier offsets plus the counts of earlier groups, summed here.
+  int base = 0;
+  if (active) {
+    if (group_base != nullptr) {
+      base = group_base[static_cast<int64_t>(k) * groups + g];
+    } else {
+      long long b = 0;
+      for (int i = lane; i < k; i += 64) b += summary[kSummaryHead + i];
+      for (int64_t c = lane; c < g; c += 64) b += chunk_sum[static_cast<int64_t>(k) * groups + c];
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) b += __shfl_xor(b, d);
+      base = static_cast<int>(b);
+    }
+  }
+  if (!is_centre) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int e = i * 64 * kWindowGroups + static_cast<int>(threadIdx.x);
+      if (e < wn) col[e] = cv[i];
+    }
+  }
+  __syncthreads();
+  if (!active) return;  // no barrier follows
+  const int ct = __popcll(mt);
+  const int excl = wave_prefix_small<7>(ct);
+  if (have) tile_off[static_cast<int64_t>(k) * tiles + tl] = base + excl;
+  const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int i = 0; i < kGroupTiles; ++i) {
+    const unsigned long long m = (i < nt) ? lane_u64(mt, i) : 0ull;
+    if ((m >> lane) & 1ull) {
+      const int32_t src = is_centre ? row[i] : col[row[i] - w0];
+      const int rank = __popcll(m & below);
+      const int64_t pos = base + __builtin_amdgcn_readlane(excl, i) + rank;
+      in_idx[pos] = src;
+      out_idx[pos] = row[i];
+      const int sbi = __builtin_amdgcn_readlane(sb, i);
+      if (!is_centre && sbi + rank < kTileSlots) tile_rows[(t0 + i) * kTileSlots + sbi + rank] = src;
+    }
+  }
+  if (k == KV - 1 && g == groups - 1 && lane == nt - 1) tile_off[static_cast<int64_t>(KV) * tiles] = base + excl + ct;
+}
+
 int grid_for(int64_t work, int per_block, int cap) {
   int64_t g = (work + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -726,10 +1059,19 @@ void launch_probe_count(const BuildPlan& p, const int4* c4, const BuildScratch& 
                        static_cast<unsigned long long>(occ_buckets(p) - 1), s.nbr, s.pos_bits, s.neg_flags,
                        s.summary);
   }
+  const int32_t* perm = nullptr;
+  if constexpr (K > 1) {
+    if (p.ordered) {
+      const unsigned windows = static_cast<unsigned>((p.n + kOrderWindow - 1) / kOrderWindow);
+      hipLaunchKernelGGL((k_order<K>), dim3(windows), dim3(kOrderThreads), 0, stream, s.pos_bits, s.neg_flags, p.n,
+                         m.perm);
+      perm = m.perm;
+    }
+  }
   const int64_t groups = (p.tiles + kGroupTiles - 1) / kGroupTiles;
   hipLaunchKernelGGL((k_count<K>), dim3(static_cast<unsigned>(groups)), dim3(1024), 0, stream,
-                     s.pos_bits, s.neg_flags, p.n, p.tiles, static_cast<int64_t>(kGroupTiles), groups, m.tile_mask,
-                     s.tile_base, s.chunk_sum, s.summary);
+                     s.pos_bits, s.neg_flags, perm, p.n, p.tiles, static_cast<int64_t>(kGroupTiles), groups,
+                     m.tile_mask, s.tile_base, s.chunk_sum, s.summary);
 }
 
 }  // namespace
@@ -748,6 +1090,7 @@ BuildPlan make_plan(int64_t n, int32_t K) {
   int64_t slots = 64;
   while (slots < kTableSlotsPerVoxel * n) slots <<= 1;
   p.table_slots = slots;
+  p.ordered = K > 1 && n >= kOrderMinRows;
   return p;
 }
 
@@ -761,6 +1104,9 @@ size_t build_scratch_bytes(const BuildPlan& p) {
   b += align_up(static_cast<size_t>(p.KV) * ((p.tiles + kGroupTiles - 1) / kGroupTiles) * sizeof(int64_t), 256);
   b += align_up(static_cast<size_t>(p.KV) * p.tiles * sizeof(int32_t), 256);
   b += align_up(static_cast<size_t>(kSummaryHead + p.KV) * sizeof(long long), 256);
+  if (p.ordered) {
+    b += align_up(static_cast<size_t>(p.KV) * ((p.tiles + kGroupTiles - 1) / kGroupTiles) * sizeof(int32_t), 256);
+  }
   return b;
 }
 
@@ -781,6 +1127,8 @@ void carve_build_scratch(const BuildPlan& p, void* base, BuildScratch* s) {
   s->tile_base = reinterpret_cast<int32_t*>(c);
   c += align_up(static_cast<size_t>(p.KV) * p.tiles * sizeof(int32_t), 256);
   s->summary = reinterpret_cast<long long*>(c);
+  c += align_up(static_cast<size_t>(kSummaryHead + p.KV) * sizeof(long long), 256);
+  s->group_base = p.ordered ? reinterpret_cast<int32_t*>(c) : nullptr;
 }
 
 size_t map_buffer_bytes(const BuildPlan& p) {
@@ -788,7 +1136,8 @@ size_t map_buffer_bytes(const BuildPlan& p) {
   const size_t tiles = static_cast<size_t>(p.KV) * p.tiles;
   return 2 * align_up(cap * sizeof(int32_t), 256) + align_up((tiles + 1) * sizeof(int32_t), 256) +
          align_up(tiles * sizeof(unsigned long long), 256) +
-         align_up(static_cast<size_t>(p.tiles) * kTileSlots * sizeof(int32_t), 256);
+         align_up(static_cast<size_t>(p.tiles) * kTileSlots * sizeof(int32_t), 256) +
+         (p.ordered ? align_up(static_cast<size_t>(p.n) * sizeof(int32_t), 256) : 0);
 }
 
 void carve_map_buffers(const BuildPlan& p, void* base, MapBuffers* m) {
@@ -804,6 +1153,8 @@ void carve_map_buffers(const BuildPlan& p, void* base, MapBuffers* m) {
   m->tile_mask = reinterpret_cast<unsigned long long*>(c);
   c += align_up(tiles * sizeof(unsigned long long), 256);
   m->tile_rows = reinterpret_cast<int32_t*>(c);
+  c += align_up(static_cast<size_t>(p.tiles) * kTileSlots * sizeof(int32_t), 256);
+  m->perm = p.ordered ? reinterpret_cast<int32_t*>(c) : nullptr;
 }
 
 hipError_t launch_build(const BuildPlan& p, const int32_t* coords, const BuildScratch& s,
@@ -828,6 +1179,20 @@ hipError_t launch_build(const BuildPlan& p, const int32_t* coords, const BuildSc
     case 5: launch_probe_count<5>(p, c4, s, m, window_mask, stream); break;
     case 7: launch_probe_count<7>(p, c4, s, m, window_mask, stream); break;
     default: return hipErrorInvalidValue;
+  }
+  if (p.ordered) {
+    const int64_t groups = (p.tiles + kGroupTiles - 1) / kGroupTiles;
+    const bool scan = groups > kScanGroups;
+    if (scan) {
+      hipLaunchKernelGGL(k_scan, dim3(static_cast<unsigned>(p.KV)), dim3(1024), 0, stream, s.chunk_sum, groups,
+                         s.summary, s.group_base);
+    }
+    const unsigned windows = static_cast<unsigned>((p.n + kOrderWindow - 1) / kOrderWindow);
+    hipLaunchKernelGGL(k_compact_window, dim3(windows, static_cast<unsigned>(p.KV)), dim3(64 * kWindowGroups), 0,
+                       stream, m.tile_mask, s.tile_base, s.nbr, m.perm, p.n, p.tiles, p.centre, p.KV, s.chunk_sum,
+                       scan ? s.group_base : nullptr, s.summary, m.in_idx, m.out_idx, m.tile_off, m.tile_rows,
+                       host_summary);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL(k_compact, dim3(static_cast<unsigned>(p.chunks), static_cast<unsigned>(p.KV)),
                      dim3(256), 0, stream, m.tile_mask, s.tile_base, s.nbr, p.n, p.tiles, p.centre, p.KV,

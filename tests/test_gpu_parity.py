@@ -1,7 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the oracle.
 
 Maps must match bit-exactly as per-offset sets (the order inside a list is
-the library's choice; it is also checked to be increasing in out_idx).
+the library's choice: the map's row order, in which every list is checked to
+be increasing, and which test_map_row_order pins to its definition).
 Features must satisfy |gpu - oracle| <= tol x RMS(oracle) + half an ulp of
 the oracle's value in the output type, element by element, with tol = 2e-2
 for fp16/bf16 and 1e-5 for fp32, the oracle computing in fp64 on the exactly
@@ -55,19 +56,27 @@ def _gpu_lists(kmap):
 
 
 def assert_map_equal(kmap, ref):
-    """Per-offset set equality, counts and offsets, plus the ordering contract."""
+    """Per-offset set equality, counts and offsets, plus the ordering
+    contract: the centre list holds every row once, in the map's row order,
+    and every other list follows that order."""
     kv = ref.K ** 3
     assert kmap.kernel_size == ref.K and kmap.n == ref.N
     assert np.array_equal(kmap.counts, ref.counts)
     assert kmap.offsets[0] == 0 and np.array_equal(np.diff(kmap.offsets), kmap.counts)
     assert kmap.total_entries == ref.total_entries
     a, b = _gpu_lists(kmap)
+    c = kv // 2
+    order = b[kmap.offsets[c]:kmap.offsets[c + 1]]
+    assert np.array_equal(np.sort(order), np.arange(ref.N)), "the centre list is not a permutation of the rows"
+    rank = np.empty(ref.N, np.int64)
+    rank[order] = np.arange(ref.N)
     for k in range(kv):
         lo, hi = kmap.offsets[k], kmap.offsets[k + 1]
         ga, gb = a[lo:hi], b[lo:hi]
-        assert np.all(np.diff(gb) > 0), f"offset {k}: out_idx not increasing"
-        ra, rb = ref.lists[k]  # the oracle's lists are ordered by output row too
-        assert np.array_equal(gb, rb) and np.array_equal(ga, ra), f"offset {k} differs"
+        assert np.all(np.diff(rank[gb]) > 0), f"offset {k}: not in the map's row order"
+        s = np.argsort(gb, kind="stable")
+        ra, rb = ref.lists[k]  # the oracle's lists are ordered by output row
+        assert np.array_equal(gb[s], rb) and np.array_equal(ga[s], ra), f"offset {k} differs"
 
 
 def _forward_check(sp, kmap, coords, K, cin, cout, dtype, seed, ref_map=None, rows=None):
@@ -176,7 +185,7 @@ def test_map_and_forward_at_the_size_limit(sp, K, boxes, cin):
     separate batches.  Every entry of every list is checked against its
     closed form (box_map.py, itself checked against the oracle on small
     boxes): the entries of offset d are the rows q of each box whose q + d
-    stays inside it, in increasing q.  The forward with all-ones features and
+    stays inside it (compared as sets).  The forward with all-ones features and
     weights gives C_in x deg(q), exact in fp16."""
     kv = K ** 3
     n = sum(lz * ly * lx for _, (lz, ly, lx) in boxes)
@@ -188,7 +197,9 @@ def test_map_and_forward_at_the_size_limit(sp, K, boxes, cin):
         p, q = box_map.box_list(boxes, K, k, DEV)
         lo, hi = int(kmap.offsets[k]), int(kmap.offsets[k + 1])
         assert kmap.counts[k] == q.numel(), f"offset {k} count"
-        assert torch.equal(b[lo:hi].long(), q) and torch.equal(a[lo:hi].long(), p), f"offset {k} entries"
+        bs, s = torch.sort(b[lo:hi].long())  # the lists follow the map's row order; compare as sets
+        assert torch.equal(bs, q) and torch.equal(a[lo:hi].long()[s], p), f"offset {k} entries"
+        del bs, s
     del a, b
     f = torch.ones((n, cin), dtype=torch.float16, device=DEV)
     w = torch.ones((kv, cin, cin), dtype=torch.float16, device=DEV)
@@ -390,6 +401,75 @@ def test_forward_workspace_reuse_across_shapes(sp):
     torch.cuda.synchronize()
     for i, ref in enumerate(alone):
         assert torch.equal(outs[2 * i].cpu(), ref) and torch.equal(outs[2 * i + 1].cpu(), ref), shapes[i]
+
+
+ORDER_WINDOW, ORDER_KEY_BITS, ORDER_MIN_ROWS = 4096, 16, 262144
+
+
+def _key_offsets(K):
+    """Offsets whose neighbour flags make a row's order key, most
+    significant first: those with every coordinate within one step of the
+    centre, in index order, then the rest in index order, 16 of them."""
+    kv, c = K ** 3, K ** 3 // 2
+    inner, outer = [], []
+    for k in range(kv):
+        if k != c:
+            (inner if max(abs(v) for v in oracle.offset_of(k, K)) <= 1 else outer).append(k)
+    return (inner + outer)[:ORDER_KEY_BITS]
+
+
+def expected_row_order(ref, K):
+    """The map's row order by its definition, from the oracle's lists: for
+    K > 1 and at least 262,144 rows, the rows of each window of 4,096
+    consecutive rows sorted stably by their 16-bit neighbour key; otherwise
+    the input order."""
+    n = ref.N
+    if K == 1 or n < ORDER_MIN_ROWS:
+        return np.arange(n)
+    key = np.zeros(n, np.uint32)
+    for i, k in enumerate(_key_offsets(K)):
+        key[ref.lists[k][1]] |= np.uint32(1) << np.uint32(ORDER_KEY_BITS - 1 - i)
+    order = np.empty(n, np.int64)
+    for s in range(0, n, ORDER_WINDOW):
+        e = min(n, s + ORDER_WINDOW)
+        order[s:e] = s + np.argsort(key[s:e], kind="stable")
+    return order
+
+
+def _tile_offset_pairs(b, offsets, kv, rank):
+    """(64-row tile, offset) pairs with an entry, tiles taken over the
+    positions `rank` gives the output rows."""
+    total = 0
+    for k in range(kv):
+        total += np.unique(rank[b[offsets[k]:offsets[k + 1]]] // 64).size
+    return total
+
+
+@pytest.mark.parametrize("index,K,bound", [(4, 3, 0.65), (4, 5, 0.8), (1, 3, None), (0, 3, None)])
+def test_map_row_order(sp, index, K, bound):
+    """The map's row order (neighbour-bitmask row reordering): the centre
+    list, which holds every row once in that order, equals the rows sorted
+    stably by their 16-bit neighbour key within windows of 4,096 rows, as
+    computed here from the oracle's lists; on the 8 batched LiDAR frames the
+    order cuts the (tile, offset) pairs the forward visits to at most `bound`
+    of the input order's.  The indoor scene (150,000 rows) and the sphere
+    shell keep the input order."""
+    layer = _workload(index).layers[0]
+    c = layer.coords
+    ref = oracle.build_map(c, K)
+    kmap = _gpu_map(sp, c, K)
+    a, b = _gpu_lists(kmap)
+    n, kv = layer.n, K ** 3
+    cen = kv // 2
+    order = b[kmap.offsets[cen]:kmap.offsets[cen + 1]]
+    assert np.array_equal(a[kmap.offsets[cen]:kmap.offsets[cen + 1]], order)
+    assert np.array_equal(order, expected_row_order(ref, K))
+    if bound is not None:
+        rank = np.empty(n, np.int64)
+        rank[order] = np.arange(n)
+        ordered = _tile_offset_pairs(b, kmap.offsets, kv, rank)
+        plain = _tile_offset_pairs(b, kmap.offsets, kv, np.arange(n))
+        assert ordered <= bound * plain, f"(tile, offset) pairs {ordered} vs {plain} in input order"
 
 
 def test_map_deterministic(sp):
@@ -725,6 +805,59 @@ def test_forward_is_repeatable_and_overwrites(sp):
     a = sp.forward(f, w, kmap, out=out).clone()
     b = sp.forward(f, w, kmap)
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ large layers (four-tile workgroups)
+
+
+@pytest.mark.parametrize("seed,extent,occ,batches,K,cin,dtype,permute", [
+    (401, 96, 0.2, 1, 3, 128, "bf16", False),   # N ~ 177k, ragged last task
+    (402, 70, 0.25, 2, 3, 128, "f16", True),    # two batches, rows permuted
+    (403, 80, 0.3, 1, 3, 64, "bf16", False),
+    (404, 64, 0.3, 2, 5, 64, "f16", True),      # K = 5: offsets beyond 64
+    (405, 62, 0.2, 3, 5, 128, "bf16", False),   # three batches, K = 5 at C = 128
+])
+def test_forward_large_layers(sp, seed, extent, occ, batches, K, cin, dtype, permute):
+    """Layers of well over 512 four-tile tasks (the four-tile workgroup path)
+    against the oracle on every output row, with sizes that leave a ragged
+    last tile and task."""
+    c = workloads.random_grid(seed, extent, occ, batches)
+    if permute:
+        c = workloads.permuted(c, seed)
+    assert c.shape[0] > 512 * 256 and c.shape[0] % 256 != 0
+    ref = oracle.build_map(c, K)
+    kmap = _gpu_map(sp, c, K)
+    f = workloads.features(c.shape[0], cin, dtype, seed + 1)
+    w = workloads.weights(K, cin, cin, dtype, seed + 2)
+    out = sp.forward(f.to(DEV), w.to(DEV), kmap).double().cpu().numpy()
+    r = ref.forward_parallel(f.double().numpy(), w.double().numpy())
+    rms = float(np.sqrt(np.mean(r ** 2)))
+    diff = np.abs(out - r)
+    assert np.all(np.isfinite(out))
+    assert np.all(diff <= TOL[dtype] * rms + HALF_ULP[dtype] * np.abs(r)), \
+        f"max |err| {float(diff.max()):.3e} vs RMS {rms:.3e}"
+
+
+@pytest.mark.parametrize("cin,K", [(128, 3), (64, 3), (64, 5)])
+def test_forward_large_routing_is_exact(sp, cin, K):
+    """Identity weights at one offset route rows exactly on the four-tile
+    path too (centre: the task's own rows, read without an index; other
+    offsets: gathered rows, with rows lacking the neighbour zeroed)."""
+    c = workloads.random_grid(410 + K, 90, 0.2, 1)
+    n = c.shape[0]
+    assert n > 512 * 256
+    kmap = _gpu_map(sp, c, K)
+    ref = oracle.build_map(c, K)
+    kv = K ** 3
+    f = workloads.features(n, cin, "bf16", 412)
+    for k in (kv // 2, 0, kv // 2 + 1, kv - 1):
+        w = torch.zeros((kv, cin, cin), dtype=torch.bfloat16)
+        w[k] = torch.eye(cin, dtype=torch.bfloat16)
+        out = sp.forward(f.to(DEV), w.to(DEV), kmap).cpu()
+        exp = torch.zeros_like(f)
+        j, q = ref.lists[k]
+        exp[torch.from_numpy(q).long()] = f[torch.from_numpy(j).long()]
+        assert torch.equal(out, exp), f"offset {k}, {cin} channels"
 
 
 # ------------------------------------------------------------------ the five workloads
