@@ -11,6 +11,9 @@ Contents
     ctypes front end of ``spconv_oracle.cpp`` (ordered-tree coordinate lookup,
     per-entry fp64 vector-matrix products).  See that file for the passages
     each step follows.
+``OracleMap.backward_data`` / ``OracleMap.backward_weights``
+    The gradients of the forward with respect to its input features and its
+    weights, each the chain rule of the forward's per-entry sum, in fp64.
 ``brute_map``
     O(N^2) pair test for tiny inputs: (j, q) is an entry of offset d iff
     coords[j] = coords[q] + (0, d).  Independent of the tree lookup.
@@ -78,6 +81,10 @@ def _lib() -> ctypes.CDLL:
         lib.oracle_forward_parallel.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int32
+        lib.oracle_backward_data.argtypes = lib.oracle_forward.argtypes
+        lib.oracle_backward_data.restype = ctypes.c_int
+        lib.oracle_backward_weights.argtypes = lib.oracle_forward.argtypes
+        lib.oracle_backward_weights.restype = ctypes.c_int
         lib.oracle_forward_rows.argtypes = [ctypes.c_void_p, _f64p, _f64p, ctypes.c_int32, ctypes.c_int32,
                                             _i64p, ctypes.c_int64, _f64p]
         lib.oracle_forward_rows.restype = ctypes.c_int
@@ -159,6 +166,36 @@ class OracleMap:
         out = np.empty((self.N, cout), np.float64)
         st = _lib().oracle_forward_parallel(self._h, _ptr(f, _f64p), _ptr(w, _f64p), cin, cout,
                                             _ptr(out, _f64p), int(threads))
+        if st != 0:
+            raise OracleError(st)
+        return out
+
+    def backward_data(self, grad_out: np.ndarray, weights: np.ndarray) -> np.ndarray:
+        """fp64 gradient with respect to the input features: grad_in[j] = sum
+        over entries (j, q) of offset k of grad_out[q] @ W[k]^T."""
+        if not self.has_lists:
+            raise ValueError("built with lists=False")
+        g = np.ascontiguousarray(np.asarray(grad_out, dtype=np.float64))
+        w = np.ascontiguousarray(np.asarray(weights, dtype=np.float64))
+        cin, cout = w.shape[1], w.shape[2]
+        assert g.shape == (self.N, cout) and w.shape[0] == self.K ** 3
+        out = np.empty((self.N, cin), np.float64)
+        st = _lib().oracle_backward_data(self._h, _ptr(g, _f64p), _ptr(w, _f64p), cin, cout, _ptr(out, _f64p))
+        if st != 0:
+            raise OracleError(st)
+        return out
+
+    def backward_weights(self, feats: np.ndarray, grad_out: np.ndarray) -> np.ndarray:
+        """fp64 gradient with respect to the weights: grad_w[k] = sum over
+        entries (j, q) of offset k of the outer product feats[j] x grad_out[q]."""
+        if not self.has_lists:
+            raise ValueError("built with lists=False")
+        f = np.ascontiguousarray(np.asarray(feats, dtype=np.float64))
+        g = np.ascontiguousarray(np.asarray(grad_out, dtype=np.float64))
+        cin, cout = f.shape[1], g.shape[1]
+        assert f.shape[0] == self.N and g.shape[0] == self.N
+        out = np.empty((self.K ** 3, cin, cout), np.float64)
+        st = _lib().oracle_backward_weights(self._h, _ptr(f, _f64p), _ptr(g, _f64p), cin, cout, _ptr(out, _f64p))
         if st != 0:
             raise OracleError(st)
         return out

@@ -227,6 +227,70 @@ int oracle_forward_parallel(const void* h, const double* feats, const double* we
   return kOk;
 }
 
+// Gradient of the forward with respect to its input features, by the chain
+// rule of the forward's sum ("Sparse convolution for point clouds", section
+// "The map and the update rule": each entry (P, Q, W_d) adds f_in(P) x W_d to
+// f_out(Q), so it adds grad_out(Q) x W_d^T to grad_in(P)):
+//   grad_in[j][ci] = sum over k, over entries (j, q) of list k, over co of
+//                    grad_out[q][co] x W[k][ci][co]
+// in fp64, from zero.  grad_out is [N][Cout], grad_in [N][Cin].
+int oracle_backward_data(const void* h, const double* grad_out, const double* weights,
+                         int32_t Cin, int32_t Cout, double* grad_in) {
+  const OracleMap* m = static_cast<const OracleMap*>(h);
+  if (grad_out == nullptr || weights == nullptr || grad_in == nullptr || Cin <= 0 || Cout <= 0) {
+    return kInvalidArg;
+  }
+  for (int64_t i = 0; i < m->N * Cin; ++i) grad_in[i] = 0.0;
+  const int32_t KV = m->K * m->K * m->K;
+  for (int32_t k = 0; k < KV; ++k) {
+    const auto& ins = m->in_idx[static_cast<size_t>(k)];
+    const auto& outs = m->out_idx[static_cast<size_t>(k)];
+    const double* Wk = weights + static_cast<int64_t>(k) * Cin * Cout;
+    for (size_t e = 0; e < ins.size(); ++e) {
+      const double* gq = grad_out + static_cast<int64_t>(outs[e]) * Cout;
+      double* gj = grad_in + static_cast<int64_t>(ins[e]) * Cin;
+      for (int32_t ci = 0; ci < Cin; ++ci) {
+        for (int32_t co = 0; co < Cout; ++co) {
+          gj[ci] += gq[co] * Wk[static_cast<int64_t>(ci) * Cout + co];
+        }
+      }
+    }
+  }
+  return kOk;
+}
+
+// Gradient of the forward with respect to the weights, by the same chain
+// rule: each entry (j, q) of list k adds the outer product f_in[j] x
+// grad_out[q] to W[k]'s gradient:
+//   grad_w[k][ci][co] = sum over entries (j, q) of list k of
+//                       feats[j][ci] x grad_out[q][co]
+// in fp64, from zero.  feats is [N][Cin], grad_out [N][Cout], grad_w
+// [K^3][Cin][Cout].
+int oracle_backward_weights(const void* h, const double* feats, const double* grad_out,
+                            int32_t Cin, int32_t Cout, double* grad_w) {
+  const OracleMap* m = static_cast<const OracleMap*>(h);
+  if (feats == nullptr || grad_out == nullptr || grad_w == nullptr || Cin <= 0 || Cout <= 0) {
+    return kInvalidArg;
+  }
+  const int32_t KV = m->K * m->K * m->K;
+  for (int64_t i = 0; i < static_cast<int64_t>(KV) * Cin * Cout; ++i) grad_w[i] = 0.0;
+  for (int32_t k = 0; k < KV; ++k) {
+    const auto& ins = m->in_idx[static_cast<size_t>(k)];
+    const auto& outs = m->out_idx[static_cast<size_t>(k)];
+    double* Gk = grad_w + static_cast<int64_t>(k) * Cin * Cout;
+    for (size_t e = 0; e < ins.size(); ++e) {
+      const double* fj = feats + static_cast<int64_t>(ins[e]) * Cin;
+      const double* gq = grad_out + static_cast<int64_t>(outs[e]) * Cout;
+      for (int32_t ci = 0; ci < Cin; ++ci) {
+        for (int32_t co = 0; co < Cout; ++co) {
+          Gk[static_cast<int64_t>(ci) * Cout + co] += fj[ci] * gq[co];
+        }
+      }
+    }
+  }
+  return kOk;
+}
+
 // Threads oracle_forward_parallel uses when asked for the default.
 int32_t oracle_max_threads(void) { return omp_get_max_threads(); }
 

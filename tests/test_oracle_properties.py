@@ -246,3 +246,102 @@ def test_synthetic_workload_statistics_small():
     m = oracle.build_map(layer.coords, 3)
     assert m.counts[13] == layer.n
     assert m.total_entries == 53274
+
+
+# ---------------------------------------------------------------- backward
+
+
+def _dense_conv3d_grads(coords, feats, w, g, K):
+    """Gradients of L = sum over active sites of <g, conv3d(zero-filled grid)>
+    (torch float64 autograd) with respect to the active sites' input features
+    and to the weights, the latter returned in the [K^3][Cin][Cout] layout."""
+    c = coords.astype(np.int64)
+    r = (K - 1) // 2
+    nb = int(c[:, 0].max()) + 1
+    lo = c[:, 1:].min(axis=0)
+    ext = c[:, 1:].max(axis=0) - lo + 1
+    cin, cout = w.shape[1], w.shape[2]
+    idx = c[:, 1:] - lo
+    grid = torch.zeros((nb, cin, *ext.tolist()), dtype=torch.float64)
+    grid[c[:, 0], :, idx[:, 0], idx[:, 1], idx[:, 2]] = torch.from_numpy(feats)
+    grid.requires_grad_(True)
+    cw = torch.from_numpy(w).reshape(K, K, K, cin, cout).permute(4, 3, 0, 1, 2).contiguous().requires_grad_(True)
+    y = torch.nn.functional.conv3d(grid, cw, padding=r)
+    loss = (y[c[:, 0], :, idx[:, 0], idx[:, 1], idx[:, 2]] * torch.from_numpy(g)).sum()
+    loss.backward()
+    gin = grid.grad[c[:, 0], :, idx[:, 0], idx[:, 1], idx[:, 2]].numpy()
+    gw = cw.grad.permute(2, 3, 4, 1, 0).reshape(K ** 3, cin, cout).numpy()
+    return gin, gw
+
+
+@pytest.mark.parametrize("seed,K,cin,cout,batches", [
+    (61, 3, 5, 7, 1), (62, 3, 8, 3, 2), (63, 5, 4, 6, 1), (64, 1, 6, 5, 1), (65, 3, 16, 12, 1),
+])
+def test_backward_matches_dense_conv3d_autograd(seed, K, cin, cout, batches):
+    """Both gradients equal torch's float64 conv3d backward on the zero-filled
+    dense grid, read at the active sites (an independent library path)."""
+    c = workloads.permuted(workloads.random_grid(seed, 9, 0.2, batches), seed)
+    rng = np.random.default_rng(seed)
+    f = rng.standard_normal((c.shape[0], cin))
+    w = rng.standard_normal((K ** 3, cin, cout))
+    g = rng.standard_normal((c.shape[0], cout))
+    m = oracle.build_map(c, K)
+    gin_ref, gw_ref = _dense_conv3d_grads(c, f, w, g, K)
+    gin = m.backward_data(g, w)
+    gw = m.backward_weights(f, g)
+    assert np.max(np.abs(gin - gin_ref)) <= 1e-12 * np.sqrt(np.mean(gin_ref ** 2))
+    assert np.max(np.abs(gw - gw_ref)) <= 1e-12 * np.sqrt(np.mean(gw_ref ** 2))
+
+
+def test_backward_adjoint_identities():
+    """<g, conv_W f> = <backward_data(g, W), f> = <W, backward_weights(f, g)>:
+    the forward is linear in f and in W, and the two gradients are its
+    adjoints."""
+    c = workloads.permuted(workloads.random_grid(66, 10, 0.25, 2), 66)
+    rng = np.random.default_rng(66)
+    f = rng.standard_normal((c.shape[0], 7))
+    w = rng.standard_normal((27, 7, 5))
+    g = rng.standard_normal((c.shape[0], 5))
+    m = oracle.build_map(c, 3)
+    lhs = float(np.sum(g * m.forward(f, w)))
+    mid = float(np.sum(m.backward_data(g, w) * f))
+    rhs = float(np.sum(w * m.backward_weights(f, g)))
+    scale = float(np.sum(np.abs(g) * np.abs(m.forward(np.abs(f), np.abs(w)))))
+    assert abs(lhs - mid) <= 1e-12 * scale and abs(lhs - rhs) <= 1e-12 * scale
+
+
+def test_backward_data_is_forward_over_the_mirror():
+    """The data gradient is the forward over the same map with the weights
+    of the mirrored offset, transposed: W'_k = W_{K^3 - 1 - k}^T ("Sparse
+    inputs and sparse convolution", section "A symmetry you can check on the
+    slide": (P, Q, d) is an entry exactly when (Q, P, -d) is)."""
+    for K in (3, 5):
+        c = workloads.permuted(workloads.random_grid(67 + K, 9, 0.3, 1), 67)
+        rng = np.random.default_rng(K)
+        w = rng.standard_normal((K ** 3, 6, 9))
+        g = rng.standard_normal((c.shape[0], 9))
+        m = oracle.build_map(c, K)
+        wm = np.ascontiguousarray(w[::-1].transpose(0, 2, 1))
+        ref = m.forward(g, wm)
+        assert np.max(np.abs(m.backward_data(g, w) - ref)) <= 1e-12 * np.sqrt(np.mean(ref ** 2))
+
+
+def test_backward_routing_special_cases():
+    """Identity weights at one offset: the data gradient routes grad_out[q]
+    back to the entry's input row (exactly); all-ones features and output
+    gradients make the weight gradient of offset k its entry count."""
+    c = workloads.random_grid(68, 8, 0.35, 1)
+    n = c.shape[0]
+    m = oracle.build_map(c, 3)
+    rng = np.random.default_rng(68)
+    g = rng.standard_normal((n, 4))
+    for k in (13, 2, 20):
+        w = np.zeros((27, 4, 4))
+        w[k] = np.eye(4)
+        exp = np.zeros((n, 4))
+        j, q = m.lists[k]
+        exp[j] = g[q]
+        assert np.array_equal(m.backward_data(g, w), exp)
+    gw = m.backward_weights(np.ones((n, 3)), np.ones((n, 2)))
+    for k in range(27):
+        assert np.all(gw[k] == m.counts[k])
