@@ -363,6 +363,54 @@ def measure(torch, sp, layer, steps, warmup, events_wanted=10):
     }
 
 
+def measure_backward(torch, sp, layer, reps=20, warmup=3):
+    """Both gradients of the forward over one map of `layer`, each timed
+    with HIP events on the launch stream (median of `reps`): the data
+    gradient (the forward over the mirrored, transposed weights, its
+    weight re-layout kernel included) and the weight gradient (gather-gather
+    MFMA sums per offset and their chunk reduction)."""
+    import numpy as np
+    import workloads
+
+    dev = torch.device("cuda:0")
+    f, w = _inputs(layer)
+    g = workloads.features(layer.n, layer.cout, layer.dtype, layer.feat_seed + 7)
+    coords = torch.from_numpy(layer.coords).to(dev)
+    f, w, g = f.to(dev), w.to(dev), g.to(dev)
+    kmap = sp.build_map(coords, layer.k)
+    gin = torch.empty_like(f)
+    gw = torch.empty((layer.k ** 3, layer.cin, layer.cout), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    t_data = timed(lambda: sp.backward_data(g, w, kmap, out=gin))
+    t_w = timed(lambda: sp.backward_weights(f, g, kmap, out=gw))
+    e = kmap.total_entries
+    kmap.free()
+    flops = 2.0 * e * layer.cin * layer.cout
+    return {
+        "data_gradient_ms": round(t_data, 4),
+        "data_gradient_tflops": round(flops / (t_data * 1e-3) / 1e12, 2),
+        "data_gradient_roofline": roofline(layer, e, t_data),
+        "weight_gradient_ms": round(t_w, 4),
+        "weight_gradient_tflops": round(flops / (t_w * 1e-3) / 1e12, 2),
+        "weight_gradient_mfma_frac": round(flops / (t_w * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[layer.dtype], 4),
+        "note": "one map, median of HIP event pairs; weight gradient written in fp32",
+    }
+
+
 def _inputs(layer):
     import workloads
 
@@ -401,6 +449,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra layers reported beside the default one")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the two gradients")
     ap.add_argument("--no-permuted", action="store_true",
                     help="skip the pass over the rows in a random order")
     ap.add_argument("--no-two-streams", action="store_true",
@@ -480,6 +529,8 @@ def main(argv=None):
                                                       args.warmup, e_total, flops)
     main_inputs = (r["feats_h"], r["w_h"])
     del r
+    if not args.no_backward:
+        result["backward"] = measure_backward(torch, sp, layer)
     if not args.no_extra and (args.workload, args.layer) == (DEFAULT_WORKLOAD, DEFAULT_LAYER):
         extra = []
         for wi, li in EXTRA_LAYERS:

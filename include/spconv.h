@@ -178,6 +178,47 @@ spconv_status spconv_forward(const void* d_feats, const void* d_weights, const s
                              void* hip_stream);
 
 /*
+ * Gradient of the forward with respect to its input features:
+ *   d_grad_in[j][:] = sum_k sum_{(j, q) in list k} d_grad_out[q][:] x W[k]^T
+ * with d_grad_out [N][c_out], d_weights [K^3][c_in][c_out] (the forward's
+ * weights, unchanged) and d_grad_in [N][c_in] (caller-allocated,
+ * overwritten), all in dtype; fp32 accumulation, rounded to dtype (to
+ * nearest even).  By the chain rule of the forward's sum, each entry
+ * (P, Q, W_d) sends grad_out(Q) x W_d^T back to P ("Sparse convolution for
+ * point clouds", section "The map and the update rule"), and since
+ * (P, Q, d) is an entry exactly when (Q, P, -d) is ("Sparse inputs and
+ * sparse convolution", section "A symmetry you can check on the slide"),
+ * this is the forward over the same map with the weights
+ * W'_k = W_{K^3 - 1 - k}^T: a short kernel writes W' into the stream's
+ * workspace and the forward's kernels run on it.  Requirements, ordering
+ * and errors as for spconv_forward with c_in and c_out exchanged
+ * (d_grad_in shares no byte with d_grad_out or d_weights).
+ */
+spconv_status spconv_backward_data(const void* d_grad_out, const void* d_weights, const spconv_map* map,
+                                   int32_t c_in, int32_t c_out, spconv_dtype dtype, void* d_grad_in,
+                                   void* hip_stream);
+
+/*
+ * Gradient of the forward with respect to the weights:
+ *   d_grad_w[k][ci][co] = sum_{(j, q) in list k} d_feats[j][ci] x d_grad_out[q][co]
+ * with d_feats [N][c_in] and d_grad_out [N][c_out] in dtype, and d_grad_w
+ * [K^3][c_in][c_out] in fp32 (caller-allocated, overwritten): each entry
+ * (P, Q, W_d) adds the outer product f_in(P) x grad_out(Q) to W_d's gradient
+ * (the chain rule of the same sum).  Products and sums are fp32: per offset,
+ * chunks of up to 16384 entries are summed on MFMA (F16/BF16 with c_in in
+ * {16, 32, 64, 128, 256} and c_out a multiple of 16; other shapes on the
+ * vector units), and the chunks' sums are added in chunk order, so the
+ * result does not depend on scheduling.  The partial sums live in the
+ * stream's workspace (K^3 x c_in x c_out x 4 bytes per chunk, ceil(N /
+ * 16384) chunks).  Requirements as for spconv_forward; d_grad_w shares no
+ * byte with the inputs.  Errors: INVALID_ARG, UNSUPPORTED, OUT_OF_MEMORY,
+ * DEVICE.
+ */
+spconv_status spconv_backward_weights(const void* d_feats, const void* d_grad_out, const spconv_map* map,
+                                      int32_t c_in, int32_t c_out, spconv_dtype dtype, float* d_grad_w,
+                                      void* hip_stream);
+
+/*
  * The same forward as spconv_forward, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation.  It calls no device allocator.  Where spconv_forward

@@ -85,6 +85,8 @@ def _lib() -> ctypes.CDLL:
         lib.oracle_backward_data.restype = ctypes.c_int
         lib.oracle_backward_weights.argtypes = lib.oracle_forward.argtypes
         lib.oracle_backward_weights.restype = ctypes.c_int
+        lib.oracle_backward_weights_parallel.argtypes = lib.oracle_forward.argtypes + [ctypes.c_int32]
+        lib.oracle_backward_weights_parallel.restype = ctypes.c_int
         lib.oracle_forward_rows.argtypes = [ctypes.c_void_p, _f64p, _f64p, ctypes.c_int32, ctypes.c_int32,
                                             _i64p, ctypes.c_int64, _f64p]
         lib.oracle_forward_rows.restype = ctypes.c_int
@@ -196,6 +198,22 @@ class OracleMap:
         assert f.shape[0] == self.N and g.shape[0] == self.N
         out = np.empty((self.K ** 3, cin, cout), np.float64)
         st = _lib().oracle_backward_weights(self._h, _ptr(f, _f64p), _ptr(g, _f64p), cin, cout, _ptr(out, _f64p))
+        if st != 0:
+            raise OracleError(st)
+        return out
+
+    def backward_weights_parallel(self, feats: np.ndarray, grad_out: np.ndarray, threads: int = 0) -> np.ndarray:
+        """``backward_weights`` with the offsets split over OpenMP threads
+        (same terms in the same order per value: bit-identical)."""
+        if not self.has_lists:
+            raise ValueError("built with lists=False")
+        f = np.ascontiguousarray(np.asarray(feats, dtype=np.float64))
+        g = np.ascontiguousarray(np.asarray(grad_out, dtype=np.float64))
+        cin, cout = f.shape[1], g.shape[1]
+        assert f.shape[0] == self.N and g.shape[0] == self.N
+        out = np.empty((self.K ** 3, cin, cout), np.float64)
+        st = _lib().oracle_backward_weights_parallel(self._h, _ptr(f, _f64p), _ptr(g, _f64p), cin, cout,
+                                                     _ptr(out, _f64p), int(threads))
         if st != 0:
             raise OracleError(st)
         return out

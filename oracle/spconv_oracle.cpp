@@ -291,6 +291,37 @@ int oracle_backward_weights(const void* h, const double* feats, const double* gr
   return kOk;
 }
 
+// The timing and large-input variant of oracle_backward_weights: the offsets
+// split over `threads` OpenMP threads (0: the runtime's default), each
+// thread writing only its offsets' gradients with the same terms in the same
+// order, so the result is bit-identical to oracle_backward_weights.
+int oracle_backward_weights_parallel(const void* h, const double* feats, const double* grad_out,
+                                     int32_t Cin, int32_t Cout, double* grad_w, int32_t threads) {
+  const OracleMap* m = static_cast<const OracleMap*>(h);
+  if (feats == nullptr || grad_out == nullptr || grad_w == nullptr || Cin <= 0 || Cout <= 0 || threads < 0) {
+    return kInvalidArg;
+  }
+  const int32_t KV = m->K * m->K * m->K;
+  const int nt = threads > 0 ? threads : omp_get_max_threads();
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+  for (int32_t k = 0; k < KV; ++k) {
+    const auto& ins = m->in_idx[static_cast<size_t>(k)];
+    const auto& outs = m->out_idx[static_cast<size_t>(k)];
+    double* Gk = grad_w + static_cast<int64_t>(k) * Cin * Cout;
+    for (int64_t i = 0; i < static_cast<int64_t>(Cin) * Cout; ++i) Gk[i] = 0.0;
+    for (size_t e = 0; e < ins.size(); ++e) {
+      const double* fj = feats + static_cast<int64_t>(ins[e]) * Cin;
+      const double* gq = grad_out + static_cast<int64_t>(outs[e]) * Cout;
+      for (int32_t ci = 0; ci < Cin; ++ci) {
+        for (int32_t co = 0; co < Cout; ++co) {
+          Gk[static_cast<int64_t>(ci) * Cout + co] += fj[ci] * gq[co];
+        }
+      }
+    }
+  }
+  return kOk;
+}
+
 // Threads oracle_forward_parallel uses when asked for the default.
 int32_t oracle_max_threads(void) { return omp_get_max_threads(); }
 

@@ -36,7 +36,8 @@ DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 EXPORTED = (
     "spconv_abi_version", "spconv_build_map", "spconv_build_map_async", "spconv_map_wait",
     "spconv_map_info", "spconv_map_counts", "spconv_map_lists", "spconv_forward",
-    "spconv_forward_noalloc", "spconv_map_free", "spconv_status_string", "spconv_last_error",
+    "spconv_forward_noalloc", "spconv_backward_data", "spconv_backward_weights", "spconv_map_free",
+    "spconv_status_string", "spconv_last_error",
 )
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -84,6 +85,10 @@ def lib() -> ctypes.CDLL:
     L.spconv_forward.restype = ctypes.c_int
     L.spconv_forward_noalloc.argtypes = L.spconv_forward.argtypes
     L.spconv_forward_noalloc.restype = ctypes.c_int
+    L.spconv_backward_data.argtypes = L.spconv_forward.argtypes
+    L.spconv_backward_data.restype = ctypes.c_int
+    L.spconv_backward_weights.argtypes = L.spconv_forward.argtypes
+    L.spconv_backward_weights.restype = ctypes.c_int
     L.spconv_map_free.argtypes, L.spconv_map_free.restype = [vp], None
     L.spconv_status_string.argtypes, L.spconv_status_string.restype = [ctypes.c_int], ctypes.c_char_p
     L.spconv_last_error.argtypes, L.spconv_last_error.restype = [], ctypes.c_char_p
@@ -160,6 +165,16 @@ def spconv_forward(d_feats: int, d_weights: int, handle: int, c_in: int, c_out: 
 def spconv_forward_noalloc(d_feats: int, d_weights: int, handle: int, c_in: int, c_out: int, dtype: int,
                            d_out: int, hip_stream: int) -> None:
     _check(lib().spconv_forward_noalloc(d_feats, d_weights, handle, c_in, c_out, dtype, d_out, hip_stream))
+
+
+def spconv_backward_data(d_grad_out: int, d_weights: int, handle: int, c_in: int, c_out: int, dtype: int,
+                         d_grad_in: int, hip_stream: int) -> None:
+    _check(lib().spconv_backward_data(d_grad_out, d_weights, handle, c_in, c_out, dtype, d_grad_in, hip_stream))
+
+
+def spconv_backward_weights(d_feats: int, d_grad_out: int, handle: int, c_in: int, c_out: int, dtype: int,
+                            d_grad_w: int, hip_stream: int) -> None:
+    _check(lib().spconv_backward_weights(d_feats, d_grad_out, handle, c_in, c_out, dtype, d_grad_w, hip_stream))
 
 
 def spconv_map_free(handle: int) -> None:
@@ -324,4 +339,63 @@ def forward(feats, weights, kmap: SpconvMap, out=None, noalloc=False):
     with _OnDevice(feats.device):
         fn = spconv_forward_noalloc if noalloc else spconv_forward
         fn(feats.data_ptr(), weights.data_ptr(), kmap.handle, cin, cout, code, out.data_ptr(), _stream())
+    return out
+
+
+def _check_pair(a, b, kmap: SpconvMap, what):
+    if not (a.is_cuda and b.is_cuda and a.is_contiguous() and b.is_contiguous()):
+        raise SpconvError(1, f"{what} must be contiguous tensors on a HIP device")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[0] != kmap.n or b.shape[0] != kmap.n:
+        raise SpconvError(1, f"{what} must be [N, C] with N = {kmap.n}")
+    if a.dtype != b.dtype:
+        raise SpconvError(1, f"{what} must share one dtype")
+
+
+def backward_data(grad_out, weights, kmap: SpconvMap, out=None):
+    """Gradient of ``forward`` with respect to its features: grad_in
+    [N, C_in] from grad_out [N, C_out] and the forward's weights
+    [K^3, C_in, C_out] (same dtype)."""
+    global _DT
+    torch = _torch()
+    if _DT is None:
+        _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if not (weights.is_cuda and weights.is_contiguous() and weights.dim() == 3):
+        raise SpconvError(1, "weights must be a contiguous [K^3, C_in, C_out] tensor on a HIP device")
+    kv, cin, cout = weights.shape
+    _check_pair(grad_out, grad_out, kmap, "grad_out")
+    if kv != kmap.kernel_volume or grad_out.shape[1] != cout or weights.dtype != grad_out.dtype:
+        raise SpconvError(1, f"shape mismatch: grad_out {tuple(grad_out.shape)}, weights {tuple(weights.shape)}")
+    code = _DT.get(grad_out.dtype)
+    if code is None:
+        raise SpconvError(4, f"dtype {grad_out.dtype} not supported")
+    if out is None:
+        out = torch.empty((kmap.n, cin), dtype=grad_out.dtype, device=grad_out.device)
+    elif not (out.is_cuda and out.is_contiguous() and out.dtype == grad_out.dtype and tuple(out.shape) == (kmap.n, cin)):
+        raise SpconvError(1, "out must be a contiguous [N, C_in] tensor of the gradient dtype")
+    with _OnDevice(grad_out.device):
+        spconv_backward_data(grad_out.data_ptr(), weights.data_ptr(), kmap.handle, cin, cout, code, out.data_ptr(),
+                             _stream())
+    return out
+
+
+def backward_weights(feats, grad_out, kmap: SpconvMap, out=None):
+    """Gradient of ``forward`` with respect to its weights: fp32
+    [K^3, C_in, C_out] from feats [N, C_in] and grad_out [N, C_out]."""
+    global _DT
+    torch = _torch()
+    if _DT is None:
+        _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    _check_pair(feats, grad_out, kmap, "feats and grad_out")
+    code = _DT.get(feats.dtype)
+    if code is None:
+        raise SpconvError(4, f"dtype {feats.dtype} not supported")
+    cin, cout = feats.shape[1], grad_out.shape[1]
+    shape = (kmap.kernel_volume, cin, cout)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=feats.device)
+    elif not (out.is_cuda and out.is_contiguous() and out.dtype == torch.float32 and tuple(out.shape) == shape):
+        raise SpconvError(1, "out must be a contiguous fp32 [K^3, C_in, C_out] tensor")
+    with _OnDevice(feats.device):
+        spconv_backward_weights(feats.data_ptr(), grad_out.data_ptr(), kmap.handle, cin, cout, code, out.data_ptr(),
+                                _stream())
     return out

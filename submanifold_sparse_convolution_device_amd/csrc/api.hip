@@ -583,6 +583,98 @@ spconv_status spconv_forward_noalloc(const void* d_feats, const void* d_weights,
   return launch_forward_path(path, a, ws, stream);
 }
 
+spconv_status spconv_backward_data(const void* d_grad_out, const void* d_weights, const spconv_map* map,
+                                   int32_t c_in, int32_t c_out, spconv_dtype dtype, void* d_grad_in,
+                                   void* hip_stream) {
+  g_last_error.clear();
+  // The data gradient is the forward of grad_out over the same map with the
+  // mirrored, transposed weights: C_out channels in, C_in out.
+  spconv::ForwardArgs a;
+  spconv_status st = forward_args(d_grad_out, d_weights, map, c_out, c_in, dtype, d_grad_in, &a);
+  if (st != SPCONV_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  st = order_after_build(map, stream);
+  if (st != SPCONV_OK) return st;
+  const size_t mirror_bytes = spconv::mirror_workspace_bytes(map->KV, c_in, c_out, static_cast<int>(dtype));
+  const ForwardPath path = forward_path(a);
+  const size_t ws_bytes = mirror_bytes + forward_workspace_bytes(path, a);
+  hipMemPool_t pool = nullptr;
+  st = pool_for(map->device, &pool);
+  if (st != SPCONV_OK) return st;
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  StreamCache* c = cache_for(map->device, stream);
+  st = grow_buffer(c->fwd, c->fwd_bytes, ws_bytes, pool, stream, "backward workspace allocation");
+  if (st != SPCONV_OK) return st;
+  const hipError_t e = spconv::launch_mirror_transpose(d_weights, c->fwd, map->KV, c_in, c_out,
+                                                       static_cast<int>(dtype), stream);
+  if (e != hipSuccess) return hip_fail(e, "weight mirror launch");
+  a.weights = c->fwd;
+  return launch_forward_path(path, a, static_cast<char*>(c->fwd) + mirror_bytes, stream);
+}
+
+spconv_status spconv_backward_weights(const void* d_feats, const void* d_grad_out, const spconv_map* map,
+                                      int32_t c_in, int32_t c_out, spconv_dtype dtype, float* d_grad_w,
+                                      void* hip_stream) {
+  g_last_error.clear();
+  if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
+  if (d_feats == nullptr || d_grad_out == nullptr || d_grad_w == nullptr) {
+    return fail(SPCONV_ERR_INVALID_ARG, "NULL feature, gradient or weight-gradient pointer");
+  }
+  if (!aligned16(d_feats) || !aligned16(d_grad_out) || !aligned16(d_grad_w)) {
+    return fail(SPCONV_ERR_INVALID_ARG, "feature and gradient buffers must be 16-byte aligned");
+  }
+  if (dtype != SPCONV_F32 && dtype != SPCONV_F16 && dtype != SPCONV_BF16) {
+    return fail(SPCONV_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(dtype));
+  }
+  const int32_t cmax = (dtype == SPCONV_F32) ? 512 : 1024;
+  if (c_in < 1 || c_out < 1 || c_in > cmax || c_out > cmax) {
+    return fail(SPCONV_ERR_INVALID_ARG, "c_in = %d, c_out = %d must lie in [1, %d]", c_in, c_out, cmax);
+  }
+  const int32_t mult = (dtype == SPCONV_F32) ? 4 : 8;
+  if (c_in % mult != 0 || c_out % mult != 0) {
+    return fail(SPCONV_ERR_UNSUPPORTED, "c_in = %d and c_out = %d must be multiples of %d", c_in, c_out, mult);
+  }
+  {
+    const uint64_t es = (dtype == SPCONV_F32) ? 4u : 2u;
+    const uint64_t gw_b = static_cast<uint64_t>(map->KV) * c_in * c_out * sizeof(float);
+    auto overlap = [](const void* p, uint64_t np, const void* q, uint64_t nq) {
+      const uint64_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
+      return a0 < b0 + nq && b0 < a0 + np;
+    };
+    if (overlap(d_grad_w, gw_b, d_feats, static_cast<uint64_t>(map->n) * c_in * es) ||
+        overlap(d_grad_w, gw_b, d_grad_out, static_cast<uint64_t>(map->n) * c_out * es)) {
+      return fail(SPCONV_ERR_INVALID_ARG, "d_grad_w overlaps the features or the output gradient");
+    }
+  }
+  spconv::WgradArgs a;
+  a.feats = d_feats;
+  a.grad_out = d_grad_out;
+  a.grad_w = d_grad_w;
+  a.in_idx = map->buf.in_idx;
+  a.out_idx = map->buf.out_idx;
+  a.tile_off = map->buf.tile_off;
+  a.n = map->n;
+  a.tiles = map->tiles;
+  a.KV = map->KV;
+  a.cin = c_in;
+  a.cout = c_out;
+  a.dtype = static_cast<int32_t>(dtype);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  spconv_status st = order_after_build(map, stream);
+  if (st != SPCONV_OK) return st;
+  hipMemPool_t pool = nullptr;
+  st = pool_for(map->device, &pool);
+  if (st != SPCONV_OK) return st;
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  StreamCache* c = cache_for(map->device, stream);
+  st = grow_buffer(c->fwd, c->fwd_bytes, spconv::wgrad_workspace_bytes(a), pool, stream,
+                   "weight-gradient workspace allocation");
+  if (st != SPCONV_OK) return st;
+  const hipError_t e = spconv::launch_wgrad(a, c->fwd, stream);
+  if (e != hipSuccess) return hip_fail(e, "weight-gradient launch");
+  return SPCONV_OK;
+}
+
 void spconv_map_free(spconv_map* map) {
   if (map == nullptr) return;
   if (map->block != nullptr) release_block(map->device, map->stream, map->block, map->block_bytes);

@@ -159,6 +159,31 @@ const uint4* workspace_zero_row(const ForwardArgs& a, const void* workspace);
 bool wide_supported(const ForwardArgs& a);
 size_t wide_workspace_bytes(const ForwardArgs& a);
 hipError_t launch_forward_wide(const ForwardArgs& a, void* workspace, hipStream_t stream);
+// Backward (backward.hip).  The data gradient runs the forward over the
+// same map with W'_k = W_{K^3-1-k}^T, which launch_mirror_transpose writes
+// ([K^3][C_out][C_in], mirror_workspace_bytes); the weight gradient needs
+// wgrad_workspace_bytes of fp32 partial sums.
+hipError_t launch_mirror_transpose(const void* w, void* wt, int KV, int cin, int cout, int dtype,
+                                   hipStream_t stream);
+size_t mirror_workspace_bytes(int KV, int cin, int cout, int dtype);
+struct WgradArgs {
+  const void* feats;     // [n][cin]
+  const void* grad_out;  // [n][cout]
+  float* grad_w;         // [KV][cin][cout], fp32
+  const int32_t* in_idx;
+  const int32_t* out_idx;
+  const int32_t* tile_off;  // KV * tiles + 1: list k starts at tile_off[k * tiles]
+  int64_t n;
+  int64_t tiles;
+  int32_t KV;
+  int32_t cin;
+  int32_t cout;
+  int32_t dtype;
+};
+int wgrad_cols(const WgradArgs& a);
+int64_t wgrad_max_chunks(const WgradArgs& a);
+size_t wgrad_workspace_bytes(const WgradArgs& a);
+hipError_t launch_wgrad(const WgradArgs& a, void* workspace, hipStream_t stream);
 // True when the small-channel kernel (every W_d resident in LDS) serves `a`.
 bool small_supported(const ForwardArgs& a);
 

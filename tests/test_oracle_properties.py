@@ -345,3 +345,13 @@ def test_backward_routing_special_cases():
     gw = m.backward_weights(np.ones((n, 3)), np.ones((n, 2)))
     for k in range(27):
         assert np.all(gw[k] == m.counts[k])
+
+
+@pytest.mark.parametrize("threads", [0, 1, 4, 30])
+def test_backward_weights_parallel_is_bit_identical(threads):
+    c = workloads.permuted(workloads.random_grid(69, 10, 0.3, 2), 69)
+    rng = np.random.default_rng(69)
+    f = rng.standard_normal((c.shape[0], 5))
+    g = rng.standard_normal((c.shape[0], 6))
+    m = oracle.build_map(c, 3)
+    assert np.array_equal(m.backward_weights(f, g), m.backward_weights_parallel(f, g, threads))
