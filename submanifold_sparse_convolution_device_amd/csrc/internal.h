@@ -180,8 +180,6 @@ struct WgradArgs {
   int32_t cout;
   int32_t dtype;
 };
-int wgrad_cols(const WgradArgs& a);
-int64_t wgrad_max_chunks(const WgradArgs& a);
 size_t wgrad_workspace_bytes(const WgradArgs& a);
 hipError_t launch_wgrad(const WgradArgs& a, void* workspace, hipStream_t stream);
 // True when the small-channel kernel (every W_d resident in LDS) serves `a`.
