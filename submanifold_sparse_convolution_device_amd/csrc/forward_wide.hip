@@ -284,7 +284,13 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
     const bool has = o.k >= 0 && ((m >> bit) & 1ull);
     const int rank = __popcll(m & ((1ull << bit) - 1ull));
     const int lo = (b < 4) ? o.lo0 : o.lo1;
-    const int32_t v = in_idx[has ? lo + rank : 0];  // the centre's list holds the row itself
+    // The centre offset reads the task's own rows (the row at each position:
+    // perm, or the position itself), not its list.
+    const int64_t qpos = q0 + 16 * b + r;
+    const bool centre = o.k == KV / 2;  // wave-uniform
+    int32_t v;
+    if (centre && perm == nullptr) v = static_cast<int32_t>(qpos);
+    else v = centre ? perm[has ? qpos : 0] : in_idx[has ? lo + rank : 0];
     // An OR with the "no entry" mask rather than a select on the loaded
     // value: a select would let the compiler move the load under a branch
     // and wait for it there.
