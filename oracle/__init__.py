@@ -11,6 +11,9 @@ Contents
     ctypes front end of ``spconv_oracle.cpp`` (ordered-tree coordinate lookup,
     per-entry fp64 vector-matrix products).  See that file for the passages
     each step follows.
+``build_map_strided`` / ``OracleMap.transpose``
+    Strided maps (downsampling, regular output definition) and their
+    transposes (upsampling); see ``spconv_oracle.cpp``.
 ``OracleMap.backward_data`` / ``OracleMap.backward_weights``
     The gradients of the forward with respect to its input features and its
     weights, each the chain rule of the forward's per-entry sum, in fp64.
@@ -92,6 +95,19 @@ def _lib() -> ctypes.CDLL:
         lib.oracle_forward_rows.restype = ctypes.c_int
         lib.oracle_neighbours.argtypes = [ctypes.c_void_p, _i64p, ctypes.c_int64, _i32p]
         lib.oracle_neighbours.restype = ctypes.c_int
+        lib.oracle_build_map_strided.argtypes = [_i32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.POINTER(ctypes.c_void_p)]
+        lib.oracle_build_map_strided.restype = ctypes.c_int
+        lib.oracle_transpose_map.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+        lib.oracle_transpose_map.restype = ctypes.c_int
+        lib.oracle_map_rows_in.argtypes = [ctypes.c_void_p]
+        lib.oracle_map_rows_in.restype = ctypes.c_int64
+        lib.oracle_map_rows_out.argtypes = [ctypes.c_void_p]
+        lib.oracle_map_rows_out.restype = ctypes.c_int64
+        lib.oracle_map_stride.argtypes = [ctypes.c_void_p]
+        lib.oracle_map_stride.restype = ctypes.c_int32
+        lib.oracle_map_out_coords.argtypes = [ctypes.c_void_p, _i32p]
+        lib.oracle_map_out_coords.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -104,20 +120,40 @@ class OracleMap:
     """Map built by the oracle.  ``lists[k]`` is ``(in_idx, out_idx)`` int32
     arrays ordered by output row.  With ``lists=False`` only the coordinate
     table is built: ``forward_rows`` and ``neighbours`` still work, the lists
-    stay empty."""
+    stay empty.  ``N`` is the number of input rows and ``N_out`` of output
+    rows (equal for a submanifold map); strided and transposed maps (see
+    ``build_map_strided``) also carry ``out_coords`` and ``stride``."""
 
     def __init__(self, coords: np.ndarray, K: int, lists: bool = True):
         coords = np.ascontiguousarray(np.asarray(coords, dtype=np.int32).reshape(-1, 4))
-        self.coords = coords
-        self.K = int(K)
-        self.N = int(coords.shape[0])
         h = ctypes.c_void_p()
         fn = _lib().oracle_build_map if lists else _lib().oracle_build_table
-        st = fn(_ptr(coords, _i32p), self.N, self.K, ctypes.byref(h))
-        self.has_lists = bool(lists)
+        st = fn(_ptr(coords, _i32p), int(coords.shape[0]), int(K), ctypes.byref(h))
         if st != 0:
             raise OracleError(st)
+        self._load(h, K, coords, None, lists)
+
+    @classmethod
+    def _wrap(cls, h, K: int, coords: np.ndarray) -> "OracleMap":
+        m = cls.__new__(cls)
+        n_out = int(_lib().oracle_map_rows_out(h))
+        out = np.empty((n_out, 4), np.int32)
+        st = _lib().oracle_map_out_coords(h, _ptr(out, _i32p))
+        if st != 0:
+            _lib().oracle_map_free(h)
+            raise OracleError(st)
+        m._load(h, K, coords, out, True)
+        return m
+
+    def _load(self, h, K: int, coords: np.ndarray, out_coords: Optional[np.ndarray], lists: bool):
         self._h = h
+        self.coords = coords
+        self.K = int(K)
+        self.N = int(_lib().oracle_map_rows_in(h))
+        self.N_out = int(_lib().oracle_map_rows_out(h))
+        self.stride = int(_lib().oracle_map_stride(h))
+        self.out_coords = out_coords
+        self.has_lists = bool(lists)
         kv = self.K ** 3
         self.counts = np.array([_lib().oracle_map_count(h, k) for k in range(kv)], dtype=np.int64)
         self.lists: List[Tuple[np.ndarray, np.ndarray]] = []
@@ -149,7 +185,7 @@ class OracleMap:
         w = np.ascontiguousarray(np.asarray(weights, dtype=np.float64))
         cin, cout = w.shape[1], w.shape[2]
         assert f.shape == (self.N, cin) and w.shape[0] == self.K ** 3
-        out = np.empty((self.N, cout), np.float64)
+        out = np.empty((self.N_out, cout), np.float64)
         st = _lib().oracle_forward(self._h, _ptr(f, _f64p), _ptr(w, _f64p), cin, cout, _ptr(out, _f64p))
         if st != 0:
             raise OracleError(st)
@@ -165,12 +201,22 @@ class OracleMap:
         w = np.ascontiguousarray(np.asarray(weights, dtype=np.float64))
         cin, cout = w.shape[1], w.shape[2]
         assert f.shape == (self.N, cin) and w.shape[0] == self.K ** 3
-        out = np.empty((self.N, cout), np.float64)
+        out = np.empty((self.N_out, cout), np.float64)
         st = _lib().oracle_forward_parallel(self._h, _ptr(f, _f64p), _ptr(w, _f64p), cin, cout,
                                             _ptr(out, _f64p), int(threads))
         if st != 0:
             raise OracleError(st)
         return out
+
+    def transpose(self) -> "OracleMap":
+        """The transposed map of a strided map (the upsampling convolution),
+        built from its own definition: outputs are this map's inputs, inputs
+        this map's outputs, entry (q, j) at offset d when s q + d = p_j."""
+        h = ctypes.c_void_p()
+        st = _lib().oracle_transpose_map(self._h, ctypes.byref(h))
+        if st != 0:
+            raise OracleError(st)
+        return OracleMap._wrap(h, self.K, self.out_coords)
 
     def backward_data(self, grad_out: np.ndarray, weights: np.ndarray) -> np.ndarray:
         """fp64 gradient with respect to the input features: grad_in[j] = sum
@@ -244,6 +290,27 @@ class OracleMap:
 
 def build_map(coords: np.ndarray, K: int) -> OracleMap:
     return OracleMap(coords, K)
+
+
+def build_map_strided(coords: np.ndarray, K: int, stride: int) -> OracleMap:
+    """Map of a strided convolution with a K^3 kernel (offset components
+    -floor((K-1)/2) .. +K-1-floor((K-1)/2)) and stride ``stride``, outputs by
+    the regular output definition in lexicographic (b, z, y, x) order (see
+    ``oracle_build_map_strided``)."""
+    coords = np.ascontiguousarray(np.asarray(coords, dtype=np.int32).reshape(-1, 4))
+    h = ctypes.c_void_p()
+    st = _lib().oracle_build_map_strided(_ptr(coords, _i32p), int(coords.shape[0]), int(K), int(stride),
+                                         ctypes.byref(h))
+    if st != 0:
+        raise OracleError(st)
+    return OracleMap._wrap(h, K, coords)
+
+
+def offset_of_any(k: int, K: int) -> Tuple[int, int, int]:
+    """Offset of index k for any kernel size: components lo .. lo + K - 1,
+    lo = -floor((K - 1) / 2) (odd K: the centred offsets of ``offset_of``)."""
+    lo = -((K - 1) // 2)
+    return (k // (K * K) + lo, (k // K) % K + lo, k % K + lo)
 
 
 def build_table(coords: np.ndarray, K: int) -> OracleMap:

@@ -54,9 +54,14 @@ using Coord = std::array<int64_t, 4>;  // (b, z, y, x)
 
 struct OracleMap {
   int32_t K = 0;
-  int64_t N = 0;
-  std::vector<Coord> coords;
-  std::map<Coord, int64_t> row_of;               // coordinate -> row index
+  int64_t N = 0;      // rows of the input side
+  int64_t N_out = 0;  // rows of the output side (N for a submanifold map)
+  int32_t stride = 1;
+  int32_t kind = 0;   // 0 submanifold, 1 strided, 2 transposed strided
+  std::vector<Coord> coords;                     // input side
+  std::map<Coord, int64_t> row_of;               // input coordinate -> row index
+  std::vector<Coord> out_coords;                 // output side (strided and transposed maps)
+  std::map<Coord, int64_t> out_row_of;           // output coordinate -> row index
   std::vector<std::vector<int32_t>> in_idx;      // per offset k
   std::vector<std::vector<int32_t>> out_idx;     // per offset k
 };
@@ -67,6 +72,34 @@ void offset_of(int32_t k, int32_t K, int64_t* dz, int64_t* dy, int64_t* dx) {
   *dz = k / (K * K) - r;
   *dy = (k / K) % K - r;
   *dx = k % K - r;
+}
+
+// Offset (dz, dy, dx) of index k for any kernel size K: each component runs
+// over lo .. lo + K - 1 with lo = -floor((K - 1) / 2), so odd sizes are
+// centred (the same offsets as offset_of) and K = 2 covers 0 and 1.
+int64_t offset_low(int32_t K) { return -static_cast<int64_t>((K - 1) / 2); }
+void offset_of_any(int32_t k, int32_t K, int64_t* dz, int64_t* dy, int64_t* dx) {
+  const int64_t lo = offset_low(K);
+  *dz = k / (K * K) + lo;
+  *dy = (k / K) % K + lo;
+  *dx = k % K + lo;
+}
+
+// Validates coordinates and fills a coordinate -> row table; 0 or a status.
+int fill_table(const int32_t* coords, int64_t N, std::vector<Coord>* rows, std::map<Coord, int64_t>* table) {
+  rows->resize(static_cast<size_t>(N));
+  for (int64_t i = 0; i < N; ++i) {
+    Coord c = {coords[4 * i + 0], coords[4 * i + 1], coords[4 * i + 2], coords[4 * i + 3]};
+    if (c[0] < 0 || c[0] >= (int64_t(1) << 15)) return kCoordRange;
+    for (int d = 1; d < 4; ++d) {
+      if (c[d] < 0 || c[d] >= (int64_t(1) << 16)) return kCoordRange;
+    }
+    (*rows)[static_cast<size_t>(i)] = c;
+  }
+  for (int64_t i = 0; i < N; ++i) {
+    if (!table->emplace((*rows)[static_cast<size_t>(i)], i).second) return kDuplicateCoord;
+  }
+  return kOk;
 }
 
 }  // namespace
@@ -97,6 +130,7 @@ int oracle_build_map_impl(const int32_t* coords, int64_t N, int32_t K, bool with
   if (m == nullptr) return kInvalidArg;
   m->K = K;
   m->N = N;
+  m->N_out = N;
   m->coords.resize(static_cast<size_t>(N));
   // Step 1: validate ranges and fill the coordinate -> row table.
   for (int64_t i = 0; i < N; ++i) {
@@ -164,7 +198,7 @@ int oracle_forward(const void* h, const double* feats, const double* weights,
   if (feats == nullptr || weights == nullptr || out == nullptr || Cin <= 0 || Cout <= 0) {
     return kInvalidArg;
   }
-  for (int64_t i = 0; i < m->N * Cout; ++i) out[i] = 0.0;
+  for (int64_t i = 0; i < m->N_out * Cout; ++i) out[i] = 0.0;
   const int32_t KV = m->K * m->K * m->K;
   for (int32_t k = 0; k < KV; ++k) {
     const auto& ins = m->in_idx[static_cast<size_t>(k)];
@@ -199,7 +233,7 @@ int oracle_forward_parallel(const void* h, const double* feats, const double* we
     return kInvalidArg;
   }
   const int32_t KV = m->K * m->K * m->K;
-  const int64_t N = m->N;
+  const int64_t N = m->N_out;  // output rows, split over the threads
   const int nt = threads > 0 ? threads : omp_get_max_threads();
 #pragma omp parallel num_threads(nt)
   {
@@ -376,6 +410,137 @@ int oracle_neighbours(const void* h, const int64_t* rows, int64_t n_rows, int32_
       auto it = m->row_of.find(Coord{cq[0], cq[1] + dz, cq[2] + dy, cq[3] + dx});
       nbr[i * KV + k] = (it == m->row_of.end()) ? -1 : static_cast<int32_t>(it->second);
     }
+  }
+  return kOk;
+}
+
+// ---- Strided maps ("Sparse inputs and sparse convolution", section "The map
+// is the computation": for each output q and offset d, look up s q + d; a hit
+// p joins the map as (p, q, W_d)) with the regular output definition of the
+// SparseConvNet blog, section 2 ("常规输出定义": an output is computed where
+// the kernel covers at least one active input).  Here the outputs are the
+// q >= 0 (in z, y, x; same batch) with an input at s q + d for some offset d
+// of the K^3 kernel (components lo .. lo + K - 1, offset_of_any), in
+// lexicographic (b, z, y, x) order; q must be representable (< 2^16).
+int oracle_build_map_strided(const int32_t* coords, int64_t N, int32_t K, int32_t stride, void** out) {
+  if (out == nullptr) return kInvalidArg;
+  *out = nullptr;
+  if (coords == nullptr || N <= 0 || K < 1 || K > 7 || stride < 1 || stride > 16) return kInvalidArg;
+  OracleMap* m = new (std::nothrow) OracleMap;
+  if (m == nullptr) return kInvalidArg;
+  m->K = K;
+  m->N = N;
+  m->stride = stride;
+  m->kind = 1;
+  // Step 1: the input table.
+  const int st = fill_table(coords, N, &m->coords, &m->row_of);
+  if (st != kOk) { delete m; return st; }
+  // Step 2: the output set, from every (input, offset) pair that lands on a
+  // grid point s q: q = (p - d) / s when that divides and is >= 0.
+  const int32_t KV = K * K * K;
+  std::map<Coord, int64_t> outs;
+  for (const Coord& p : m->coords) {
+    for (int32_t k = 0; k < KV; ++k) {
+      int64_t d[3];
+      offset_of_any(k, K, &d[0], &d[1], &d[2]);
+      Coord q = {p[0], 0, 0, 0};
+      bool ok = true;
+      for (int i = 0; i < 3; ++i) {
+        const int64_t v = p[1 + i] - d[i];
+        if (v < 0 || v % stride != 0 || v / stride >= (int64_t(1) << 16)) { ok = false; break; }
+        q[1 + i] = v / stride;
+      }
+      if (ok) outs.emplace(q, 0);
+    }
+  }
+  int64_t row = 0;
+  for (auto& kv : outs) {
+    kv.second = row++;
+    m->out_coords.push_back(kv.first);
+  }
+  m->out_row_of = std::move(outs);
+  m->N_out = row;
+  // Step 3: the double loop over outputs q (in order) and offsets k with a
+  // lookup of s q + d; a hit p adds (in = p, out = q) to list k.
+  m->in_idx.assign(static_cast<size_t>(KV), {});
+  m->out_idx.assign(static_cast<size_t>(KV), {});
+  for (int64_t q = 0; q < m->N_out; ++q) {
+    const Coord& cq = m->out_coords[static_cast<size_t>(q)];
+    for (int32_t k = 0; k < KV; ++k) {
+      int64_t dz, dy, dx;
+      offset_of_any(k, K, &dz, &dy, &dx);
+      const Coord p = {cq[0], stride * cq[1] + dz, stride * cq[2] + dy, stride * cq[3] + dx};
+      auto it = m->row_of.find(p);
+      if (it != m->row_of.end()) {
+        m->in_idx[static_cast<size_t>(k)].push_back(static_cast<int32_t>(it->second));
+        m->out_idx[static_cast<size_t>(k)].push_back(static_cast<int32_t>(q));
+      }
+    }
+  }
+  *out = m;
+  return kOk;
+}
+
+// The transpose of a strided map (the upsampling convolution): its outputs
+// are the strided map's inputs (in their order) and its inputs the strided
+// map's outputs.  Built from its own definition, not by swapping the lists:
+// for each output j (input p_j of the strided map) and offset k, the input is
+// the strided output q with s q + d = p_j, i.e. q = (p_j - d) / s when that
+// divides, is >= 0 and is an output; the entry is (in = q, out = j).
+int oracle_transpose_map(const void* h, void** out) {
+  if (out == nullptr) return kInvalidArg;
+  *out = nullptr;
+  const OracleMap* m = static_cast<const OracleMap*>(h);
+  if (m == nullptr || m->kind != 1) return kInvalidArg;
+  OracleMap* t = new (std::nothrow) OracleMap;
+  if (t == nullptr) return kInvalidArg;
+  t->K = m->K;
+  t->stride = m->stride;
+  t->kind = 2;
+  t->N = m->N_out;
+  t->N_out = m->N;
+  t->coords = m->out_coords;
+  t->row_of = m->out_row_of;
+  t->out_coords = m->coords;
+  t->out_row_of = m->row_of;
+  const int32_t K = m->K, KV = K * K * K, s = m->stride;
+  t->in_idx.assign(static_cast<size_t>(KV), {});
+  t->out_idx.assign(static_cast<size_t>(KV), {});
+  for (int64_t j = 0; j < t->N_out; ++j) {
+    const Coord& pj = t->out_coords[static_cast<size_t>(j)];
+    for (int32_t k = 0; k < KV; ++k) {
+      int64_t d[3];
+      offset_of_any(k, K, &d[0], &d[1], &d[2]);
+      Coord q = {pj[0], 0, 0, 0};
+      bool ok = true;
+      for (int i = 0; i < 3; ++i) {
+        const int64_t v = pj[1 + i] - d[i];
+        if (v < 0 || v % s != 0) { ok = false; break; }
+        q[1 + i] = v / s;
+      }
+      if (!ok) continue;
+      auto it = t->row_of.find(q);
+      if (it != t->row_of.end()) {
+        t->in_idx[static_cast<size_t>(k)].push_back(static_cast<int32_t>(it->second));
+        t->out_idx[static_cast<size_t>(k)].push_back(static_cast<int32_t>(j));
+      }
+    }
+  }
+  *out = t;
+  return kOk;
+}
+
+// Rows of the input and output sides, and the stride.
+int64_t oracle_map_rows_in(const void* h) { return static_cast<const OracleMap*>(h)->N; }
+int64_t oracle_map_rows_out(const void* h) { return static_cast<const OracleMap*>(h)->N_out; }
+int32_t oracle_map_stride(const void* h) { return static_cast<const OracleMap*>(h)->stride; }
+
+// Output coordinates of a strided or transposed map into [N_out][4] (b, z, y, x).
+int oracle_map_out_coords(const void* h, int32_t* out) {
+  const OracleMap* m = static_cast<const OracleMap*>(h);
+  if (out == nullptr || m->kind == 0) return kInvalidArg;
+  for (size_t i = 0; i < m->out_coords.size(); ++i) {
+    for (int d = 0; d < 4; ++d) out[4 * i + d] = static_cast<int32_t>(m->out_coords[i][static_cast<size_t>(d)]);
   }
   return kOk;
 }
