@@ -82,8 +82,16 @@ typedef enum spconv_dtype {
 /* Opaque kernel map.  Owns its device buffers until spconv_map_free. */
 typedef struct spconv_map spconv_map;
 
+/* Kinds of map (spconv_map_geometry). */
+typedef enum spconv_map_kind {
+  SPCONV_MAP_SUBMANIFOLD = 0, /* outputs = inputs (spconv_build_map)            */
+  SPCONV_MAP_STRIDED = 1,     /* downsampling (spconv_build_map_strided)          */
+  SPCONV_MAP_TRANSPOSED = 2   /* upsampling, a strided map's transpose            */
+} spconv_map_kind;
+
 /* Version of this ABI (incremented on any incompatible change; 2: lists in
- * the map's row order instead of increasing out_idx). */
+ * the map's row order instead of increasing out_idx; 3: strided and
+ * transposed maps, whose input and output rows differ). */
 int32_t spconv_abi_version(void);
 
 /*
@@ -192,7 +200,10 @@ spconv_status spconv_forward(const void* d_feats, const void* d_weights, const s
  * W'_k = W_{K^3 - 1 - k}^T: a short kernel writes W' into the stream's
  * workspace and the forward's kernels run on it.  Requirements, ordering
  * and errors as for spconv_forward with c_in and c_out exchanged
- * (d_grad_in shares no byte with d_grad_out or d_weights).
+ * (d_grad_in shares no byte with d_grad_out or d_weights).  Submanifold maps
+ * only (UNSUPPORTED otherwise): the data gradient of a strided map is the
+ * forward over its transpose (spconv_map_transpose) with the weights W[k]^T,
+ * and that of a transposed map the forward over the strided map with W[k]^T.
  */
 spconv_status spconv_backward_data(const void* d_grad_out, const void* d_weights, const spconv_map* map,
                                    int32_t c_in, int32_t c_out, spconv_dtype dtype, void* d_grad_in,
@@ -204,15 +215,18 @@ spconv_status spconv_backward_data(const void* d_grad_out, const void* d_weights
  * with d_feats [N][c_in] and d_grad_out [N][c_out] in dtype, and d_grad_w
  * [K^3][c_in][c_out] in fp32 (caller-allocated, overwritten): each entry
  * (P, Q, W_d) adds the outer product f_in(P) x grad_out(Q) to W_d's gradient
- * (the chain rule of the same sum).  Products and sums are fp32: per offset,
- * chunks of up to 16384 entries are summed on MFMA (F16/BF16 with c_in in
- * {16, 32, 64, 128, 256} and c_out a multiple of 16; other shapes on the
- * vector units), and the chunks' sums are added in chunk order, so the
- * result does not depend on scheduling.  The partial sums live in the
- * stream's workspace (K^3 x c_in x c_out x 4 bytes per chunk, ceil(N /
- * 16384) chunks).  Requirements as for spconv_forward; d_grad_w shares no
- * byte with the inputs.  Errors: INVALID_ARG, UNSUPPORTED, OUT_OF_MEMORY,
- * DEVICE.
+ * (the chain rule of the same sum).  Products and sums are fp32: each
+ * offset's entries are cut by ranges of consecutive 64-row output tiles
+ * (about 2048 (range, column group, offset) units per call), each range
+ * summed on MFMA (F16/BF16 with c_in in {16, 32, 64, 128, 256} and c_out a
+ * multiple of 16, except c_in = 256 with c_out not a multiple of 32; other
+ * shapes on the vector units), and the ranges' sums are added in range
+ * order, so the result does not depend on scheduling.  The partial sums live
+ * in the stream's workspace (K^3 x c_in x c_out x 4 bytes per range).  Any
+ * map kind: d_feats has the map's input rows, d_grad_out its output rows
+ * (spconv_map_geometry).  Requirements as for spconv_forward; d_grad_w
+ * shares no byte with the inputs.  Errors: INVALID_ARG, UNSUPPORTED,
+ * OUT_OF_MEMORY, DEVICE.
  */
 spconv_status spconv_backward_weights(const void* d_feats, const void* d_grad_out, const spconv_map* map,
                                       int32_t c_in, int32_t c_out, spconv_dtype dtype, float* d_grad_w,
@@ -243,6 +257,68 @@ spconv_status spconv_backward_weights(const void* d_feats, const void* d_grad_ou
 spconv_status spconv_forward_noalloc(const void* d_feats, const void* d_weights, const spconv_map* map,
                                      int32_t c_in, int32_t c_out, spconv_dtype dtype, void* d_out,
                                      void* hip_stream);
+
+/*
+ * Builds the kernel map of a strided (downsampling) sparse convolution with a
+ * K x K x K kernel and stride `stride` over the n_in voxels at d_coords
+ * (device int32 [n_in][4], (b, z, y, x), unique).
+ *
+ * Offsets: each component of d runs over lo .. lo + K - 1 with
+ * lo = -floor((K - 1) / 2) (centred for odd K; K = 2 covers 0 and 1), index
+ * k(d) = ((dz - lo) K + (dy - lo)) K + (dx - lo); weights [K^3][c_in][c_out].
+ * Outputs: the regular output definition (SparseConvNet blog, section 2: an
+ * output is computed where the kernel covers at least one active input) on
+ * the grid of stride `stride`: every q >= 0 (same b) with an input at
+ * stride x q + d for some offset d, in lexicographic (b, z, y, x) order
+ * (spconv_map_out_coords; K = 2, stride 2 gives unique(coords // 2)).
+ * Entries: for each output q and offset d, the input at stride x q + d, if
+ * active, adds (in, q, W_d) ("Sparse inputs and sparse convolution", section
+ * "The map is the computation": look up s q + d).  There is no identity
+ * offset; the forward (spconv_forward) reads d_feats [n_in][c_in] and writes
+ * d_out [n_out][c_out].  Lists are grouped by offset, in increasing output
+ * row within an offset.
+ *
+ * Work: the input table (the same device hash as spconv_build_map), every
+ * (input, offset) candidate output key, a device radix sort and unique of
+ * the keys, a host read of the number of outputs (one wait), then a probe of
+ * every offset for every output and the per-offset compaction.  The build
+ * synchronises hip_stream twice.
+ *
+ * Errors: INVALID_ARG (NULL or misaligned pointers, n_in <= 0, n_in x
+ * ceil(K / stride)^3 >= 2^31, n_out x K^3 >= 2^31), UNSUPPORTED (K not in
+ * [1, 5], stride not in [1, 16]), DUPLICATE_COORD, COORD_RANGE,
+ * OUT_OF_MEMORY, DEVICE.  On success *out_map is a new map (it may have no
+ * outputs: then every forward over it writes nothing), else NULL.
+ */
+spconv_status spconv_build_map_strided(const int32_t* d_coords, int64_t n_in, int32_t kernel_size, int32_t stride,
+                                       void* hip_stream, spconv_map** out_map);
+
+/*
+ * The transpose of a strided map: the upsampling convolution from the
+ * strided map's outputs back onto its inputs.  Its outputs are the strided
+ * map's inputs (in their order; spconv_map_out_coords) and its entries the
+ * strided map's, reversed: (q, p, W_d) for every (p, q, W_d), found by
+ * probing, for each of its outputs p and offsets d, the strided output q
+ * with stride x q + d = p.  Lists in increasing output row within an offset.
+ * The forward over it reads d_feats [n_out of the strided map][c_in] and
+ * writes d_out [n_in of the strided map][c_out] with weights
+ * [K^3][c_in][c_out].  Synchronises hip_stream once.
+ *
+ * Errors: INVALID_ARG (NULL pointers, not on the map's device), UNSUPPORTED
+ * (map not strided), OUT_OF_MEMORY, DEVICE.  The strided map stays valid and
+ * independent of the new one.
+ */
+spconv_status spconv_map_transpose(spconv_map* map, void* hip_stream, spconv_map** out_map);
+
+/* Input rows, output rows, stride (1 for a submanifold map) and kind
+ * (spconv_map_kind) of a map; any output pointer may be NULL. */
+spconv_status spconv_map_geometry(const spconv_map* map, int64_t* n_in, int64_t* n_out, int32_t* stride,
+                                  int32_t* kind);
+
+/* Borrowed device pointer to the output coordinates (int32 [n_out][4]) of a
+ * strided or transposed map, valid until spconv_map_free.  UNSUPPORTED for a
+ * submanifold map, whose outputs are its inputs. */
+spconv_status spconv_map_out_coords(const spconv_map* map, const int32_t** d_out_coords);
 
 /* Releases a map.  Its buffers go back, in the order of the build's stream,
  * to that stream's cache of map blocks (or to the pool); the caller must not

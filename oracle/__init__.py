@@ -226,7 +226,7 @@ class OracleMap:
         g = np.ascontiguousarray(np.asarray(grad_out, dtype=np.float64))
         w = np.ascontiguousarray(np.asarray(weights, dtype=np.float64))
         cin, cout = w.shape[1], w.shape[2]
-        assert g.shape == (self.N, cout) and w.shape[0] == self.K ** 3
+        assert g.shape == (self.N_out, cout) and w.shape[0] == self.K ** 3
         out = np.empty((self.N, cin), np.float64)
         st = _lib().oracle_backward_data(self._h, _ptr(g, _f64p), _ptr(w, _f64p), cin, cout, _ptr(out, _f64p))
         if st != 0:
@@ -241,7 +241,7 @@ class OracleMap:
         f = np.ascontiguousarray(np.asarray(feats, dtype=np.float64))
         g = np.ascontiguousarray(np.asarray(grad_out, dtype=np.float64))
         cin, cout = f.shape[1], g.shape[1]
-        assert f.shape[0] == self.N and g.shape[0] == self.N
+        assert f.shape[0] == self.N and g.shape[0] == self.N_out
         out = np.empty((self.K ** 3, cin, cout), np.float64)
         st = _lib().oracle_backward_weights(self._h, _ptr(f, _f64p), _ptr(g, _f64p), cin, cout, _ptr(out, _f64p))
         if st != 0:
@@ -256,7 +256,7 @@ class OracleMap:
         f = np.ascontiguousarray(np.asarray(feats, dtype=np.float64))
         g = np.ascontiguousarray(np.asarray(grad_out, dtype=np.float64))
         cin, cout = f.shape[1], g.shape[1]
-        assert f.shape[0] == self.N and g.shape[0] == self.N
+        assert f.shape[0] == self.N and g.shape[0] == self.N_out
         out = np.empty((self.K ** 3, cin, cout), np.float64)
         st = _lib().oracle_backward_weights_parallel(self._h, _ptr(f, _f64p), _ptr(g, _f64p), cin, cout,
                                                      _ptr(out, _f64p), int(threads))

@@ -36,9 +36,11 @@ DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 EXPORTED = (
     "spconv_abi_version", "spconv_build_map", "spconv_build_map_async", "spconv_map_wait",
     "spconv_map_info", "spconv_map_counts", "spconv_map_lists", "spconv_forward",
-    "spconv_forward_noalloc", "spconv_backward_data", "spconv_backward_weights", "spconv_map_free",
+    "spconv_forward_noalloc", "spconv_backward_data", "spconv_backward_weights", "spconv_build_map_strided",
+    "spconv_map_transpose", "spconv_map_geometry", "spconv_map_out_coords", "spconv_map_free",
     "spconv_status_string", "spconv_last_error",
 )
+MAP_KINDS = {0: "submanifold", 1: "strided", 2: "transposed"}
 
 _LIB: Optional[ctypes.CDLL] = None
 
@@ -89,6 +91,15 @@ def lib() -> ctypes.CDLL:
     L.spconv_backward_data.restype = ctypes.c_int
     L.spconv_backward_weights.argtypes = L.spconv_forward.argtypes
     L.spconv_backward_weights.restype = ctypes.c_int
+    L.spconv_build_map_strided.argtypes = [vp, i64, i32, i32, vp, ctypes.POINTER(vp)]
+    L.spconv_build_map_strided.restype = ctypes.c_int
+    L.spconv_map_transpose.argtypes = [vp, vp, ctypes.POINTER(vp)]
+    L.spconv_map_transpose.restype = ctypes.c_int
+    L.spconv_map_geometry.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i32),
+                                      ctypes.POINTER(i32)]
+    L.spconv_map_geometry.restype = ctypes.c_int
+    L.spconv_map_out_coords.argtypes = [vp, ctypes.POINTER(vp)]
+    L.spconv_map_out_coords.restype = ctypes.c_int
     L.spconv_map_free.argtypes, L.spconv_map_free.restype = [vp], None
     L.spconv_status_string.argtypes, L.spconv_status_string.restype = [ctypes.c_int], ctypes.c_char_p
     L.spconv_last_error.argtypes, L.spconv_last_error.restype = [], ctypes.c_char_p
@@ -177,6 +188,32 @@ def spconv_backward_weights(d_feats: int, d_grad_out: int, handle: int, c_in: in
     _check(lib().spconv_backward_weights(d_feats, d_grad_out, handle, c_in, c_out, dtype, d_grad_w, hip_stream))
 
 
+def spconv_build_map_strided(d_coords: int, n_in: int, kernel_size: int, stride: int, hip_stream: int) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().spconv_build_map_strided(d_coords, n_in, kernel_size, stride, hip_stream, ctypes.byref(h)))
+    return int(h.value)
+
+
+def spconv_map_transpose(handle: int, hip_stream: int) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().spconv_map_transpose(handle, hip_stream, ctypes.byref(h)))
+    return int(h.value)
+
+
+def spconv_map_geometry(handle: int) -> Tuple[int, int, int, int]:
+    n_in, n_out = ctypes.c_int64(), ctypes.c_int64()
+    stride, kind = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().spconv_map_geometry(handle, ctypes.byref(n_in), ctypes.byref(n_out), ctypes.byref(stride),
+                                     ctypes.byref(kind)))
+    return n_in.value, n_out.value, stride.value, kind.value
+
+
+def spconv_map_out_coords(handle: int) -> int:
+    p = ctypes.c_void_p()
+    _check(lib().spconv_map_out_coords(handle, ctypes.byref(p)))
+    return int(p.value or 0)
+
+
 def spconv_map_free(handle: int) -> None:
     lib().spconv_map_free(handle)
 
@@ -224,15 +261,44 @@ class _OnDevice:
 
 
 class SpconvMap:
-    """A kernel map on the GPU (owns the C handle)."""
+    """A kernel map on the GPU (owns the C handle).  ``n`` is its number of
+    output rows and ``n_in`` of input rows (equal for a submanifold map);
+    ``kind`` is "submanifold", "strided" or "transposed"."""
 
-    def __init__(self, handle: int, device, kernel_size: int, n: int):
+    def __init__(self, handle: int, device, kernel_size: int, n: int, n_in: Optional[int] = None,
+                 stride: int = 1, kind: str = "submanifold"):
         self.handle = handle
         self.device = device
         self.kernel_size, self.n = kernel_size, n
+        self.n_in = n if n_in is None else n_in
+        self.stride, self.kind = stride, kind
         self.kernel_volume = self.kernel_size ** 3
         self._counts = None
         self._total = None
+
+    @classmethod
+    def _from_handle(cls, h: int, device, kernel_size: int) -> "SpconvMap":
+        n_in, n_out, stride, kind = spconv_map_geometry(h)
+        return cls(h, device, kernel_size, n_out, n_in, stride, MAP_KINDS[kind])
+
+    def out_coords(self):
+        """Output coordinates (int32 [n, 4] device tensor, a stream-ordered
+        copy) of a strided or transposed map."""
+        torch = _torch()
+        src = spconv_map_out_coords(self.handle)
+        out = torch.empty((self.n, 4), dtype=torch.int32, device=self.device)
+        if self.n:
+            with _OnDevice(self.device):
+                rc = lib().hipMemcpyAsync(out.data_ptr(), src, 16 * self.n, 3, _stream())
+                if rc != 0:
+                    raise SpconvError(6, f"hipMemcpyAsync failed with {rc}")
+        return out
+
+    def transpose(self) -> "SpconvMap":
+        """The transposed (upsampling) map of a strided map."""
+        with _OnDevice(self.device):
+            h = spconv_map_transpose(self.handle, _stream())
+        return SpconvMap._from_handle(h, self.device, self.kernel_size)
 
     def wait(self) -> None:
         """Waits for the build (a no-op once done); raises its device error."""
@@ -302,12 +368,27 @@ def build_map(coords, kernel_size: int, wait: bool = True) -> SpconvMap:
     return SpconvMap(h, coords.device, int(kernel_size), int(coords.shape[0]))
 
 
+def build_map_strided(coords, kernel_size: int, stride: int) -> SpconvMap:
+    """Kernel map of a strided (downsampling) convolution with a K^3 kernel
+    (offset components -floor((K-1)/2) ..) over int32 [N, 4] coordinates on a
+    HIP device; its outputs (``out_coords``) follow the regular output
+    definition in lexicographic order."""
+    torch = _torch()
+    if not (isinstance(coords, torch.Tensor) and coords.is_cuda and coords.dtype == torch.int32
+            and coords.dim() == 2 and coords.shape[1] == 4 and coords.is_contiguous()):
+        raise SpconvError(1, "coords must be a contiguous int32 [N, 4] tensor on a HIP device")
+    with _OnDevice(coords.device):
+        h = spconv_build_map_strided(coords.data_ptr(), coords.shape[0], int(kernel_size), int(stride), _stream())
+    return SpconvMap._from_handle(h, coords.device, int(kernel_size))
+
+
 _DT = None
 
 
 def forward(feats, weights, kmap: SpconvMap, out=None, noalloc=False):
-    """f_out = submanifold convolution of feats [N, C_in] with weights
-    [K^3, C_in, C_out] over ``kmap``; returns out [N, C_out] (same dtype).
+    """f_out = sparse convolution of feats [n_in, C_in] with weights
+    [K^3, C_in, C_out] over ``kmap``; returns out [n, C_out] (same dtype;
+    n_in = n for a submanifold map).
     With ``noalloc`` the call goes to ``spconv_forward_noalloc`` (the
     library's fixed per-device scratch instead of an allocated workspace;
     ``out`` must then be given, so that nothing is allocated here either)."""
@@ -319,11 +400,12 @@ def forward(feats, weights, kmap: SpconvMap, out=None, noalloc=False):
         raise SpconvError(1, "feats and weights must be contiguous tensors on a HIP device")
     if feats.dim() != 2 or weights.dim() != 3:
         raise SpconvError(1, "feats must be [N, C_in] and weights [K^3, C_in, C_out]")
-    n, cin = feats.shape
+    n_in, cin = feats.shape
+    n = kmap.n
     kv, wcin, cout = weights.shape
-    if n != kmap.n or kv != kmap.kernel_volume or wcin != cin:
+    if n_in != kmap.n_in or kv != kmap.kernel_volume or wcin != cin:
         raise SpconvError(1, f"shape mismatch: feats {tuple(feats.shape)}, weights "
-                             f"{tuple(weights.shape)}, map N={kmap.n} K^3={kmap.kernel_volume}")
+                             f"{tuple(weights.shape)}, map n_in={kmap.n_in} K^3={kmap.kernel_volume}")
     dt = feats.dtype
     if weights.dtype != dt:
         raise SpconvError(1, "feats and weights must share one dtype")
@@ -342,11 +424,12 @@ def forward(feats, weights, kmap: SpconvMap, out=None, noalloc=False):
     return out
 
 
-def _check_pair(a, b, kmap: SpconvMap, what):
+def _check_pair(a, b, kmap: SpconvMap, what, rows_a=None):
+    rows_a = kmap.n if rows_a is None else rows_a
     if not (a.is_cuda and b.is_cuda and a.is_contiguous() and b.is_contiguous()):
         raise SpconvError(1, f"{what} must be contiguous tensors on a HIP device")
-    if a.dim() != 2 or b.dim() != 2 or a.shape[0] != kmap.n or b.shape[0] != kmap.n:
-        raise SpconvError(1, f"{what} must be [N, C] with N = {kmap.n}")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[0] != rows_a or b.shape[0] != kmap.n:
+        raise SpconvError(1, f"{what} must be [{rows_a}, C] and [{kmap.n}, C]")
     if a.dtype != b.dtype:
         raise SpconvError(1, f"{what} must share one dtype")
 
@@ -369,9 +452,10 @@ def backward_data(grad_out, weights, kmap: SpconvMap, out=None):
     if code is None:
         raise SpconvError(4, f"dtype {grad_out.dtype} not supported")
     if out is None:
-        out = torch.empty((kmap.n, cin), dtype=grad_out.dtype, device=grad_out.device)
-    elif not (out.is_cuda and out.is_contiguous() and out.dtype == grad_out.dtype and tuple(out.shape) == (kmap.n, cin)):
-        raise SpconvError(1, "out must be a contiguous [N, C_in] tensor of the gradient dtype")
+        out = torch.empty((kmap.n_in, cin), dtype=grad_out.dtype, device=grad_out.device)
+    elif not (out.is_cuda and out.is_contiguous() and out.dtype == grad_out.dtype
+              and tuple(out.shape) == (kmap.n_in, cin)):
+        raise SpconvError(1, "out must be a contiguous [n_in, C_in] tensor of the gradient dtype")
     with _OnDevice(grad_out.device):
         spconv_backward_data(grad_out.data_ptr(), weights.data_ptr(), kmap.handle, cin, cout, code, out.data_ptr(),
                              _stream())
@@ -380,12 +464,12 @@ def backward_data(grad_out, weights, kmap: SpconvMap, out=None):
 
 def backward_weights(feats, grad_out, kmap: SpconvMap, out=None):
     """Gradient of ``forward`` with respect to its weights: fp32
-    [K^3, C_in, C_out] from feats [N, C_in] and grad_out [N, C_out]."""
+    [K^3, C_in, C_out] from feats [n_in, C_in] and grad_out [n, C_out]."""
     global _DT
     torch = _torch()
     if _DT is None:
         _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-    _check_pair(feats, grad_out, kmap, "feats and grad_out")
+    _check_pair(feats, grad_out, kmap, "feats and grad_out", rows_a=kmap.n_in)
     code = _DT.get(feats.dtype)
     if code is None:
         raise SpconvError(4, f"dtype {feats.dtype} not supported")

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspconv.so")
-SOURCES = ["api.hip", "map_build.hip", "forward.hip", "forward_tiled.hip", "forward_wide.hip", "backward.hip"]
+SOURCES = ["api.hip", "map_build.hip", "map_strided.hip", "forward.hip", "forward_tiled.hip", "forward_wide.hip",
+           "backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

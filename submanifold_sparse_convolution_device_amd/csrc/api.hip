@@ -3,6 +3,7 @@
 // launches.  No compute happens here.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -34,7 +35,13 @@ struct spconv_map {
   hipStream_t stream = nullptr;
   int32_t K = 0;
   int32_t KV = 0;
-  int64_t n = 0;
+  int64_t n = 0;      // output rows (the forward's rows and tiles)
+  int64_t n_in = 0;   // input rows (n for a submanifold map)
+  int32_t centre = 0;  // offset whose list is the identity, -1 for none
+  int32_t stride = 1;
+  int32_t kind = 0;    // SPCONV_MAP_SUBMANIFOLD, _STRIDED or _TRANSPOSED
+  int32_t* out_coords = nullptr;  // [n][4] (strided and transposed maps; in the block)
+  int32_t* in_coords = nullptr;   // [n_in][4] copy (strided and transposed maps; in the block)
   int64_t tiles = 0;
   void* block = nullptr;  // one pool allocation holding the MapBuffers
   size_t block_bytes = 0;
@@ -293,7 +300,9 @@ spconv_status noalloc_scratch(int device, void** out) {
 spconv_status forward_args(const void* d_feats, const void* d_weights, const spconv_map* map, int32_t c_in,
                            int32_t c_out, spconv_dtype dtype, void* d_out, spconv::ForwardArgs* out) {
   if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
-  if (d_feats == nullptr || d_weights == nullptr || d_out == nullptr) {
+  // A side with no rows (a strided map without outputs, or its transpose)
+  // may be NULL: nothing of it is read or written.
+  if ((d_feats == nullptr && map->n_in > 0) || d_weights == nullptr || (d_out == nullptr && map->n > 0)) {
     return fail(SPCONV_ERR_INVALID_ARG, "NULL feature, weight or output pointer");
   }
   if (!aligned16(d_feats) || !aligned16(d_weights) || !aligned16(d_out)) {
@@ -316,7 +325,7 @@ spconv_status forward_args(const void* d_feats, const void* d_weights, const spc
     // weights: it must not share a byte with either.
     const uint64_t es = (dtype == SPCONV_F32) ? 4u : 2u;
     const uint64_t out_b = static_cast<uint64_t>(map->n) * c_out * es;
-    const uint64_t in_b = static_cast<uint64_t>(map->n) * c_in * es;
+    const uint64_t in_b = static_cast<uint64_t>(map->n_in) * c_in * es;
     const uint64_t w_b = static_cast<uint64_t>(map->KV) * c_in * c_out * es;
     auto overlap = [](const void* p, uint64_t np, const void* q, uint64_t nq) {
       const uint64_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
@@ -342,6 +351,18 @@ spconv_status forward_args(const void* d_feats, const void* d_weights, const spc
   a.cin = c_in;
   a.cout = c_out;
   a.dtype = static_cast<int32_t>(dtype);
+  a.centre = map->centre;
+  a.n_in = map->n_in;
+  return SPCONV_OK;
+}
+
+// A map known to hold no entries (a strided map with no outputs, or its
+// transpose): the forward writes zeros and launches no kernel.
+bool known_empty(const spconv_map* map) { return map->slot == nullptr && map->total == 0; }
+
+spconv_status zero_output(void* d_out, int64_t rows, int32_t c_out, spconv_dtype dtype, hipStream_t stream) {
+  const size_t es = (dtype == SPCONV_F32) ? 4u : 2u;
+  if (rows > 0) SPCONV_HIP(hipMemsetAsync(d_out, 0, static_cast<size_t>(rows) * c_out * es, stream), "hipMemsetAsync");
   return SPCONV_OK;
 }
 
@@ -390,11 +411,60 @@ spconv_status launch_forward_path(ForwardPath path, const spconv::ForwardArgs& a
   return SPCONV_OK;
 }
 
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Block layout of a strided or transposed map: the lists (cap entries), tile
+// offsets, masks and slot table over `tiles` output tiles, then the output
+// and input coordinates.
+struct GeneralLayout {
+  size_t list_b, tile_off_b, mask_b, rows_b, out_c_b, in_c_b;
+};
+GeneralLayout general_layout(int64_t tiles, int32_t KV, int64_t cap, int64_t n_out, int64_t n_in, size_t* total) {
+  GeneralLayout l;
+  const size_t t = static_cast<size_t>(KV) * tiles;
+  l.list_b = align256(static_cast<size_t>(cap) * sizeof(int32_t));
+  l.tile_off_b = align256((t + 1) * sizeof(int32_t));
+  l.mask_b = align256(std::max<size_t>(t, 1) * sizeof(unsigned long long));
+  l.rows_b = align256(std::max<size_t>(static_cast<size_t>(tiles), 1) * spconv::kTileSlots * sizeof(int32_t));
+  l.out_c_b = align256(std::max<size_t>(static_cast<size_t>(n_out), 1) * 4 * sizeof(int32_t));
+  l.in_c_b = align256(std::max<size_t>(static_cast<size_t>(n_in), 1) * 4 * sizeof(int32_t));
+  *total = 2 * l.list_b + l.tile_off_b + l.mask_b + l.rows_b + l.out_c_b + l.in_c_b;
+  return l;
+}
+void carve_general(const GeneralLayout& l, spconv_map* m) {
+  char* c = static_cast<char*>(m->block);
+  m->buf.in_idx = reinterpret_cast<int32_t*>(c);
+  c += l.list_b;
+  m->buf.out_idx = reinterpret_cast<int32_t*>(c);
+  c += l.list_b;
+  m->buf.tile_off = reinterpret_cast<int32_t*>(c);
+  c += l.tile_off_b;
+  m->buf.tile_mask = reinterpret_cast<unsigned long long*>(c);
+  c += l.mask_b;
+  m->buf.tile_rows = reinterpret_cast<int32_t*>(c);
+  c += l.rows_b;
+  m->buf.perm = nullptr;
+  m->out_coords = reinterpret_cast<int32_t*>(c);
+  c += l.out_c_b;
+  m->in_coords = reinterpret_cast<int32_t*>(c);
+}
+
+// A map with no entries: complete at once (no summary to wait for).
+void mark_empty(spconv_map* m) {
+  if (m->slot != nullptr) {
+    release_slot(m->device, m->slot);
+    m->slot = nullptr;
+  }
+  m->counts.assign(static_cast<size_t>(m->KV), 0);
+  m->offsets.assign(static_cast<size_t>(m->KV) + 1, 0);
+  m->total = 0;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t spconv_abi_version(void) { return 2; }
+int32_t spconv_abi_version(void) { return 3; }
 
 const char* spconv_status_string(spconv_status s) {
   switch (s) {
@@ -476,6 +546,8 @@ spconv_status spconv_build_map_async(const int32_t* d_coords, int64_t n, int32_t
   m->K = kernel_size;
   m->KV = KV;
   m->n = n;
+  m->n_in = n;
+  m->centre = (KV - 1) / 2;
   m->tiles = p.tiles;
   *out_map = m;
   return SPCONV_OK;
@@ -538,6 +610,7 @@ spconv_status spconv_forward(const void* d_feats, const void* d_weights, const s
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   st = order_after_build(map, stream);
   if (st != SPCONV_OK) return st;
+  if (known_empty(map)) return zero_output(d_out, map->n, c_out, dtype, stream);
   const ForwardPath path = forward_path(a);
   const size_t ws_bytes = forward_workspace_bytes(path, a);
   if (ws_bytes == 0) return launch_forward_path(path, a, nullptr, stream);
@@ -580,6 +653,7 @@ spconv_status spconv_forward_noalloc(const void* d_feats, const void* d_weights,
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   st = order_after_build(map, stream);
   if (st != SPCONV_OK) return st;
+  if (known_empty(map)) return zero_output(d_out, map->n, c_out, dtype, stream);
   return launch_forward_path(path, a, ws, stream);
 }
 
@@ -587,6 +661,11 @@ spconv_status spconv_backward_data(const void* d_grad_out, const void* d_weights
                                    int32_t c_in, int32_t c_out, spconv_dtype dtype, void* d_grad_in,
                                    void* hip_stream) {
   g_last_error.clear();
+  if (map != nullptr && map->kind != SPCONV_MAP_SUBMANIFOLD) {
+    return fail(SPCONV_ERR_UNSUPPORTED,
+                "the data gradient of a strided or transposed map is the forward over its transpose "
+                "(spconv_map_transpose) with the weights W[k]^T");
+  }
   // The data gradient is the forward of grad_out over the same map with the
   // mirrored, transposed weights: C_out channels in, C_in out.
   spconv::ForwardArgs a;
@@ -617,7 +696,7 @@ spconv_status spconv_backward_weights(const void* d_feats, const void* d_grad_ou
                                       void* hip_stream) {
   g_last_error.clear();
   if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
-  if (d_feats == nullptr || d_grad_out == nullptr || d_grad_w == nullptr) {
+  if ((d_feats == nullptr && map->n_in > 0) || (d_grad_out == nullptr && map->n > 0) || d_grad_w == nullptr) {
     return fail(SPCONV_ERR_INVALID_ARG, "NULL feature, gradient or weight-gradient pointer");
   }
   if (!aligned16(d_feats) || !aligned16(d_grad_out) || !aligned16(d_grad_w)) {
@@ -641,7 +720,7 @@ spconv_status spconv_backward_weights(const void* d_feats, const void* d_grad_ou
       const uint64_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
       return a0 < b0 + nq && b0 < a0 + np;
     };
-    if (overlap(d_grad_w, gw_b, d_feats, static_cast<uint64_t>(map->n) * c_in * es) ||
+    if (overlap(d_grad_w, gw_b, d_feats, static_cast<uint64_t>(map->n_in) * c_in * es) ||
         overlap(d_grad_w, gw_b, d_grad_out, static_cast<uint64_t>(map->n) * c_out * es)) {
       return fail(SPCONV_ERR_INVALID_ARG, "d_grad_w overlaps the features or the output gradient");
     }
@@ -654,6 +733,7 @@ spconv_status spconv_backward_weights(const void* d_feats, const void* d_grad_ou
   a.out_idx = map->buf.out_idx;
   a.tile_off = map->buf.tile_off;
   a.n = map->n;
+  a.n_in = map->n_in;
   a.tiles = map->tiles;
   a.KV = map->KV;
   a.cin = c_in;
@@ -662,6 +742,11 @@ spconv_status spconv_backward_weights(const void* d_feats, const void* d_grad_ou
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   spconv_status st = order_after_build(map, stream);
   if (st != SPCONV_OK) return st;
+  if (known_empty(map)) {
+    SPCONV_HIP(hipMemsetAsync(d_grad_w, 0, static_cast<size_t>(map->KV) * c_in * c_out * sizeof(float), stream),
+               "hipMemsetAsync");
+    return SPCONV_OK;
+  }
   hipMemPool_t pool = nullptr;
   st = pool_for(map->device, &pool);
   if (st != SPCONV_OK) return st;
@@ -672,6 +757,275 @@ spconv_status spconv_backward_weights(const void* d_feats, const void* d_grad_ou
   if (st != SPCONV_OK) return st;
   const hipError_t e = spconv::launch_wgrad(a, c->fwd, stream);
   if (e != hipSuccess) return hip_fail(e, "weight-gradient launch");
+  return SPCONV_OK;
+}
+
+spconv_status spconv_build_map_strided(const int32_t* d_coords, int64_t n_in, int32_t kernel_size, int32_t stride,
+                                       void* hip_stream, spconv_map** out_map) {
+  g_last_error.clear();
+  if (out_map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "out_map is NULL");
+  *out_map = nullptr;
+  if (d_coords == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "d_coords is NULL");
+  if (!aligned16(d_coords)) return fail(SPCONV_ERR_INVALID_ARG, "d_coords is not 16-byte aligned");
+  if (n_in <= 0) return fail(SPCONV_ERR_INVALID_ARG, "n_in = %lld must be positive", (long long)n_in);
+  if (kernel_size < 1 || kernel_size > 5) {
+    return fail(SPCONV_ERR_UNSUPPORTED, "kernel_size = %d not in [1, 5] for a strided map", kernel_size);
+  }
+  if (stride < 1 || stride > 16) return fail(SPCONV_ERR_UNSUPPORTED, "stride = %d not in [1, 16]", stride);
+  const spconv::OutCoordPlan op = spconv::out_coord_plan(n_in, kernel_size, stride);
+  if (op.m >= (int64_t(1) << 31)) {
+    return fail(SPCONV_ERR_INVALID_ARG, "n_in x ceil(K / stride)^3 = %lld must stay below 2^31", (long long)op.m);
+  }
+  const int32_t KV = kernel_size * kernel_size * kernel_size;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  int device = 0;
+  SPCONV_HIP(hipGetDevice(&device), "hipGetDevice");
+  hipMemPool_t pool = nullptr;
+  spconv_status st = pool_for(device, &pool);
+  if (st != SPCONV_OK) return st;
+  spconv_map* m = new (std::nothrow) spconv_map;
+  if (m == nullptr) return fail(SPCONV_ERR_OUT_OF_MEMORY, "host allocation");
+  m->device = device;
+  m->stream = stream;
+  m->K = kernel_size;
+  m->KV = KV;
+  m->n_in = n_in;
+  m->centre = -1;
+  m->stride = stride;
+  m->kind = SPCONV_MAP_STRIDED;
+  st = acquire_slot(device, &m->slot);
+  if (st != SPCONV_OK) {
+    delete m;
+    return st;
+  }
+  // Phase 1: the input table, the outputs' keys sorted and counted; the host
+  // reads the flags and the number of outputs (the map's size depends on it).
+  const int64_t slots = spconv::table_slots_for(n_in);
+  const size_t table_b = align256(static_cast<size_t>(slots) * sizeof(ulonglong2));
+  const size_t occ_b = align256(static_cast<size_t>(slots / 4) * sizeof(uint4));
+  const size_t sum_b = align256(static_cast<size_t>(spconv::kSummaryHead + KV) * sizeof(long long));
+  const size_t a_bytes = table_b + occ_b + sum_b + spconv::out_coord_scratch_bytes(op);
+  void* a_buf = nullptr;
+  void* b_buf = nullptr;
+  auto discard = [&](spconv_status s2) {
+    if (m->block != nullptr) (void)hipFreeAsync(m->block, stream);
+    if (a_buf != nullptr) (void)hipFreeAsync(a_buf, stream);
+    if (b_buf != nullptr) (void)hipFreeAsync(b_buf, stream);
+    if (m->slot != nullptr) release_slot(device, m->slot);
+    delete m;
+    return s2;
+  };
+  hipError_t e = hipMallocFromPoolAsync(&a_buf, a_bytes, pool, stream);
+  if (e != hipSuccess) return discard(hip_fail(e, "strided map workspace allocation"));
+  char* ac = static_cast<char*>(a_buf);
+  ulonglong2* table = reinterpret_cast<ulonglong2*>(ac);
+  uint4* occ = reinterpret_cast<uint4*>(ac + table_b);
+  long long* summary = reinterpret_cast<long long*>(ac + table_b + occ_b);
+  void* sort_scratch = ac + table_b + occ_b + sum_b;
+  e = spconv::launch_table_build(d_coords, n_in, table, slots, occ, summary, spconv::kSummaryHead + KV, stream);
+  if (e == hipSuccess) e = spconv::launch_out_coords_count(op, d_coords, sort_scratch, summary + 1, stream);
+  if (e == hipSuccess) {
+    e = hipMemcpyAsync(m->slot->host, summary, 2 * sizeof(long long), hipMemcpyDeviceToHost, stream);
+  }
+  if (e == hipSuccess) e = hipEventRecord(m->slot->done, stream);
+  if (e == hipSuccess) e = hipEventSynchronize(m->slot->done);
+  if (e != hipSuccess) return discard(hip_fail(e, "strided map build"));
+  const unsigned long long flags = static_cast<unsigned long long>(m->slot->host[0]);
+  if (flags & spconv::kFlagRange) {
+    return discard(fail(SPCONV_ERR_COORD_RANGE, "a coordinate is outside b in [0, 2^15), z, y, x in [0, 2^16)"));
+  }
+  if (flags & spconv::kFlagDuplicate) {
+    return discard(fail(SPCONV_ERR_DUPLICATE_COORD, "two rows share one (b, z, y, x) coordinate"));
+  }
+  if (flags & spconv::kFlagTableFull) return discard(fail(SPCONV_ERR_DEVICE, "internal: hash table probe exceeded its bound"));
+  const int64_t n_out = m->slot->host[1];
+  if (n_out * KV >= (int64_t(1) << 31)) {
+    return discard(fail(SPCONV_ERR_INVALID_ARG, "n_out x K^3 = %lld x %d must stay below 2^31", (long long)n_out, KV));
+  }
+  // Phase 2: the map over the n_out outputs.
+  const int64_t cap = std::max<int64_t>(64, std::min<int64_t>(static_cast<int64_t>(KV) * n_out, op.m));
+  m->n = n_out;
+  m->tiles = (n_out + spconv::kTileRows - 1) / spconv::kTileRows;
+  size_t block_bytes = 0;
+  const GeneralLayout lay = general_layout(m->tiles, KV, cap, n_out, n_in, &block_bytes);
+  e = hipMallocFromPoolAsync(&m->block, block_bytes, pool, stream);
+  if (e != hipSuccess) return discard(hip_fail(e, "map allocation"));
+  m->block_bytes = block_bytes;
+  carve_general(lay, m);
+  if (n_out > 0) {
+    e = hipMallocFromPoolAsync(&b_buf, spconv::general_scratch_bytes(n_out, kernel_size), pool, stream);
+    if (e != hipSuccess) return discard(hip_fail(e, "strided map workspace allocation"));
+  }
+  e = spconv::launch_out_coords_write(op, sort_scratch, m->out_coords, stream);
+  if (e == hipSuccess) {
+    e = hipMemcpyAsync(m->in_coords, d_coords, static_cast<size_t>(n_in) * 4 * sizeof(int32_t),
+                       hipMemcpyDeviceToDevice, stream);
+  }
+  if (e == hipSuccess && n_out > 0) {
+    spconv::GeneralMapArgs g;
+    g.qcoords = m->out_coords;
+    g.nq = n_out;
+    g.table = table;
+    g.table_slots = slots;
+    g.K = kernel_size;
+    g.lo = -((kernel_size - 1) / 2);
+    g.stride = stride;
+    g.mode = 0;
+    spconv::carve_general_scratch(n_out, kernel_size, b_buf, &g);
+    g.summary = summary;
+    g.host_summary = m->slot->device;
+    g.map = m->buf;
+    e = spconv::launch_general_map(g, stream);
+  }
+  if (e != hipSuccess) return discard(hip_fail(e, "strided map launch"));
+  if (n_out == 0) {
+    mark_empty(m);
+  } else {
+    e = hipEventRecord(m->slot->done, stream);
+    if (e != hipSuccess) return discard(hip_fail(e, "hipEventRecord"));
+  }
+  (void)hipFreeAsync(a_buf, stream);
+  if (b_buf != nullptr) (void)hipFreeAsync(b_buf, stream);
+  a_buf = b_buf = nullptr;
+  st = finish_build(m);
+  if (st != SPCONV_OK) {
+    spconv_map_free(m);
+    return st;
+  }
+  *out_map = m;
+  return SPCONV_OK;
+}
+
+spconv_status spconv_map_transpose(spconv_map* map, void* hip_stream, spconv_map** out_map) {
+  g_last_error.clear();
+  if (out_map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "out_map is NULL");
+  *out_map = nullptr;
+  if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
+  if (map->kind != SPCONV_MAP_STRIDED) {
+    return fail(SPCONV_ERR_UNSUPPORTED, "only a strided map has a transpose here (a submanifold map is its own, "
+                                        "with mirrored weights)");
+  }
+  spconv_status st = finish_build(map);
+  if (st != SPCONV_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  int device = 0;
+  SPCONV_HIP(hipGetDevice(&device), "hipGetDevice");
+  if (device != map->device) {
+    return fail(SPCONV_ERR_INVALID_ARG, "the current device (%d) is not the map's (%d)", device, map->device);
+  }
+  st = order_after_build(map, stream);
+  if (st != SPCONV_OK) return st;
+  hipMemPool_t pool = nullptr;
+  st = pool_for(device, &pool);
+  if (st != SPCONV_OK) return st;
+  spconv_map* t = new (std::nothrow) spconv_map;
+  if (t == nullptr) return fail(SPCONV_ERR_OUT_OF_MEMORY, "host allocation");
+  t->device = device;
+  t->stream = stream;
+  t->K = map->K;
+  t->KV = map->KV;
+  t->n = map->n_in;
+  t->n_in = map->n;
+  t->centre = -1;
+  t->stride = map->stride;
+  t->kind = SPCONV_MAP_TRANSPOSED;
+  t->tiles = (t->n + spconv::kTileRows - 1) / spconv::kTileRows;
+  void* a_buf = nullptr;
+  auto discard = [&](spconv_status s2) {
+    if (t->block != nullptr) (void)hipFreeAsync(t->block, stream);
+    if (a_buf != nullptr) (void)hipFreeAsync(a_buf, stream);
+    if (t->slot != nullptr) release_slot(device, t->slot);
+    delete t;
+    return s2;
+  };
+  st = acquire_slot(device, &t->slot);
+  if (st != SPCONV_OK) {
+    delete t;
+    return st;
+  }
+  const int64_t cap = std::max<int64_t>(64, map->total);
+  size_t block_bytes = 0;
+  const GeneralLayout lay = general_layout(t->tiles, t->KV, cap, t->n, t->n_in, &block_bytes);
+  hipError_t e = hipMallocFromPoolAsync(&t->block, block_bytes, pool, stream);
+  if (e != hipSuccess) return discard(hip_fail(e, "map allocation"));
+  t->block_bytes = block_bytes;
+  carve_general(lay, t);
+  e = hipMemcpyAsync(t->out_coords, map->in_coords, static_cast<size_t>(t->n) * 4 * sizeof(int32_t),
+                     hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess && t->n_in > 0) {
+    e = hipMemcpyAsync(t->in_coords, map->out_coords, static_cast<size_t>(t->n_in) * 4 * sizeof(int32_t),
+                       hipMemcpyDeviceToDevice, stream);
+  }
+  if (e != hipSuccess) return discard(hip_fail(e, "hipMemcpyAsync"));
+  if (map->total == 0) {
+    mark_empty(t);
+    *out_map = t;
+    return SPCONV_OK;
+  }
+  // The strided map's outputs in a table; each of its inputs probes the
+  // outputs q' with stride x q' + d = p.
+  const int64_t slots = spconv::table_slots_for(t->n_in);
+  const size_t table_b = align256(static_cast<size_t>(slots) * sizeof(ulonglong2));
+  const size_t occ_b = align256(static_cast<size_t>(slots / 4) * sizeof(uint4));
+  const size_t sum_b = align256(static_cast<size_t>(spconv::kSummaryHead + t->KV) * sizeof(long long));
+  e = hipMallocFromPoolAsync(&a_buf, table_b + occ_b + sum_b + spconv::general_scratch_bytes(t->n, t->K), pool,
+                             stream);
+  if (e != hipSuccess) return discard(hip_fail(e, "transpose workspace allocation"));
+  char* ac = static_cast<char*>(a_buf);
+  ulonglong2* table = reinterpret_cast<ulonglong2*>(ac);
+  uint4* occ = reinterpret_cast<uint4*>(ac + table_b);
+  long long* summary = reinterpret_cast<long long*>(ac + table_b + occ_b);
+  e = spconv::launch_table_build(map->out_coords, t->n_in, table, slots, occ, summary, spconv::kSummaryHead + t->KV,
+                                 stream);
+  if (e == hipSuccess) {
+    spconv::GeneralMapArgs g;
+    g.qcoords = t->out_coords;
+    g.nq = t->n;
+    g.table = table;
+    g.table_slots = slots;
+    g.K = t->K;
+    g.lo = -((t->K - 1) / 2);
+    g.stride = t->stride;
+    g.mode = 1;
+    spconv::carve_general_scratch(t->n, t->K, ac + table_b + occ_b + sum_b, &g);
+    g.summary = summary;
+    g.host_summary = t->slot->device;
+    g.map = t->buf;
+    e = spconv::launch_general_map(g, stream);
+  }
+  if (e == hipSuccess) e = hipEventRecord(t->slot->done, stream);
+  if (e != hipSuccess) return discard(hip_fail(e, "transpose launch"));
+  (void)hipFreeAsync(a_buf, stream);
+  a_buf = nullptr;
+  st = finish_build(t);
+  if (st == SPCONV_OK && t->total != map->total) {
+    st = fail(SPCONV_ERR_DEVICE, "internal: the transpose holds %lld entries, the map %lld", (long long)t->total,
+              (long long)map->total);
+  }
+  if (st != SPCONV_OK) {
+    spconv_map_free(t);
+    return st;
+  }
+  *out_map = t;
+  return SPCONV_OK;
+}
+
+spconv_status spconv_map_geometry(const spconv_map* map, int64_t* n_in, int64_t* n_out, int32_t* stride,
+                                  int32_t* kind) {
+  if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
+  if (n_in) *n_in = map->n_in;
+  if (n_out) *n_out = map->n;
+  if (stride) *stride = map->stride;
+  if (kind) *kind = map->kind;
+  return SPCONV_OK;
+}
+
+spconv_status spconv_map_out_coords(const spconv_map* map, const int32_t** d_out_coords) {
+  if (map == nullptr || d_out_coords == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "NULL argument");
+  if (map->kind == SPCONV_MAP_SUBMANIFOLD) {
+    return fail(SPCONV_ERR_UNSUPPORTED, "a submanifold map's outputs are its inputs (the caller's coordinates)");
+  }
+  *d_out_coords = map->out_coords;
   return SPCONV_OK;
 }
 

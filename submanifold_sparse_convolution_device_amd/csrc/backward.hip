@@ -173,8 +173,8 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t* __restrict__ feat
                                                const int32_t* __restrict__ in_idx,
                                                const int32_t* __restrict__ out_idx,
                                                const int32_t* __restrict__ tile_off, int64_t tiles, int tpc,
-                                               int chunks, int groups, int KV, int cout, int n_rows,
-                                               float* __restrict__ part) {
+                                               int chunks, int groups, int KV, int cout, int f_rows,
+                                               int g_rows, float* __restrict__ part) {
   using S = WgradShape<CIN, COLS>;
   constexpr int NLW = S::NLW, CBW = S::CBW, OBW = S::OBW, SEGF = S::SEGF, SEGG = S::SEGG;
   extern __shared__ uint4 wstage[];  // [STAGES][F rows | G rows]
@@ -207,6 +207,7 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t* __restrict__ feat
   uint32_t c_off[NLW], c_ix[NLW];
   const char* c_base[NLW];
   int64_t c_pitch[NLW];
+  int32_t c_last[NLW];  // last row of the copy's source array
   uint32_t c_lds[NLW];
 #pragma unroll
   for (int ii = 0; ii < NLW; ++ii) {
@@ -222,6 +223,7 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t* __restrict__ feat
     c_ix[ii] = static_cast<uint32_t>((t / S::IPW) * S::IDX_WAVE + 4 * (t % S::IPW));
     c_base[ii] = isf ? reinterpret_cast<const char*>(feats) : reinterpret_cast<const char*>(gout + col0);
     c_pitch[ii] = isf ? 2 * CIN : 2 * static_cast<int64_t>(cout);
+    c_last[ii] = isf ? f_rows - 1 : g_rows - 1;
     c_lds[ii] = static_cast<uint32_t>((isf ? 0 : S::F_BYTES) + jj * 1024);
   }
   const uint64_t zero = reinterpret_cast<uint64_t>(kWgradZero);
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t* __restrict__ feat
       const int e = e0 + r * S::ROWS + c_row[ii];
       const uint64_t keep = e < e1 ? ~0ull : 0ull;
       const int32_t row = rows[ii];
-      const int32_t rc = row < 0 ? 0 : (row > n_rows - 1 ? n_rows - 1 : row);
+      const int32_t rc = row < 0 ? 0 : (row > c_last[ii] ? c_last[ii] : row);
       const uint64_t row_addr =
           reinterpret_cast<uint64_t>(c_base[ii]) + static_cast<uint64_t>(static_cast<int64_t>(rc) * c_pitch[ii]);
       const uint64_t addr = ((row_addr & keep) | (zero & ~keep)) + c_off[ii];
@@ -543,7 +545,7 @@ hipError_t launch_wgrad_mfma(const WgradArgs& a, const WgradPlan& pl, float* par
   hipLaunchKernelGGL((k_wgrad<T, CIN, COLS>), dim3(static_cast<unsigned>(grid)), dim3(256), S::lds_bytes(), stream,
                      static_cast<const uint16_t*>(a.feats), static_cast<const uint16_t*>(a.grad_out), a.in_idx,
                      a.out_idx, a.tile_off, a.tiles, pl.tpc, pl.chunks, pl.groups, a.KV, a.cout,
-                     static_cast<int>(a.n), part);
+                     static_cast<int>(a.n_in), static_cast<int>(a.n), part);
   return hipGetLastError();
 }
 

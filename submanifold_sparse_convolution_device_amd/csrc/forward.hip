@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void k_forward(
     const T* __restrict__ feats, const T* __restrict__ weights, T* __restrict__ out,
     const int32_t* __restrict__ in_idx, const unsigned long long* __restrict__ tile_mask,
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ perm, int64_t n, int64_t tiles, int KV,
-    int cin, int cout) {
+    int cin, int cout, int centre) {
   constexpr int NCB = CB / 16;
   constexpr int VEC = Elem<T>::kVec;
   constexpr int CHUNK = Elem<T>::kChunk;
@@ -167,7 +167,8 @@ __global__ __launch_bounds__(kThreads) void k_forward(
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int centre = (KV - 1) / 2;
+  // centre: the offset whose list is the identity (read by position), or -1
+  // for maps without one (strided and transposed maps).
   const int row_in_tile = wave * 16 + r;
   const int64_t q = q0 + row_in_tile;  // position in the map's row order
   const int32_t qrow = q < n ? (perm != nullptr ? perm[q] : static_cast<int32_t>(q)) : -1;  // its row
@@ -906,6 +907,9 @@ hipError_t launch_small(const ForwardArgs& a, hipStream_t stream) {
 template <typename T>
 hipError_t try_small(const ForwardArgs& a, hipStream_t stream) {
   if (a.KV > 32) return hipErrorNotSupported;  // one 32-bit word of offsets
+  // The centre runs as a dense GEMM on the tile's own rows: maps without an
+  // identity offset (strided, transposed) take the generic kernel.
+  if (a.centre != (a.KV - 1) / 2) return hipErrorNotSupported;
   constexpr size_t kBudget = kSmallLdsCap;
   if constexpr (sizeof(T) == 2) {
     if (a.cin == 32 && a.cout == 32 && SmallShape<T, 32, 32>::lds_bytes(a.KV, kSmallWaves) <= kBudget) return launch_small<T, 32, 32>(a, stream);
@@ -925,7 +929,7 @@ hipError_t launch_typed(const ForwardArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((k_forward<T, CB>), grid, dim3(kThreads), lds, stream,
                      static_cast<const T*>(a.feats), static_cast<const T*>(a.weights),
                      static_cast<T*>(a.out), a.in_idx, a.tile_mask, a.tile_off, a.perm, a.n, a.tiles, a.KV,
-                     a.cin, a.cout);
+                     a.cin, a.cout, a.centre);
   return hipGetLastError();
 }
 
@@ -950,7 +954,7 @@ hipError_t dispatch(const ForwardArgs& a, hipStream_t stream) {
 }
 
 bool small_supported(const ForwardArgs& a) {
-  if (a.KV > 32) return false;
+  if (a.KV > 32 || a.centre != (a.KV - 1) / 2) return false;  // the centre runs as a dense GEMM on the tile's rows
   if (a.dtype == 0) {
     return a.cin == 16 && (a.cout == 16 || a.cout == 32);
   }

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(512) void k_forward_tiled(
     const T* __restrict__ feats, const uint4* __restrict__ wop, T* __restrict__ out,
     const int32_t* __restrict__ in_idx, const int32_t* __restrict__ tile_off,
     const unsigned long long* __restrict__ tile_mask, const int32_t* __restrict__ perm, int64_t n, int64_t tiles,
-    int KV, int cout) {
+    int KV, int cout, int centre) {
   using Sh = TiledShape<CIN, CB, QB>;
   constexpr int NCH = Sh::NCH, NCB = Sh::NCB, WSLICE = Sh::WSLICE;
   constexpr int UNITS_PER_TILE = 4 / QB;  // waves per 64-row tile
@@ -134,7 +134,6 @@ __global__ __launch_bounds__(512) void k_forward_tiled(
   const bool active = (t < tiles) && (q_first < n);
   const int cbg0 = blockIdx.y * NCB;  // first 16-column block
   const int ncbg = cout / 16;
-  const int centre = (KV - 1) / 2;
 
   // Offset k's tile mask (all 64 rows of the tile: list ranks count every
   // earlier row) and list start, in lane k (k < 64) or lane k - 64 (k >= 64).
@@ -346,7 +345,7 @@ hipError_t launch_tiled_shape(const ForwardArgs& a, const uint4* wop, int nw, hi
   }
   hipLaunchKernelGGL((k_forward_tiled<T, CIN, CB, QB>), grid, dim3(64 * nw), lds, stream,
                      static_cast<const T*>(a.feats), wop, static_cast<T*>(a.out), a.in_idx, a.tile_off,
-                     a.tile_mask, a.perm, a.n, a.tiles, a.KV, a.cout);
+                     a.tile_mask, a.perm, a.n, a.tiles, a.KV, a.cout, a.centre);
   return hipGetLastError();
 }
 

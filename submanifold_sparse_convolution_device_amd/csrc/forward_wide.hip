@@ -192,7 +192,7 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
     const int32_t* __restrict__ in_idx, const int32_t* __restrict__ tile_off,
     const unsigned long long* __restrict__ tile_mask, const uint4* __restrict__ zero_row,
     const int32_t* __restrict__ perm, int64_t n, int64_t tiles, int64_t tasks, int groups, int splits,
-    float* __restrict__ part, int KV, int cout) {
+    float* __restrict__ part, int KV, int cout, int centre_k) {
   using Sh = WideShape<CIN, TB, NCB, NW>;
   constexpr int NCH = Sh::NCH, BPW = Sh::BPW, TPT = Sh::TPT;
   constexpr int SEG = Sh::SEG, RPI = Sh::RPI, IPB = Sh::IPB, RP = Sh::RP, BLOCK_BYTES = Sh::BLOCK_BYTES;
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
     // The centre offset reads the task's own rows (the row at each position:
     // perm, or the position itself), not its list.
     const int64_t qpos = q0 + 16 * b + r;
-    const bool centre = o.k == KV / 2;  // wave-uniform
+    const bool centre = o.k == centre_k;  // wave-uniform; centre_k = -1: no identity offset
     int32_t v;
     if (centre && perm == nullptr) v = static_cast<int32_t>(qpos);
     else v = centre ? perm[has ? qpos : 0] : in_idx[has ? lo + rank : 0];
@@ -491,7 +491,7 @@ hipError_t launch_wide_shape(const ForwardArgs& a, int splits, const uint4* wop,
   hipLaunchKernelGGL((k_forward_wide<T, CIN, TB, NCB, NW>), dim3(static_cast<unsigned>(grid)), dim3(64 * NW),
                      Sh::lds_bytes(), stream, static_cast<const uint16_t*>(a.feats), wop, static_cast<T*>(a.out),
                      a.in_idx, a.tile_off, a.tile_mask, zero_row, a.perm, a.n, a.tiles, tasks, groups, splits, part,
-                     a.KV, a.cout);
+                     a.KV, a.cout, a.centre);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const int64_t count4 = a.n * a.cout / 4;

@@ -140,6 +140,8 @@ struct ForwardArgs {
   int32_t cin;
   int32_t cout;
   int32_t dtype;
+  int32_t centre;   // offset whose list is the identity (read by position), -1: none (strided maps)
+  int64_t n_in;     // rows of feats (n for a submanifold map)
 };
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream);
 
@@ -173,7 +175,8 @@ struct WgradArgs {
   const int32_t* in_idx;
   const int32_t* out_idx;
   const int32_t* tile_off;  // KV * tiles + 1: list k starts at tile_off[k * tiles]
-  int64_t n;
+  int64_t n;     // output rows (grad_out)
+  int64_t n_in;  // input rows (feats)
   int64_t tiles;
   int32_t KV;
   int32_t cin;
@@ -184,5 +187,52 @@ size_t wgrad_workspace_bytes(const WgradArgs& a);
 hipError_t launch_wgrad(const WgradArgs& a, void* workspace, hipStream_t stream);
 // True when the small-channel kernel (every W_d resident in LDS) serves `a`.
 bool small_supported(const ForwardArgs& a);
+
+// ---- Strided maps and their transposes (map_strided.hip, map_build.hip) ----
+// Output coordinates of a strided map: candidates, sort and unique.  m =
+// n_in x ca^3 candidate keys (ca = ceil(K / stride) choices per axis),
+// sorted in blocks of 4096.
+struct OutCoordPlan {
+  int64_t n_in = 0;
+  int K = 0, lo = 0, stride = 0, ca = 0;
+  int64_t m = 0;
+  int64_t blocks = 0;
+};
+OutCoordPlan out_coord_plan(int64_t n_in, int K, int stride);
+size_t out_coord_scratch_bytes(const OutCoordPlan& p);
+// Candidates, sort and per-block run counts; the number of outputs goes to
+// *n_out (a device word).
+hipError_t launch_out_coords_count(const OutCoordPlan& p, const int32_t* coords, void* scratch, long long* n_out,
+                                   hipStream_t stream);
+// The outputs' coordinates (int32 [n_out][4]) from the same scratch.
+hipError_t launch_out_coords_write(const OutCoordPlan& p, void* scratch, int32_t* out_coords, hipStream_t stream);
+
+// Coordinate table of n rows (table_slots_for(n) slots, a quarter as many
+// occupancy buckets); clears summary[0 .. summary_len) and raises the
+// duplicate and range flags in summary[0].
+int64_t table_slots_for(int64_t n);
+hipError_t launch_table_build(const int32_t* coords, int64_t n, ulonglong2* table, int64_t table_slots, uint4* occ,
+                              long long* summary, int summary_len, hipStream_t stream);
+// A map without an identity offset over nq output rows (query coordinates
+// qcoords): every offset probed in the other side's table (mode 0: the input
+// at stride x q + d; mode 1: the strided output q' with stride x q' + d = p),
+// then tile masks and lists as for a submanifold map (centre -1).
+struct GeneralMapArgs {
+  const int32_t* qcoords = nullptr;
+  int64_t nq = 0;
+  const ulonglong2* table = nullptr;
+  int64_t table_slots = 0;
+  int K = 0, lo = 0, stride = 1, mode = 0;
+  uint32_t* flags = nullptr;   // nq x 4 words
+  int32_t* nbr = nullptr;      // K^3 x nq
+  int64_t* chunk_sum = nullptr;
+  int32_t* tile_base = nullptr;
+  long long* summary = nullptr;       // per-offset totals at kSummaryHead + k (zero on entry)
+  long long* host_summary = nullptr;  // the summary is copied here when the lists are done
+  MapBuffers map;
+};
+size_t general_scratch_bytes(int64_t nq, int K);
+void carve_general_scratch(int64_t nq, int K, void* base, GeneralMapArgs* g);
+hipError_t launch_general_map(const GeneralMapArgs& g, hipStream_t stream);
 
 }  // namespace spconv

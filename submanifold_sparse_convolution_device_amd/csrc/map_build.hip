@@ -1038,6 +1038,146 @@ int grid_for(int64_t work, int per_block, int cap) {
   return static_cast<int>(g);
 }
 
+// ---- Strided maps and their transposes ------------------------------------
+// One lane per row of the map's output side (query q, coordinates qc[q]); for
+// every offset k of the K^3 kernel (components lo .. lo + K - 1) the row of
+// the other side that pairs with it, looked up in that side's table:
+//   mode 0 (strided map; "Sparse inputs and sparse convolution", section "The
+//          map is the computation": look up s q + d): the input at s q + d;
+//   mode 1 (its transpose): the strided output q' with s q' + d = p, p the
+//          query's coordinates, when (p - d) / s is integral and >= 0.
+// nbr[k][q] = that row or -1, and bit k of the query's flag words is set on a
+// hit.  All offsets are probed (no mirror symmetry halves them here).  A
+// batch of kAllBatch lookups issues its preferred-slot loads together.
+constexpr int kAllBatch = 8;
+constexpr int kAllFlagWords = 4;  // K <= 5: K^3 <= 125 offsets
+__global__ __launch_bounds__(256) void k_probe_all(const int4* __restrict__ qc, int64_t nq,
+                                                   const ulonglong2* __restrict__ table,
+                                                   unsigned long long window_mask, int K, int lo, int s, int mode,
+                                                   int32_t* __restrict__ nbr, uint32_t* __restrict__ flags,
+                                                   long long* summary) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (q >= nq) return;
+  const int4 c = qc[q];
+  const int KV = K * K * K;
+  uint32_t fw[kAllFlagWords] = {0u, 0u, 0u, 0u};
+  bool overflow = false;
+  for (int k0 = 0; k0 < KV; k0 += kAllBatch) {
+    unsigned long long key[kAllBatch];
+    bool ok[kAllBatch];
+    ulonglong2 e[kAllBatch];
+#pragma unroll
+    for (int j = 0; j < kAllBatch; ++j) {
+      const int k = k0 + j;
+      const int d[3] = {k / (K * K) + lo, (k / K) % K + lo, k % K + lo};
+      const int p[3] = {c.y, c.z, c.w};
+      int t[3];
+      bool good = k < KV;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        if (mode == 0) {
+          t[i] = s * p[i] + d[i];
+          good = good && t[i] >= 0 && t[i] < 65536;
+        } else {
+          const int v = p[i] - d[i];
+          t[i] = v >= 0 ? v / s : -1;
+          good = good && v >= 0 && v % s == 0;
+        }
+      }
+      ok[j] = good;
+      key[j] = good ? pack_key(c.x, t[0], t[1], t[2]) : kEmptyKey;
+    }
+#pragma unroll
+    for (int j = 0; j < kAllBatch; ++j) {
+      e[j] = make_ulonglong2(kEmptyKey, 0ull);
+      if (ok[j]) e[j] = table[preferred_slot(key[j], window_mask)];
+    }
+#pragma unroll
+    for (int j = 0; j < kAllBatch; ++j) {
+      const int k = k0 + j;
+      if (k >= KV) break;
+      int64_t row = -1;
+      if (ok[j]) {
+        if (e[j].x == key[j]) {
+          row = static_cast<int64_t>(static_cast<uint32_t>(e[j].y));
+        } else if (e[j].x != kEmptyKey && ((e[j].y >> 32) & kSlotDisplaced) != 0ull) {
+          row = find_row_scan(key[j], table, window_mask, overflow);
+        }
+      }
+      nbr[static_cast<int64_t>(k) * nq + q] = static_cast<int32_t>(row);
+      if (row >= 0) fw[k >> 5] |= 1u << (k & 31);
+    }
+  }
+#pragma unroll
+  for (int w = 0; w < kAllFlagWords; ++w) flags[q * kAllFlagWords + w] = fw[w];
+  if (overflow) raise_flag(summary, kFlagTableFull);
+}
+
+// Tile masks of a map without an identity offset: as k_count (one tile of 64
+// output rows per wave, one group of kGroupTiles tiles per workgroup), from
+// the probe's flag words; every offset's entries count in the slot bases.
+template <int NS>
+__global__ __launch_bounds__(1024) void k_count_all(const uint32_t* __restrict__ flags, int KV, int64_t n,
+                                                    int64_t tiles, int64_t group_tiles, int64_t chunks,
+                                                    unsigned long long* __restrict__ tile_mask,
+                                                    int32_t* __restrict__ tile_base,
+                                                    int64_t* __restrict__ chunk_sum, long long* summary) {
+  const int64_t chunk = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int cnt[NS];
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) cnt[sl] = 0;
+  for (int64_t g = 0; g < group_tiles; g += kGroupTiles) {
+    const int64_t t = chunk * group_tiles + g + wave;
+    if (t >= tiles) break;
+    const int64_t q = t * kTileRows + lane;
+    const bool valid = q < n;
+    uint32_t fw[kAllFlagWords];
+#pragma unroll
+    for (int w = 0; w < kAllFlagWords; ++w) fw[w] = valid ? flags[q * kAllFlagWords + w] : 0u;
+    unsigned long long mine[NS];
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+      mine[sl] = 0ull;
+#pragma unroll
+      for (int jj = 0; jj < 64; ++jj) {
+        const int k = sl * 64 + jj;
+        if (k < KV) {
+          const unsigned long long bal = __ballot(((fw[k >> 5] >> (k & 31)) & 1u) != 0u);
+          if (lane == jj) mine[sl] = bal;
+        }
+      }
+    }
+    int before = 0;
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+      const int k = sl * 64 + lane;
+      const int cc = k < KV ? static_cast<int>(__popcll(mine[sl])) : 0;
+      const int excl = wave_prefix_small<7>(cc);
+      if (k < KV) {
+        tile_mask[static_cast<int64_t>(k) * tiles + t] = mine[sl];
+        tile_base[static_cast<int64_t>(k) * tiles + t] = before + excl;
+      }
+      before += __builtin_amdgcn_readlane(excl + cc, 63);
+      cnt[sl] += cc;
+    }
+  }
+  __shared__ int part[kGroupTiles][NS * 64];
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) part[wave][sl * 64 + lane] = cnt[sl];
+  __syncthreads();
+  for (int k = threadIdx.x; k < KV; k += 1024) {
+    int sum = 0;
+#pragma unroll
+    for (int w = 0; w < kGroupTiles; ++w) sum += part[w][k];
+    chunk_sum[static_cast<int64_t>(k) * chunks + chunk] = sum;
+    if (sum != 0) {
+      atomicAdd(reinterpret_cast<unsigned long long*>(&summary[kSummaryHead + k]),
+                static_cast<unsigned long long>(sum));
+    }
+  }
+}
+
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // The negative-half flag records are cleared (in 16-byte units); the probe
@@ -1199,6 +1339,81 @@ hipError_t launch_build(const BuildPlan& p, const int32_t* coords, const BuildSc
                      p.group_tiles, p.chunks, s.chunk_sum, s.summary, m.in_idx, m.out_idx,
                      m.tile_off, m.tile_rows, host_summary);
   return hipGetLastError();
+}
+
+hipError_t launch_table_build(const int32_t* coords, int64_t n, ulonglong2* table, int64_t table_slots, uint4* occ,
+                              long long* summary, int summary_len, hipStream_t stream) {
+  const int64_t buckets = table_slots / 4;
+  const int64_t units = table_slots + buckets;
+  const int64_t init_blocks = (units + 256 * kInitUnits - 1) / (256 * kInitUnits);
+  hipLaunchKernelGGL(k_init, dim3(static_cast<unsigned>(init_blocks)), dim3(256), 0, stream,
+                     reinterpret_cast<uint4*>(table), table_slots, occ, buckets, static_cast<uint4*>(nullptr),
+                     int64_t(0), summary, summary_len);
+  const unsigned long long window_mask = static_cast<unsigned long long>(table_slots / kWindowSlots) - 1ull;
+  const int4* c4 = reinterpret_cast<const int4*>(coords);
+  const unsigned gx = static_cast<unsigned>((n + 255) / 256);
+  hipLaunchKernelGGL(k_claim, dim3(gx), dim3(256), 0, stream, c4, n, table, reinterpret_cast<uint8_t*>(occ),
+                     window_mask, static_cast<unsigned long long>(buckets - 1));
+  hipLaunchKernelGGL(k_insert, dim3(gx), dim3(256), 0, stream, c4, n, table, window_mask, summary);
+  return hipGetLastError();
+}
+
+int64_t table_slots_for(int64_t n) {
+  int64_t slots = 64;
+  while (slots < kTableSlotsPerVoxel * n) slots <<= 1;
+  return slots;
+}
+
+hipError_t launch_general_map(const GeneralMapArgs& g, hipStream_t stream) {
+  if (g.nq <= 0) return hipSuccess;
+  const unsigned long long window_mask = static_cast<unsigned long long>(g.table_slots / kWindowSlots) - 1ull;
+  hipLaunchKernelGGL(k_probe_all, dim3(static_cast<unsigned>((g.nq + 255) / 256)), dim3(256), 0, stream,
+                     reinterpret_cast<const int4*>(g.qcoords), g.nq, g.table, window_mask, g.K, g.lo, g.stride,
+                     g.mode, g.nbr, g.flags, g.summary);
+  const int64_t tiles = (g.nq + kTileRows - 1) / kTileRows;
+  const int64_t groups = (tiles + kGroupTiles - 1) / kGroupTiles;
+  const int KV = g.K * g.K * g.K;
+  if (KV <= 64) {
+    hipLaunchKernelGGL(k_count_all<1>, dim3(static_cast<unsigned>(groups)), dim3(1024), 0, stream, g.flags, KV,
+                       g.nq, tiles, static_cast<int64_t>(kGroupTiles), groups, g.map.tile_mask, g.tile_base,
+                       g.chunk_sum, g.summary);
+  } else {
+    hipLaunchKernelGGL(k_count_all<2>, dim3(static_cast<unsigned>(groups)), dim3(1024), 0, stream, g.flags, KV,
+                       g.nq, tiles, static_cast<int64_t>(kGroupTiles), groups, g.map.tile_mask, g.tile_base,
+                       g.chunk_sum, g.summary);
+  }
+  // k_compact with chunks of whole groups, at most kMaxChunks of them
+  const int64_t groups_per_chunk = (groups + kMaxChunks - 1) / kMaxChunks;
+  const int64_t group_tiles = groups_per_chunk * kGroupTiles;
+  const int64_t chunks = (tiles + group_tiles - 1) / group_tiles;
+  hipLaunchKernelGGL(k_compact, dim3(static_cast<unsigned>(chunks), static_cast<unsigned>(KV)), dim3(256), 0, stream,
+                     g.map.tile_mask, g.tile_base, g.nbr, g.nq, tiles, -1, KV, group_tiles, chunks, g.chunk_sum,
+                     g.summary, g.map.in_idx, g.map.out_idx, g.map.tile_off, g.map.tile_rows, g.host_summary);
+  return hipGetLastError();
+}
+
+size_t general_scratch_bytes(int64_t nq, int K) {
+  const int64_t KV = static_cast<int64_t>(K) * K * K;
+  const int64_t tiles = (nq + kTileRows - 1) / kTileRows;
+  const int64_t groups = (tiles + kGroupTiles - 1) / kGroupTiles;
+  return align_up(static_cast<size_t>(nq) * kAllFlagWords * sizeof(uint32_t), 256) +
+         align_up(static_cast<size_t>(KV) * nq * sizeof(int32_t), 256) +
+         align_up(static_cast<size_t>(KV) * groups * sizeof(int64_t), 256) +
+         align_up(static_cast<size_t>(KV) * tiles * sizeof(int32_t), 256);
+}
+
+void carve_general_scratch(int64_t nq, int K, void* base, GeneralMapArgs* g) {
+  const int64_t KV = static_cast<int64_t>(K) * K * K;
+  const int64_t tiles = (nq + kTileRows - 1) / kTileRows;
+  const int64_t groups = (tiles + kGroupTiles - 1) / kGroupTiles;
+  char* c = static_cast<char*>(base);
+  g->flags = reinterpret_cast<uint32_t*>(c);
+  c += align_up(static_cast<size_t>(nq) * kAllFlagWords * sizeof(uint32_t), 256);
+  g->nbr = reinterpret_cast<int32_t*>(c);
+  c += align_up(static_cast<size_t>(KV) * nq * sizeof(int32_t), 256);
+  g->chunk_sum = reinterpret_cast<int64_t*>(c);
+  c += align_up(static_cast<size_t>(KV) * groups * sizeof(int64_t), 256);
+  g->tile_base = reinterpret_cast<int32_t*>(c);
 }
 
 }  // namespace spconv

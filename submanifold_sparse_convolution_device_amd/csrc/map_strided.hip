@@ -1,0 +1,322 @@
+// Output coordinates of a strided sparse convolution on gfx950.
+//
+// A strided map ("Sparse inputs and sparse convolution", section "The map is
+// the computation": for each output q and offset d, look up s q + d) has the
+// outputs of the regular output definition (SparseConvNet blog, section 2:
+// an output is computed where the kernel covers at least one active input):
+// the grid points q >= 0 with an input at s q + d for some offset d of the
+// K^3 kernel (components lo .. lo + K - 1, lo = -floor((K - 1) / 2)).  They
+// are produced in lexicographic (b, z, y, x) order, the order a unique-based
+// voxelizer emits:
+//   k_out_candidates  one lane per input p: per axis the kernel components d
+//                     with p - d divisible by s and (p - d) / s in
+//                     [0, 2^16); every combination's packed key
+//                     (b << 48 | z << 32 | y << 16 | x, whose order is the
+//                     lexicographic order), unused slots ~0;
+//   radix sort        stable LSD over the 8 bytes of the keys: per pass a
+//                     digit histogram per block of 4096 keys (k_rs_count), an
+//                     exclusive scan over (digit, block) (k_scan_excl) and a
+//                     stable scatter (k_rs_scatter: ranks within a block by
+//                     ballots, in element order);
+//   unique            a key that differs from its predecessor (and is not ~0)
+//                     starts a run: per-block counts, their exclusive scan
+//                     (the total is the number of outputs) and the unpacked
+//                     coordinates at their ranks.
+#include "internal.h"
+
+namespace spconv {
+namespace {
+
+constexpr int kSortThreads = 1024;
+constexpr int kSortPer = 4;
+constexpr int kSortBlock = kSortThreads * kSortPer;
+constexpr int kSortWaves = kSortThreads / 64;
+constexpr unsigned long long kNoKey = ~0ull;
+
+__device__ __forceinline__ unsigned long long pack_out(int b, int z, int y, int x) {
+  return (static_cast<unsigned long long>(static_cast<uint32_t>(b)) << 48) |
+         (static_cast<unsigned long long>(static_cast<uint32_t>(z)) << 32) |
+         (static_cast<unsigned long long>(static_cast<uint32_t>(y)) << 16) |
+         static_cast<unsigned long long>(static_cast<uint32_t>(x));
+}
+
+constexpr int kMaxAxisChoices = 8;
+
+// The grid coordinates q = (p - d) / s of one axis, for the kernel components
+// d in lo .. lo + K - 1 that divide evenly and land in [0, 2^16).
+__device__ __forceinline__ int axis_choices(int p, int K, int lo, int s, int (&q)[kMaxAxisChoices]) {
+  int n = 0;
+  for (int d = lo; d < lo + K; ++d) {
+    const int v = p - d;
+    if (v >= 0 && v % s == 0 && v / s < 65536 && n < kMaxAxisChoices) q[n++] = v / s;
+  }
+  return n;
+}
+
+// One lane per input row; `ca` choices per axis at most, ca^3 key slots per
+// input.
+__global__ __launch_bounds__(256) void k_out_candidates(const int4* __restrict__ coords, int64_t n, int K, int lo,
+                                                        int s, int ca, unsigned long long* __restrict__ keys) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int4 c = coords[i];
+  const int64_t base = i * static_cast<int64_t>(ca) * ca * ca;
+  const bool in_range = c.x >= 0 && c.x < 32768 && c.y >= 0 && c.y < 65536 && c.z >= 0 && c.z < 65536 &&
+                        c.w >= 0 && c.w < 65536;  // out-of-range inputs are reported by the table build
+  int qz[kMaxAxisChoices], qy[kMaxAxisChoices], qx[kMaxAxisChoices];
+  const int nz = in_range ? axis_choices(c.y, K, lo, s, qz) : 0;
+  const int ny = in_range ? axis_choices(c.z, K, lo, s, qy) : 0;
+  const int nx = in_range ? axis_choices(c.w, K, lo, s, qx) : 0;
+  for (int a = 0; a < ca; ++a)
+    for (int b = 0; b < ca; ++b)
+      for (int e = 0; e < ca; ++e) {
+        const bool ok = a < nz && b < ny && e < nx;
+        keys[base + (a * ca + b) * ca + e] = ok ? pack_out(c.x, qz[a], qy[b], qx[e]) : kNoKey;
+      }
+}
+
+// Element e of a block sits in round (e / 64) mod kSortPer of wave
+// e / (kSortPer x 64), lane e mod 64, so a wave's rounds walk its elements in
+// order and ranks by (wave, round, lane) are ranks in element order.
+__device__ __forceinline__ int64_t sort_index(int64_t block, int wave, int j, int lane) {
+  return block * kSortBlock + (static_cast<int64_t>(wave) * kSortPer + j) * 64 + lane;
+}
+
+// Digit histogram of one block: hist[d * blocks + block].
+__global__ __launch_bounds__(kSortThreads) void k_rs_count(const unsigned long long* __restrict__ keys, int64_t m,
+                                                           int shift, int64_t blocks, uint32_t* __restrict__ hist) {
+  __shared__ uint32_t h[256];
+  for (int i = threadIdx.x; i < 256; i += kSortThreads) h[i] = 0u;
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < kSortPer; ++j) {
+    const int64_t g = sort_index(blockIdx.x, wave, j, lane);
+    if (g < m) atomicAdd(&h[(keys[g] >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  for (int d = threadIdx.x; d < 256; d += kSortThreads) hist[static_cast<int64_t>(d) * blocks + blockIdx.x] = h[d];
+}
+
+// In-place exclusive scan of `count` values by one workgroup: each thread
+// sums a contiguous run, the runs' sums are scanned across the workgroup,
+// and each thread rewrites its run.  The total goes to *total when non-null.
+__global__ __launch_bounds__(1024) void k_scan_excl(uint32_t* __restrict__ v, int64_t count,
+                                                    long long* __restrict__ total) {
+  __shared__ unsigned long long wsum[16];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t per = (count + 1023) / 1024;
+  const int64_t lo = tid * per;
+  const int64_t hi = (lo + per < count) ? lo + per : count;
+  unsigned long long sum = 0;
+  for (int64_t i = lo; i < hi; ++i) sum += v[i];
+  unsigned long long incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  unsigned long long base = incl - sum;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  for (int64_t i = lo; i < hi; ++i) {
+    const uint32_t x = v[i];
+    v[i] = static_cast<uint32_t>(base);
+    base += x;
+  }
+  if (tid == 1023 && total != nullptr) {
+    unsigned long long all = 0;
+    for (int w = 0; w < 16; ++w) all += wsum[w];
+    *total = static_cast<long long>(all);
+  }
+}
+
+// Stable scatter of one block for the byte at `shift`: key at element e goes
+// to offs[d * blocks + block] (the scanned histogram) + its rank among the
+// block's keys of digit d that precede it.
+__global__ __launch_bounds__(kSortThreads) void k_rs_scatter(const unsigned long long* __restrict__ in,
+                                                             unsigned long long* __restrict__ out, int64_t m,
+                                                             int shift, int64_t blocks,
+                                                             const uint32_t* __restrict__ offs) {
+  __shared__ uint32_t hist[kSortWaves * 256];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  uint32_t* row = hist + wave * 256;
+  for (int d = lane; d < 256; d += 64) row[d] = 0u;
+  unsigned long long key[kSortPer];
+  uint32_t dig[kSortPer], rank[kSortPer];
+  bool valid[kSortPer];
+#pragma unroll
+  for (int j = 0; j < kSortPer; ++j) {
+    const int64_t g = sort_index(blockIdx.x, wave, j, lane);
+    valid[j] = g < m;
+    key[j] = valid[j] ? in[g] : kNoKey;
+    const uint32_t d = static_cast<uint32_t>((key[j] >> shift) & 255u);
+    dig[j] = d;
+    unsigned long long peers = __ballot(valid[j]);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const unsigned long long bb = __ballot((d >> b) & 1u);
+      peers &= ((d >> b) & 1u) ? bb : ~bb;
+    }
+    rank[j] = static_cast<uint32_t>(__popcll(peers & below));
+    const uint32_t cnt = static_cast<uint32_t>(__popcll(peers));
+    // lanes of one digit read the count so far and write the same new count
+    // (a wave's LDS operations run in order, so round j sees the rounds before)
+    const uint32_t before = row[d];
+    rank[j] += before;
+    if (valid[j]) row[d] = before + cnt;
+  }
+  __syncthreads();
+  // per digit: each wave's start within the block
+  if (threadIdx.x < 256) {
+    const int d = threadIdx.x;
+    uint32_t run = 0u;
+#pragma unroll
+    for (int w = 0; w < kSortWaves; ++w) {
+      const uint32_t c = hist[w * 256 + d];
+      hist[w * 256 + d] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kSortPer; ++j) {
+    if (valid[j]) {
+      const uint32_t d = dig[j];
+      const int64_t pos = static_cast<int64_t>(offs[static_cast<int64_t>(d) * blocks + blockIdx.x]) + hist[wave * 256 + d] + rank[j];
+      out[pos] = key[j];
+    }
+  }
+}
+
+__device__ __forceinline__ bool run_start(const unsigned long long* __restrict__ keys, int64_t g, int64_t m) {
+  if (g >= m) return false;
+  const unsigned long long k = keys[g];
+  return k != kNoKey && (g == 0 || keys[g - 1] != k);
+}
+
+// Runs starting in each block.
+__global__ __launch_bounds__(kSortThreads) void k_uniq_count(const unsigned long long* __restrict__ keys, int64_t m,
+                                                             uint32_t* __restrict__ cnt) {
+  __shared__ uint32_t total;
+  if (threadIdx.x == 0) total = 0u;
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t c = 0u;
+#pragma unroll
+  for (int j = 0; j < kSortPer; ++j) c += run_start(keys, sort_index(blockIdx.x, wave, j, lane), m) ? 1u : 0u;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  if (lane == 0) atomicAdd(&total, c);
+  __syncthreads();
+  if (threadIdx.x == 0) cnt[blockIdx.x] = total;
+}
+
+// The coordinates of each run's key at offs[block] + its rank in the block.
+__global__ __launch_bounds__(kSortThreads) void k_uniq_write(const unsigned long long* __restrict__ keys, int64_t m,
+                                                             const uint32_t* __restrict__ offs,
+                                                             int4* __restrict__ out) {
+  __shared__ uint32_t wtot[kSortWaves];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  bool st[kSortPer];
+  uint32_t rank[kSortPer];
+  uint32_t run = 0u;
+#pragma unroll
+  for (int j = 0; j < kSortPer; ++j) {
+    st[j] = run_start(keys, sort_index(blockIdx.x, wave, j, lane), m);
+    const unsigned long long b = __ballot(st[j]);
+    rank[j] = run + static_cast<uint32_t>(__popcll(b & below));
+    run += static_cast<uint32_t>(__popcll(b));
+  }
+  if (lane == 0) wtot[wave] = run;
+  __syncthreads();
+  uint32_t base = offs[blockIdx.x];
+  for (int w = 0; w < wave; ++w) base += wtot[w];
+#pragma unroll
+  for (int j = 0; j < kSortPer; ++j) {
+    if (st[j]) {
+      const unsigned long long k = keys[sort_index(blockIdx.x, wave, j, lane)];
+      out[base + rank[j]] = make_int4(static_cast<int>(k >> 48), static_cast<int>((k >> 32) & 0xffffull),
+                                      static_cast<int>((k >> 16) & 0xffffull), static_cast<int>(k & 0xffffull));
+    }
+  }
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+struct OutScratch {
+  unsigned long long* a;
+  unsigned long long* b;
+  uint32_t* hist;
+  uint32_t* cnt;
+};
+
+OutScratch carve_out_scratch(const OutCoordPlan& p, void* base) {
+  OutScratch s;
+  char* c = static_cast<char*>(base);
+  s.a = reinterpret_cast<unsigned long long*>(c);
+  c += align256(static_cast<size_t>(p.m) * sizeof(unsigned long long));
+  s.b = reinterpret_cast<unsigned long long*>(c);
+  c += align256(static_cast<size_t>(p.m) * sizeof(unsigned long long));
+  s.hist = reinterpret_cast<uint32_t*>(c);
+  c += align256(static_cast<size_t>(256) * p.blocks * sizeof(uint32_t));
+  s.cnt = reinterpret_cast<uint32_t*>(c);
+  return s;
+}
+
+}  // namespace
+
+OutCoordPlan out_coord_plan(int64_t n_in, int K, int stride) {
+  OutCoordPlan p;
+  p.n_in = n_in;
+  p.K = K;
+  p.lo = -((K - 1) / 2);
+  p.stride = stride;
+  p.ca = (K + stride - 1) / stride;
+  p.m = n_in * p.ca * p.ca * p.ca;
+  p.blocks = (p.m + kSortBlock - 1) / kSortBlock;
+  return p;
+}
+
+size_t out_coord_scratch_bytes(const OutCoordPlan& p) {
+  return 2 * align256(static_cast<size_t>(p.m) * sizeof(unsigned long long)) +
+         align256(static_cast<size_t>(256) * p.blocks * sizeof(uint32_t)) +
+         align256(static_cast<size_t>(p.blocks) * sizeof(uint32_t));
+}
+
+hipError_t launch_out_coords_count(const OutCoordPlan& p, const int32_t* coords, void* scratch, long long* n_out,
+                                   hipStream_t stream) {
+  const OutScratch s = carve_out_scratch(p, scratch);
+  hipLaunchKernelGGL(k_out_candidates, dim3(static_cast<unsigned>((p.n_in + 255) / 256)), dim3(256), 0, stream,
+                     reinterpret_cast<const int4*>(coords), p.n_in, p.K, p.lo, p.stride, p.ca, s.a);
+  unsigned long long* src = s.a;
+  unsigned long long* dst = s.b;
+  const unsigned grid = static_cast<unsigned>(p.blocks);
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 8 * pass;
+    hipLaunchKernelGGL(k_rs_count, dim3(grid), dim3(kSortThreads), 0, stream, src, p.m, shift, p.blocks, s.hist);
+    hipLaunchKernelGGL(k_scan_excl, dim3(1), dim3(1024), 0, stream, s.hist, static_cast<int64_t>(256) * p.blocks,
+                       static_cast<long long*>(nullptr));
+    hipLaunchKernelGGL(k_rs_scatter, dim3(grid), dim3(kSortThreads), 0, stream, src, dst, p.m, shift, p.blocks,
+                       s.hist);
+    unsigned long long* t = src;
+    src = dst;
+    dst = t;
+  }
+  // eight passes: the sorted keys are back in s.a
+  hipLaunchKernelGGL(k_uniq_count, dim3(grid), dim3(kSortThreads), 0, stream, s.a, p.m, s.cnt);
+  hipLaunchKernelGGL(k_scan_excl, dim3(1), dim3(1024), 0, stream, s.cnt, p.blocks, n_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_out_coords_write(const OutCoordPlan& p, void* scratch, int32_t* out_coords, hipStream_t stream) {
+  const OutScratch s = carve_out_scratch(p, scratch);
+  hipLaunchKernelGGL(k_uniq_write, dim3(static_cast<unsigned>(p.blocks)), dim3(kSortThreads), 0, stream, s.a, p.m,
+                     s.cnt, reinterpret_cast<int4*>(out_coords));
+  return hipGetLastError();
+}
+
+}  // namespace spconv

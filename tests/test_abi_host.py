@@ -33,7 +33,7 @@ def test_single_hip_runtime_mapped():
 
 
 def test_abi_version_and_status_strings():
-    assert sp.spconv_abi_version() == 2
+    assert sp.spconv_abi_version() == 3
     for code, name in sp.STATUS.items():
         assert sp.spconv_status_string(code) == name
 

@@ -158,9 +158,9 @@ def lidar_frame(seed: int, batch: int = 0, beams: int = 64, azimuths: int = 2048
 
 
 def coarsen(coords: np.ndarray) -> np.ndarray:
-    """Next level of a U-Net-like pyramid: ``unique((b, z//2, y//2, x//2))``.
-    The strided convolution that would produce it is outside the submanifold
-    path; the coarser coordinate set is prepared here as an input."""
+    """Next level of a U-Net-like pyramid: ``unique((b, z//2, y//2, x//2))``,
+    the outputs of a K = 2, stride 2 strided map of the level (the library's
+    strided map produces the same coordinates; the tests check it)."""
     c = coords.astype(np.int64).copy()
     c[:, 1:] //= 2
     return _lexsort_unique(c)
