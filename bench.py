@@ -58,13 +58,24 @@ def roofline(layer, e, fwd_ms, traffic=None):
     sets it, and `achieved`/`peak`/`frac` are in that side's unit.  Both
     fractions are reported beside it."""
     kv = layer.k ** 3
-    flops = 2.0 * e * layer.cin * layer.cout
     nbytes = algorithmic_forward_bytes(layer.n, e, kv, layer.cin, layer.cout, layer.dtype)
+    return roofline_of(2.0 * e * layer.cin * layer.cout, nbytes, fwd_ms, layer.dtype, traffic)
+
+
+def strided_forward_bytes(n_in, n_out, e, kv, cin, cout, dtype):
+    """Minimum HBM bytes of a forward over a strided or transposed map: the
+    input rows read once, the output rows written once, the weights once and
+    8 bytes of row indices per entry (no entry is an identity)."""
+    s = 4 if dtype == "f32" else 2
+    return n_in * cin * s + n_out * cout * s + kv * cin * cout * s + 8 * e
+
+
+def roofline_of(flops, nbytes, fwd_ms, dtype, traffic=None):
     ai = flops / nbytes
     t = fwd_ms * 1e-3
     gbs = nbytes / t / 1e9
     tflops = flops / t / 1e12
-    mfma_peak = MFMA_PEAK_TFLOPS[layer.dtype]
+    mfma_peak = MFMA_PEAK_TFLOPS[dtype]
     hbm_frac = gbs / HBM_PEAK_GBS
     mfma_frac = tflops / mfma_peak
     mfma_bound = mfma_peak * 1e12 < ai * HBM_PEAK_GBS * 1e9
@@ -411,6 +422,72 @@ def measure_backward(torch, sp, layer, reps=20, warmup=3):
     }
 
 
+def measure_strided(torch, sp, coords_np, K=3, stride=2, cin=64, cout=128, dtype="bf16", reps=10):
+    """The strided (downsampling) convolution between pyramid levels and its
+    transpose (upsampling back), on the given coordinates: map builds (host
+    wall time of the call, which waits for the device; median of `reps`) and
+    forwards (HIP event pairs on the launch stream, median of `reps`)."""
+    import numpy as np
+    import workloads
+
+    dev = torch.device("cuda:0")
+    coords = torch.from_numpy(coords_np).to(dev)
+    torch.cuda.synchronize()
+
+    def wall(fn):
+        # two untimed calls first; each new map replaces (and frees) the last
+        ts, res = [], None
+        for _ in range(reps + 2):
+            res = None
+            t0 = time.perf_counter()
+            res = fn()
+            torch.cuda.synchronize()
+            ts.append((time.perf_counter() - t0) * 1e3)
+        return float(np.median(ts[2:])), res
+
+    def events(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    t_build, kmap = wall(lambda: sp.build_map_strided(coords, K, stride))
+    t_tr, tmap = wall(kmap.transpose)
+    f = workloads.features(kmap.n_in, cin, dtype, 900).to(dev)
+    w = workloads.weights(K, cin, cout, dtype, 901).to(dev)
+    out = torch.empty((kmap.n, cout), dtype=f.dtype, device=dev)
+    t_down = events(lambda: sp.forward(f, w, kmap, out=out))
+    g = workloads.features(kmap.n, cout, dtype, 902).to(dev)
+    wt = workloads.weights(K, cout, cin, dtype, 903).to(dev)
+    up = torch.empty((kmap.n_in, cin), dtype=f.dtype, device=dev)
+    t_up = events(lambda: sp.forward(g, wt, tmap, out=up))
+    e = kmap.total_entries
+    kv = K ** 3
+    res = {
+        "kernel": K, "stride": stride, "n_in": int(kmap.n_in), "n_out": int(kmap.n), "map_entries": int(e),
+        "c_in": cin, "c_out": cout, "dtype": dtype,
+        "map_build_ms": round(t_build, 4), "transpose_build_ms": round(t_tr, 4),
+        "down_forward_ms": round(t_down, 4),
+        "down_roofline": roofline_of(2.0 * e * cin * cout,
+                                     strided_forward_bytes(kmap.n_in, kmap.n, e, kv, cin, cout, dtype), t_down, dtype),
+        "up_forward_ms": round(t_up, 4),
+        "up_roofline": roofline_of(2.0 * e * cin * cout,
+                                   strided_forward_bytes(kmap.n, kmap.n_in, e, kv, cout, cin, dtype), t_up, dtype),
+        "note": "map builds: host wall time of the call (it waits for the device twice); forwards: HIP event pairs",
+    }
+    tmap.free()
+    kmap.free()
+    return res
+
+
 def _inputs(layer):
     import workloads
 
@@ -450,6 +527,7 @@ def main(argv=None):
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra layers reported beside the default one")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the two gradients")
+    ap.add_argument("--no-strided", action="store_true", help="skip timing the strided convolution")
     ap.add_argument("--no-permuted", action="store_true",
                     help="skip the pass over the rows in a random order")
     ap.add_argument("--no-two-streams", action="store_true",
@@ -531,6 +609,8 @@ def main(argv=None):
     del r
     if not args.no_backward:
         result["backward"] = measure_backward(torch, sp, layer)
+    if not args.no_strided:
+        result["strided"] = measure_strided(torch, sp, layer.coords)
     if not args.no_extra and (args.workload, args.layer) == (DEFAULT_WORKLOAD, DEFAULT_LAYER):
         extra = []
         for wi, li in EXTRA_LAYERS:

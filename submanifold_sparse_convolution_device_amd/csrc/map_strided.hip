@@ -15,8 +15,9 @@
 //                     lexicographic order), unused slots ~0;
 //   radix sort        stable LSD over the 8 bytes of the keys: per pass a
 //                     digit histogram per block of 4096 keys (k_rs_count), an
-//                     exclusive scan over (digit, block) (k_scan_excl) and a
-//                     stable scatter (k_rs_scatter: ranks within a block by
+//                     exclusive scan over (digit, block) (per tile of 4096
+//                     counts, then the tiles' totals, then each tile's prefix
+//                     added) and a stable scatter (k_rs_scatter: ranks within a block by
 //                     ballots, in element order);
 //   unique            a key that differs from its predecessor (and is not ~0)
 //                     starts a run: per-block counts, their exclusive scan
@@ -130,6 +131,47 @@ __global__ __launch_bounds__(1024) void k_scan_excl(uint32_t* __restrict__ v, in
     for (int w = 0; w < 16; ++w) all += wsum[w];
     *total = static_cast<long long>(all);
   }
+}
+
+// Multi-workgroup exclusive scan, pass 1: workgroup t scans its tile of
+// kScanTile values in place (thread i holds values 4 i .. 4 i + 3 of the tile)
+// and writes the tile's total to part[t].  Pass 2 scans part (k_scan_excl,
+// one workgroup, few values); pass 3 (k_scan_add) adds each tile's prefix.
+constexpr int kScanTile = 4096;
+__global__ __launch_bounds__(1024) void k_scan_tile(uint32_t* __restrict__ v, int64_t count,
+                                                    uint32_t* __restrict__ part) {
+  __shared__ uint32_t wsum[16];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kScanTile + 4 * tid;
+  uint32_t x[4];
+  uint32_t sum = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[j] = (base + j < count) ? v[base + j] : 0u;
+    sum += x[j];
+  }
+  uint32_t incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t run = incl - sum;
+  for (int w = 0; w < wave; ++w) run += wsum[w];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (base + j < count) v[base + j] = run;
+    run += x[j];
+  }
+  if (tid == 1023) part[blockIdx.x] = run;  // the last thread's running value is the tile's total
+}
+
+__global__ __launch_bounds__(256) void k_scan_add(uint32_t* __restrict__ v, int64_t count,
+                                                  const uint32_t* __restrict__ part) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < count) v[i] += part[i / kScanTile];
 }
 
 // Stable scatter of one block for the byte at `shift`: key at element e goes
@@ -252,7 +294,19 @@ struct OutScratch {
   unsigned long long* b;
   uint32_t* hist;
   uint32_t* cnt;
+  uint32_t* part;  // tile totals of the multi-workgroup scan
 };
+
+int64_t scan_tiles(int64_t count) { return (count + kScanTile - 1) / kScanTile; }
+
+// Exclusive scan of v[0 .. count) in place; the total to *total when non-null.
+void launch_scan(uint32_t* v, int64_t count, uint32_t* part, long long* total, hipStream_t stream) {
+  const int64_t tiles = scan_tiles(count);
+  hipLaunchKernelGGL(k_scan_tile, dim3(static_cast<unsigned>(tiles)), dim3(1024), 0, stream, v, count, part);
+  hipLaunchKernelGGL(k_scan_excl, dim3(1), dim3(1024), 0, stream, part, tiles, total);
+  hipLaunchKernelGGL(k_scan_add, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0, stream, v, count,
+                     static_cast<const uint32_t*>(part));
+}
 
 OutScratch carve_out_scratch(const OutCoordPlan& p, void* base) {
   OutScratch s;
@@ -264,6 +318,8 @@ OutScratch carve_out_scratch(const OutCoordPlan& p, void* base) {
   s.hist = reinterpret_cast<uint32_t*>(c);
   c += align256(static_cast<size_t>(256) * p.blocks * sizeof(uint32_t));
   s.cnt = reinterpret_cast<uint32_t*>(c);
+  c += align256(static_cast<size_t>(p.blocks) * sizeof(uint32_t));
+  s.part = reinterpret_cast<uint32_t*>(c);
   return s;
 }
 
@@ -284,7 +340,8 @@ OutCoordPlan out_coord_plan(int64_t n_in, int K, int stride) {
 size_t out_coord_scratch_bytes(const OutCoordPlan& p) {
   return 2 * align256(static_cast<size_t>(p.m) * sizeof(unsigned long long)) +
          align256(static_cast<size_t>(256) * p.blocks * sizeof(uint32_t)) +
-         align256(static_cast<size_t>(p.blocks) * sizeof(uint32_t));
+         align256(static_cast<size_t>(p.blocks) * sizeof(uint32_t)) +
+         align256(static_cast<size_t>(scan_tiles(256 * p.blocks)) * sizeof(uint32_t));
 }
 
 hipError_t launch_out_coords_count(const OutCoordPlan& p, const int32_t* coords, void* scratch, long long* n_out,
@@ -298,8 +355,7 @@ hipError_t launch_out_coords_count(const OutCoordPlan& p, const int32_t* coords,
   for (int pass = 0; pass < 8; ++pass) {
     const int shift = 8 * pass;
     hipLaunchKernelGGL(k_rs_count, dim3(grid), dim3(kSortThreads), 0, stream, src, p.m, shift, p.blocks, s.hist);
-    hipLaunchKernelGGL(k_scan_excl, dim3(1), dim3(1024), 0, stream, s.hist, static_cast<int64_t>(256) * p.blocks,
-                       static_cast<long long*>(nullptr));
+    launch_scan(s.hist, static_cast<int64_t>(256) * p.blocks, s.part, nullptr, stream);
     hipLaunchKernelGGL(k_rs_scatter, dim3(grid), dim3(kSortThreads), 0, stream, src, dst, p.m, shift, p.blocks,
                        s.hist);
     unsigned long long* t = src;
@@ -308,7 +364,7 @@ hipError_t launch_out_coords_count(const OutCoordPlan& p, const int32_t* coords,
   }
   // eight passes: the sorted keys are back in s.a
   hipLaunchKernelGGL(k_uniq_count, dim3(grid), dim3(kSortThreads), 0, stream, s.a, p.m, s.cnt);
-  hipLaunchKernelGGL(k_scan_excl, dim3(1), dim3(1024), 0, stream, s.cnt, p.blocks, n_out);
+  launch_scan(s.cnt, p.blocks, s.part, n_out, stream);
   return hipGetLastError();
 }
 
