@@ -25,6 +25,9 @@ Contents
     "Sparse inputs and sparse convolution", section "What a dense convolution
     does to empty space", and the SparseConvNet blog, section 2 (regular
     output definition).
+``adaptive_groups`` / ``padded_rows``
+    The adaptive grouping of offsets into padded batched products (epsilon,
+    S), from "TorchSparse: regular computation from irregular sparsity".
 ``mac_count``
     Entries x Cin x Cout: "Sparse inputs and sparse convolution", section
     "A symmetry you can check on the slide" (MACs per layer).
@@ -384,6 +387,56 @@ def conventional_entries(active: Iterable[Tuple[int, ...]], shape: Tuple[int, ..
             if all(0 <= a[i] + o[i] < shape[i] for i in range(d)):
                 n += 1
     return n
+
+
+def adaptive_groups(counts: Sequence[int], epsilon: float, S: float, centre: Optional[int] = None) -> List[List[int]]:
+    """Offset groups of the adaptive grouping of "TorchSparse: regular
+    computation from irregular sparsity", sections "The spectrum: separate,
+    dense, grouped" and "How the groups are chosen".
+
+    The offsets with entries, the identity offset ``centre`` apart (it runs
+    on its own), are walked in decreasing map size (ties by index) and cut
+    into runs: a run grows while its redundant computation ratio, the padded
+    rows over all rows of the padded batch (m x max - sum) / (m x max), stays
+    at or below ``epsilon``, and a new run starts the moment the next offset
+    would take it above.  A run whose largest map is at least ``S`` runs as
+    separate matrix products (each offset its own group); the others run as
+    one batched product each, padded to their largest map.  So epsilon = 1
+    with S unbounded is one dense batch, S = 0 is separate computation, and
+    epsilon = 0 groups offsets of equal map size only (the mirror pairs of a
+    submanifold map: symmetric grouping).  The centre, when given and
+    non-empty, comes first as a group of its own."""
+    order = sorted((k for k in range(len(counts)) if counts[k] > 0 and k != centre),
+                   key=lambda k: (-int(counts[k]), k))
+    runs: List[List[int]] = []
+    cur: List[int] = []
+    for k in order:
+        cand = cur + [k]
+        mx = max(int(counts[j]) for j in cand)
+        tot = sum(int(counts[j]) for j in cand)
+        ratio = (len(cand) * mx - tot) / (len(cand) * mx)
+        if cur and ratio > epsilon:
+            runs.append(cur)
+            cur = [k]
+        else:
+            cur = cand
+    if cur:
+        runs.append(cur)
+    groups: List[List[int]] = []
+    if centre is not None and counts[centre] > 0:
+        groups.append([centre])
+    for g in runs:
+        if max(int(counts[j]) for j in g) >= S:
+            groups.extend([[j] for j in g])
+        else:
+            groups.append(g)
+    return groups
+
+
+def padded_rows(counts: Sequence[int], groups: Sequence[Sequence[int]]) -> int:
+    """Rows the grouped computation runs: every member of a group padded to
+    the group's largest map."""
+    return sum(len(g) * max(int(counts[j]) for j in g) for g in groups)
 
 
 def mac_count(entries: int, cin: int, cout: int) -> int:
