@@ -91,7 +91,8 @@ typedef enum spconv_map_kind {
 
 /* Version of this ABI (incremented on any incompatible change; 2: lists in
  * the map's row order instead of increasing out_idx; 3: strided and
- * transposed maps, whose input and output rows differ). */
+ * transposed maps, whose input and output rows differ; 4: the grouped
+ * dataflow, its plan and the dataflow selector). */
 int32_t spconv_abi_version(void);
 
 /*
@@ -319,6 +320,103 @@ spconv_status spconv_map_geometry(const spconv_map* map, int64_t* n_in, int64_t*
  * strided or transposed map, valid until spconv_map_free.  UNSUPPORTED for a
  * submanifold map, whose outputs are its inputs. */
 spconv_status spconv_map_out_coords(const spconv_map* map, const int32_t** d_out_coords);
+
+/* ---- Weight-stationary forward with adaptive grouping ----
+ *
+ * The comparison dataflow of "TorchSparse: regular computation from
+ * irregular sparsity", sections "The spectrum: separate, dense, grouped" and
+ * "How the groups are chosen": gather the input rows of each offset into a
+ * batch, multiply each batch by its W_d, scatter the products back onto the
+ * output rows.  Offsets run in groups, one batched product each, every
+ * member padded with zero rows to the group's largest map; the padded rows
+ * are computed (the redundant work the grouping trades for fewer, larger
+ * products) and their products dropped.
+ *
+ * The groups for (epsilon, S): the offsets with entries, the identity offset
+ * of a submanifold map apart (it forms a group of its own, first), walked in
+ * decreasing map size (ties by lower index) and cut into runs; a run takes
+ * the next offset while its redundant ratio (m x max - sum) / (m x max) over
+ * its m maps stays at most epsilon (computed in double precision), else that
+ * offset starts the next run.  A run whose largest map is at least S runs as
+ * separate products, one per offset; every other run is one group.  So
+ * epsilon = 1 with S = +inf is one dense batch of the non-identity offsets,
+ * S = 0 is fully separate computation, and epsilon = 0 groups equal map
+ * sizes only (the mirror pairs of a submanifold map).
+ */
+typedef enum spconv_dataflow_kind {
+  SPCONV_DATAFLOW_FUSED = 0,   /* spconv_forward's output-stationary kernels */
+  SPCONV_DATAFLOW_GROUPED = 1  /* spconv_forward_grouped with (epsilon, S) */
+} spconv_dataflow_kind;
+
+/* The choice spconv_select_dataflow makes for one layer configuration. */
+typedef struct spconv_dataflow {
+  int32_t kind;        /* spconv_dataflow_kind */
+  int32_t groups;      /* groups of the chosen plan (0 for the fused dataflow) */
+  double epsilon;      /* the chosen plan's epsilon and S (grouped only) */
+  double S;
+  float ms;            /* measured time per call of the chosen dataflow */
+  float fused_ms;      /* measured time per call of the fused dataflow */
+  int32_t candidates;  /* distinct candidates timed (the fused one included) */
+  int32_t reserved;
+} spconv_dataflow;
+
+/*
+ * The groups of (epsilon, S) over `map` (see above), in execution order:
+ * h_offsets[i] is the offset index of entry i and h_groups[i] its group
+ * (0, 1, ...; the entries of a group are consecutive, in decreasing map
+ * size).  Offsets without entries are in no group.  capacity is the length
+ * of h_offsets and h_groups (K^3 always suffices); either may be NULL, as
+ * may any of n_entries, n_groups and padded_rows (sum over entries of their
+ * group's largest map: the rows the batched products run).
+ *
+ * Waits for the map's build if it is still running.  Errors: INVALID_ARG
+ * (NULL map, epsilon or S negative or NaN, capacity below the entries), and
+ * the build's own errors.
+ */
+spconv_status spconv_group_plan(spconv_map* map, double epsilon, double S, int32_t capacity, int32_t* h_offsets,
+                                int32_t* h_groups, int32_t* n_entries, int32_t* n_groups, int64_t* padded_rows);
+
+/*
+ * Forward over `map` in the grouped weight-stationary dataflow: the same
+ * result as spconv_forward (same arguments, layouts and aliasing rules),
+ * computed as one gather of every offset's padded batch, one MFMA batched
+ * product per group (fp32 products) and one deterministic reduction of the
+ * products in offset order per output row, rounded once to the dtype.
+ * Needs f16 or bf16, c_in % 32 == 0, c_out % 16 == 0.  Its workspace
+ * (weights in operand order, the padded batches, one fp32 row of c_out per
+ * map entry) comes from the stream's cached forward workspace.
+ *
+ * Waits for the map's build if it is still running (the plan is made on the
+ * host from the counts).  Errors: those of spconv_forward, INVALID_ARG
+ * (epsilon or S negative or NaN), UNSUPPORTED (dtype or channel counts).
+ */
+spconv_status spconv_forward_grouped(const void* d_feats, const void* d_weights, spconv_map* map, int32_t c_in,
+                                     int32_t c_out, spconv_dtype dtype, double epsilon, double S, void* d_out,
+                                     void* hip_stream);
+
+/*
+ * Per-configuration dataflow selector, after the Sparse Autotuner of
+ * "TorchSparse: regular computation from irregular sparsity", section
+ * "TorchSparse++: overlap memory with computation" (one configuration chosen
+ * per layer from a design space holding gather-GEMM-scatter with grouping
+ * and the fused dataflow): times, on the caller's buffers, the
+ * fused forward and the grouped forward for every (epsilon, S) of the grid
+ * (plans equal to an earlier one skipped), each once untimed and then
+ * `reps` times between two events on hip_stream, and reports the fastest
+ * in *best (ties go to the earlier candidate; the fused one is first).  A
+ * NULL grid takes the default: epsilon in {0, 0.1, 0.2, 0.3, 0.5, 1}, S in
+ * {+inf, 65536, 16384, 0}.  The grouped candidates are skipped where the
+ * grouped forward is unsupported (fp32, channel counts).  On return d_out
+ * holds the chosen dataflow's output.  Synchronises hip_stream once per
+ * candidate.
+ *
+ * Errors: those of spconv_forward, INVALID_ARG (NULL best, reps not in
+ * [1, 1000], a grid longer than 64 or holding a negative or NaN value).
+ */
+spconv_status spconv_select_dataflow(const void* d_feats, const void* d_weights, spconv_map* map, int32_t c_in,
+                                     int32_t c_out, spconv_dtype dtype, const double* epsilons, int32_t n_epsilons,
+                                     const double* thresholds, int32_t n_thresholds, int32_t reps, void* d_out,
+                                     void* hip_stream, spconv_dataflow* best);
 
 /* Releases a map.  Its buffers go back, in the order of the build's stream,
  * to that stream's cache of map blocks (or to the pool); the caller must not

@@ -37,10 +37,19 @@ EXPORTED = (
     "spconv_abi_version", "spconv_build_map", "spconv_build_map_async", "spconv_map_wait",
     "spconv_map_info", "spconv_map_counts", "spconv_map_lists", "spconv_forward",
     "spconv_forward_noalloc", "spconv_backward_data", "spconv_backward_weights", "spconv_build_map_strided",
-    "spconv_map_transpose", "spconv_map_geometry", "spconv_map_out_coords", "spconv_map_free",
-    "spconv_status_string", "spconv_last_error",
+    "spconv_map_transpose", "spconv_map_geometry", "spconv_map_out_coords", "spconv_group_plan",
+    "spconv_forward_grouped", "spconv_select_dataflow", "spconv_map_free", "spconv_status_string",
+    "spconv_last_error",
 )
 MAP_KINDS = {0: "submanifold", 1: "strided", 2: "transposed"}
+DATAFLOWS = {0: "fused", 1: "grouped"}
+
+
+class spconv_dataflow(ctypes.Structure):
+    """Mirror of the C struct spconv_dataflow."""
+    _fields_ = [("kind", ctypes.c_int32), ("groups", ctypes.c_int32), ("epsilon", ctypes.c_double),
+                ("S", ctypes.c_double), ("ms", ctypes.c_float), ("fused_ms", ctypes.c_float),
+                ("candidates", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 _LIB: Optional[ctypes.CDLL] = None
 
@@ -100,6 +109,14 @@ def lib() -> ctypes.CDLL:
     L.spconv_map_geometry.restype = ctypes.c_int
     L.spconv_map_out_coords.argtypes = [vp, ctypes.POINTER(vp)]
     L.spconv_map_out_coords.restype = ctypes.c_int
+    f64, pi32 = ctypes.c_double, ctypes.POINTER(i32)
+    L.spconv_group_plan.argtypes = [vp, f64, f64, i32, pi32, pi32, pi32, pi32, ctypes.POINTER(i64)]
+    L.spconv_group_plan.restype = ctypes.c_int
+    L.spconv_forward_grouped.argtypes = [vp, vp, vp, i32, i32, ctypes.c_int, f64, f64, vp, vp]
+    L.spconv_forward_grouped.restype = ctypes.c_int
+    L.spconv_select_dataflow.argtypes = [vp, vp, vp, i32, i32, ctypes.c_int, ctypes.POINTER(f64), i32,
+                                         ctypes.POINTER(f64), i32, i32, vp, vp, ctypes.POINTER(spconv_dataflow)]
+    L.spconv_select_dataflow.restype = ctypes.c_int
     L.spconv_map_free.argtypes, L.spconv_map_free.restype = [vp], None
     L.spconv_status_string.argtypes, L.spconv_status_string.restype = [ctypes.c_int], ctypes.c_char_p
     L.spconv_last_error.argtypes, L.spconv_last_error.restype = [], ctypes.c_char_p
@@ -212,6 +229,38 @@ def spconv_map_out_coords(handle: int) -> int:
     p = ctypes.c_void_p()
     _check(lib().spconv_map_out_coords(handle, ctypes.byref(p)))
     return int(p.value or 0)
+
+
+def spconv_group_plan(handle: int, epsilon: float, S: float, kernel_volume: int):
+    """(offsets, groups, n_groups, padded_rows) of the plan: offsets and
+    group indices of the entries in execution order."""
+    offs = (ctypes.c_int32 * kernel_volume)()
+    grp = (ctypes.c_int32 * kernel_volume)()
+    n, ng, pad = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check(lib().spconv_group_plan(handle, float(epsilon), float(S), kernel_volume, offs, grp, ctypes.byref(n),
+                                   ctypes.byref(ng), ctypes.byref(pad)))
+    return list(offs[:n.value]), list(grp[:n.value]), ng.value, pad.value
+
+
+def spconv_forward_grouped(d_feats: int, d_weights: int, handle: int, c_in: int, c_out: int, dtype: int,
+                           epsilon: float, S: float, d_out: int, hip_stream: int) -> None:
+    _check(lib().spconv_forward_grouped(d_feats, d_weights, handle, c_in, c_out, dtype, float(epsilon), float(S),
+                                        d_out, hip_stream))
+
+
+def spconv_select_dataflow(d_feats: int, d_weights: int, handle: int, c_in: int, c_out: int, dtype: int,
+                           epsilons, thresholds, reps: int, d_out: int, hip_stream: int) -> spconv_dataflow:
+    def grid(v):
+        if v is None:
+            return None, 0
+        arr = (ctypes.c_double * len(v))(*[float(x) for x in v])
+        return arr, len(v)
+    e, ne = grid(epsilons)
+    t, nt = grid(thresholds)
+    best = spconv_dataflow()
+    _check(lib().spconv_select_dataflow(d_feats, d_weights, handle, c_in, c_out, dtype, e, ne, t, nt, int(reps),
+                                        d_out, hip_stream, ctypes.byref(best)))
+    return best
 
 
 def spconv_map_free(handle: int) -> None:
@@ -483,3 +532,75 @@ def backward_weights(feats, grad_out, kmap: SpconvMap, out=None):
         spconv_backward_weights(feats.data_ptr(), grad_out.data_ptr(), kmap.handle, cin, cout, code, out.data_ptr(),
                                 _stream())
     return out
+
+
+def _forward_operands(feats, weights, kmap: SpconvMap, out):
+    """Checks the operands of a forward and returns (c_in, c_out, dtype
+    code, out)."""
+    global _DT
+    torch = _torch()
+    if _DT is None:
+        _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if not (feats.is_cuda and weights.is_cuda and feats.is_contiguous() and weights.is_contiguous()):
+        raise SpconvError(1, "feats and weights must be contiguous tensors on a HIP device")
+    if feats.dim() != 2 or weights.dim() != 3:
+        raise SpconvError(1, "feats must be [N, C_in] and weights [K^3, C_in, C_out]")
+    n_in, cin = feats.shape
+    kv, wcin, cout = weights.shape
+    if n_in != kmap.n_in or kv != kmap.kernel_volume or wcin != cin:
+        raise SpconvError(1, f"shape mismatch: feats {tuple(feats.shape)}, weights "
+                             f"{tuple(weights.shape)}, map n_in={kmap.n_in} K^3={kmap.kernel_volume}")
+    dt = feats.dtype
+    if weights.dtype != dt:
+        raise SpconvError(1, "feats and weights must share one dtype")
+    code = _DT.get(dt)
+    if code is None:
+        raise SpconvError(4, f"dtype {dt} not supported")
+    if out is None:
+        out = torch.empty((kmap.n, cout), dtype=dt, device=feats.device)
+    elif not (out.is_cuda and out.is_contiguous() and out.dtype == dt and tuple(out.shape) == (kmap.n, cout)):
+        raise SpconvError(1, "out must be a contiguous [N, C_out] tensor of the feature dtype")
+    return cin, cout, code, out
+
+
+def group_plan(kmap: SpconvMap, epsilon: float, S: float):
+    """The offset groups of the adaptive grouping with (epsilon, S) over
+    ``kmap``, in execution order (a list of lists of offset indices), and the
+    rows of the padded batches."""
+    offs, grp, ng, pad = spconv_group_plan(kmap.handle, epsilon, S, kmap.kernel_volume)
+    groups = [[] for _ in range(ng)]
+    for k, g in zip(offs, grp):
+        groups[g].append(k)
+    return groups, pad
+
+
+def forward_grouped(feats, weights, kmap: SpconvMap, epsilon: float, S: float = float("inf"), out=None):
+    """``forward`` in the weight-stationary dataflow with adaptive grouping
+    (epsilon, S): gather, one batched MFMA product per group, reduction
+    (f16 / bf16, C_in % 32 == 0, C_out % 16 == 0)."""
+    cin, cout, code, out = _forward_operands(feats, weights, kmap, out)
+    with _OnDevice(feats.device):
+        spconv_forward_grouped(feats.data_ptr(), weights.data_ptr(), kmap.handle, cin, cout, code, epsilon, S,
+                               out.data_ptr(), _stream())
+    return out
+
+
+def select_dataflow(feats, weights, kmap: SpconvMap, epsilons=None, thresholds=None, reps: int = 3, out=None):
+    """Times the fused forward and the grouped forward over a grid of
+    (epsilon, S) on these operands and returns (choice, out): choice is a
+    dict (dataflow, groups, epsilon, S, ms, fused_ms, candidates) and out
+    holds the chosen dataflow's result."""
+    cin, cout, code, out = _forward_operands(feats, weights, kmap, out)
+    with _OnDevice(feats.device):
+        b = spconv_select_dataflow(feats.data_ptr(), weights.data_ptr(), kmap.handle, cin, cout, code, epsilons,
+                                   thresholds, reps, out.data_ptr(), _stream())
+    choice = {"dataflow": DATAFLOWS.get(b.kind, str(b.kind)), "groups": b.groups, "epsilon": b.epsilon, "S": b.S,
+              "ms": b.ms, "fused_ms": b.fused_ms, "candidates": b.candidates}
+    return choice, out
+
+
+def forward_with(choice, feats, weights, kmap: SpconvMap, out=None):
+    """The forward in the dataflow ``select_dataflow`` chose."""
+    if choice["dataflow"] == "grouped":
+        return forward_grouped(feats, weights, kmap, choice["epsilon"], choice["S"], out=out)
+    return forward(feats, weights, kmap, out=out)

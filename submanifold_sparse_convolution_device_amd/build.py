@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspconv.so")
 SOURCES = ["api.hip", "map_build.hip", "map_strided.hip", "forward.hip", "forward_tiled.hip", "forward_wide.hip",
-           "backward.hip"]
+           "backward.hip", "grouped.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
@@ -27,7 +27,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
 # Per-source extra flags.  The weight-gradient kernels keep their MFMA
 # accumulators in ordinary VGPRs: with accumulation registers the allocator
 # shuttles them between the two register files inside the pipelined loop.
-EXTRA_FLAGS = {"backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA_FLAGS = {"backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "grouped.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -299,12 +300,9 @@ spconv_status noalloc_scratch(int device, void** out) {
 // Validates a forward call and fills its launch arguments.
 spconv_status forward_args(const void* d_feats, const void* d_weights, const spconv_map* map, int32_t c_in,
                            int32_t c_out, spconv_dtype dtype, void* d_out, spconv::ForwardArgs* out) {
+  // Checks that need no map first, then those that read it.
   if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
-  // A side with no rows (a strided map without outputs, or its transpose)
-  // may be NULL: nothing of it is read or written.
-  if ((d_feats == nullptr && map->n_in > 0) || d_weights == nullptr || (d_out == nullptr && map->n > 0)) {
-    return fail(SPCONV_ERR_INVALID_ARG, "NULL feature, weight or output pointer");
-  }
+  if (d_weights == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "NULL weight pointer");
   if (!aligned16(d_feats) || !aligned16(d_weights) || !aligned16(d_out)) {
     return fail(SPCONV_ERR_INVALID_ARG, "feature, weight and output buffers must be 16-byte aligned");
   }
@@ -319,6 +317,11 @@ spconv_status forward_args(const void* d_feats, const void* d_weights, const spc
   if (c_in % mult != 0 || c_out % mult != 0) {
     return fail(SPCONV_ERR_UNSUPPORTED, "c_in = %d and c_out = %d must be multiples of %d", c_in,
                 c_out, mult);
+  }
+  // A side with no rows (a strided map without outputs, or its transpose)
+  // may be NULL: nothing of it is read or written.
+  if ((d_feats == nullptr && map->n_in > 0) || (d_out == nullptr && map->n > 0)) {
+    return fail(SPCONV_ERR_INVALID_ARG, "NULL feature or output pointer");
   }
   {
     // The output is written while other workgroups still read input rows and
@@ -460,11 +463,56 @@ void mark_empty(spconv_map* m) {
   m->total = 0;
 }
 
+
+// ---- grouped (weight-stationary) forward ----
+
+spconv_status check_plan_args(double epsilon, double S) {
+  if (!(epsilon >= 0.0) || !(S >= 0.0)) {
+    return fail(SPCONV_ERR_INVALID_ARG, "epsilon = %g and S = %g must be >= 0 (S may be +inf)", epsilon, S);
+  }
+  return SPCONV_OK;
+}
+
+// Launches the grouped forward of `a` with `plan` from the stream's cached
+// forward workspace.
+spconv_status launch_grouped(const spconv_map* map, const spconv::ForwardArgs& a, const spconv::GroupPlan& plan,
+                             hipStream_t stream) {
+  hipMemPool_t pool = nullptr;
+  spconv_status st = pool_for(map->device, &pool);
+  if (st != SPCONV_OK) return st;
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  StreamCache* c = cache_for(map->device, stream);
+  st = grow_buffer(c->fwd, c->fwd_bytes, spconv::grouped_workspace_bytes(a, plan), pool, stream,
+                   "forward workspace allocation");
+  if (st != SPCONV_OK) return st;
+  const hipError_t e = spconv::launch_forward_grouped(a, plan, c->fwd, stream);
+  if (e != hipSuccess) return hip_fail(e, "grouped forward launch");
+  return SPCONV_OK;
+}
+
+// The fused forward (the path spconv_forward takes) from the stream's cache.
+spconv_status launch_fused(const spconv_map* map, const spconv::ForwardArgs& a, hipStream_t stream) {
+  const ForwardPath path = forward_path(a);
+  const size_t ws_bytes = forward_workspace_bytes(path, a);
+  if (ws_bytes == 0) return launch_forward_path(path, a, nullptr, stream);
+  hipMemPool_t pool = nullptr;
+  spconv_status st = pool_for(map->device, &pool);
+  if (st != SPCONV_OK) return st;
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  StreamCache* c = cache_for(map->device, stream);
+  st = grow_buffer(c->fwd, c->fwd_bytes, ws_bytes, pool, stream, "forward workspace allocation");
+  if (st != SPCONV_OK) return st;
+  return launch_forward_path(path, a, c->fwd, stream);
+}
+
+bool same_plan(const spconv::GroupPlan& x, const spconv::GroupPlan& y) {
+  return x.entries == y.entries && x.entry_group == y.entry_group;
+}
 }  // namespace
 
 extern "C" {
 
-int32_t spconv_abi_version(void) { return 3; }
+int32_t spconv_abi_version(void) { return 4; }
 
 const char* spconv_status_string(spconv_status s) {
   switch (s) {
@@ -1026,6 +1074,156 @@ spconv_status spconv_map_out_coords(const spconv_map* map, const int32_t** d_out
     return fail(SPCONV_ERR_UNSUPPORTED, "a submanifold map's outputs are its inputs (the caller's coordinates)");
   }
   *d_out_coords = map->out_coords;
+  return SPCONV_OK;
+}
+
+spconv_status spconv_group_plan(spconv_map* map, double epsilon, double S, int32_t capacity, int32_t* h_offsets,
+                                int32_t* h_groups, int32_t* n_entries, int32_t* n_groups, int64_t* padded_rows) {
+  g_last_error.clear();
+  if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
+  spconv_status st = check_plan_args(epsilon, S);
+  if (st != SPCONV_OK) return st;
+  st = finish_build(map);
+  if (st != SPCONV_OK) return st;
+  const spconv::GroupPlan plan = spconv::make_group_plan(map->counts.data(), map->KV, map->centre, epsilon, S);
+  const int32_t n = static_cast<int32_t>(plan.entries.size());
+  if ((h_offsets != nullptr || h_groups != nullptr) && capacity < n) {
+    return fail(SPCONV_ERR_INVALID_ARG, "capacity %d below the plan's %d entries", capacity, n);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    if (h_offsets) h_offsets[i] = plan.entries[i];
+    if (h_groups) h_groups[i] = plan.entry_group[i];
+  }
+  if (n_entries) *n_entries = n;
+  if (n_groups) *n_groups = plan.groups;
+  if (padded_rows) *padded_rows = plan.padded_rows;
+  return SPCONV_OK;
+}
+
+spconv_status spconv_forward_grouped(const void* d_feats, const void* d_weights, spconv_map* map, int32_t c_in,
+                                     int32_t c_out, spconv_dtype dtype, double epsilon, double S, void* d_out,
+                                     void* hip_stream) {
+  g_last_error.clear();
+  spconv::ForwardArgs a;
+  spconv_status st = forward_args(d_feats, d_weights, map, c_in, c_out, dtype, d_out, &a);
+  if (st != SPCONV_OK) return st;
+  st = check_plan_args(epsilon, S);
+  if (st != SPCONV_OK) return st;
+  if (!spconv::grouped_supported(a)) {
+    return fail(SPCONV_ERR_UNSUPPORTED, "the grouped forward needs f16 or bf16, c_in %% 32 == 0 and c_out %% 16 == 0");
+  }
+  st = finish_build(map);
+  if (st != SPCONV_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (map->total == 0) return zero_output(d_out, map->n, c_out, dtype, stream);
+  const spconv::GroupPlan plan = spconv::make_group_plan(map->counts.data(), map->KV, map->centre, epsilon, S);
+  return launch_grouped(map, a, plan, stream);
+}
+
+spconv_status spconv_select_dataflow(const void* d_feats, const void* d_weights, spconv_map* map, int32_t c_in,
+                                     int32_t c_out, spconv_dtype dtype, const double* epsilons, int32_t n_epsilons,
+                                     const double* thresholds, int32_t n_thresholds, int32_t reps, void* d_out,
+                                     void* hip_stream, spconv_dataflow* best) {
+  g_last_error.clear();
+  if (best == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "best is NULL");
+  spconv::ForwardArgs a;
+  spconv_status st = forward_args(d_feats, d_weights, map, c_in, c_out, dtype, d_out, &a);
+  if (st != SPCONV_OK) return st;
+  if (reps < 1 || reps > 1000) return fail(SPCONV_ERR_INVALID_ARG, "reps = %d not in [1, 1000]", reps);
+  static const double kEps[] = {0.0, 0.1, 0.2, 0.3, 0.5, 1.0};
+  static const double kS[] = {HUGE_VAL, 65536.0, 16384.0, 0.0};
+  if (epsilons == nullptr) {
+    epsilons = kEps;
+    n_epsilons = static_cast<int32_t>(sizeof(kEps) / sizeof(kEps[0]));
+  }
+  if (thresholds == nullptr) {
+    thresholds = kS;
+    n_thresholds = static_cast<int32_t>(sizeof(kS) / sizeof(kS[0]));
+  }
+  if (n_epsilons < 0 || n_thresholds < 0 || n_epsilons > 64 || n_thresholds > 64) {
+    return fail(SPCONV_ERR_INVALID_ARG, "grids of %d and %d values (at most 64 each)", n_epsilons, n_thresholds);
+  }
+  for (int32_t i = 0; i < n_epsilons; ++i) {
+    st = check_plan_args(epsilons[i], 0.0);
+    if (st != SPCONV_OK) return st;
+  }
+  for (int32_t i = 0; i < n_thresholds; ++i) {
+    st = check_plan_args(0.0, thresholds[i]);
+    if (st != SPCONV_OK) return st;
+  }
+  st = finish_build(map);
+  if (st != SPCONV_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  std::memset(best, 0, sizeof(*best));
+  best->kind = SPCONV_DATAFLOW_FUSED;
+  if (map->total == 0) {
+    best->candidates = 1;
+    return zero_output(d_out, map->n, c_out, dtype, stream);
+  }
+  // Candidates: the fused forward, then each distinct plan of the grid.
+  struct Candidate {
+    bool grouped;
+    double epsilon, S;
+    spconv::GroupPlan plan;
+  };
+  std::vector<Candidate> cands;
+  cands.push_back({false, 0.0, 0.0, {}});
+  if (spconv::grouped_supported(a)) {
+    for (int32_t j = 0; j < n_thresholds; ++j) {
+      for (int32_t i = 0; i < n_epsilons; ++i) {
+        spconv::GroupPlan p =
+            spconv::make_group_plan(map->counts.data(), map->KV, map->centre, epsilons[i], thresholds[j]);
+        bool seen = false;
+        for (size_t c = 1; c < cands.size() && !seen; ++c) seen = same_plan(cands[c].plan, p);
+        if (!seen) cands.push_back({true, epsilons[i], thresholds[j], std::move(p)});
+      }
+    }
+  }
+  auto run = [&](const Candidate& c) {
+    return c.grouped ? launch_grouped(map, a, c.plan, stream) : launch_fused(map, a, stream);
+  };
+  hipEvent_t t0 = nullptr, t1 = nullptr;
+  SPCONV_HIP(hipEventCreate(&t0), "hipEventCreate");
+  hipError_t ec = hipEventCreate(&t1);
+  if (ec != hipSuccess) {
+    (void)hipEventDestroy(t0);
+    return hip_fail(ec, "hipEventCreate");
+  }
+  size_t win = 0;
+  float win_ms = 0.f;
+  for (size_t c = 0; c < cands.size() && st == SPCONV_OK; ++c) {
+    st = run(cands[c]);  // warm-up (workspace growth, first-touch)
+    if (st != SPCONV_OK) break;
+    ec = hipEventRecord(t0, stream);
+    for (int32_t r = 0; r < reps && st == SPCONV_OK && ec == hipSuccess; ++r) st = run(cands[c]);
+    if (st != SPCONV_OK) break;
+    if (ec == hipSuccess) ec = hipEventRecord(t1, stream);
+    if (ec == hipSuccess) ec = hipEventSynchronize(t1);
+    float ms = 0.f;
+    if (ec == hipSuccess) ec = hipEventElapsedTime(&ms, t0, t1);
+    if (ec != hipSuccess) {
+      st = hip_fail(ec, "dataflow timing");
+      break;
+    }
+    ms /= static_cast<float>(reps);
+    if (c == 0) best->fused_ms = ms;
+    if (c == 0 || ms < win_ms) {
+      win = c;
+      win_ms = ms;
+    }
+  }
+  (void)hipEventDestroy(t0);
+  (void)hipEventDestroy(t1);
+  if (st != SPCONV_OK) return st;
+  // Leave the winner's result in d_out.
+  st = run(cands[win]);
+  if (st != SPCONV_OK) return st;
+  best->kind = cands[win].grouped ? SPCONV_DATAFLOW_GROUPED : SPCONV_DATAFLOW_FUSED;
+  best->groups = cands[win].grouped ? cands[win].plan.groups : 0;
+  best->epsilon = cands[win].epsilon;
+  best->S = cands[win].S;
+  best->ms = win_ms;
+  best->candidates = static_cast<int32_t>(cands.size());
   return SPCONV_OK;
 }
 

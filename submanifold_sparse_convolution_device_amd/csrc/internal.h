@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <vector>
 
 namespace spconv {
 
@@ -234,5 +235,26 @@ struct GeneralMapArgs {
 size_t general_scratch_bytes(int64_t nq, int K);
 void carve_general_scratch(int64_t nq, int K, void* base, GeneralMapArgs* g);
 hipError_t launch_general_map(const GeneralMapArgs& g, hipStream_t stream);
+
+// ---- Weight-stationary forward with adaptive grouping (grouped.hip) ----
+// At most K^3 = 343 offsets (K = 7).
+constexpr int kMaxGroupEntries = 343;
+// The groups of one (epsilon, S) choice over a map's per-offset counts:
+// entries (offsets) in execution order, group by group; every member of a
+// group is padded to the group's largest map.
+struct GroupPlan {
+  std::vector<int> entries;        // offset of each entry
+  std::vector<int> entry_group;    // group of each entry
+  std::vector<int> group_first;    // first entry of each group, then the entry count
+  std::vector<int64_t> group_pad;  // rows of each member of a group (its largest map)
+  int groups = 0;
+  int64_t padded_rows = 0;         // rows of the padded batches (sum over entries of pad)
+  int64_t list_rows = 0;           // entries of the map (sum over entries of their list sizes)
+  int64_t tiles = 0;               // 64-row gather tiles over all entries
+};
+GroupPlan make_group_plan(const int64_t* counts, int KV, int centre, double epsilon, double S);
+bool grouped_supported(const ForwardArgs& a);
+size_t grouped_workspace_bytes(const ForwardArgs& a, const GroupPlan& p);
+hipError_t launch_forward_grouped(const ForwardArgs& a, const GroupPlan& p, void* workspace, hipStream_t stream);
 
 }  // namespace spconv

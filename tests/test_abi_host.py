@@ -33,7 +33,7 @@ def test_single_hip_runtime_mapped():
 
 
 def test_abi_version_and_status_strings():
-    assert sp.spconv_abi_version() == 3
+    assert sp.spconv_abi_version() == 4
     for code, name in sp.STATUS.items():
         assert sp.spconv_status_string(code) == name
 
@@ -77,10 +77,10 @@ def test_forward_host_validation():
     fake = 4096
     fake_map = 8192  # never dereferenced on these error paths
     f = sp.spconv_forward
+    # (a NULL feature or output pointer is legal for a map side without rows,
+    # so those cases need a real map: tests/test_gpu_grouped.py)
     assert _status_of(f, fake, fake, 0, 32, 32, 1, fake, 0) == "SPCONV_ERR_INVALID_ARG"
-    assert _status_of(f, 0, fake, fake_map, 32, 32, 1, fake, 0) == "SPCONV_ERR_INVALID_ARG"
     assert _status_of(f, fake, 0, fake_map, 32, 32, 1, fake, 0) == "SPCONV_ERR_INVALID_ARG"
-    assert _status_of(f, fake, fake, fake_map, 32, 32, 1, 0, 0) == "SPCONV_ERR_INVALID_ARG"
     assert _status_of(f, fake + 2, fake, fake_map, 32, 32, 1, fake, 0) == "SPCONV_ERR_INVALID_ARG"
     assert _status_of(f, fake, fake, fake_map, 32, 32, 7, fake, 0) == "SPCONV_ERR_UNSUPPORTED"
     assert _status_of(f, fake, fake, fake_map, 0, 32, 1, fake, 0) == "SPCONV_ERR_INVALID_ARG"
@@ -88,6 +88,20 @@ def test_forward_host_validation():
     assert _status_of(f, fake, fake, fake_map, 1024, 16, 0, fake, 0) == "SPCONV_ERR_INVALID_ARG"
     assert _status_of(f, fake, fake, fake_map, 20, 32, 1, fake, 0) == "SPCONV_ERR_UNSUPPORTED"
     assert _status_of(f, fake, fake, fake_map, 32, 6, 0, fake, 0) == "SPCONV_ERR_UNSUPPORTED"
+
+
+def test_grouped_host_validation():
+    """The grouped forward, its plan and the selector reject bad arguments
+    before they read the map or touch the device."""
+    fake, fake_map = 4096, 8192
+    g = sp.spconv_forward_grouped
+    assert _status_of(g, fake, fake, 0, 32, 32, 1, 0.1, 1e9, fake, 0) == "SPCONV_ERR_INVALID_ARG"
+    assert _status_of(g, fake, 0, fake_map, 32, 32, 1, 0.1, 1e9, fake, 0) == "SPCONV_ERR_INVALID_ARG"
+    assert _status_of(g, fake, fake, fake_map, 32, 32, 7, 0.1, 1e9, fake, 0) == "SPCONV_ERR_UNSUPPORTED"
+    assert _status_of(sp.spconv_group_plan, 0, 0.1, 1e9, 27) == "SPCONV_ERR_INVALID_ARG"
+    sel = sp.spconv_select_dataflow
+    assert _status_of(sel, fake, fake, 0, 32, 32, 1, None, None, 3, fake, 0) == "SPCONV_ERR_INVALID_ARG"
+    assert _status_of(sel, fake, fake, fake_map, 32, 32, 9, None, None, 3, fake, 0) == "SPCONV_ERR_UNSUPPORTED"
 
 
 def test_map_queries_reject_null():
