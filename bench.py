@@ -16,7 +16,11 @@ Prints ONE JSON line.  ``value`` is the whole-step effective throughput
 including the centre ones); the map-build rate and the forward-only rate are
 reported beside it.  ``roofline`` describes the fused forward kernel measured
 with HIP events on the stream it runs on (recorded on about ten of the timed
-steps); ``cpu_baseline`` times the CPU oracle on the host.
+steps); ``cpu_baseline`` times the CPU oracle on the host.  Beside the step,
+the line reports the two gradients, the strided convolution and its
+transpose, and the weight-stationary grouped dataflow (gather, batched
+products, reduction) against the fused forward with the library's
+per-layer dataflow selector.
 """
 from __future__ import annotations
 
@@ -488,6 +492,89 @@ def measure_strided(torch, sp, coords_np, K=3, stride=2, cin=64, cout=128, dtype
     return res
 
 
+def grouped_dataflow_bytes(n, e, padded, kv, cin, cout, dtype):
+    """Minimum HBM bytes of the gather-GEMM-scatter dataflow with padded
+    batches: the gather reads each entry's input row (and its 4-byte index)
+    and writes the padded batch; the batched products read the batch and the
+    weights and write one fp32 product row per entry; the reduction reads
+    those and writes each output row once."""
+    s = ELEM[dtype]
+    gather = e * cin * s + 4 * e + padded * cin * s
+    gemm = padded * cin * s + kv * cin * cout * s + e * cout * 4
+    reduce = e * cout * 4 + n * cout * s
+    return gather + gemm + reduce
+
+
+# Plans of the grouped dataflow timed beside the fused forward:
+# (label, epsilon, S).
+DATAFLOW_PLANS = (("dense", 1.0, float("inf")), ("symmetric", 0.0, float("inf")),
+                  ("adaptive", 0.2, float("inf")), ("separate", 0.0, 0.0))
+DATAFLOW_LAYERS = ((4, 0), (1, 0), (3, 6))
+
+
+def measure_dataflows(torch, sp, cases, reps=10):
+    """Fused forward against the weight-stationary grouped dataflow on each
+    (workload, layer): HIP event pairs on the launch stream (median of
+    `reps`) for the fused forward and each plan of DATAFLOW_PLANS, then the
+    library's selector over its default (epsilon, S) grid.  The roofline of
+    the fastest grouped plan is taken against that dataflow's own bytes
+    (grouped_dataflow_bytes) and its executed (padded) products."""
+    import numpy as np
+    import workloads
+
+    dev = torch.device("cuda:0")
+
+    def events(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    out_rows = []
+    for wi, li in cases:
+        wl = workloads.make_workload(wi)
+        layer = wl.layers[li]
+        print(f"[bench] dataflows: workload={wl.name} layer={li} N={layer.n} K={layer.k} "
+              f"C={layer.cin}->{layer.cout} {layer.dtype}", file=sys.stderr, flush=True)
+        f, w = _inputs(layer)
+        f, w = f.to(dev), w.to(dev)
+        kmap = sp.build_map(torch.from_numpy(layer.coords).to(dev), layer.k)
+        out = torch.empty((layer.n, layer.cout), dtype=f.dtype, device=dev)
+        e = kmap.total_entries
+        kv = layer.k ** 3
+        row = {"workload": wl.name, "layer": li, "n_voxels": layer.n, "map_entries": int(e), "kernel": layer.k,
+               "c_in": layer.cin, "c_out": layer.cout, "dtype": layer.dtype,
+               "fused_ms": round(events(lambda: sp.forward(f, w, kmap, out=out)), 4)}
+        best = None
+        for label, eps, S in DATAFLOW_PLANS:
+            groups, padded = sp.group_plan(kmap, eps, S)
+            t = events(lambda: sp.forward_grouped(f, w, kmap, eps, S, out=out))
+            row[label] = {"epsilon": eps, "S": S if np.isfinite(S) else "inf", "groups": len(groups),
+                          "padded_rows": int(padded), "ms": round(t, 4)}
+            if best is None or t < best[0]:
+                best = (t, label, padded)
+        t, label, padded = best
+        row["grouped_best"] = label
+        row["grouped_best_roofline"] = roofline_of(
+            2.0 * padded * layer.cin * layer.cout,
+            grouped_dataflow_bytes(layer.n, e, padded, kv, layer.cin, layer.cout, layer.dtype), t, layer.dtype)
+        row["fused_speedup_over_best_grouped"] = round(t / row["fused_ms"], 2)
+        choice, _ = sp.select_dataflow(f, w, kmap, reps=3, out=out)
+        row["selector"] = {k: (v if not isinstance(v, float) or np.isfinite(v) else "inf")
+                           for k, v in choice.items()}
+        kmap.free()
+        out_rows.append(row)
+    return out_rows
+
+
 def _inputs(layer):
     import workloads
 
@@ -528,6 +615,8 @@ def main(argv=None):
                     help="skip the extra layers reported beside the default one")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the two gradients")
     ap.add_argument("--no-strided", action="store_true", help="skip timing the strided convolution")
+    ap.add_argument("--no-dataflows", action="store_true",
+                    help="skip timing the grouped weight-stationary dataflow against the fused forward")
     ap.add_argument("--no-permuted", action="store_true",
                     help="skip the pass over the rows in a random order")
     ap.add_argument("--no-two-streams", action="store_true",
@@ -611,6 +700,8 @@ def main(argv=None):
         result["backward"] = measure_backward(torch, sp, layer)
     if not args.no_strided:
         result["strided"] = measure_strided(torch, sp, layer.coords)
+    if not args.no_dataflows:
+        result["dataflows"] = measure_dataflows(torch, sp, DATAFLOW_LAYERS)
     if not args.no_extra and (args.workload, args.layer) == (DEFAULT_WORKLOAD, DEFAULT_LAYER):
         extra = []
         for wi, li in EXTRA_LAYERS:

@@ -405,7 +405,13 @@ def adaptive_groups(counts: Sequence[int], epsilon: float, S: float, centre: Opt
     with S unbounded is one dense batch, S = 0 is separate computation, and
     epsilon = 0 groups offsets of equal map size only (the mirror pairs of a
     submanifold map: symmetric grouping).  The centre, when given and
-    non-empty, comes first as a group of its own."""
+    non-empty, comes first as a group of its own.
+
+    The page describes the paper's two-pointer scan in kernel order but sorts
+    by map size in its worked figure and its tuner; the size order is the one
+    under which epsilon = 0 is the symmetric grouping it names (the mirror
+    offsets k and K^3 - 1 - k are never adjacent in kernel order), so it is
+    the order taken here."""
     order = sorted((k for k in range(len(counts)) if counts[k] > 0 and k != centre),
                    key=lambda k: (-int(counts[k]), k))
     runs: List[List[int]] = []

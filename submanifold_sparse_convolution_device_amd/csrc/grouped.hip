@@ -21,8 +21,11 @@
 // the identity offset apart, in decreasing map size (ties by index), cut into
 // runs while the padded rows stay at most epsilon of a run's padded batch; a
 // run whose largest map is at least S runs as separate products (each offset
-// padded to its own size only).  The host makes the plan from the map's
-// counts; a one-wave kernel writes the device's entry table.
+// padded to its own size only).  (The page describes the paper's scan in
+// kernel order but sorts by size in its figure and tuner; only the size order
+// makes epsilon = 0 pair the mirror offsets, its symmetric grouping.)  The
+// host makes the plan from the map's counts; a one-wave kernel writes the
+// device's entry table.
 #include "internal.h"
 
 #include <algorithm>
@@ -61,6 +64,8 @@ constexpr int kGsRows = 64;          // rows of a gather tile
 constexpr int kGsWgRows = 256;       // batch rows one GEMM workgroup streams through its weights
 constexpr int kGsQB = 2;             // 16-row blocks a wave computes at once
 constexpr int kGsWeightLds = 32768;  // bytes of a workgroup's weight slice
+constexpr int kReduceRows = 16;      // output rows of a reduction workgroup
+constexpr int kReduceBatch = 8;      // product rows a reduction thread loads before adding them
 
 // One entry of the grouped computation: one offset, its list and its padded
 // rows in the batch buffer.
@@ -239,11 +244,14 @@ __global__ __launch_bounds__(256) void k_gs_gemm(const uint16_t* __restrict__ A,
   }
 }
 
-// Reduce: workgroup = one 64-row output tile.  The tile's masks and first
-// list positions per offset are staged in LDS; then each thread sums 4
-// columns of one row over the offsets present, in offset order, from Y (the
-// entry's list position: the tile's first position plus its rank in the
-// mask), and writes the row once, rounded to the dtype.
+// Reduce: workgroup = kReduceRows rows of one 64-row output tile (so that
+// small maps still fill the chip).  The tile's masks and first list
+// positions per offset are staged in LDS; then each thread sums 4 columns of
+// one row over the offsets present, in offset order, from Y (the entry's list
+// position: the tile's first position plus its rank in the mask), and writes
+// the row once, rounded to the dtype.  A thread issues the loads of
+// kReduceBatch offsets before adding them (latency, not bandwidth, bounds
+// the small layers).
 template <typename T>
 __global__ __launch_bounds__(256) void k_gs_reduce(const float* __restrict__ Y,
                                                    const unsigned long long* __restrict__ tile_mask,
@@ -252,27 +260,40 @@ __global__ __launch_bounds__(256) void k_gs_reduce(const float* __restrict__ Y,
                                                    int KV, int cout, T* __restrict__ out) {
   __shared__ unsigned long long s_mask[kMaxGroupEntries];
   __shared__ int32_t s_pos[kMaxGroupEntries];
-  const int64_t t = blockIdx.x;
-  for (int k = threadIdx.x; k < KV; k += 256) {
+  const int64_t t = blockIdx.x / (kGsRows / kReduceRows);
+  const int r0 = static_cast<int>(blockIdx.x % (kGsRows / kReduceRows)) * kReduceRows;
+  for (int k = threadIdx.x; k < KV; k += blockDim.x) {
     s_mask[k] = tile_mask[static_cast<int64_t>(k) * tiles + t];
     s_pos[k] = tile_off[static_cast<int64_t>(k) * tiles + t];
   }
   __syncthreads();
   const int tpr = cout / 4;  // threads per row, 4 columns each (cout <= 1024: tpr <= 256)
-  const int rows_per_pass = 256 / tpr;
+  const int rows_per_pass = static_cast<int>(blockDim.x) / tpr;
   if (static_cast<int>(threadIdx.x) >= rows_per_pass * tpr) return;
   const int c4 = threadIdx.x % tpr;
-  for (int rr = threadIdx.x / tpr; rr < kGsRows; rr += rows_per_pass) {
+  for (int rr = r0 + static_cast<int>(threadIdx.x) / tpr; rr < r0 + kReduceRows; rr += rows_per_pass) {
     const int64_t q = t * kGsRows + rr;
     if (q >= n) break;
     const unsigned long long below = (rr == 0) ? 0ull : (~0ull >> (64 - rr));
+    // The sums run in offset order; an absent offset adds +0, which changes
+    // no sum (acc starts at +0, so it is never -0).
     floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < KV; ++k) {
-      const unsigned long long m = s_mask[k];
-      if ((m >> rr) & 1ull) {
-        const int64_t yr = static_cast<int64_t>(s_pos[k]) + __popcll(m & below);
-        acc += *reinterpret_cast<const floatx4*>(Y + yr * cout + 4 * c4);
+    for (int k0 = 0; k0 < KV; k0 += kReduceBatch) {
+      floatx4 v[kReduceBatch];
+#pragma unroll
+      for (int j = 0; j < kReduceBatch; ++j) {
+        const int k = k0 + j;
+        v[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (k < KV) {
+          const unsigned long long m = s_mask[k];
+          if ((m >> rr) & 1ull) {
+            const int64_t yr = static_cast<int64_t>(s_pos[k]) + __popcll(m & below);
+            v[j] = *reinterpret_cast<const floatx4*>(Y + yr * cout + 4 * c4);
+          }
+        }
       }
+#pragma unroll
+      for (int j = 0; j < kReduceBatch; ++j) acc += v[j];
     }
     const int64_t orow = perm != nullptr ? static_cast<int64_t>(perm[q]) : q;
     u16x4 o;
@@ -365,7 +386,10 @@ hipError_t launch_typed(const ForwardArgs& a, const GroupPlan& p, void* ws, hipS
       }
     }
   }
-  hipLaunchKernelGGL(k_gs_reduce<T>, dim3(static_cast<unsigned>(a.tiles)), dim3(256), 0, stream,
+  // kReduceRows rows of tpr threads each, at most 256 threads
+  const unsigned reduce_threads = static_cast<unsigned>(std::min(256, kReduceRows * (a.cout / 4)));
+  hipLaunchKernelGGL(k_gs_reduce<T>, dim3(static_cast<unsigned>(a.tiles * (kGsRows / kReduceRows))),
+                     dim3(reduce_threads), 0, stream,
                      static_cast<const float*>(Y), a.tile_mask, a.tile_off, a.perm, a.n, a.tiles, a.KV, a.cout,
                      static_cast<T*>(a.out));
   return hipGetLastError();
