@@ -63,7 +63,16 @@
 extern "C" {
 #endif
 
-typedef enum spconv_status {
+/* The enumerations are 32-bit integers on the ABI.  C++ gives them that
+ * underlying type explicitly, so that any int32 a caller passes is a value
+ * of the type (and an unknown one is rejected, not undefined). */
+#ifdef __cplusplus
+#define SPCONV_ENUM(name) enum name : int32_t
+#else
+#define SPCONV_ENUM(name) enum name
+#endif
+
+typedef SPCONV_ENUM(spconv_status) {
   SPCONV_OK = 0,
   SPCONV_ERR_INVALID_ARG = 1,     /* null pointer, bad size, misaligned buffer, K/C mismatch   */
   SPCONV_ERR_DUPLICATE_COORD = 2, /* two rows share one (b, z, y, x) (detected on the device)  */
@@ -73,7 +82,7 @@ typedef enum spconv_status {
   SPCONV_ERR_DEVICE = 6           /* a HIP runtime call failed                                 */
 } spconv_status;
 
-typedef enum spconv_dtype {
+typedef SPCONV_ENUM(spconv_dtype) {
   SPCONV_F32 = 0,  /* fp32 features and weights, fp32 products and accumulation                */
   SPCONV_F16 = 1,  /* fp16 features and weights, fp32 accumulation, output rounded to nearest even */
   SPCONV_BF16 = 2  /* bf16 features and weights, fp32 accumulation, output rounded to nearest even */
@@ -83,7 +92,7 @@ typedef enum spconv_dtype {
 typedef struct spconv_map spconv_map;
 
 /* Kinds of map (spconv_map_geometry). */
-typedef enum spconv_map_kind {
+typedef SPCONV_ENUM(spconv_map_kind) {
   SPCONV_MAP_SUBMANIFOLD = 0, /* outputs = inputs (spconv_build_map)            */
   SPCONV_MAP_STRIDED = 1,     /* downsampling (spconv_build_map_strided)          */
   SPCONV_MAP_TRANSPOSED = 2   /* upsampling, a strided map's transpose            */
@@ -343,7 +352,7 @@ spconv_status spconv_map_out_coords(const spconv_map* map, const int32_t** d_out
  * S = 0 is fully separate computation, and epsilon = 0 groups equal map
  * sizes only (the mirror pairs of a submanifold map).
  */
-typedef enum spconv_dataflow_kind {
+typedef SPCONV_ENUM(spconv_dataflow_kind) {
   SPCONV_DATAFLOW_FUSED = 0,   /* spconv_forward's output-stationary kernels */
   SPCONV_DATAFLOW_GROUPED = 1  /* spconv_forward_grouped with (epsilon, S) */
 } spconv_dataflow_kind;
@@ -375,6 +384,19 @@ typedef struct spconv_dataflow {
  */
 spconv_status spconv_group_plan(spconv_map* map, double epsilon, double S, int32_t capacity, int32_t* h_offsets,
                                 int32_t* h_groups, int32_t* n_entries, int32_t* n_groups, int64_t* padded_rows);
+
+/*
+ * The same plan from per-offset map sizes the caller supplies (host memory,
+ * h_counts[k] for k < kernel_volume; centre is the identity offset that runs
+ * on its own, or -1 for none): no map and no device involved.  Errors:
+ * INVALID_ARG (NULL h_counts, kernel_volume not in [1, 343], centre not in
+ * [-1, kernel_volume), a count not in [0, 2^40), epsilon or S negative or
+ * NaN, capacity below the entries).
+ */
+spconv_status spconv_group_plan_counts(const int64_t* h_counts, int32_t kernel_volume, int32_t centre,
+                                       double epsilon, double S, int32_t capacity, int32_t* h_offsets,
+                                       int32_t* h_groups, int32_t* n_entries, int32_t* n_groups,
+                                       int64_t* padded_rows);
 
 /*
  * Forward over `map` in the grouped weight-stationary dataflow: the same

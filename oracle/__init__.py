@@ -65,8 +65,10 @@ class OracleError(RuntimeError):
 def _lib() -> ctypes.CDLL:
     global _LIB
     if _LIB is None:
-        path = _build.LIB
-        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+        # SPCONV_ORACLE_LIB names another build of the same source (the tests'
+        # sanitizer build); by default the in-tree library, rebuilt when stale.
+        path = os.environ.get("SPCONV_ORACLE_LIB") or _build.LIB
+        if path == _build.LIB and (not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC)):
             _build.build()
         lib = ctypes.CDLL(path)
         lib.oracle_build_map.argtypes = [_i32p, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]

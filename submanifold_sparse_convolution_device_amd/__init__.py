@@ -19,7 +19,9 @@ from typing import Optional, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libspconv.so")
+# SPCONV_LIB_PATH names another build of the same library (the tests' host-only
+# sanitizer build); by default the in-tree libspconv.so.
+LIB_PATH = os.environ.get("SPCONV_LIB_PATH") or os.path.join(_HERE, "libspconv.so")
 
 STATUS = {
     0: "SPCONV_OK",
@@ -37,7 +39,7 @@ EXPORTED = (
     "spconv_abi_version", "spconv_build_map", "spconv_build_map_async", "spconv_map_wait",
     "spconv_map_info", "spconv_map_counts", "spconv_map_lists", "spconv_forward",
     "spconv_forward_noalloc", "spconv_backward_data", "spconv_backward_weights", "spconv_build_map_strided",
-    "spconv_map_transpose", "spconv_map_geometry", "spconv_map_out_coords", "spconv_group_plan",
+    "spconv_map_transpose", "spconv_map_geometry", "spconv_map_out_coords", "spconv_group_plan", "spconv_group_plan_counts",
     "spconv_forward_grouped", "spconv_select_dataflow", "spconv_map_free", "spconv_status_string",
     "spconv_last_error",
 )
@@ -112,6 +114,9 @@ def lib() -> ctypes.CDLL:
     f64, pi32 = ctypes.c_double, ctypes.POINTER(i32)
     L.spconv_group_plan.argtypes = [vp, f64, f64, i32, pi32, pi32, pi32, pi32, ctypes.POINTER(i64)]
     L.spconv_group_plan.restype = ctypes.c_int
+    L.spconv_group_plan_counts.argtypes = [ctypes.POINTER(i64), i32, i32, f64, f64, i32, pi32, pi32, pi32, pi32,
+                                           ctypes.POINTER(i64)]
+    L.spconv_group_plan_counts.restype = ctypes.c_int
     L.spconv_forward_grouped.argtypes = [vp, vp, vp, i32, i32, ctypes.c_int, f64, f64, vp, vp]
     L.spconv_forward_grouped.restype = ctypes.c_int
     L.spconv_select_dataflow.argtypes = [vp, vp, vp, i32, i32, ctypes.c_int, ctypes.POINTER(f64), i32,
@@ -239,6 +244,19 @@ def spconv_group_plan(handle: int, epsilon: float, S: float, kernel_volume: int)
     n, ng, pad = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
     _check(lib().spconv_group_plan(handle, float(epsilon), float(S), kernel_volume, offs, grp, ctypes.byref(n),
                                    ctypes.byref(ng), ctypes.byref(pad)))
+    return list(offs[:n.value]), list(grp[:n.value]), ng.value, pad.value
+
+
+def spconv_group_plan_counts(counts, epsilon: float, S: float, centre: int = -1):
+    """(offsets, groups, n_groups, padded_rows) of the plan over the given
+    per-offset map sizes (no map, no device)."""
+    kv = len(counts)
+    arr = (ctypes.c_int64 * max(kv, 1))(*[int(c) for c in counts])
+    offs = (ctypes.c_int32 * max(kv, 1))()
+    grp = (ctypes.c_int32 * max(kv, 1))()
+    n, ng, pad = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check(lib().spconv_group_plan_counts(arr, kv, int(centre), float(epsilon), float(S), kv, offs, grp,
+                                          ctypes.byref(n), ctypes.byref(ng), ctypes.byref(pad)))
     return list(offs[:n.value]), list(grp[:n.value]), ng.value, pad.value
 
 
@@ -568,6 +586,16 @@ def group_plan(kmap: SpconvMap, epsilon: float, S: float):
     ``kmap``, in execution order (a list of lists of offset indices), and the
     rows of the padded batches."""
     offs, grp, ng, pad = spconv_group_plan(kmap.handle, epsilon, S, kmap.kernel_volume)
+    groups = [[] for _ in range(ng)]
+    for k, g in zip(offs, grp):
+        groups[g].append(k)
+    return groups, pad
+
+
+def group_plan_counts(counts, epsilon: float, S: float, centre: Optional[int] = None):
+    """The groups (a list of lists of offset indices, in execution order) and
+    padded rows of the adaptive grouping over per-offset map sizes."""
+    offs, grp, ng, pad = spconv_group_plan_counts(counts, epsilon, S, -1 if centre is None else centre)
     groups = [[] for _ in range(ng)]
     for k, g in zip(offs, grp):
         groups[g].append(k)

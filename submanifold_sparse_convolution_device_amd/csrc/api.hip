@@ -1077,15 +1077,27 @@ spconv_status spconv_map_out_coords(const spconv_map* map, const int32_t** d_out
   return SPCONV_OK;
 }
 
-spconv_status spconv_group_plan(spconv_map* map, double epsilon, double S, int32_t capacity, int32_t* h_offsets,
-                                int32_t* h_groups, int32_t* n_entries, int32_t* n_groups, int64_t* padded_rows) {
+spconv_status spconv_group_plan_counts(const int64_t* h_counts, int32_t kernel_volume, int32_t centre,
+                                       double epsilon, double S, int32_t capacity, int32_t* h_offsets,
+                                       int32_t* h_groups, int32_t* n_entries, int32_t* n_groups,
+                                       int64_t* padded_rows) {
   g_last_error.clear();
-  if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
+  if (h_counts == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "h_counts is NULL");
+  if (kernel_volume < 1 || kernel_volume > spconv::kMaxGroupEntries) {
+    return fail(SPCONV_ERR_INVALID_ARG, "kernel_volume = %d not in [1, %d]", kernel_volume,
+                spconv::kMaxGroupEntries);
+  }
+  if (centre < -1 || centre >= kernel_volume) {
+    return fail(SPCONV_ERR_INVALID_ARG, "centre = %d not in [-1, %d)", centre, kernel_volume);
+  }
+  for (int32_t k = 0; k < kernel_volume; ++k) {
+    if (h_counts[k] < 0 || h_counts[k] >= (int64_t(1) << 40)) {
+      return fail(SPCONV_ERR_INVALID_ARG, "count %lld of offset %d not in [0, 2^40)", (long long)h_counts[k], k);
+    }
+  }
   spconv_status st = check_plan_args(epsilon, S);
   if (st != SPCONV_OK) return st;
-  st = finish_build(map);
-  if (st != SPCONV_OK) return st;
-  const spconv::GroupPlan plan = spconv::make_group_plan(map->counts.data(), map->KV, map->centre, epsilon, S);
+  const spconv::GroupPlan plan = spconv::make_group_plan(h_counts, kernel_volume, centre, epsilon, S);
   const int32_t n = static_cast<int32_t>(plan.entries.size());
   if ((h_offsets != nullptr || h_groups != nullptr) && capacity < n) {
     return fail(SPCONV_ERR_INVALID_ARG, "capacity %d below the plan's %d entries", capacity, n);
@@ -1098,6 +1110,18 @@ spconv_status spconv_group_plan(spconv_map* map, double epsilon, double S, int32
   if (n_groups) *n_groups = plan.groups;
   if (padded_rows) *padded_rows = plan.padded_rows;
   return SPCONV_OK;
+}
+
+spconv_status spconv_group_plan(spconv_map* map, double epsilon, double S, int32_t capacity, int32_t* h_offsets,
+                                int32_t* h_groups, int32_t* n_entries, int32_t* n_groups, int64_t* padded_rows) {
+  g_last_error.clear();
+  if (map == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "map is NULL");
+  spconv_status st = check_plan_args(epsilon, S);
+  if (st != SPCONV_OK) return st;
+  st = finish_build(map);
+  if (st != SPCONV_OK) return st;
+  return spconv_group_plan_counts(map->counts.data(), map->KV, map->centre, epsilon, S, capacity, h_offsets,
+                                  h_groups, n_entries, n_groups, padded_rows);
 }
 
 spconv_status spconv_forward_grouped(const void* d_feats, const void* d_weights, spconv_map* map, int32_t c_in,

@@ -34,6 +34,8 @@
 // (row 4 (l / 16) + i, column l mod 16) sits in accumulator i of lane l.
 #include "internal.h"
 
+#include <cstdlib>
+
 namespace spconv {
 namespace {
 
@@ -602,7 +604,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
     const T* __restrict__ feats, const T* __restrict__ weights, T* __restrict__ out,
     const int32_t* __restrict__ in_idx, const int32_t* __restrict__ tile_off,
     const unsigned long long* __restrict__ tile_mask, const int32_t* __restrict__ tile_rows,
-    const int32_t* __restrict__ perm, int64_t n, int64_t tiles, int KV, int tw) {
+    const int32_t* __restrict__ perm, int64_t n, int64_t tiles, int KV, int tw, int spin_limit) {
   using Sh = SmallShape<T, CIN, COUT>;
   constexpr int CHUNK = Sh::CHUNK, VEC = Sh::VEC, NCH = Sh::NCH, NCB = Sh::NCB, ROWV = Sh::ROWV;
   extern __shared__ uint4 smem4[];
@@ -630,7 +632,9 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
   // half then gathers its own entries instead of the tile taking a second
   // gather round); a lighter one (at least kSplitMin entries, and only when
   // its owner has no later tile) is shared: the spare computes its upper
-  // half from the owner's stage once the owner flags it filled.
+  // half from the owner's stage once the owner flags it filled.  That wait is
+  // bounded (spin_limit sleeps): a spare still waiting then gathers its half
+  // tile itself, as for a heavy tile, so no wave's progress rests on another's.
   int* s_tile = reinterpret_cast<int*>(wl + static_cast<size_t>(KV) * NCB * NCH * 64 +
                                        static_cast<size_t>(nw) * ROWV * kStageStride);
   int* s_weight = s_tile + kSmallWaves;
@@ -788,14 +792,30 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
       }
     }
     for (int s0 = 0; s0 < tm.total; s0 += kStageEntries) {
-      const int s1 = (tm.total - s0 < kStageEntries) ? tm.total : s0 + kStageEntries;
+      int s1 = (tm.total - s0 < kStageEntries) ? tm.total : s0 + kStageEntries;
       if (shared_from >= 0) {
-        // the owner's stage: wait until its owner has filled it
-        while (__hip_atomic_load(&s_ready[shared_from], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) !=
-               static_cast<int>(t)) {
+        // the owner's stage: wait until its owner has filled it (the flag is
+        // read into a scalar, so the loop is wave-uniform); spin_limit < 0
+        // skips the wait
+        bool ready = false;
+        for (int spins = 0; spin_limit >= 0; ++spins) {
+          ready = __builtin_amdgcn_readfirstlane(__hip_atomic_load(&s_ready[shared_from], __ATOMIC_ACQUIRE,
+                                                                   __HIP_MEMORY_SCOPE_WORKGROUP)) ==
+                  static_cast<int>(t);
+          if (ready || spins >= spin_limit) break;
           __builtin_amdgcn_s_sleep(1);
         }
-      } else {
+        if (!ready) {
+          // gather the upper half itself, into its own stage: one stage
+          // holds it (the owner's whole tile fitted one, s0 = 0)
+          shared_from = -1;
+          stage_g = stage + g * kStageStride;
+          tm = window_meta(mk_full, lok_full, row_lo, row_hi, KV, centre, lane);
+          issue_first();
+          s1 = tm.total;
+        }
+      }
+      if (shared_from < 0) {
         wave_lds_sync();  // earlier reads of the stage are done
         commit_stage<ROWV>(stage, rows, lane);
         wave_lds_sync();
@@ -858,6 +878,20 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
   }
 }
 
+// Sleeps a spare wave waits for its owner's stage before gathering its rows
+// itself (s_sleep 1 is 64 clocks: about 1.7 ms in all, far beyond the few
+// microseconds an owner takes to fill its stage).  The environment variable
+// SPCONV_SMALL_SPIN_LIMIT overrides it at each launch (-1: never wait), for
+// tests that run the fallback.
+int small_spin_limit() {
+  int limit = 1 << 16;
+  if (const char* v = std::getenv("SPCONV_SMALL_SPIN_LIMIT")) {
+    const long x = std::strtol(v, nullptr, 10);
+    if (x >= -1 && x <= (1 << 24)) limit = static_cast<int>(x);
+  }
+  return limit;
+}
+
 int device_cu_count() {
   static int cus = 0;
   if (cus == 0) {
@@ -899,7 +933,7 @@ hipError_t launch_small(const ForwardArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((k_forward_small<T, CIN, COUT>), dim3(grid), dim3(static_cast<unsigned>(waves) * 64), lds, stream,
                      static_cast<const T*>(a.feats), static_cast<const T*>(a.weights),
                      static_cast<T*>(a.out), a.in_idx, a.tile_off, a.tile_mask, a.tile_rows, a.perm, a.n,
-                     a.tiles, a.KV, static_cast<int>(tw));
+                     a.tiles, a.KV, static_cast<int>(tw), small_spin_limit());
   return hipGetLastError();
 }
 

@@ -796,6 +796,39 @@ def test_forward_single_voxel_and_isolated(sp):
     _forward_check(sp, _gpu_map(sp, iso, 3), iso, 3, 32, 16, "bf16", seed=2)
 
 
+@pytest.mark.parametrize("index,seed", [(1, None), (None, 31)])
+def test_forward_small_spare_fallback(sp, monkeypatch, index, seed):
+    """A spare wave of the small-channel forward that shares its owner's
+    stage waits a bounded time, then gathers its half tile itself.  With the
+    wait skipped (SPCONV_SMALL_SPIN_LIMIT = -1) or cut to one check (0), the
+    output is bit-identical to the default one (same products, same order)
+    and matches the oracle: the indoor scene (C = 32 f16, ten owner waves and
+    two spares per workgroup; 2,298 of its 2,344 tiles hold 64 to 128
+    non-centre entries, the range whose upper half a spare shares) and a
+    random grid with shared and heavy tiles (C = 16 f32, one owner and two
+    spares per workgroup)."""
+    if index is not None:
+        layer = _workload(index).layers[0]
+        c, K, cin, cout, dtype = layer.coords, layer.k, layer.cin, layer.cout, layer.dtype
+    else:
+        c, K, cin, cout, dtype = workloads.random_grid(seed, 40, 0.08, 1), 3, 16, 16, "f32"
+    kmap = _gpu_map(sp, c, K)
+    f = workloads.features(c.shape[0], cin, dtype, 5).to(DEV)
+    w = workloads.weights(K, cin, cout, dtype, 6).to(DEV)
+    monkeypatch.delenv("SPCONV_SMALL_SPIN_LIMIT", raising=False)
+    base = sp.forward(f, w, kmap)
+    for limit in ("-1", "0"):
+        monkeypatch.setenv("SPCONV_SMALL_SPIN_LIMIT", limit)
+        got = sp.forward(f, w, kmap)
+        torch.cuda.synchronize()
+        assert torch.equal(got, base), f"limit {limit}"
+    monkeypatch.delenv("SPCONV_SMALL_SPIN_LIMIT")
+    ref = oracle.build_map(c, K).forward(f.double().cpu().numpy(), w.double().cpu().numpy())
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    diff = np.abs(base.double().cpu().numpy() - ref)
+    assert np.all(diff <= TOL[dtype] * rms + HALF_ULP[dtype] * np.abs(ref))
+
+
 def test_forward_is_repeatable_and_overwrites(sp):
     c = workloads.random_grid(23, 16, 0.2, 1)
     kmap = _gpu_map(sp, c, 3)
