@@ -1051,17 +1051,42 @@ int grid_for(int64_t work, int per_block, int cap) {
 // batch of kAllBatch lookups issues its preferred-slot loads together.
 constexpr int kAllBatch = 8;
 constexpr int kAllFlagWords = 4;  // K <= 5: K^3 <= 125 offsets
+template <int K>
 __global__ __launch_bounds__(256) void k_probe_all(const int4* __restrict__ qc, int64_t nq,
                                                    const ulonglong2* __restrict__ table,
-                                                   unsigned long long window_mask, int K, int lo, int s, int mode,
+                                                   unsigned long long window_mask, int lo, int s, int mode,
                                                    int32_t* __restrict__ nbr, uint32_t* __restrict__ flags,
                                                    long long* summary) {
+  constexpr int KV = K * K * K;
   const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (q >= nq) return;
   const int4 c = qc[q];
-  const int KV = K * K * K;
+  // Per axis, the coordinate each kernel component probes (-1: none): the
+  // offsets combine one component per axis, so the divisions run K times per
+  // axis instead of once per offset.
+  int tq[3][K];
+  {
+    const int p[3] = {c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+#pragma unroll
+      for (int dd = 0; dd < K; ++dd) {
+        const int d = dd + lo;
+        int t;
+        if (mode == 0) {
+          t = s * p[i] + d;
+          t = (t >= 0 && t < 65536) ? t : -1;
+        } else {
+          const int v = p[i] - d;
+          t = (v >= 0 && v % s == 0) ? v / s : -1;
+        }
+        tq[i][dd] = t;
+      }
+    }
+  }
   uint32_t fw[kAllFlagWords] = {0u, 0u, 0u, 0u};
   bool overflow = false;
+#pragma unroll
   for (int k0 = 0; k0 < KV; k0 += kAllBatch) {
     unsigned long long key[kAllBatch];
     bool ok[kAllBatch];
@@ -1069,23 +1094,14 @@ __global__ __launch_bounds__(256) void k_probe_all(const int4* __restrict__ qc, 
 #pragma unroll
     for (int j = 0; j < kAllBatch; ++j) {
       const int k = k0 + j;
-      const int d[3] = {k / (K * K) + lo, (k / K) % K + lo, k % K + lo};
-      const int p[3] = {c.y, c.z, c.w};
-      int t[3];
-      bool good = k < KV;
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        if (mode == 0) {
-          t[i] = s * p[i] + d[i];
-          good = good && t[i] >= 0 && t[i] < 65536;
-        } else {
-          const int v = p[i] - d[i];
-          t[i] = v >= 0 ? v / s : -1;
-          good = good && v >= 0 && v % s == 0;
-        }
+      if (k < KV) {
+        const int tz = tq[0][k / (K * K)], ty = tq[1][(k / K) % K], tx = tq[2][k % K];
+        ok[j] = tz >= 0 && ty >= 0 && tx >= 0;
+        key[j] = ok[j] ? pack_key(c.x, tz, ty, tx) : kEmptyKey;
+      } else {
+        ok[j] = false;
+        key[j] = kEmptyKey;
       }
-      ok[j] = good;
-      key[j] = good ? pack_key(c.x, t[0], t[1], t[2]) : kEmptyKey;
     }
 #pragma unroll
     for (int j = 0; j < kAllBatch; ++j) {
@@ -1095,17 +1111,18 @@ __global__ __launch_bounds__(256) void k_probe_all(const int4* __restrict__ qc, 
 #pragma unroll
     for (int j = 0; j < kAllBatch; ++j) {
       const int k = k0 + j;
-      if (k >= KV) break;
-      int64_t row = -1;
-      if (ok[j]) {
-        if (e[j].x == key[j]) {
-          row = static_cast<int64_t>(static_cast<uint32_t>(e[j].y));
-        } else if (e[j].x != kEmptyKey && ((e[j].y >> 32) & kSlotDisplaced) != 0ull) {
-          row = find_row_scan(key[j], table, window_mask, overflow);
+      if (k < KV) {
+        int64_t row = -1;
+        if (ok[j]) {
+          if (e[j].x == key[j]) {
+            row = static_cast<int64_t>(static_cast<uint32_t>(e[j].y));
+          } else if (e[j].x != kEmptyKey && ((e[j].y >> 32) & kSlotDisplaced) != 0ull) {
+            row = find_row_scan(key[j], table, window_mask, overflow);
+          }
         }
+        nbr[static_cast<int64_t>(k) * nq + q] = static_cast<int32_t>(row);
+        if (row >= 0) fw[k >> 5] |= 1u << (k & 31);
       }
-      nbr[static_cast<int64_t>(k) * nq + q] = static_cast<int32_t>(row);
-      if (row >= 0) fw[k >> 5] |= 1u << (k & 31);
     }
   }
 #pragma unroll
@@ -1367,9 +1384,34 @@ int64_t table_slots_for(int64_t n) {
 hipError_t launch_general_map(const GeneralMapArgs& g, hipStream_t stream) {
   if (g.nq <= 0) return hipSuccess;
   const unsigned long long window_mask = static_cast<unsigned long long>(g.table_slots / kWindowSlots) - 1ull;
-  hipLaunchKernelGGL(k_probe_all, dim3(static_cast<unsigned>((g.nq + 255) / 256)), dim3(256), 0, stream,
-                     reinterpret_cast<const int4*>(g.qcoords), g.nq, g.table, window_mask, g.K, g.lo, g.stride,
-                     g.mode, g.nbr, g.flags, g.summary);
+  {
+    const dim3 grid(static_cast<unsigned>((g.nq + 255) / 256));
+    const int4* qc = reinterpret_cast<const int4*>(g.qcoords);
+    switch (g.K) {
+      case 1:
+        hipLaunchKernelGGL(k_probe_all<1>, grid, dim3(256), 0, stream, qc, g.nq, g.table, window_mask, g.lo, g.stride,
+                           g.mode, g.nbr, g.flags, g.summary);
+        break;
+      case 2:
+        hipLaunchKernelGGL(k_probe_all<2>, grid, dim3(256), 0, stream, qc, g.nq, g.table, window_mask, g.lo, g.stride,
+                           g.mode, g.nbr, g.flags, g.summary);
+        break;
+      case 3:
+        hipLaunchKernelGGL(k_probe_all<3>, grid, dim3(256), 0, stream, qc, g.nq, g.table, window_mask, g.lo, g.stride,
+                           g.mode, g.nbr, g.flags, g.summary);
+        break;
+      case 4:
+        hipLaunchKernelGGL(k_probe_all<4>, grid, dim3(256), 0, stream, qc, g.nq, g.table, window_mask, g.lo, g.stride,
+                           g.mode, g.nbr, g.flags, g.summary);
+        break;
+      case 5:
+        hipLaunchKernelGGL(k_probe_all<5>, grid, dim3(256), 0, stream, qc, g.nq, g.table, window_mask, g.lo, g.stride,
+                           g.mode, g.nbr, g.flags, g.summary);
+        break;
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
   const int64_t tiles = (g.nq + kTileRows - 1) / kTileRows;
   const int64_t groups = (tiles + kGroupTiles - 1) / kGroupTiles;
   const int KV = g.K * g.K * g.K;

@@ -158,6 +158,22 @@ def test_batched_frames_downsampled(sp):
     _check_out(got, ref.forward_parallel(f.double().numpy(), w.double().numpy()), "bf16")
 
 
+@pytest.mark.parametrize("K,s", [(3, 2), (2, 2), (5, 1)])
+def test_widest_output_keys(sp, K, s):
+    """Inputs at both ends of every coordinate range (b up to 2^15 - 1,
+    z, y, x up to 2^16 - 1): the output keys need all their bits (every
+    radix pass runs), and the map still equals the oracle's."""
+    rng = np.random.default_rng(900 + K + s)
+    lo = np.array([[0, 0, 0, 0]], np.int64) + rng.integers(0, 3, size=(12, 4))
+    hi = np.array([[32767, 65535, 65535, 65535]], np.int64) - rng.integers(0, 3, size=(12, 4))
+    c = np.unique(np.concatenate([lo, hi]), axis=0).astype(np.int32)
+    c = workloads.permuted(c, 5)
+    ref = oracle.build_map_strided(c, K, s)
+    kmap = sp.build_map_strided(_coords(c), K, s)
+    _assert_map(kmap, ref)
+    _assert_map(kmap.transpose(), ref.transpose())
+
+
 def test_no_outputs(sp):
     """A 1^3 kernel at stride 2 sees only inputs at even coordinates: with
     none, the map has no outputs; its forward writes nothing, its transpose's
