@@ -104,6 +104,7 @@ def roofline_of(flops, nbytes, fwd_ms, dtype, traffic=None):
 # the profile and the kernel sources whose sha256 it was taken on.
 TRAFFIC_PROFILES = {
     (4, 0): ("k_forward_wide_batch8_k3_c128_bf16_hbm_traffic.md", ("forward_wide.hip", "forward_tiled.hip")),
+    (4, 1): ("k_forward_wide_batch8_k5_c64_bf16_hbm_traffic.md", ("forward_wide.hip", "forward_tiled.hip")),
     (1, 0): ("k_forward_small_indoor_c32_f16_hbm_traffic.md", ("forward.hip",)),
 }
 
@@ -369,12 +370,81 @@ def measure(torch, sp, layer, steps, warmup, events_wanted=10):
     assert retire(prev) == e_total
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # The whole synchronous build call (kernels and the one summary read-back)
+    # by the host clock, median of ten after the steps above warmed it.
+    calls = []
+    for _ in range(10):
+        c0 = time.perf_counter()
+        kmap = sp.build_map(coords, layer.k)
+        calls.append((time.perf_counter() - c0) * 1e3)
+        kmap.free()
+    torch.cuda.synchronize()
     return {
+        "build_call_ms": float(np.median(calls)),
         "ms_step": (t1 - t0) * 1e3 / steps,
         "build_ms": float(np.mean([ev[0].elapsed_time(ev[1]) for ev in events.values()])),
         "fwd_ms": float(np.mean([ev[1].elapsed_time(ev[2]) for ev in events.values()])),
         "e_total": e_total,
         "coords": coords, "feats": feats, "w": w, "feats_h": feats_h, "w_h": w_h,
+    }
+
+
+def build_roofline(n, e, k, build_ms):
+    """Roofline of one map build by the survey's byte model per voxel: 16
+    (coordinates) + 12 (insert: key and value) + 12 per probe of the
+    (K^3 - 1) / 2 half offsets + 8 per non-centre entry written; beside it
+    the line-granular bound, a 64-byte line per random probe.  Integer work:
+    the ceiling is HBM bandwidth."""
+    half = (k ** 3 - 1) // 2
+    per_voxel = 16 + 12 + 12 * half + 8 * (e / n - 1)
+    per_voxel_lines = 16 + 12 + 64 * half + 8 * (e / n - 1)
+    t = build_ms * 1e-3
+    gbs = n * per_voxel / t / 1e9
+    return {
+        "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_voxel": round(per_voxel, 1),
+        "frac_line_granular": round(n * per_voxel_lines / t / 1e9 / HBM_PEAK_GBS, 4),
+        "bytes_per_voxel_line_granular": round(per_voxel_lines, 1),
+        "time_at_roofline_us": round(n * per_voxel / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+    }
+
+
+def measure_ceilings(torch, reps=10):
+    """The chip's ceilings as measured here: a 1 GiB device-to-device copy
+    (read + write bytes per second) and a dense 8192^3 bf16 matrix product
+    (PyTorch's library GEMM), each the median of `reps` HIP event pairs."""
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+
+    def events(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    src = torch.empty(1 << 29, dtype=torch.float16, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    t_copy = events(lambda: dst.copy_(src))
+    del src, dst
+    m = 8192
+    x = torch.randn((m, m), device=dev).to(torch.bfloat16)
+    y = torch.randn((m, m), device=dev).to(torch.bfloat16)
+    t_mm = events(lambda: torch.matmul(x, y))
+    del x, y
+    return {
+        "hbm_copy_gbs": round(2 * (1 << 30) / (t_copy * 1e-3) / 1e9, 1),
+        "bf16_gemm_tflops": round(2 * m ** 3 / (t_mm * 1e-3) / 1e12, 1),
+        "note": "device copy of 1 GiB (read + write) and an 8192^3 bf16 GEMM, median of HIP event pairs",
     }
 
 
@@ -596,6 +666,8 @@ def layer_summary(wl, layer, li, r, traffic):
         "value": round(flops / (r["ms_step"] * 1e-3) / 1e12, 4),
         "map_build_ms": round(r["build_ms"], 4),
         "map_build_mvoxel_per_s": round(layer.n / (r["build_ms"] * 1e-3) / 1e6, 2),
+        "map_build_call_ms": round(r["build_call_ms"], 4),
+        "map_build_roofline": build_roofline(layer.n, r["e_total"], layer.k, r["build_ms"]),
         "forward_ms": round(r["fwd_ms"], 4),
         "forward_tflops": round(flops / (r["fwd_ms"] * 1e-3) / 1e12, 4),
         "roofline": roofline(layer, r["e_total"], r["fwd_ms"], traffic),
@@ -611,6 +683,7 @@ def main(argv=None):
                     help="workload index 0..4 (default: the 8 batched LiDAR frames)")
     ap.add_argument("--layer", type=int, default=DEFAULT_LAYER, help="layer of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip measuring the copy and GEMM ceilings")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra layers reported beside the default one")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the two gradients")
@@ -677,6 +750,8 @@ def main(argv=None):
         },
         "map_build_mvoxel_per_s": summary["map_build_mvoxel_per_s"],
         "map_build_ms": summary["map_build_ms"],
+        "map_build_call_ms": summary["map_build_call_ms"],
+        "map_build_roofline": summary["map_build_roofline"],
         "forward_ms": summary["forward_ms"],
         "forward_tflops": summary["forward_tflops"],
         "roofline": rl,
@@ -713,6 +788,16 @@ def main(argv=None):
             extra.append(layer_summary(xwl, xl, li, xr, recorded_traffic(wi, li)))
             del xr
         result["other_layers"] = extra
+    if not args.no_ceilings:
+        c = measure_ceilings(torch)
+        fwd_s = summary["forward_ms"] * 1e-3
+        nbytes = rl["algorithmic_bytes_per_launch"]
+        c["forward_frac_of_measured"] = round(min(
+            1.0, max(flops / fwd_s / 1e12 / c["bf16_gemm_tflops"], nbytes / fwd_s / 1e9 / c["hbm_copy_gbs"])), 4) \
+            if layer.dtype != "f32" else None
+        c["forward_mfma_frac_of_measured"] = round(flops / fwd_s / 1e12 / c["bf16_gemm_tflops"], 4)
+        c["forward_hbm_frac_of_measured"] = round(nbytes / fwd_s / 1e9 / c["hbm_copy_gbs"], 4)
+        result["ceilings_measured"] = c
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(layer, *main_inputs)
