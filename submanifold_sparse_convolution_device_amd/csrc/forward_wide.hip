@@ -16,8 +16,10 @@
 // The task walks the offsets that occur in its rows.  Per offset d:
 //   * the gathered input rows of the task's blocks (B operands, zero for
 //     rows without a neighbour at d) are copied from global memory straight
-//     into LDS (global_load_lds: lane l of a load writes 16 bytes at l x 16),
-//     whole rows per copy, shared by all waves of the workgroup;
+//     into LDS (buffer loads to LDS: lane l of a load writes 16 bytes at
+//     l x 16; a row without a neighbour reads past the buffer's end, where
+//     the load's bounds check returns zeros), whole rows per copy, shared by
+//     all waves of the workgroup;
 //   * each wave keeps its slice of W_d (A operands, from a copy of the weights
 //     in operand order) in registers and applies it to every block present;
 // and the work is software-pipelined: while offset i runs on MFMA, the
@@ -178,21 +180,28 @@ __device__ __forceinline__ int seg_swizzle(int i) {
   return (i / RP) & ((SEG < 16 ? SEG : 16) - 1);
 }
 
+// Buffer resource word 3 for raw 32-bit-element loads (gfx9 data format 32,
+// no swizzle): the bounds check then compares each byte offset with the
+// record count, the buffer's size in bytes.
+constexpr int kBufferWord3 = 0x00020000;
+// Largest feature buffer the row copies address (see wide_supported).
+constexpr int64_t kWideMaxFeatureBytes = (int64_t{1} << 32) - 4096;
+
 // Per-offset state the pipeline carries: the offset, and for each of the
 // (up to) two tiles its row mask and first list position (wave-uniform).
 struct OffsetRef {
   int k;
   unsigned long long m0, m1;
   int lo0, lo1;
+  uint32_t pm;  // bit b: 16-row block b has at least one entry
 };
 
 template <typename T, int CIN, int TB, int NCB, int NW>
 __global__ __launch_bounds__(64 * NW) void k_forward_wide(
     const uint16_t* __restrict__ feats_raw, const uint4* __restrict__ wop, T* __restrict__ out,
     const int32_t* __restrict__ in_idx, const int32_t* __restrict__ tile_off,
-    const unsigned long long* __restrict__ tile_mask, const uint4* __restrict__ zero_row,
-    const int32_t* __restrict__ perm, int64_t n, int64_t tiles, int64_t tasks, int groups, int splits,
-    float* __restrict__ part, int KV, int cout, int centre_k) {
+    const unsigned long long* __restrict__ tile_mask, const int32_t* __restrict__ perm, int64_t n, int64_t n_in,
+    int64_t tiles, int64_t tasks, int groups, int splits, float* __restrict__ part, int KV, int cout, int centre_k) {
   using Sh = WideShape<CIN, TB, NCB, NW>;
   constexpr int NCH = Sh::NCH, BPW = Sh::BPW, TPT = Sh::TPT;
   constexpr int SEG = Sh::SEG, RPI = Sh::RPI, IPB = Sh::IPB, RP = Sh::RP, BLOCK_BYTES = Sh::BLOCK_BYTES;
@@ -239,21 +248,30 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
   unsigned long long todo0 = __ballot((mA0 | mA1) != 0ull), todo1 = __ballot((mB0 | mB1) != 0ull);
   // With splits > 1 the task's offsets are dealt round-robin over the
   // splits workgroups of the unit, each summing its share into its own fp32
-  // partial output; offsets of other shares are skipped here.
-  // (splits is a power of two.)
-  int seen = 0;
-  const int share_u = __builtin_amdgcn_readfirstlane(share);
-  const int smask = __builtin_amdgcn_readfirstlane(splits - 1);
+  // partial output: the share's offsets are picked out of the task's once,
+  // here.  (splits is a power of two.)
+  if (splits > 1) {
+    const int share_u = __builtin_amdgcn_readfirstlane(share);
+    const int smask = __builtin_amdgcn_readfirstlane(splits - 1);
+    unsigned long long keep0 = 0ull, keep1 = 0ull;
+    int seen = 0;
+    for (unsigned long long t = todo0; t != 0ull; t &= t - 1ull)
+      if ((seen++ & smask) == share_u) keep0 |= t & (~t + 1ull);
+    for (unsigned long long t = todo1; t != 0ull; t &= t - 1ull)
+      if ((seen++ & smask) == share_u) keep1 |= t & (~t + 1ull);
+    todo0 = keep0;
+    todo1 = keep1;
+  }
   auto pick = [&](unsigned long long& todo, int base) -> int {
-    while (todo != 0ull) {
-      const int kk = base + __ffsll(static_cast<long long>(todo)) - 1;
-      todo &= todo - 1ull;
-      if ((seen++ & smask) == share_u) return kk;
-    }
-    return -1;
+    if (todo == 0ull) return -1;
+    const int kk = base + __ffsll(static_cast<long long>(todo)) - 1;
+    todo &= todo - 1ull;
+    return kk;
   };
+  // The next offset's state; pm, the blocks present, is computed here once
+  // for the tests around that offset's MFMA groups and row copies.
   auto next_ref = [&]() -> OffsetRef {
-    OffsetRef o{-1, 0ull, 0ull, 0, 0};
+    OffsetRef o{-1, 0ull, 0ull, 0, 0, 0u};
     int k = pick(todo0, 0);
     if (k < 0) k = pick(todo1, 64);
     if (k >= 0) {
@@ -263,13 +281,13 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
       o.m1 = lane_u64(k < 64 ? mA1 : mB1, s);
       o.lo0 = lane_i32(k < 64 ? lA0 : lB0, s);
       o.lo1 = lane_i32(k < 64 ? lA1 : lB1, s);
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        const unsigned long long m = (b < 4) ? o.m0 : o.m1;
+        if (((m >> (16 * (b & 3))) & 0xffffull) != 0ull) o.pm |= 1u << b;
+      }
     }
     return o;
-  };
-  // Row mask of block b (16 bits) at offset o.
-  auto block_bits = [&](const OffsetRef& o, int b) -> unsigned long long {
-    const unsigned long long m = (b < 4) ? o.m0 : o.m1;
-    return (m >> (16 * (b & 3))) & 0xffffull;
   };
 
   // The loads that prepare an offset, one at a time so that they can be
@@ -299,8 +317,11 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
   //   Row copy j (< BPW x IPB): rows [RPI q, RPI q + RPI) of staged block
   //     jj (q = j % IPB, jj = j / IPB), whole rows, from global memory
   //     straight into B stage `buf`: lane l copies segment (l % SEG) ^ swizzle
-  //     of row RPI q + l / SEG, whose input row is srow[j] (-1: a zero row).
-  //     A block with no entry at the offset is skipped (its MFMAs are too).
+  //     of row RPI q + l / SEG, whose input row is srow[j] (-1: no entry;
+  //     its byte offset wraps to just below 2^32, past the end of the
+  //     features, whose size the host keeps below that, so the load returns
+  //     zeros).  A block with no entry at the offset is skipped (its MFMAs
+  //     are too).
   //     srow comes from copy_rows, which moves the index of row i from lane
   //     i of idx (a cross-lane read, done before the MFMAs start, where its
   //     wait costs nothing).
@@ -313,18 +334,17 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
 #pragma unroll
     for (int j = 0; j < Sh::LOADS_B; ++j) asm volatile("" : "+v"(srow[j]));
   };
+  const __amdgpu_buffer_rsrc_t frsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(feats_raw), 0, static_cast<int>(static_cast<uint32_t>(n_in * CIN * 2)), kBufferWord3);
   auto stage_b_one = [&](const OffsetRef& o, int buf, const int32_t (&srow)[Sh::LOADS_B], int j) {
     const int jj = j / IPB, q = j % IPB;
     const int b = wave + NW * jj;
-    if (block_bits(o, b) == 0ull) return;  // wave-uniform
+    if (((o.pm >> b) & 1u) == 0u) return;  // wave-uniform
     const int i = RPI * q + lane / SEG;
     const int c = (lane % SEG) ^ seg_swizzle<SEG, RP>(i);
-    const int32_t src_row = srow[j];
-    const void* src = (src_row >= 0)
-                          ? static_cast<const void*>(feats_raw + static_cast<int64_t>(src_row) * CIN + c * 8)
-                          : static_cast<const void*>(zero_row + c);
+    const uint32_t voff = static_cast<uint32_t>(srow[j]) * (CIN * 2u) + static_cast<uint32_t>(c) * 16u;
     uint4* dst = bstage + ((buf * TB + b) * BLOCK_BYTES + q * RPI * SEG * 16) / 16;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(frsrc, (lds_void*)dst, 16, static_cast<int>(voff), 0, 0, 0);
   };
   //   Weight load j (< NCB x NCH): this wave's slice of W_k in operand order.
   const int ncbg = cout / 16;
@@ -351,11 +371,7 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
   // MFMA groups of the blocks, where they issue while the matrix core is
   // busy instead of stalling the wave before the offset starts.
   auto run = [&](const OffsetRef& o, int buf, const uint4 (&a)[NCB][NCH], auto&& load) {
-    uint32_t pm = 0u;  // blocks with at least one entry
-#pragma unroll
-    for (int b = 0; b < TB; ++b)
-      if (block_bits(o, b) != 0ull) pm |= 1u << b;
-    pm = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(pm)));
+    const uint32_t pm = o.pm;
     constexpr int kSlots = NCH * TB;
     // Lane (g, r) reads row r, segment 4 ch + g (swizzled) of each block;
     // chunk ch + 1's reads are in flight while chunk ch runs on MFMA, the
@@ -474,8 +490,7 @@ __global__ __launch_bounds__(256) void k_reduce_splits(const float* __restrict__
 }
 
 template <typename T, int CIN, int TB, int NCB, int NW>
-hipError_t launch_wide_shape(const ForwardArgs& a, int splits, const uint4* wop, const uint4* zero_row,
-                             float* part, hipStream_t stream) {
+hipError_t launch_wide_shape(const ForwardArgs& a, int splits, const uint4* wop, float* part, hipStream_t stream) {
   using Sh = WideShape<CIN, TB, NCB, NW>;
   const int64_t tasks = (a.tiles + Sh::TPT - 1) / Sh::TPT;
   const int groups = a.cout / Sh::COLS;
@@ -490,7 +505,7 @@ hipError_t launch_wide_shape(const ForwardArgs& a, int splits, const uint4* wop,
   const int64_t grid = (tasks * groups * splits + 7) / 8 * 8;
   hipLaunchKernelGGL((k_forward_wide<T, CIN, TB, NCB, NW>), dim3(static_cast<unsigned>(grid)), dim3(64 * NW),
                      Sh::lds_bytes(), stream, static_cast<const uint16_t*>(a.feats), wop, static_cast<T*>(a.out),
-                     a.in_idx, a.tile_off, a.tile_mask, zero_row, a.perm, a.n, a.tiles, tasks, groups, splits, part,
+                     a.in_idx, a.tile_off, a.tile_mask, a.perm, a.n, a.n_in, a.tiles, tasks, groups, splits, part,
                      a.KV, a.cout, a.centre);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
@@ -561,20 +576,20 @@ bool choose_wide(const ForwardArgs& a, WideChoice* out) {
 }
 
 template <typename T, int CIN, int NCB>
-hipError_t launch_wide_cin(const ForwardArgs& a, const WideChoice& c, const uint4* wop, const uint4* zero_row,
-                           float* part, hipStream_t stream) {
+hipError_t launch_wide_cin(const ForwardArgs& a, const WideChoice& c, const uint4* wop, float* part,
+                           hipStream_t stream) {
   if (c.tb != 4) return hipErrorNotSupported;
-  if (c.nw == 4) return launch_wide_shape<T, CIN, 4, NCB, 4>(a, c.splits, wop, zero_row, part, stream);
-  if (c.nw == 2) return launch_wide_shape<T, CIN, 4, NCB, 2>(a, c.splits, wop, zero_row, part, stream);
-  return launch_wide_shape<T, CIN, 4, NCB, 1>(a, c.splits, wop, zero_row, part, stream);
+  if (c.nw == 4) return launch_wide_shape<T, CIN, 4, NCB, 4>(a, c.splits, wop, part, stream);
+  if (c.nw == 2) return launch_wide_shape<T, CIN, 4, NCB, 2>(a, c.splits, wop, part, stream);
+  return launch_wide_shape<T, CIN, 4, NCB, 1>(a, c.splits, wop, part, stream);
 }
 
 template <typename T>
-hipError_t launch_wide_typed(const ForwardArgs& a, const WideChoice& c, const uint4* wop, const uint4* zero_row,
-                             float* part, hipStream_t stream) {
-  if (a.cin == 64) return launch_wide_cin<T, 64, 2>(a, c, wop, zero_row, part, stream);
-  if (a.cin == 128) return launch_wide_cin<T, 128, 4>(a, c, wop, zero_row, part, stream);
-  return launch_wide_cin<T, 256, 2>(a, c, wop, zero_row, part, stream);
+hipError_t launch_wide_typed(const ForwardArgs& a, const WideChoice& c, const uint4* wop, float* part,
+                             hipStream_t stream) {
+  if (a.cin == 64) return launch_wide_cin<T, 64, 2>(a, c, wop, part, stream);
+  if (a.cin == 128) return launch_wide_cin<T, 128, 4>(a, c, wop, part, stream);
+  return launch_wide_cin<T, 256, 2>(a, c, wop, part, stream);
 }
 
 }  // namespace
@@ -583,6 +598,9 @@ bool wide_supported(const ForwardArgs& a) {
   if (a.dtype != 1 && a.dtype != 2) return false;
   if (a.KV > 128) return false;
   if (a.cin != 64 && a.cin != 128 && a.cin != 256) return false;
+  // Row copies address the features with 32-bit byte offsets, and a missing
+  // row's offset (just below 2^32) must stay past their end.
+  if (a.n_in * a.cin * 2 > kWideMaxFeatureBytes) return false;
   WideChoice c;
   return choose_wide(a, &c);
 }
@@ -598,10 +616,9 @@ hipError_t launch_forward_wide(const ForwardArgs& a, void* workspace, hipStream_
   WideChoice c;
   if (!choose_wide(a, &c)) return hipErrorNotSupported;
   const uint4* wop = static_cast<const uint4*>(workspace);
-  const uint4* zero_row = workspace_zero_row(a, workspace);
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + tiled_workspace_bytes(a));
-  if (a.dtype == 1) return launch_wide_typed<_Float16>(a, c, wop, zero_row, part, stream);
-  return launch_wide_typed<__bf16>(a, c, wop, zero_row, part, stream);
+  if (a.dtype == 1) return launch_wide_typed<_Float16>(a, c, wop, part, stream);
+  return launch_wide_typed<__bf16>(a, c, wop, part, stream);
 }
 
 }  // namespace spconv

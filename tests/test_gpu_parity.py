@@ -209,6 +209,37 @@ def test_map_and_forward_at_the_size_limit(sp, K, boxes, cin):
     kmap.free()
 
 
+@pytest.mark.parametrize("boxes", [
+    [(0, (256, 256, 255)), (1, (1, 16, 4095))],  # 16,777,200 rows: 2^32 - 4096 feature bytes at C = 128
+    [(0, (256, 256, 256))]])                     # 16 rows more
+def test_forward_wide_feature_bytes_limit(sp, boxes):
+    """The wide path addresses the features with 32-bit byte offsets (a row
+    without an entry wraps to an offset past their end, where the copy reads
+    zeros).  At C = 128 fp16 the first case's features fill the largest
+    buffer that path takes, so the last rows sit just below 2^32 bytes; the
+    second is past it and runs on the next path.  Channel 0 of row p holds
+    1 + p mod 7 (the other channels zero) and the weights are ones, so every
+    output column of row q is the sum of 1 + p mod 7 over q's entries (exact
+    in fp16), from the boxes' closed-form lists."""
+    K, cin = 3, 128
+    n = sum(lz * ly * lx for _, (lz, ly, lx) in boxes)
+    c = box_map.box_rows(boxes, DEV)
+    kmap = sp.build_map(c, K)
+    rowval = torch.arange(n, device=DEV) % 7 + 1
+    f = torch.zeros((n, cin), dtype=torch.float16, device=DEV)
+    f[:, 0] = rowval.to(torch.float16)
+    w = torch.ones((K ** 3, cin, cin), dtype=torch.float16, device=DEV)
+    out = sp.forward(f, w, kmap)
+    del f
+    expect = torch.zeros(n, dtype=torch.int64, device=DEV)
+    for k in range(K ** 3):
+        p, q = box_map.box_list(boxes, K, k, DEV)
+        expect.index_add_(0, q, rowval[p])
+        del p, q
+    assert torch.equal(out, expect.to(torch.float16)[:, None].expand(n, cin))
+    kmap.free()
+
+
 def test_map_device_errors(sp):
     dup = np.array([[0, 1, 2, 3], [0, 5, 5, 5], [0, 1, 2, 3]], np.int32)
     with pytest.raises(sp.SpconvError) as e:
