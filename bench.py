@@ -14,7 +14,9 @@ once this step's work is queued.
 Prints ONE JSON line.  ``value`` is the whole-step effective throughput
 2 |map| C_in C_out / t_step in TFLOP/s (|map| counts real entries only,
 including the centre ones); the map-build rate and the forward-only rate are
-reported beside it.  ``roofline`` describes the fused forward kernel measured
+reported beside it, with the forward alone timed per call and with its
+weights prepared once (spconv_weights_prepare: the weight re-layout out of
+the call).  ``roofline`` describes the fused forward kernel measured
 with HIP events on the stream it runs on (recorded on about ten of the timed
 steps); ``cpu_baseline`` times the CPU oracle on the host.  Beside the step,
 the line reports the two gradients, the strided convolution and its
@@ -37,12 +39,13 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 # The largest configuration that fits one GPU: 8 batched LiDAR frames
-# (640,812 voxels), K=3, C=128, bf16.  Its K=5 C=64 layer and the indoor
-# scene (150k voxels, K=3, C=32, fp16) are timed the same way and reported
-# beside it in the same line.
+# (640,812 voxels), K=3, C=128, bf16.  Its K=5 C=64 layer, the indoor
+# scene (150k voxels, K=3, C=32, fp16) and the U-Net stack's C=256 layer
+# (4,789 voxels, bf16) are timed the same way and reported beside it in the
+# same line.
 DEFAULT_WORKLOAD = 4
 DEFAULT_LAYER = 0
-EXTRA_LAYERS = ((4, 1), (1, 0))
+EXTRA_LAYERS = ((4, 1), (1, 0), (3, 6))
 PERMUTATION_SEED = 7  # the random row order of the permuted pass
 
 ELEM = {"f32": 4, "f16": 2, "bf16": 2}
@@ -379,7 +382,32 @@ def measure(torch, sp, layer, steps, warmup, events_wanted=10):
         calls.append((time.perf_counter() - c0) * 1e3)
         kmap.free()
     torch.cuda.synchronize()
+    # The forward alone on one map, as called per step (weights re-laid out
+    # in the call) and with weights prepared once (spconv_weights_prepare):
+    # HIP event pairs, the two taking turns in rounds of 10 (so that clock
+    # drift meets both alike), median of 40 each.
+    kmap = sp.build_map(coords, layer.k)
+    pw = sp.prepare_weights(w)
+    fwd = {"call": lambda: sp.forward(feats, w, kmap, out=out),
+           "prepared": lambda: sp.forward_prepared(feats, pw, kmap, out=out)}
+    times = {name: [] for name in fwd}
+    for rnd in range(4):
+        for name, fn in fwd.items():
+            for _ in range(2):
+                fn()
+            for _ in range(10):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                b.synchronize()
+                times[name].append(a.elapsed_time(b))
+    alone = {name: float(np.median(ts)) for name, ts in times.items()}
+    pw.free()
+    kmap.free()
+    torch.cuda.synchronize()
     return {
+        "fwd_call_ms": alone["call"], "fwd_prepared_ms": alone["prepared"],
         "build_call_ms": float(np.median(calls)),
         "ms_step": (t1 - t0) * 1e3 / steps,
         "build_ms": float(np.mean([ev[0].elapsed_time(ev[1]) for ev in events.values()])),
@@ -670,6 +698,9 @@ def layer_summary(wl, layer, li, r, traffic):
         "map_build_roofline": build_roofline(layer.n, r["e_total"], layer.k, r["build_ms"]),
         "forward_ms": round(r["fwd_ms"], 4),
         "forward_tflops": round(flops / (r["fwd_ms"] * 1e-3) / 1e12, 4),
+        "forward_alone_ms": round(r["fwd_call_ms"], 4),
+        "forward_prepared_ms": round(r["fwd_prepared_ms"], 4),
+        "forward_prepared_tflops": round(flops / (r["fwd_prepared_ms"] * 1e-3) / 1e12, 4),
         "roofline": roofline(layer, r["e_total"], r["fwd_ms"], traffic),
     }
 
@@ -754,6 +785,9 @@ def main(argv=None):
         "map_build_roofline": summary["map_build_roofline"],
         "forward_ms": summary["forward_ms"],
         "forward_tflops": summary["forward_tflops"],
+        "forward_alone_ms": summary["forward_alone_ms"],
+        "forward_prepared_ms": summary["forward_prepared_ms"],
+        "forward_prepared_tflops": summary["forward_prepared_tflops"],
         "roofline": rl,
     }
     # The same steps with two frames in flight: step i on stream i mod 2, each

@@ -91,6 +91,11 @@ typedef SPCONV_ENUM(spconv_dtype) {
 /* Opaque kernel map.  Owns its device buffers until spconv_map_free. */
 typedef struct spconv_map spconv_map;
 
+/* Opaque copy of one layer's weights, prepared for repeated forwards
+ * (spconv_weights_prepare).  Owns its device buffers until
+ * spconv_weights_free. */
+typedef struct spconv_weights spconv_weights;
+
 /* Kinds of map (spconv_map_geometry). */
 typedef SPCONV_ENUM(spconv_map_kind) {
   SPCONV_MAP_SUBMANIFOLD = 0, /* outputs = inputs (spconv_build_map)            */
@@ -101,7 +106,7 @@ typedef SPCONV_ENUM(spconv_map_kind) {
 /* Version of this ABI (incremented on any incompatible change; 2: lists in
  * the map's row order instead of increasing out_idx; 3: strided and
  * transposed maps, whose input and output rows differ; 4: the grouped
- * dataflow, its plan and the dataflow selector). */
+ * dataflow, its plan and the dataflow selector; 5: prepared weights). */
 int32_t spconv_abi_version(void);
 
 /*
@@ -267,6 +272,49 @@ spconv_status spconv_backward_weights(const void* d_feats, const void* d_grad_ou
 spconv_status spconv_forward_noalloc(const void* d_feats, const void* d_weights, const spconv_map* map,
                                      int32_t c_in, int32_t c_out, spconv_dtype dtype, void* d_out,
                                      void* hip_stream);
+
+/*
+ * Prepares one layer's weights for repeated forwards (spconv_forward_prepared)
+ * with the same weights, as in inference, where a layer's W_d stay fixed over
+ * many calls ("Sparse convolution for point clouds", section "The map and the
+ * update rule": the update applies W_d to every entry of offset d).  The
+ * forward's wide and tiled kernels read W_d in MFMA operand order, a layout
+ * spconv_forward writes into its workspace on every call (one small launch);
+ * here it is written once.
+ *
+ * d_weights: device [kernel_volume][c_in][c_out] of dtype, 16-byte aligned,
+ * only read, and copied: later changes to it do not reach the handle.
+ * kernel_volume: K^3 of the maps the handle will be used with, in [1, 343].
+ * c_in, c_out, dtype: as for spconv_forward.  On SPCONV_OK *out is a handle
+ * that holds a device copy of the weights and, for F16/BF16 with c_in in
+ * {32, 64, 128, 256}, c_out a multiple of 16 and kernel_volume <= 128, the
+ * operand-order copy (the shapes whose forward uses it).  Device memory is
+ * allocated on the current device (which the handle is bound to); the copies
+ * are enqueued on hip_stream (NULL: the legacy default stream), so work on
+ * another stream that uses the handle must be ordered after it.
+ * Errors: INVALID_ARG (NULL pointer, misaligned weights, kernel_volume or
+ * channels out of range), UNSUPPORTED (dtype, channel multiples),
+ * OUT_OF_MEMORY, DEVICE.  On error *out is NULL.
+ */
+spconv_status spconv_weights_prepare(const void* d_weights, int32_t kernel_volume, int32_t c_in, int32_t c_out,
+                                     spconv_dtype dtype, void* hip_stream, spconv_weights** out);
+
+/*
+ * The forward of spconv_forward with prepared weights: c_in, c_out and dtype
+ * are the handle's, and the wide and tiled paths read its operand-order copy
+ * instead of writing one.  The output is bit-identical to spconv_forward with
+ * the weights the handle copied.  Requirements, ordering after the map's
+ * build and the stream's workspace as for spconv_forward; the map's kernel
+ * volume and device must be the handle's.  Errors: INVALID_ARG (NULL handle
+ * or map, kernel volume or device mismatch, and those of spconv_forward),
+ * UNSUPPORTED, OUT_OF_MEMORY, DEVICE.
+ */
+spconv_status spconv_forward_prepared(const void* d_feats, const spconv_weights* weights, const spconv_map* map,
+                                      void* d_out, void* hip_stream);
+
+/* Frees a handle from spconv_weights_prepare (NULL is ignored).  Waits for
+ * the device's work in flight, which may still read it. */
+void spconv_weights_free(spconv_weights* weights);
 
 /*
  * Builds the kernel map of a strided (downsampling) sparse convolution with a

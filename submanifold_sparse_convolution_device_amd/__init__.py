@@ -41,7 +41,7 @@ EXPORTED = (
     "spconv_forward_noalloc", "spconv_backward_data", "spconv_backward_weights", "spconv_build_map_strided",
     "spconv_map_transpose", "spconv_map_geometry", "spconv_map_out_coords", "spconv_group_plan", "spconv_group_plan_counts",
     "spconv_forward_grouped", "spconv_select_dataflow", "spconv_map_free", "spconv_status_string",
-    "spconv_last_error",
+    "spconv_last_error", "spconv_weights_prepare", "spconv_forward_prepared", "spconv_weights_free",
 )
 MAP_KINDS = {0: "submanifold", 1: "strided", 2: "transposed"}
 DATAFLOWS = {0: "fused", 1: "grouped"}
@@ -98,6 +98,11 @@ def lib() -> ctypes.CDLL:
     L.spconv_forward.restype = ctypes.c_int
     L.spconv_forward_noalloc.argtypes = L.spconv_forward.argtypes
     L.spconv_forward_noalloc.restype = ctypes.c_int
+    L.spconv_weights_prepare.argtypes = [vp, i32, i32, i32, ctypes.c_int, vp, ctypes.POINTER(vp)]
+    L.spconv_weights_prepare.restype = ctypes.c_int
+    L.spconv_forward_prepared.argtypes = [vp, vp, vp, vp, vp]
+    L.spconv_forward_prepared.restype = ctypes.c_int
+    L.spconv_weights_free.argtypes, L.spconv_weights_free.restype = [vp], None
     L.spconv_backward_data.argtypes = L.spconv_forward.argtypes
     L.spconv_backward_data.restype = ctypes.c_int
     L.spconv_backward_weights.argtypes = L.spconv_forward.argtypes
@@ -198,6 +203,21 @@ def spconv_forward(d_feats: int, d_weights: int, handle: int, c_in: int, c_out: 
 def spconv_forward_noalloc(d_feats: int, d_weights: int, handle: int, c_in: int, c_out: int, dtype: int,
                            d_out: int, hip_stream: int) -> None:
     _check(lib().spconv_forward_noalloc(d_feats, d_weights, handle, c_in, c_out, dtype, d_out, hip_stream))
+
+
+def spconv_weights_prepare(d_weights: int, kernel_volume: int, c_in: int, c_out: int, dtype: int,
+                           hip_stream: int) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().spconv_weights_prepare(d_weights, kernel_volume, c_in, c_out, dtype, hip_stream, ctypes.byref(h)))
+    return int(h.value)
+
+
+def spconv_forward_prepared(d_feats: int, weights: int, handle: int, d_out: int, hip_stream: int) -> None:
+    _check(lib().spconv_forward_prepared(d_feats, weights, handle, d_out, hip_stream))
+
+
+def spconv_weights_free(weights: int) -> None:
+    lib().spconv_weights_free(weights)
 
 
 def spconv_backward_data(d_grad_out: int, d_weights: int, handle: int, c_in: int, c_out: int, dtype: int,
@@ -488,6 +508,64 @@ def forward(feats, weights, kmap: SpconvMap, out=None, noalloc=False):
     with _OnDevice(feats.device):
         fn = spconv_forward_noalloc if noalloc else spconv_forward
         fn(feats.data_ptr(), weights.data_ptr(), kmap.handle, cin, cout, code, out.data_ptr(), _stream())
+    return out
+
+
+class PreparedWeights:
+    """A layer's weights copied once for repeated forwards
+    (``spconv_weights_prepare``); later changes to the tensor it was made
+    from do not reach it."""
+
+    def __init__(self, weights):
+        global _DT
+        torch = _torch()
+        if _DT is None:
+            _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+        if not (weights.is_cuda and weights.is_contiguous() and weights.dim() == 3):
+            raise SpconvError(1, "weights must be a contiguous [K^3, C_in, C_out] tensor on a HIP device")
+        code = _DT.get(weights.dtype)
+        if code is None:
+            raise SpconvError(4, f"dtype {weights.dtype} not supported")
+        self.kernel_volume, self.c_in, self.c_out = (int(v) for v in weights.shape)
+        self.dtype, self.device, self.handle = weights.dtype, weights.device, None
+        with _OnDevice(weights.device):
+            self.handle = spconv_weights_prepare(weights.data_ptr(), self.kernel_volume, self.c_in, self.c_out,
+                                                 code, _stream())
+
+    def free(self) -> None:
+        if self.handle:
+            spconv_weights_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def prepare_weights(weights) -> PreparedWeights:
+    """Prepares [K^3, C_in, C_out] weights for ``forward_prepared``."""
+    return PreparedWeights(weights)
+
+
+def forward_prepared(feats, pw: PreparedWeights, kmap: SpconvMap, out=None):
+    """``forward`` with prepared weights (bit-identical output)."""
+    torch = _torch()
+    if pw.handle is None:
+        raise SpconvError(1, "the prepared weights were freed")
+    if not (feats.is_cuda and feats.is_contiguous() and feats.dim() == 2 and feats.dtype == pw.dtype):
+        raise SpconvError(1, "feats must be a contiguous [N, C_in] tensor on a HIP device of the weights' dtype")
+    if feats.shape[0] != kmap.n_in or feats.shape[1] != pw.c_in or pw.kernel_volume != kmap.kernel_volume:
+        raise SpconvError(1, f"shape mismatch: feats {tuple(feats.shape)}, weights "
+                             f"[{pw.kernel_volume}, {pw.c_in}, {pw.c_out}], map n_in={kmap.n_in} "
+                             f"K^3={kmap.kernel_volume}")
+    if out is None:
+        out = torch.empty((kmap.n, pw.c_out), dtype=pw.dtype, device=feats.device)
+    elif not (out.is_cuda and out.is_contiguous() and out.dtype == pw.dtype and tuple(out.shape) == (kmap.n, pw.c_out)):
+        raise SpconvError(1, "out must be a contiguous [N, C_out] tensor of the feature dtype")
+    with _OnDevice(feats.device):
+        spconv_forward_prepared(feats.data_ptr(), pw.handle, kmap.handle, out.data_ptr(), _stream())
     return out
 
 

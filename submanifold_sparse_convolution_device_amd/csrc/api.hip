@@ -56,6 +56,17 @@ struct spconv_map {
   std::vector<int64_t> offsets;  // KV + 1
 };
 
+// A copy of one layer's weights made for repeated forwards: the raw
+// [K^3][C_in][C_out] copy and, for the shapes the wide and tiled paths take,
+// the same weights in MFMA operand order with the zero row after them.
+struct spconv_weights {
+  int device = 0;
+  int32_t KV = 0, c_in = 0, c_out = 0;
+  spconv_dtype dtype = SPCONV_F32;
+  void* raw = nullptr;
+  void* prepared = nullptr;  // NULL for shapes that never use it
+};
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -390,7 +401,7 @@ ForwardPath forward_path(const spconv::ForwardArgs& a) {
 
 size_t forward_workspace_bytes(ForwardPath path, const spconv::ForwardArgs& a) {
   if (path == ForwardPath::kWide) return spconv::wide_workspace_bytes(a);
-  if (path == ForwardPath::kTiled) return spconv::tiled_workspace_bytes(a);
+  if (path == ForwardPath::kTiled) return a.prepared != nullptr ? 0 : spconv::tiled_workspace_bytes(a);
   return 0;
 }
 
@@ -400,7 +411,7 @@ spconv_status launch_forward_path(ForwardPath path, const spconv::ForwardArgs& a
   hipError_t e;
   switch (path) {
     case ForwardPath::kWide:
-      e = spconv::launch_prep_weights(a, ws, stream);
+      e = a.prepared != nullptr ? hipSuccess : spconv::launch_prep_weights(a, ws, stream);
       if (e == hipSuccess) e = spconv::launch_forward_wide(a, ws, stream);
       break;
     case ForwardPath::kTiled:
@@ -512,7 +523,7 @@ bool same_plan(const spconv::GroupPlan& x, const spconv::GroupPlan& y) {
 
 extern "C" {
 
-int32_t spconv_abi_version(void) { return 4; }
+int32_t spconv_abi_version(void) { return 5; }
 
 const char* spconv_status_string(spconv_status s) {
   switch (s) {
@@ -703,6 +714,95 @@ spconv_status spconv_forward_noalloc(const void* d_feats, const void* d_weights,
   if (st != SPCONV_OK) return st;
   if (known_empty(map)) return zero_output(d_out, map->n, c_out, dtype, stream);
   return launch_forward_path(path, a, ws, stream);
+}
+
+spconv_status spconv_weights_prepare(const void* d_weights, int32_t kernel_volume, int32_t c_in, int32_t c_out,
+                                     spconv_dtype dtype, void* hip_stream, spconv_weights** out) {
+  g_last_error.clear();
+  if (out == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (d_weights == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "NULL weight pointer");
+  if (!aligned16(d_weights)) return fail(SPCONV_ERR_INVALID_ARG, "the weights must be 16-byte aligned");
+  if (dtype != SPCONV_F32 && dtype != SPCONV_F16 && dtype != SPCONV_BF16) {
+    return fail(SPCONV_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(dtype));
+  }
+  if (kernel_volume < 1 || kernel_volume > 343) {
+    return fail(SPCONV_ERR_INVALID_ARG, "kernel_volume = %d must lie in [1, 343]", kernel_volume);
+  }
+  const int32_t cmax = (dtype == SPCONV_F32) ? 512 : 1024;
+  if (c_in < 1 || c_out < 1 || c_in > cmax || c_out > cmax) {
+    return fail(SPCONV_ERR_INVALID_ARG, "c_in = %d, c_out = %d must lie in [1, %d]", c_in, c_out, cmax);
+  }
+  const int32_t mult = (dtype == SPCONV_F32) ? 4 : 8;
+  if (c_in % mult != 0 || c_out % mult != 0) {
+    return fail(SPCONV_ERR_UNSUPPORTED, "c_in = %d and c_out = %d must be multiples of %d", c_in, c_out, mult);
+  }
+  int device = 0;
+  SPCONV_HIP(hipGetDevice(&device), "hipGetDevice");
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  auto* w = new (std::nothrow) spconv_weights;
+  if (w == nullptr) return fail(SPCONV_ERR_OUT_OF_MEMORY, "host allocation of the weight handle");
+  w->device = device;
+  w->KV = kernel_volume;
+  w->c_in = c_in;
+  w->c_out = c_out;
+  w->dtype = dtype;
+  const size_t raw_b = static_cast<size_t>(kernel_volume) * c_in * c_out * (dtype == SPCONV_F32 ? 4 : 2);
+  // The operand-order copy exists for the shapes of the wide and tiled paths
+  // (F16/BF16, C_in in {32, 64, 128, 256}, C_out a multiple of 16, K^3 <= 128).
+  spconv::ForwardArgs a;
+  a.weights = d_weights;
+  a.KV = kernel_volume;
+  a.cin = c_in;
+  a.cout = c_out;
+  a.dtype = static_cast<int32_t>(dtype);
+  const bool with_prepared = dtype != SPCONV_F32 && kernel_volume <= 128 && c_out % 16 == 0 &&
+                             (c_in == 32 || c_in == 64 || c_in == 128 || c_in == 256);
+  hipError_t e = hipMalloc(&w->raw, raw_b);
+  if (e == hipSuccess && with_prepared) e = hipMalloc(&w->prepared, spconv::tiled_workspace_bytes(a));
+  if (e != hipSuccess) {
+    spconv_weights_free(w);
+    return e == hipErrorOutOfMemory ? fail(SPCONV_ERR_OUT_OF_MEMORY, "weight copy allocation")
+                                    : hip_fail(e, "weight copy allocation");
+  }
+  e = hipMemcpyAsync(w->raw, d_weights, raw_b, hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess && with_prepared) e = spconv::launch_prep_weights(a, w->prepared, stream);
+  if (e != hipSuccess) {
+    spconv_weights_free(w);
+    return hip_fail(e, "weight preparation");
+  }
+  *out = w;
+  return SPCONV_OK;
+}
+
+spconv_status spconv_forward_prepared(const void* d_feats, const spconv_weights* weights, const spconv_map* map,
+                                      void* d_out, void* hip_stream) {
+  g_last_error.clear();
+  if (weights == nullptr) return fail(SPCONV_ERR_INVALID_ARG, "weights is NULL");
+  if (map != nullptr && map->KV != weights->KV) {
+    return fail(SPCONV_ERR_INVALID_ARG, "the map has %d offsets, the weights %d", map->KV, weights->KV);
+  }
+  if (map != nullptr && map->device != weights->device) {
+    return fail(SPCONV_ERR_INVALID_ARG, "the map is on device %d, the weights on %d", map->device, weights->device);
+  }
+  spconv::ForwardArgs a;
+  spconv_status st = forward_args(d_feats, weights->raw, map, weights->c_in, weights->c_out, weights->dtype, d_out,
+                                  &a);
+  if (st != SPCONV_OK) return st;
+  a.prepared = weights->prepared;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  st = order_after_build(map, stream);
+  if (st != SPCONV_OK) return st;
+  if (known_empty(map)) return zero_output(d_out, map->n, weights->c_out, weights->dtype, stream);
+  return launch_fused(map, a, stream);
+}
+
+void spconv_weights_free(spconv_weights* weights) {
+  if (weights == nullptr) return;
+  // hipFree waits for the device's work in flight, which may still read them.
+  if (weights->raw != nullptr) (void)hipFree(weights->raw);
+  if (weights->prepared != nullptr) (void)hipFree(weights->prepared);
+  delete weights;
 }
 
 spconv_status spconv_backward_data(const void* d_grad_out, const void* d_weights, const spconv_map* map,

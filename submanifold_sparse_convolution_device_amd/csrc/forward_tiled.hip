@@ -417,9 +417,11 @@ hipError_t launch_prep_weights(const ForwardArgs& a, void* workspace, hipStream_
 }
 
 hipError_t launch_forward_tiled(const ForwardArgs& a, void* workspace, hipStream_t stream) {
-  const hipError_t e = launch_prep_weights(a, workspace, stream);
-  if (e != hipSuccess) return e;
-  const uint4* wop = static_cast<const uint4*>(workspace);
+  if (a.prepared == nullptr) {
+    const hipError_t e = launch_prep_weights(a, workspace, stream);
+    if (e != hipSuccess) return e;
+  }
+  const uint4* wop = static_cast<const uint4*>(a.prepared != nullptr ? a.prepared : workspace);
   if (a.dtype == 1) return launch_tiled_typed<_Float16>(a, wop, stream);
   return launch_tiled_typed<__bf16>(a, wop, stream);
 }

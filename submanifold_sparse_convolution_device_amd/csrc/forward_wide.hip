@@ -607,7 +607,7 @@ bool wide_supported(const ForwardArgs& a) {
 
 size_t wide_workspace_bytes(const ForwardArgs& a) {
   WideChoice c;
-  const size_t base = tiled_workspace_bytes(a);
+  const size_t base = a.prepared != nullptr ? 0 : tiled_workspace_bytes(a);
   if (!choose_wide(a, &c) || c.splits == 1) return base;
   return base + static_cast<size_t>(c.splits) * a.n * a.cout * sizeof(float);
 }
@@ -615,8 +615,9 @@ size_t wide_workspace_bytes(const ForwardArgs& a) {
 hipError_t launch_forward_wide(const ForwardArgs& a, void* workspace, hipStream_t stream) {
   WideChoice c;
   if (!choose_wide(a, &c)) return hipErrorNotSupported;
-  const uint4* wop = static_cast<const uint4*>(workspace);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + tiled_workspace_bytes(a));
+  const uint4* wop = static_cast<const uint4*>(a.prepared != nullptr ? a.prepared : workspace);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         (a.prepared != nullptr ? 0 : tiled_workspace_bytes(a)));
   if (a.dtype == 1) return launch_wide_typed<_Float16>(a, c, wop, part, stream);
   return launch_wide_typed<__bf16>(a, c, wop, part, stream);
 }

@@ -143,11 +143,16 @@ struct ForwardArgs {
   int32_t dtype;
   int32_t centre;   // offset whose list is the identity (read by position), -1: none (strided maps)
   int64_t n_in;     // rows of feats (n for a submanifold map)
+  // The weights already in MFMA operand order with the zero row after them
+  // (what launch_prep_weights writes, tiled_workspace_bytes(a) bytes), or
+  // NULL: the wide and tiled paths then write that copy into their workspace.
+  const void* prepared = nullptr;
 };
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream);
 
 // Mid / large channel path (forward_tiled.hip): needs a workspace of
-// tiled_workspace_bytes(a) bytes for the weights in MFMA operand order.
+// tiled_workspace_bytes(a) bytes for the weights in MFMA operand order
+// (none when a.prepared holds them).
 bool tiled_supported(const ForwardArgs& a);
 size_t tiled_workspace_bytes(const ForwardArgs& a);
 hipError_t launch_forward_tiled(const ForwardArgs& a, void* workspace, hipStream_t stream);
@@ -157,8 +162,9 @@ hipError_t launch_prep_weights(const ForwardArgs& a, void* workspace, hipStream_
 const uint4* workspace_zero_row(const ForwardArgs& a, const void* workspace);
 // Wide path (forward_wide.hip): gathered rows staged in LDS, shared by the
 // waves of a workgroup.  Its workspace (wide_workspace_bytes(a) bytes) starts
-// with the prepared weights and zero row (launch_prep_weights), followed by
-// fp32 partial outputs when a small layer splits its offsets.
+// with the prepared weights and zero row (launch_prep_weights; absent when
+// a.prepared holds them), followed by fp32 partial outputs when a small
+// layer splits its offsets.
 bool wide_supported(const ForwardArgs& a);
 size_t wide_workspace_bytes(const ForwardArgs& a);
 hipError_t launch_forward_wide(const ForwardArgs& a, void* workspace, hipStream_t stream);

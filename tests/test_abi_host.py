@@ -33,7 +33,7 @@ def test_single_hip_runtime_mapped():
 
 
 def test_abi_version_and_status_strings():
-    assert sp.spconv_abi_version() == 4
+    assert sp.spconv_abi_version() == 5
     for code, name in sp.STATUS.items():
         assert sp.spconv_status_string(code) == name
 
@@ -102,6 +102,25 @@ def test_grouped_host_validation():
     sel = sp.spconv_select_dataflow
     assert _status_of(sel, fake, fake, 0, 32, 32, 1, None, None, 3, fake, 0) == "SPCONV_ERR_INVALID_ARG"
     assert _status_of(sel, fake, fake, fake_map, 32, 32, 9, None, None, 3, fake, 0) == "SPCONV_ERR_UNSUPPORTED"
+
+
+def test_prepared_weights_host_validation():
+    """Weight preparation and the prepared forward reject bad arguments
+    before any device work."""
+    fake = 4096
+    p = sp.spconv_weights_prepare
+    assert _status_of(p, 0, 27, 32, 32, 1, 0) == "SPCONV_ERR_INVALID_ARG"
+    assert _status_of(p, fake + 8, 27, 32, 32, 1, 0) == "SPCONV_ERR_INVALID_ARG"
+    assert _status_of(p, fake, 27, 32, 32, 7, 0) == "SPCONV_ERR_UNSUPPORTED"
+    for kv in (0, 344, -1):
+        assert _status_of(p, fake, kv, 32, 32, 1, 0) == "SPCONV_ERR_INVALID_ARG"
+    assert _status_of(p, fake, 27, 0, 32, 1, 0) == "SPCONV_ERR_INVALID_ARG"
+    assert _status_of(p, fake, 27, 32, 2048, 1, 0) == "SPCONV_ERR_INVALID_ARG"
+    assert _status_of(p, fake, 27, 20, 32, 1, 0) == "SPCONV_ERR_UNSUPPORTED"
+    st = sp.lib().spconv_weights_prepare(fake, 27, 32, 32, 1, None, None)
+    assert sp.STATUS[st] == "SPCONV_ERR_INVALID_ARG"
+    assert _status_of(sp.spconv_forward_prepared, fake, 0, 8192, fake, 0) == "SPCONV_ERR_INVALID_ARG"
+    sp.spconv_weights_free(0)  # NULL is ignored
 
 
 def test_map_queries_reject_null():
