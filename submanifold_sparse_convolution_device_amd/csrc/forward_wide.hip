@@ -29,6 +29,9 @@
 // for all of them (and, by a barrier, for the other waves' row copies).
 #include "internal.h"
 
+#include <type_traits>
+#include <utility>
+
 namespace spconv {
 namespace {
 
@@ -88,40 +91,29 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// The B operands of the TB blocks of one 32-wide ci chunk: TB 16-byte LDS
-// reads at `addr` + j * STRIDE bytes, left in flight.  Written as asm
-// because the compiler, unable to tell the two stage buffers apart, would
-// otherwise wait for every copy into LDS still in flight before each read,
-// the next offset's included; the asm also keeps it from waiting for the
-// reads themselves before their registers are needed.
-template <int TB, int STRIDE>
-__device__ __forceinline__ void read_stage(uint32_t addr, u32x4 (&v)[TB]) {
-  static_assert((TB - 1) * STRIDE < 65536, "ds_read offset range");
-  if constexpr (TB == 8) {
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:%9\n\t"
-        "ds_read_b128 %2, %8 offset:%10\n\t"
-        "ds_read_b128 %3, %8 offset:%11\n\t"
-        "ds_read_b128 %4, %8 offset:%12\n\t"
-        "ds_read_b128 %5, %8 offset:%13\n\t"
-        "ds_read_b128 %6, %8 offset:%14\n\t"
-        "ds_read_b128 %7, %8 offset:%15"
-        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
-        : "v"(addr), "i"(STRIDE), "i"(2 * STRIDE), "i"(3 * STRIDE), "i"(4 * STRIDE), "i"(5 * STRIDE),
-          "i"(6 * STRIDE), "i"(7 * STRIDE)
-        : "memory");
-  } else {
-    static_assert(TB == 4, "tasks of 4 or 8 blocks");
-    asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %4 offset:%5\n\t"
-        "ds_read_b128 %2, %4 offset:%6\n\t"
-        "ds_read_b128 %3, %4 offset:%7"
-        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-        : "v"(addr), "i"(STRIDE), "i"(2 * STRIDE), "i"(3 * STRIDE)
-        : "memory");
-  }
+// The B operands of one staged block read block by block (read_chunks) are
+// written as asm because the compiler, unable to tell the two stage buffers
+// apart, would otherwise wait for every copy into LDS still in flight before
+// each read, the next offset's included; the asm also keeps it from waiting
+// for the reads themselves before their registers are needed.
+template <int... I, typename F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N - 1, in order.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
+// The NCH chunks of one staged block: one 16-byte LDS read per chunk at
+// addr[ch] + OFF, left in flight.
+template <int NCH, int OFF>
+__device__ __forceinline__ void read_chunks(const uint32_t (&addr)[NCH], u32x4 (&v)[NCH]) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset range");
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v[ch]) : "v"(addr[ch]), "i"(OFF) : "memory");
 }
 
 // Waits until at most N LDS (or scalar-memory) operations are in flight and
@@ -130,7 +122,9 @@ __device__ __forceinline__ void read_stage(uint32_t addr, u32x4 (&v)[TB]) {
 template <int N, int TB>
 __device__ __forceinline__ void wait_lgkm(u32x4 (&v)[TB]) {
   static_assert(N >= 0 && N < 16, "lgkmcnt range");
-  if constexpr (TB == 8) {
+  if constexpr (TB == 2) {
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(v[0]), "+v"(v[1]) : "i"(N) : "memory");
+  } else if constexpr (TB == 8) {
     asm volatile("s_waitcnt lgkmcnt(%8)"
                  : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
                  : "i"(N)
@@ -314,17 +308,17 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
     // and wait for it there.
     idx[j] = v | (has ? 0 : -1);
   };
-  //   Row copy j (< BPW x IPB): rows [RPI q, RPI q + RPI) of staged block
-  //     jj (q = j % IPB, jj = j / IPB), whole rows, from global memory
-  //     straight into B stage `buf`: lane l copies segment (l % SEG) ^ swizzle
-  //     of row RPI q + l / SEG, whose input row is srow[j] (-1: no entry;
-  //     its byte offset wraps to just below 2^32, past the end of the
-  //     features, whose size the host keeps below that, so the load returns
-  //     zeros).  A block with no entry at the offset is skipped (its MFMAs
-  //     are too).
-  //     srow comes from copy_rows, which moves the index of row i from lane
-  //     i of idx (a cross-lane read, done before the MFMAs start, where its
-  //     wait costs nothing).
+  //   Row copies of the wave's staged block jj (< BPW), IPB of them under
+  //     one test of the block's bit (a block with no entry at the offset is
+  //     skipped, its MFMAs too): copy q moves rows [RPI q, RPI q + RPI) of
+  //     the block, whole rows, from global memory straight into B stage
+  //     `buf`; lane l copies segment (l % SEG) ^ swizzle of row RPI q + l /
+  //     SEG, whose input row is srow[jj IPB + q] (-1: no entry; its byte
+  //     offset wraps to just below 2^32, past the end of the features, whose
+  //     size the host keeps below that, so the load returns zeros).  srow
+  //     comes from copy_rows, which moves the index of row i from lane i of
+  //     idx (a cross-lane read, done before the MFMAs start, where its wait
+  //     costs nothing).
   auto copy_rows = [&](const int32_t (&idx)[BPW], int32_t (&srow)[Sh::LOADS_B]) {
 #pragma unroll
     for (int j = 0; j < Sh::LOADS_B; ++j) srow[j] = __shfl(idx[j / IPB], RPI * (j % IPB) + lane / SEG);
@@ -336,15 +330,17 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
   };
   const __amdgpu_buffer_rsrc_t frsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(feats_raw), 0, static_cast<int>(static_cast<uint32_t>(n_in * CIN * 2)), kBufferWord3);
-  auto stage_b_one = [&](const OffsetRef& o, int buf, const int32_t (&srow)[Sh::LOADS_B], int j) {
-    const int jj = j / IPB, q = j % IPB;
+  auto stage_block = [&](const OffsetRef& o, int buf, const int32_t (&srow)[Sh::LOADS_B], int jj) {
     const int b = wave + NW * jj;
     if (((o.pm >> b) & 1u) == 0u) return;  // wave-uniform
-    const int i = RPI * q + lane / SEG;
-    const int c = (lane % SEG) ^ seg_swizzle<SEG, RP>(i);
-    const uint32_t voff = static_cast<uint32_t>(srow[j]) * (CIN * 2u) + static_cast<uint32_t>(c) * 16u;
-    uint4* dst = bstage + ((buf * TB + b) * BLOCK_BYTES + q * RPI * SEG * 16) / 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(frsrc, (lds_void*)dst, 16, static_cast<int>(voff), 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < IPB; ++q) {
+      const int i = RPI * q + lane / SEG;
+      const int c = (lane % SEG) ^ seg_swizzle<SEG, RP>(i);
+      const uint32_t voff = static_cast<uint32_t>(srow[jj * IPB + q]) * (CIN * 2u) + static_cast<uint32_t>(c) * 16u;
+      uint4* dst = bstage + ((buf * TB + b) * BLOCK_BYTES + q * RPI * SEG * 16) / 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(frsrc, (lds_void*)dst, 16, static_cast<int>(voff), 0, 0, 0);
+    }
   };
   //   Weight load j (< NCB x NCH): this wave's slice of W_k in operand order.
   const int ncbg = cout / 16;
@@ -355,7 +351,7 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
     a[cb][ch] = wop[((static_cast<int64_t>(k) * ncbg + cb0 + cb) * NCH + ch) * 64 + lane];
   };
   constexpr int A = Sh::LOADS_A, B = Sh::LOADS_B, I = Sh::LOADS_I;
-  constexpr int kLoads = A + B + I;
+  constexpr int kLoads = BPW + A + I;  // items: copy groups, weights, indices
 
   floatx4 acc[TB][NCB];
 #pragma unroll
@@ -365,42 +361,46 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
 
   typedef __attribute__((address_space(3))) uint4 lds_uint4;
   const uint32_t stage_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_uint4*)bstage));
-  // MFMAs of offset o from stage `buf` and weights a.  The loads of the next
-  // offset (load(item), items 0 .. kLoads - 1: rows, weights, then the
-  // indices of the offset after) are issued a few at a time between the
-  // MFMA groups of the blocks, where they issue while the matrix core is
-  // busy instead of stalling the wave before the offset starts.
-  auto run = [&](const OffsetRef& o, int buf, const uint4 (&a)[NCB][NCH], auto&& load) {
-    const uint32_t pm = o.pm;
-    constexpr int kSlots = NCH * TB;
-    // Lane (g, r) reads row r, segment 4 ch + g (swizzled) of each block;
-    // chunk ch + 1's reads are in flight while chunk ch runs on MFMA, the
-    // wait before a chunk's MFMAs leaving only the newer chunk's reads.
-    u32x4 bv[2][TB];
-    const uint32_t base = stage_addr + static_cast<uint32_t>(buf * TB * BLOCK_BYTES + r * SEG * 16);
+  // Per-lane LDS addresses of the NCH chunks of block 0 of stage 0: lane
+  // (g, r) reads row r, segment 4 ch + g (swizzled); other blocks and the
+  // other stage are immediate offsets.
+  uint32_t caddr[NCH];
+  {
     const int swz = seg_swizzle<SEG, RP>(r);
-    auto chunk_addr = [&](int ch) { return base + static_cast<uint32_t>(((4 * ch + g) ^ swz) * 16); };
-    read_stage<TB, BLOCK_BYTES>(chunk_addr(0), bv[0]);
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-      if (ch + 1 < NCH) {
-        read_stage<TB, BLOCK_BYTES>(chunk_addr(ch + 1), bv[(ch + 1) & 1]);
-        wait_lgkm<TB, TB>(bv[ch & 1]);
+    for (int ch = 0; ch < NCH; ++ch)
+      caddr[ch] = stage_addr + static_cast<uint32_t>(r * SEG * 16 + ((4 * ch + g) ^ swz) * 16);
+  }
+  // MFMAs of offset o from stage BUF and weights a, block by block (one
+  // test of the block's bit per block).  The loads of the next offset
+  // (load(item), items 0 .. kLoads - 1: the row-copy groups, weights, then
+  // the indices of the offset after) are issued a few at a time after each
+  // block's MFMAs, where they issue while the matrix core is busy instead
+  // of stalling the wave before the offset starts.
+  auto run = [&](const OffsetRef& o, auto buf_tag, const uint4 (&a)[NCB][NCH], auto&& load) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const uint32_t pm = o.pm;
+    // Block-major: block b + 1's chunks are read while block b runs on MFMA.
+    u32x4 bv[2][NCH];
+    read_chunks<NCH, BUF * TB * BLOCK_BYTES>(caddr, bv[0]);
+    static_for<TB>([&](auto b_tag) {
+      constexpr int b = decltype(b_tag)::value;
+      if constexpr (b + 1 < TB) {
+        read_chunks<NCH, (BUF * TB + b + 1) * BLOCK_BYTES>(caddr, bv[(b + 1) & 1]);
+        wait_lgkm<NCH, NCH>(bv[b & 1]);
       } else {
-        wait_lgkm<0, TB>(bv[ch & 1]);
+        wait_lgkm<0, NCH>(bv[b & 1]);
       }
+      if (pm & (1u << b)) {
 #pragma unroll
-      for (int b = 0; b < TB; ++b) {
-        if (pm & (1u << b)) {
+        for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb)
-            acc[b][cb] = mfma<T>(a[cb][ch], __builtin_bit_cast(uint4, bv[ch & 1][b]), acc[b][cb]);
-        }
-        const int slot = ch * TB + b;
-#pragma unroll
-        for (int it = slot * kLoads / kSlots; it < (slot + 1) * kLoads / kSlots; ++it) load(it);
+            acc[b][cb] = mfma<T>(a[cb][ch], __builtin_bit_cast(uint4, bv[b & 1][ch]), acc[b][cb]);
       }
-    }
+#pragma unroll
+      for (int it = b * kLoads / TB; it < (b + 1) * kLoads / TB; ++it) load(it);
+    });
   };
 
   // Prologue: indices of offsets 0 and 1, weights and rows of offset 0 (the
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
   int32_t srow[Sh::LOADS_B];
   copy_rows(ix0, srow);
 #pragma unroll
-  for (int j = 0; j < B; ++j) stage_b_one(o0, 0, srow, j);
+  for (int jj = 0; jj < BPW; ++jj) stage_block(o0, 0, srow, jj);
 
   // Steady state, two offsets per trip so that the register sets alternate
   // without copies.  One step: wait for every load of the step before (this
@@ -432,10 +432,10 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
     wait_vm<0>();
     lds_barrier();
     copy_rows(ix1, srow);
-    run(o0, 0, ax, [&](int it) {
-      if (it < B) stage_b_one(o1, 1, srow, it);
-      else if (it < B + A) load_a_one(o1, ay, it - B);
-      else load_idx_one(o2, ix0, it - B - A);
+    run(o0, std::integral_constant<int, 0>{}, ax, [&](int it) {
+      if (it < BPW) stage_block(o1, 1, srow, it);
+      else if (it < BPW + A) load_a_one(o1, ay, it - BPW);
+      else load_idx_one(o2, ix0, it - BPW - A);
     });
     if (o1.k < 0) break;
     OffsetRef o3 = next_ref();
@@ -443,10 +443,10 @@ __global__ __launch_bounds__(64 * NW) void k_forward_wide(
     wait_vm<0>();
     lds_barrier();
     copy_rows(ix0, srow);
-    run(o1, 1, ay, [&](int it) {
-      if (it < B) stage_b_one(o2, 0, srow, it);
-      else if (it < B + A) load_a_one(o2, ax, it - B);
-      else load_idx_one(o3, ix1, it - B - A);
+    run(o1, std::integral_constant<int, 1>{}, ay, [&](int it) {
+      if (it < BPW) stage_block(o2, 0, srow, it);
+      else if (it < BPW + A) load_a_one(o2, ax, it - BPW);
+      else load_idx_one(o3, ix1, it - BPW - A);
     });
     if (o2.k < 0) break;
     o0 = o2;

@@ -19,7 +19,7 @@
 // (the key, EMPTY, or another key in an unmarked slot: absent) except in the
 // few marked slots, where the window is scanned.
 //
-// Pipeline (one stream, six launches, seven or eight for an ordered map; the last one
+// Pipeline (one stream, six launches, eight for an ordered map; the last one
 // also writes the small summary into the host's pinned memory):
 //   k_init     clear the table, the negative-half neighbour flags and the
 //              summary
@@ -42,8 +42,7 @@
 //   k_count    per 64-row tile (of positions of the row order) and offset, a
 //              ballot of the flags is the tile's row mask; per-group counts
 //              and per-offset totals
-//   k_scan     (ordered maps of more than kScanGroups groups) per offset:
-//              each group's first list position
+//   k_scan     (ordered maps) per offset: each group's first list position
 //   k_compact  per (offset, chunk): the list start from the totals and the
 //              counts of earlier chunks, then each entry's place from the tile
 //              masks; lists come out grouped by offset ("sorted by weight
@@ -929,8 +928,10 @@ __global__ __launch_bounds__(1024) void k_scan(const int64_t* __restrict__ chunk
 // positions of a window hold a permutation of the window's rows, so the
 // probe's neighbour column of those rows at offset k (nbr[k][w0 .. w0 +
 // window)) is first copied into LDS with coalesced loads and then read
-// through perm.  A group's first list position comes from k_scan when there
-// are more than kScanGroups groups, else each wave sums the counts before it.
+// through perm.  A group's first list position comes from k_scan (a
+// launch of its own: summing the counts of the groups before it here, one
+// dependent load round per 64 groups, took 14 us longer at K = 5 on 8 LiDAR
+// frames).
 // Wave w places the entries of group w of the window: each
 // tile's first list position (group_base plus the earlier tiles' counts, a
 // wave prefix sum) goes to tile_off[k][t], and each entry, at its rank in the
@@ -941,13 +942,12 @@ __global__ __launch_bounds__(1024) void k_scan(const int64_t* __restrict__ chunk
 // also writes tile_off[KV * tiles] = E, and the first one hands the summary
 // to the host's pinned slot.
 constexpr int kWindowGroups = kOrderWindow / (kTileRows * kGroupTiles);
-constexpr int64_t kScanGroups = 4096;
 static_assert(kWindowGroups * kTileRows * kGroupTiles == kOrderWindow, "whole groups per window");
 __global__ __launch_bounds__(64 * kWindowGroups) void k_compact_window(
     const unsigned long long* __restrict__ tile_mask, const int32_t* __restrict__ tile_base,
     const int32_t* __restrict__ nbr, const int32_t* __restrict__ perm, int64_t n, int64_t tiles, int centre,
-    int KV, const int64_t* __restrict__ chunk_sum, const int32_t* __restrict__ group_base,
-    const long long* __restrict__ summary, int32_t* __restrict__ in_idx, int32_t* __restrict__ out_idx,
+    int KV, const int32_t* __restrict__ group_base, const long long* __restrict__ summary,
+    int32_t* __restrict__ in_idx, int32_t* __restrict__ out_idx,
     int32_t* __restrict__ tile_off, int32_t* __restrict__ tile_rows, long long* __restrict__ host_summary) {
   __shared__ int32_t col[kOrderWindow];
   const int k = blockIdx.y;
@@ -987,21 +987,8 @@ __global__ __launch_bounds__(64 * kWindowGroups) void k_compact_window(
     const int64_t q = (t0 + i) * kTileRows + lane;
     row[i] = ((m >> lane) & 1ull) ? perm[q] : static_cast<int32_t>(w0);
   }
-  // This group's first list position: from k_scan for many groups, else the
-  // totals of earlier offsets plus the counts of earlier groups, summed here.
-  int base = 0;
-  if (active) {
-    if (group_base != nullptr) {
-      base = group_base[static_cast<int64_t>(k) * groups + g];
-    } else {
-      long long b = 0;
-      for (int i = lane; i < k; i += 64) b += summary[kSummaryHead + i];
-      for (int64_t c = lane; c < g; c += 64) b += chunk_sum[static_cast<int64_t>(k) * groups + c];
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) b += __shfl_xor(b, d);
-      base = static_cast<int>(b);
-    }
-  }
+  // This group's first list position (k_scan).
+  const int base = active ? group_base[static_cast<int64_t>(k) * groups + g] : 0;
   if (!is_centre) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
@@ -1339,16 +1326,12 @@ hipError_t launch_build(const BuildPlan& p, const int32_t* coords, const BuildSc
   }
   if (p.ordered) {
     const int64_t groups = (p.tiles + kGroupTiles - 1) / kGroupTiles;
-    const bool scan = groups > kScanGroups;
-    if (scan) {
-      hipLaunchKernelGGL(k_scan, dim3(static_cast<unsigned>(p.KV)), dim3(1024), 0, stream, s.chunk_sum, groups,
-                         s.summary, s.group_base);
-    }
+    hipLaunchKernelGGL(k_scan, dim3(static_cast<unsigned>(p.KV)), dim3(1024), 0, stream, s.chunk_sum, groups,
+                       s.summary, s.group_base);
     const unsigned windows = static_cast<unsigned>((p.n + kOrderWindow - 1) / kOrderWindow);
     hipLaunchKernelGGL(k_compact_window, dim3(windows, static_cast<unsigned>(p.KV)), dim3(64 * kWindowGroups), 0,
-                       stream, m.tile_mask, s.tile_base, s.nbr, m.perm, p.n, p.tiles, p.centre, p.KV, s.chunk_sum,
-                       scan ? s.group_base : nullptr, s.summary, m.in_idx, m.out_idx, m.tile_off, m.tile_rows,
-                       host_summary);
+                       stream, m.tile_mask, s.tile_base, s.nbr, m.perm, p.n, p.tiles, p.centre, p.KV, s.group_base,
+                       s.summary, m.in_idx, m.out_idx, m.tile_off, m.tile_rows, host_summary);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_compact, dim3(static_cast<unsigned>(p.chunks), static_cast<unsigned>(p.KV)),
