@@ -162,8 +162,14 @@ __device__ __forceinline__ int wg_swz(int i) {
   else return 0;
 }
 
-// 512 zero bytes: the source of staged rows past a range's last entry.
-__device__ uint4 kWgradZero[32];
+// Buffer resource word 3 for raw 32-bit-element loads (gfx9 data format 32,
+// no swizzle): the bounds check compares each byte offset with the record
+// count, the buffer's size in bytes.
+constexpr int kBufferWord3 = 0x00020000;
+// Largest feature or gradient buffer the row copies address with 32-bit
+// byte offsets (a missing row's offset, just below 2^32, must stay past its
+// end).
+constexpr int64_t kWgradMaxBytes = (int64_t{1} << 32) - 4096;
 
 // Grid: units (tile range p, column group cg, offset k), k fastest, dealt so
 // that consecutive units run on one XCD.  Each unit writes the fp32 partial
@@ -205,9 +211,8 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t* __restrict__ feat
   // the copy's LDS offset in a stage.
   int c_row[NLW];
   uint32_t c_off[NLW], c_ix[NLW];
-  const char* c_base[NLW];
-  int64_t c_pitch[NLW];
-  int32_t c_last[NLW];  // last row of the copy's source array
+  bool c_isf[NLW];
+  uint32_t c_pitch[NLW];
   uint32_t c_lds[NLW];
 #pragma unroll
   for (int ii = 0; ii < NLW; ++ii) {
@@ -221,12 +226,19 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t* __restrict__ feat
     c_row[ii] = row;
     c_off[ii] = static_cast<uint32_t>(16 * (isf ? cf : cgp));
     c_ix[ii] = static_cast<uint32_t>((t / S::IPW) * S::IDX_WAVE + 4 * (t % S::IPW));
-    c_base[ii] = isf ? reinterpret_cast<const char*>(feats) : reinterpret_cast<const char*>(gout + col0);
-    c_pitch[ii] = isf ? 2 * CIN : 2 * static_cast<int64_t>(cout);
-    c_last[ii] = isf ? f_rows - 1 : g_rows - 1;
+    c_isf[ii] = isf;
+    c_pitch[ii] = isf ? 2u * CIN : 2u * static_cast<uint32_t>(cout);
     c_lds[ii] = static_cast<uint32_t>((isf ? 0 : S::F_BYTES) + jj * 1024);
   }
-  const uint64_t zero = reinterpret_cast<uint64_t>(kWgradZero);
+  // Buffer resources over the two sources (32-bit byte offsets; the host
+  // keeps both below 2^32 - 4096 bytes): a row past the range's end gets
+  // index -1, whose offset wraps past the buffer's end, where the load's
+  // bounds check returns zeros.
+  const __amdgpu_buffer_rsrc_t frsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(feats), 0, static_cast<int>(static_cast<uint32_t>(f_rows) * (2u * CIN)), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t grsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(gout + col0), 0,
+      static_cast<int>(static_cast<uint32_t>(g_rows) * (2u * static_cast<uint32_t>(cout)) - 2u * col0), kBufferWord3);
   typedef __attribute__((address_space(3))) uint4 lds_uint4;
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_uint4*)wstage));
   const uint32_t idx_base = lds_base + static_cast<uint32_t>(S::STAGES * S::STAGE_BYTES);
@@ -248,9 +260,10 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t* __restrict__ feat
     }
   };
   // Row copies of round r into `stage`, their indices read from area `area`
-  // (complete and visible: see the pipeline); a row past the range's end is
-  // copied from the zero row (selected with masks, not a branch).  The index
-  // is also clamped into the input's rows, so no copy can leave the arrays.
+  // (complete and visible: see the pipeline); a row past the range's end
+  // takes index -1, which the buffer load's bounds check turns into zeros,
+  // as it does any index outside the source, so no copy can leave the
+  // arrays.
   auto copy = [&](int r, int stage, int area) {
     int32_t rows[NLW];
     const uint32_t ia = idx_base + static_cast<uint32_t>(area * S::IDX_AREA);
@@ -263,14 +276,11 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t* __restrict__ feat
 #pragma unroll
     for (int ii = 0; ii < NLW; ++ii) {
       const int e = e0 + r * S::ROWS + c_row[ii];
-      const uint64_t keep = e < e1 ? ~0ull : 0ull;
-      const int32_t row = rows[ii];
-      const int32_t rc = row < 0 ? 0 : (row > c_last[ii] ? c_last[ii] : row);
-      const uint64_t row_addr =
-          reinterpret_cast<uint64_t>(c_base[ii]) + static_cast<uint64_t>(static_cast<int64_t>(rc) * c_pitch[ii]);
-      const uint64_t addr = ((row_addr & keep) | (zero & ~keep)) + c_off[ii];
+      const int32_t row = e < e1 ? rows[ii] : -1;
+      const uint32_t voff = static_cast<uint32_t>(row) * c_pitch[ii] + c_off[ii];
       uint4* dst = wstage + (static_cast<uint32_t>(stage * S::STAGE_BYTES) + c_lds[ii]) / 16;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(addr), (lds_void*)dst, 16, 0, 0);
+      if (c_isf[ii]) __builtin_amdgcn_raw_ptr_buffer_load_lds(frsrc, (lds_void*)dst, 16, static_cast<int>(voff), 0, 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(grsrc, (lds_void*)dst, 16, static_cast<int>(voff), 0, 0, 0);
     }
   };
 
@@ -500,6 +510,7 @@ bool wgrad_mfma_shape(const WgradArgs& a, int cols) {
   if (a.dtype != 1 && a.dtype != 2) return false;
   if (a.cin != 16 && a.cin != 32 && a.cin != 64 && a.cin != 128 && a.cin != 256) return false;
   if (a.cout % 16 != 0) return false;
+  if (a.n_in * a.cin * 2 > kWgradMaxBytes || a.n * a.cout * 2 > kWgradMaxBytes) return false;
   return !(a.cin == 256 && cols == 16);
 }
 

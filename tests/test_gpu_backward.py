@@ -25,6 +25,7 @@ import numpy as np
 import pytest
 import torch
 
+import box_map
 import oracle
 import workloads
 
@@ -156,3 +157,33 @@ def test_backward_batched_frames(sp, li):
     fd, gd = f.double().numpy(), g.double().numpy()
     _check_wgrad(gw, ref.backward_weights_parallel(fd, gd), ref.backward_weights_parallel(np.abs(fd), np.abs(gd)),
                  _wgrad_rel(layer.n, K, layer.cin, layer.cout, layer.dtype))
+
+
+@pytest.mark.parametrize("boxes", [
+    [(0, (256, 256, 255)), (1, (1, 16, 4095))],  # 16,777,200 rows: 2^32 - 4096 bytes at C = 128
+    [(0, (256, 256, 256))]])                     # 16 rows more: the generic kernel
+def test_wgrad_source_bytes_limit(sp, boxes):
+    """The MFMA weight gradient addresses features and gradients with 32-bit
+    byte offsets (a row past a range wraps to an offset past their end); at
+    C = 128 fp16 the first case's sources fill the largest buffers it takes,
+    so the last rows sit just below 2^32 bytes, and the second case runs on
+    the generic kernel.  Channel 0 of row p is 1 where p mod 1024 = 1023
+    (else 0, as are the other channels) and the gradient is all ones, so
+    grad_W[k][0][co] counts offset k's entries (p, q) with p mod 1024 = 1023
+    and every other value is 0: exact in fp32, from the boxes' closed-form
+    lists."""
+    K, c = 3, 128
+    n = sum(lz * ly * lx for _, (lz, ly, lx) in boxes)
+    kmap = sp.build_map(box_map.box_rows(boxes, DEV), K)
+    f = torch.zeros((n, c), dtype=torch.float16, device=DEV)
+    f[1023::1024, 0] = 1.0
+    g = torch.ones((n, c), dtype=torch.float16, device=DEV)
+    gw = sp.backward_weights(f, g, kmap)
+    del f, g
+    expect = torch.zeros((K ** 3, c, c), dtype=torch.float32, device=DEV)
+    for k in range(K ** 3):
+        p, _ = box_map.box_list(boxes, K, k, DEV)
+        expect[k, 0, :] = float(int(((p % 1024) == 1023).sum()))
+        del p
+    assert torch.equal(gw, expect)
+    kmap.free()
