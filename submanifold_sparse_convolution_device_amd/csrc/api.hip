@@ -131,6 +131,9 @@ struct StreamCache {
   hipStream_t stream = nullptr;
   void* scratch = nullptr;  // map build workspace
   size_t scratch_bytes = 0;
+  // Table slots of the last build launched on the scratch, whose table and
+  // occupancy map it leaves clear (0: not known clear).
+  int64_t clear_slots = 0;
   void* fwd = nullptr;  // forward workspace
   size_t fwd_bytes = 0;
   std::vector<std::pair<void*, size_t>> blocks;  // map blocks released on this stream
@@ -577,8 +580,10 @@ spconv_status spconv_build_map_async(const int32_t* d_coords, int64_t n, int32_t
   // on this stream); the cache lock also serialises enqueueing on a stream.
   std::lock_guard<std::mutex> lock(g_cache_mu);
   StreamCache* c = cache_for(device, stream);
+  void* const scratch_before = c->scratch;
   st = grow_buffer(c->scratch, c->scratch_bytes, spconv::build_scratch_bytes(p), pool, stream,
                    "workspace allocation");
+  if (c->scratch != scratch_before) c->clear_slots = 0;  // new memory
   if (st == SPCONV_OK) st = take_block(c, spconv::map_buffer_bytes(p), pool, &m->block, &m->block_bytes);
   if (st != SPCONV_OK) {
     release_slot(device, m->slot);
@@ -595,8 +600,14 @@ spconv_status spconv_build_map_async(const int32_t* d_coords, int64_t n, int32_t
     return st;
   };
 
-  hipError_t e = spconv::launch_build(p, d_coords, s, m->buf, m->slot->device, stream);
+  // The table sits at the start of the scratch, so a clear table of the same
+  // size is this build's table.  Until the launches succeed it is not known
+  // clear.
+  const bool table_clear = c->clear_slots == p.table_slots;
+  c->clear_slots = 0;
+  hipError_t e = spconv::launch_build(p, d_coords, s, m->buf, m->slot->device, table_clear, stream);
   if (e != hipSuccess) return discard(hip_fail(e, "map build launch"));
+  c->clear_slots = p.ordered ? 0 : p.table_slots;  // k_compact leaves an unordered map's table clear
   e = hipEventRecord(m->slot->done, stream);
   if (e != hipSuccess) return discard(hip_fail(e, "hipEventRecord"));
 

@@ -120,9 +120,12 @@ void carve_map_buffers(const BuildPlan& p, void* base, MapBuffers* m);
 
 // The whole map build (all asynchronous on `stream`).  When it completes,
 // host_summary (pinned host memory, kSummaryHead + KV values) holds the flags
-// and the per-offset counts.
+// and the per-offset counts, and for a map in the input order (!p.ordered)
+// the scratch's coordinate table and occupancy map are clear again.
+// table_clear: they are clear already (the last build on this scratch was
+// such a map with the same table size), so the clearing launch is skipped.
 hipError_t launch_build(const BuildPlan& p, const int32_t* coords, const BuildScratch& s,
-                        const MapBuffers& m, long long* host_summary, hipStream_t stream);
+                        const MapBuffers& m, long long* host_summary, bool table_clear, hipStream_t stream);
 
 // Forward launch.  dtype: 0 f32, 1 f16, 2 bf16.
 struct ForwardArgs {

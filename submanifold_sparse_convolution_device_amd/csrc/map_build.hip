@@ -19,12 +19,14 @@
 // (the key, EMPTY, or another key in an unmarked slot: absent) except in the
 // few marked slots, where the window is scanned.
 //
-// Pipeline (one stream, six launches, eight for an ordered map; the last one
-// also writes the small summary into the host's pinned memory):
-//   k_init     clear the table, the negative-half neighbour flags and the
-//              summary
+// Pipeline (one stream, six launches, eight for an ordered map, one fewer
+// when the table is already clear; the last one also writes the small
+// summary into the host's pinned memory):
+//   k_init     clear the table and the occupancy map, unless the previous
+//              build on the same scratch (same table size) left them clear
 //   k_claim    one lane per voxel: a plain store of its row claims its
-//              preferred slot (last writer wins)
+//              preferred slot (last writer wins); it also clears the
+//              voxel's negative-half flags, and the summary
 //   k_insert   one lane per voxel: the winner writes its key; a loser is a
 //              duplicate of the winner or takes the first unreserved free slot
 //              by CAS (the only atomics of the insert)
@@ -47,10 +49,12 @@
 //              counts of earlier chunks, then each entry's place from the tile
 //              masks; lists come out grouped by offset ("sorted by weight
 //              offset", section "Nine entries become two") and in the row
-//              order within an offset.  An ordered map uses k_compact_window:
-//              per (offset, window), the probe's neighbour column of the
-//              window's rows staged in LDS with coalesced loads, then read
-//              through the permutation.
+//              order within an offset; then its grid clears the table and
+//              the occupancy map for the next build on the scratch.  An
+//              ordered map uses k_compact_window: per (offset, window), the
+//              probe's neighbour column of the window's rows staged in LDS
+//              with coalesced loads, then read through the permutation (its
+//              table is cleared by k_init in the next build).
 // The lists are sized for the bound of K^3 entries per voxel, so nothing on
 // the device waits for the host; the host reads the summary once at the end.
 #include "internal.h"
@@ -129,49 +133,51 @@ __device__ __forceinline__ void raise_flag(long long* summary, unsigned long lon
   atomicOr(reinterpret_cast<unsigned long long*>(summary), bit);
 }
 
-// Clears the table slots to (EMPTY, row -1, no flags), the occupancy map and
-// the negative-half flags (all in 16-byte units: kInitUnits per thread, a
-// workgroup's stores contiguous) and the summary.
+// Unit i of the table's clear state (16 bytes each): table slot i as
+// (EMPTY, row -1, no flags) for i < slots, then occupancy bucket i - slots as
+// zeros.
+__device__ __forceinline__ void clear_table_unit(uint4* table, int64_t slots, uint4* occ, int64_t buckets,
+                                                 int64_t i) {
+  if (i < slots) {
+    table[i] = make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0u);  // key ~0, row -1, no flags
+  } else if (i - slots < buckets) {
+    occ[i - slots] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// Clears the table slots and the occupancy map (kInitUnits 16-byte units per
+// thread, a workgroup's stores contiguous).  A build whose scratch's last
+// build left a table of the same size clear (k_compact, the last kernel of a
+// map in the input order, clears it) skips this launch.
 constexpr int kInitUnits = 4;
-__global__ __launch_bounds__(256) void k_init(uint4* table, int64_t slots, uint4* occ, int64_t buckets,
-                                              uint4* flags, int64_t nflags, long long* summary,
-                                              int summary_len) {
+__global__ __launch_bounds__(256) void k_init(uint4* table, int64_t slots, uint4* occ, int64_t buckets) {
   const int64_t base = static_cast<int64_t>(blockIdx.x) * blockDim.x * kInitUnits + threadIdx.x;
-  const uint4 empty = make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0u);  // key ~0, row -1, no flags
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-  for (int u = 0; u < kInitUnits; ++u) {
-    int64_t i = base + static_cast<int64_t>(u) * blockDim.x;
-    if (i < slots) {
-      table[i] = empty;
-      continue;
-    }
-    i -= slots;
-    if (i < buckets) {
-      occ[i] = zero;
-      continue;
-    }
-    i -= buckets;
-    if (i < nflags) flags[i] = zero;
-  }
-  if (blockIdx.x == 0) {
-    for (int i = threadIdx.x; i < summary_len; i += blockDim.x) summary[i] = 0;
-  }
+  for (int u = 0; u < kInitUnits; ++u) clear_table_unit(table, slots, occ, buckets, base + u * blockDim.x);
 }
 
 // Insert, phase 1 (one lane per voxel): claim the preferred slot of the home
 // window with a plain store of the row; the last writer wins.  The voxel's
-// byte of the occupancy map is set too (every writer stores 1).
+// byte of the occupancy map is set too (every writer stores 1).  Each lane
+// also clears its voxel's negative-half flag record (nbu 16-byte units; the
+// probe, a later kernel, sets them), and the first workgroup the summary.
 __global__ __launch_bounds__(256) void k_claim(const int4* __restrict__ coords, int64_t n, ulonglong2* table,
                                                uint8_t* occ, unsigned long long window_mask,
-                                               unsigned long long bucket_mask) {
+                                               unsigned long long bucket_mask, uint4* neg, int nbu,
+                                               long long* summary, int summary_len) {
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < summary_len; i += blockDim.x) summary[i] = 0;
+  }
   const int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (v >= n) return;
   const int4 c = coords[v];
-  if (!voxel_in_range(c)) return;  // reported by phase 2
-  const unsigned long long key = pack_key(c.x, c.y, c.z, c.w);
-  *slot_row(&table[preferred_slot(key, window_mask)]) = static_cast<uint32_t>(v);
-  occ[occ_bucket(c.x, c.y, c.z, c.w >> 4, bucket_mask) * 16 + (c.w & 15)] = 1;
+  if (voxel_in_range(c)) {  // out of range: reported by phase 2
+    const unsigned long long key = pack_key(c.x, c.y, c.z, c.w);
+    *slot_row(&table[preferred_slot(key, window_mask)]) = static_cast<uint32_t>(v);
+    occ[occ_bucket(c.x, c.y, c.z, c.w >> 4, bucket_mask) * 16 + (c.w & 15)] = 1;
+  }
+  // after the load (a store before it would hold up its wait)
+  for (int u = 0; u < nbu; ++u) neg[v * nbu + u] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 __device__ __forceinline__ bool same_voxel(int4 a, int4 b) {
@@ -789,7 +795,8 @@ __global__ __launch_bounds__(256) void k_compact(const unsigned long long* __res
                                                  int32_t* __restrict__ out_idx,
                                                  int32_t* __restrict__ tile_off,
                                                  int32_t* __restrict__ tile_rows,
-                                                 long long* __restrict__ host_summary) {
+                                                 long long* __restrict__ host_summary, uint4* table,
+                                                 int64_t slots, uint4* occ, int64_t buckets) {
   const int k = blockIdx.y;
   const int64_t chunk = blockIdx.x;
   // The summary is final (its writers ran in earlier kernels): the first
@@ -876,6 +883,13 @@ __global__ __launch_bounds__(256) void k_compact(const unsigned long long* __res
   if (k == KV - 1 && chunk == chunks - 1 && wave == 3 && lane == 0) {
     tile_off[static_cast<int64_t>(KV) * tiles] = static_cast<int32_t>(base);
   }
+  // The coordinate table and occupancy map (slots > 0) are no longer read
+  // (the probe, their last reader, has completed): leave them clear for the
+  // next build on this scratch, spread over the whole grid.
+  const int64_t wg = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * gridDim.y * blockDim.x;
+  for (int64_t i = wg * blockDim.x + threadIdx.x; i < slots + buckets; i += stride)
+    clear_table_unit(table, slots, occ, buckets, i);
 }
 
 // Ordered maps, one workgroup per offset k (1024 threads): list positions.
@@ -1184,12 +1198,6 @@ __global__ __launch_bounds__(1024) void k_count_all(const uint32_t* __restrict__
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// The negative-half flag records are cleared (in 16-byte units); the probe
-// writes every row's positive-half bits, and the centre is implicit.
-int64_t negative_flag_units(const BuildPlan& p) {
-  return static_cast<int64_t>(neg_bytes(p.K)) / 16 * p.n;
-}
-
 // Occupancy buckets: a power of two, one per 4 table slots (at least one
 // per voxel), so that about a quarter to a half are in use.
 int64_t occ_buckets(const BuildPlan& p) { return p.table_slots / 4; }
@@ -1302,20 +1310,21 @@ void carve_map_buffers(const BuildPlan& p, void* base, MapBuffers* m) {
 }
 
 hipError_t launch_build(const BuildPlan& p, const int32_t* coords, const BuildScratch& s,
-                        const MapBuffers& m, long long* host_summary, hipStream_t stream) {
-  const int64_t nflags = negative_flag_units(p);
-  const int64_t units = p.table_slots + occ_buckets(p) + nflags;
-  const int64_t init_blocks = (units + 256 * kInitUnits - 1) / (256 * kInitUnits);
-  hipLaunchKernelGGL(k_init, dim3(static_cast<unsigned>(init_blocks)), dim3(256), 0, stream,
-                     reinterpret_cast<uint4*>(s.table), p.table_slots, s.occ, occ_buckets(p),
-                     reinterpret_cast<uint4*>(s.neg_flags), nflags, s.summary, kSummaryHead + p.KV);
+                        const MapBuffers& m, long long* host_summary, bool table_clear, hipStream_t stream) {
+  if (!table_clear) {
+    const int64_t units = p.table_slots + occ_buckets(p);
+    const int64_t init_blocks = (units + 256 * kInitUnits - 1) / (256 * kInitUnits);
+    hipLaunchKernelGGL(k_init, dim3(static_cast<unsigned>(init_blocks)), dim3(256), 0, stream,
+                       reinterpret_cast<uint4*>(s.table), p.table_slots, s.occ, occ_buckets(p));
+  }
   const unsigned long long window_mask =
       static_cast<unsigned long long>(p.table_slots / kWindowSlots) - 1ull;
   const int4* c4 = reinterpret_cast<const int4*>(coords);
   const unsigned gx = static_cast<unsigned>((p.n + 255) / 256);
   hipLaunchKernelGGL(k_claim, dim3(gx), dim3(256), 0, stream, c4, p.n, s.table,
                      reinterpret_cast<uint8_t*>(s.occ), window_mask,
-                     static_cast<unsigned long long>(occ_buckets(p) - 1));
+                     static_cast<unsigned long long>(occ_buckets(p) - 1), reinterpret_cast<uint4*>(s.neg_flags),
+                     neg_bytes(p.K) / 16, s.summary, kSummaryHead + p.KV);
   hipLaunchKernelGGL(k_insert, dim3(gx), dim3(256), 0, stream, c4, p.n, s.table, window_mask, s.summary);
   switch (p.K) {
     case 1: launch_probe_count<1>(p, c4, s, m, window_mask, stream); break;
@@ -1337,7 +1346,8 @@ hipError_t launch_build(const BuildPlan& p, const int32_t* coords, const BuildSc
   hipLaunchKernelGGL(k_compact, dim3(static_cast<unsigned>(p.chunks), static_cast<unsigned>(p.KV)),
                      dim3(256), 0, stream, m.tile_mask, s.tile_base, s.nbr, p.n, p.tiles, p.centre, p.KV,
                      p.group_tiles, p.chunks, s.chunk_sum, s.summary, m.in_idx, m.out_idx,
-                     m.tile_off, m.tile_rows, host_summary);
+                     m.tile_off, m.tile_rows, host_summary, reinterpret_cast<uint4*>(s.table), p.table_slots,
+                     s.occ, occ_buckets(p));
   return hipGetLastError();
 }
 
@@ -1347,13 +1357,13 @@ hipError_t launch_table_build(const int32_t* coords, int64_t n, ulonglong2* tabl
   const int64_t units = table_slots + buckets;
   const int64_t init_blocks = (units + 256 * kInitUnits - 1) / (256 * kInitUnits);
   hipLaunchKernelGGL(k_init, dim3(static_cast<unsigned>(init_blocks)), dim3(256), 0, stream,
-                     reinterpret_cast<uint4*>(table), table_slots, occ, buckets, static_cast<uint4*>(nullptr),
-                     int64_t(0), summary, summary_len);
+                     reinterpret_cast<uint4*>(table), table_slots, occ, buckets);
   const unsigned long long window_mask = static_cast<unsigned long long>(table_slots / kWindowSlots) - 1ull;
   const int4* c4 = reinterpret_cast<const int4*>(coords);
   const unsigned gx = static_cast<unsigned>((n + 255) / 256);
   hipLaunchKernelGGL(k_claim, dim3(gx), dim3(256), 0, stream, c4, n, table, reinterpret_cast<uint8_t*>(occ),
-                     window_mask, static_cast<unsigned long long>(buckets - 1));
+                     window_mask, static_cast<unsigned long long>(buckets - 1), static_cast<uint4*>(nullptr), 0, summary,
+                     summary_len);
   hipLaunchKernelGGL(k_insert, dim3(gx), dim3(256), 0, stream, c4, n, table, window_mask, summary);
   return hipGetLastError();
 }
@@ -1413,7 +1423,8 @@ hipError_t launch_general_map(const GeneralMapArgs& g, hipStream_t stream) {
   const int64_t chunks = (tiles + group_tiles - 1) / group_tiles;
   hipLaunchKernelGGL(k_compact, dim3(static_cast<unsigned>(chunks), static_cast<unsigned>(KV)), dim3(256), 0, stream,
                      g.map.tile_mask, g.tile_base, g.nbr, g.nq, tiles, -1, KV, group_tiles, chunks, g.chunk_sum,
-                     g.summary, g.map.in_idx, g.map.out_idx, g.map.tile_off, g.map.tile_rows, g.host_summary);
+                     g.summary, g.map.in_idx, g.map.out_idx, g.map.tile_off, g.map.tile_rows, g.host_summary,
+                     static_cast<uint4*>(nullptr), int64_t(0), static_cast<uint4*>(nullptr), int64_t(0));
   return hipGetLastError();
 }
 

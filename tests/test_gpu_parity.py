@@ -320,9 +320,11 @@ def test_map_sequence_on_one_stream(sp):
 def test_map_same_plan_repeated_on_one_stream(sp):
     """Builds of different voxel sets with the same n and K, back to back on
     one stream without host waits, so each reuses the workspace of the one
-    before with the same layout: nothing of an earlier build leaks into a
-    later one (a stale key would show up as a false neighbour), also after a
-    build that failed on duplicates and around a build with another K."""
+    before with the same layout, including the coordinate table that build
+    left clear (no clearing launch then): nothing of an earlier build leaks
+    into a later one (a stale key would show up as a false neighbour), also
+    after a build that failed on duplicates and around a build with another
+    K."""
     grids = [workloads.permuted(workloads.random_grid(seed, 40, 0.3, 2), seed) for seed in (61, 62, 63, 64)]
     n0 = min(g.shape[0] for g in grids)
     n0 -= n0 % 64 - 37 if n0 % 64 >= 37 else n0 % 64 + 27  # a ragged last tile
