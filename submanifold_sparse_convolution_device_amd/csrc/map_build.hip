@@ -340,6 +340,10 @@ __device__ __forceinline__ void emit_pair(int j, int64_t q, int32_t p, int64_t n
   neg_flags[static_cast<int64_t>(p) * NB + kneg] = 1;
 }
 
+// Rows fit 27 bits (n K^3 < 2^31 with K >= 3), lookup indices of a step the
+// other 5.
+constexpr int kHitRowBits = 27;
+
 // One lane per voxel Q: the (K^3 - 1) / 2 offsets after the centre, a few
 // lines of neighbours at a time, each in rounds of loads:
 //   1. the occupancy bucket(s) of every line (two when its x range crosses a
@@ -367,6 +371,18 @@ __global__ __launch_bounds__(256) void k_probe(const int4* __restrict__ coords, 
   constexpr int kMaxLook = kLinesPerStep * L::W;   // lookups of a step (<= 32)
   constexpr int kCand = 4, kPend = 2;              // loads per lane per round of steps 2 and 3
   static_assert(kMaxLook <= 32, "a step's lookups fit a 32-bit mask");
+  static_assert(kMaxLook <= (1 << (32 - kHitRowBits)), "a lookup index fits the hit's high bits");
+  // A step's hits (lookup index in the step, high bits; the neighbour's row,
+  // low bits), in LDS: the lane's e-th at hits[e * 256 + lane in the
+  // workgroup].  Kept out of registers, where an array indexed by the lookup
+  // costs a compare and a select per element at every write, and out of
+  // global memory until the step's last load (a store before a load would
+  // hold up that load's wait).
+  __shared__ uint32_t hits[kMaxLook * 256];
+  auto record = [&](int js, int64_t p, int& nh) {
+    hits[nh * 256 + threadIdx.x] = (static_cast<uint32_t>(js) << kHitRowBits) | static_cast<uint32_t>(p);
+    ++nh;
+  };
   const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (q >= n) return;
   const int4 c = coords[q];
@@ -421,9 +437,7 @@ __global__ __launch_bounds__(256) void k_probe(const int4* __restrict__ coords, 
         }
       }
     }
-    int32_t row[kMaxLook];
-#pragma unroll
-    for (int i = 0; i < kMaxLook; ++i) row[i] = -1;
+    int nh = 0;  // hits of the step so far, in hits[] (LDS)
     uint32_t pend = 0u;
     // 2. preferred slots of the candidates
     while (cand != 0u) {
@@ -446,12 +460,7 @@ __global__ __launch_bounds__(256) void k_probe(const int4* __restrict__ coords, 
         if (js[u] >= 0) {
           if (sv[u].x == ks[u]) {
             const int64_t p = static_cast<int64_t>(static_cast<uint32_t>(sv[u].y));
-            if (p < n) {
-#pragma unroll
-              for (int i = 0; i < kMaxLook; ++i) {
-                if (i == js[u]) row[i] = static_cast<int32_t>(p);
-              }
-            }
+            if (p < n) record(js[u], p, nh);
           } else if (sv[u].x != kEmptyKey &&
                      (static_cast<uint32_t>(sv[u].y >> 32) & kSlotDisplaced) != 0u) {
             pend |= 1u << js[u];
@@ -489,24 +498,15 @@ __global__ __launch_bounds__(256) void k_probe(const int4* __restrict__ coords, 
             empty |= (wv[u][s2].x == kEmptyKey);
           }
           if (p < 0 && !empty) p = find_row_scan(ks[u], table, window_mask, overflow);  // full window
-          if (p >= 0 && p < n) {
-#pragma unroll
-            for (int i = 0; i < kMaxLook; ++i) {
-              if (i == js[u]) row[i] = static_cast<int32_t>(p);
-            }
-          }
+          if (p >= 0 && p < n) record(js[u], p, nh);
         }
       }
     }
-    const int lend = (l0 + kLinesPerStep < L::kLines) ? l0 + kLinesPerStep : L::kLines;
-    const int jn = L::first(lend - 1) + L::count(lend - 1) - j0;  // lookups of the step
-#pragma unroll
-    for (int i = 0; i < kMaxLook; ++i) {
-      if (i < jn && row[i] >= 0) {
-        const int j = j0 + i;
-        bits[j >> 5] |= 1u << (j & 31);
-        emit_pair<K>(j, q, row[i], n, nbr, neg_flags);
-      }
+    for (int e = 0; e < nh; ++e) {
+      const uint32_t hv = hits[e * 256 + threadIdx.x];
+      const int j = j0 + static_cast<int>(hv >> kHitRowBits);
+      bits[j >> 5] |= 1u << (j & 31);
+      emit_pair<K>(j, q, static_cast<int32_t>(hv & ((1u << kHitRowBits) - 1u)), n, nbr, neg_flags);
     }
   }
 #pragma unroll
