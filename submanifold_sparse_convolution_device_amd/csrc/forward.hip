@@ -70,25 +70,27 @@ struct Elem<_Float16> {
   static constexpr int kVec = 8;
   static constexpr int kChunk = 32;  // one 16x16x32 MFMA: 4 lane groups x 8
   static constexpr int kPad = 8;
-  __device__ static void store4(_Float16* dst, floatx4 v) {
+  __device__ static u16x4 pack4(floatx4 v) {
     u16x4 o;
     for (int i = 0; i < 4; ++i) {
       const _Float16 h = static_cast<_Float16>(v[i]);  // v_cvt_f16_f32: round to nearest even
       o[i] = __builtin_bit_cast(uint16_t, h);
     }
-    *reinterpret_cast<u16x4*>(dst) = o;
+    return o;
   }
+  __device__ static void store4(_Float16* dst, floatx4 v) { *reinterpret_cast<u16x4*>(dst) = pack4(v); }
 };
 template <>
 struct Elem<__bf16> {
   static constexpr int kVec = 8;
   static constexpr int kChunk = 32;
   static constexpr int kPad = 8;
-  __device__ static void store4(__bf16* dst, floatx4 v) {
+  __device__ static u16x4 pack4(floatx4 v) {
     u16x4 o;
     for (int i = 0; i < 4; ++i) o[i] = bf16_bits_rne(v[i]);
-    *reinterpret_cast<u16x4*>(dst) = o;
+    return o;
   }
+  __device__ static void store4(__bf16* dst, floatx4 v) { *reinterpret_cast<u16x4*>(dst) = pack4(v); }
 };
 
 // One ci-chunk of MFMA work for NCB co-blocks.  b_src is the lane's gathered
@@ -869,7 +871,28 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_forward_small(
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       const int64_t q = q0 + qb * 16 + r;
-      if (q < n && qb * 16 >= row_lo && qb * 16 < row_hi) {
+      const bool mine = qb * 16 >= row_lo && qb * 16 < row_hi;  // wave-uniform
+      if constexpr (sizeof(T) == 2 && NCB % 2 == 0) {
+        // 16-bit outputs in 16-byte pieces: each pair of column blocks is
+        // regrouped between lanes l and l ^ 16 (one v_permlane16_swap per
+        // dword) so that every lane holds 8 consecutive columns (an even g
+        // 32 p + 4 g .. + 7, an odd g 32 p + 16 + 4 (g - 1) .. + 7), and a
+        // store writes 64 contiguous bytes of each of 16 rows rather than
+        // 8-byte fragments.
+        if (mine) {
+          const int64_t row = q < n ? (perm != nullptr ? static_cast<int64_t>(perm[q]) : q) : -1;
+#pragma unroll
+          for (int p = 0; p < NCB / 2; ++p) {
+            const uint2 x = __builtin_bit_cast(uint2, Elem<T>::pack4(acc[qb][2 * p]));
+            const uint2 y = __builtin_bit_cast(uint2, Elem<T>::pack4(acc[qb][2 * p + 1]));
+            const auto s0 = __builtin_amdgcn_permlane16_swap(x.x, y.x, false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(x.y, y.y, false, false);
+            if (row >= 0)
+              *reinterpret_cast<uint4*>(out + row * COUT + 32 * p + 4 * (g & ~1) + 16 * (g & 1)) =
+                  uint4{s0[0], s1[0], s0[1], s1[1]};
+          }
+        }
+      } else if (q < n && mine) {
         const int64_t row = perm != nullptr ? static_cast<int64_t>(perm[q]) : q;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) Elem<T>::store4(out + row * COUT + cb * 16 + 4 * g, acc[qb][cb]);
