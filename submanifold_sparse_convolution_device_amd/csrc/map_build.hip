@@ -1037,13 +1037,6 @@ __global__ __launch_bounds__(64 * kWindowGroups) void k_compact_window(
   if (k == KV - 1 && g == groups - 1 && lane == nt - 1) tile_off[static_cast<int64_t>(KV) * tiles] = base + excl + ct;
 }
 
-int grid_for(int64_t work, int per_block, int cap) {
-  int64_t g = (work + per_block - 1) / per_block;
-  if (g < 1) g = 1;
-  if (g > cap) g = cap;
-  return static_cast<int>(g);
-}
-
 // ---- Strided maps and their transposes ------------------------------------
 // One lane per row of the map's output side (query q, coordinates qc[q]); for
 // every offset k of the K^3 kernel (components lo .. lo + K - 1) the row of
