@@ -27,6 +27,10 @@
 // i + 2 are loaded, their load instructions spread between the MFMA groups
 // so that they issue in the matrix core's shadow.  A step begins by waiting
 // for all of them (and, by a barrier, for the other waves' row copies).
+// The epilogue rounds the accumulators, regroups pairs of column blocks
+// between lanes so that each lane holds 8 consecutive columns of its row,
+// and streams them out with non-temporal 16-byte stores (split offsets
+// write fp32 partials instead, summed by k_reduce_splits).
 #include "internal.h"
 
 #include <type_traits>
