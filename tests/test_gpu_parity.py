@@ -293,6 +293,40 @@ def test_async_build_matches_sync_and_defers_errors(sp):
     assert sp.build_map(dc, 3).total_entries == ref.total_entries
 
 
+def test_ordered_builds_after_other_and_failed_builds(sp):
+    """Maps in the neighbour-set row order (at least 262,144 rows) built one
+    after another on the stream's reused scratch, with the same table size:
+    keys a build left in the coordinate table would show up as neighbours
+    that do not exist.  The 8 batched frames shifted one step along x, built
+    right after the frames and again after two failed builds of the same
+    size (one row twice; one coordinate out of range), match the oracle's
+    map in full each time."""
+    a = _workload(4).layers[0].coords
+    b = a.copy()
+    b[:, 3] += 1
+    assert b[:, 3].max() < 65536
+    ref_b = oracle.build_map(b, 3)
+    _gpu_map(sp, a, 3).free()
+    kb = _gpu_map(sp, b, 3)
+    assert_map_equal(kb, ref_b)
+    kb.free()
+    dup = np.concatenate([a, a[7:8]])
+    with pytest.raises(sp.SpconvError) as e:
+        _gpu_map(sp, dup, 3)
+    assert e.value.name == "SPCONV_ERR_DUPLICATE_COORD"
+    kb = _gpu_map(sp, b, 3)
+    assert_map_equal(kb, ref_b)
+    kb.free()
+    bad = a.copy()
+    bad[12345, 2] = 70000
+    with pytest.raises(sp.SpconvError) as e:
+        _gpu_map(sp, bad, 3)
+    assert e.value.name == "SPCONV_ERR_COORD_RANGE"
+    kb = _gpu_map(sp, b, 3)
+    assert_map_equal(kb, ref_b)
+    kb.free()
+
+
 def test_map_sequence_on_one_stream(sp):
     """Builds enqueued back to back on one stream without host waits,
     growing, shrinking and changing K (so the stream's reused workspace is
