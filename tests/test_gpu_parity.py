@@ -759,8 +759,9 @@ def test_forward_rejects_overlapping_output(sp):
 def test_forward_rounds_ties_to_even(sp, dtype, cin, cout):
     """Sums that fall exactly halfway between two values of the output type
     (1 + odd x half an ulp, with several signs and binades) come out rounded
-    to the even neighbour in every kernel (small, wide with and without
-    split offsets, tiled, generic); the epilogue's rule, checked exactly.
+    to the even neighbour in every kernel (small, wide with split offsets,
+    tiled, generic; the wide kernel without splits in the next test); the
+    epilogue's rule, checked exactly.
     Row 0 gets a + b from the centre and the +x offset (channel 0 only),
     row 1 gets a alone."""
     c = np.array([[0, 0, 0, 0], [0, 0, 0, 1]], np.int32)
@@ -786,6 +787,40 @@ def test_forward_rounds_ties_to_even(sp, dtype, cin, cout):
     assert np.all(units - np.floor(units) == 0.5)
     assert torch.equal(out[0], exp0), f"row 0: {out[0][:8]} vs {exp0[:8]}"
     assert torch.equal(out[1], torch.from_numpy(a).to(tdt))
+
+
+@pytest.mark.parametrize("dtype,cin,cout", [("f16", 64, 64), ("bf16", 128, 128), ("f16", 128, 128),
+                                            ("bf16", 256, 256), ("bf16", 256, 32)])
+def test_forward_rounds_ties_to_even_unsplit(sp, dtype, cin, cout):
+    """The same exact ties on a map with 16,384 more voxels, isolated (in
+    another batch, 4 apart along x), so that the wide kernel has enough
+    tiles to run without splitting offsets: its own epilogue rounds (the
+    lanes' regrouped 16-byte stores) instead of the split reduction.  Rows 0
+    and 1 as above; every isolated row, with zero features, is zero."""
+    extra = 16384
+    c = np.zeros((2 + extra, 4), np.int32)
+    c[1, 3] = 1
+    c[2:, 0] = 1
+    c[2:, 3] = 4 * np.arange(extra)
+    n = c.shape[0]
+    assert (n + 63) // 64 >= 256
+    kmap = _gpu_map(sp, c, 3)
+    tdt = TORCH_DT[dtype]
+    half_ulp = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+    co = np.arange(cout)
+    scale = np.array([1.0, -1.0, 2.0, -4.0])[co % 4]
+    a = scale
+    b = scale * half_ulp * (2 * ((co // 4) % 4) + 1)
+    f = torch.zeros((n, cin), dtype=tdt)
+    f[:2, 0] = 1.0
+    w = torch.zeros((27, cin, cout), dtype=tdt)
+    w[13, 0] = torch.from_numpy(a).to(tdt)
+    w[14, 0] = torch.from_numpy(b).to(tdt)
+    out = sp.forward(f.to(DEV), w.to(DEV), kmap).cpu()
+    exp0 = torch.from_numpy(a + b).to(torch.float32).to(tdt)
+    assert torch.equal(out[0], exp0), f"row 0: {out[0][:8]} vs {exp0[:8]}"
+    assert torch.equal(out[1], torch.from_numpy(a).to(tdt))
+    assert not torch.any(out[2:] != 0)
 
 
 @pytest.mark.parametrize("dtype,cin,cout", [("f16", 32, 32), ("bf16", 64, 64), ("bf16", 128, 48),
