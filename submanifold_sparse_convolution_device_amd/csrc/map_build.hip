@@ -19,7 +19,7 @@
 // (the key, EMPTY, or another key in an unmarked slot: absent) except in the
 // few marked slots, where the window is scanned.
 //
-// Pipeline (one stream, six launches, eight for an ordered map, one fewer
+// Pipeline (one stream, six launches, seven for an ordered map, one fewer
 // when the table is already clear; the last one also writes the small
 // summary into the host's pinned memory):
 //   k_init     clear the table and the occupancy map, unless the previous
@@ -40,8 +40,8 @@
 //              are plain stores.
 //   k_order    (ordered maps) per window of kOrderWindow rows, the rows sorted
 //              by a 16-bit key of their neighbour flags: the map's row order
-//              (perm)
-//   k_count    per 64-row tile (of positions of the row order) and offset, a
+//              (perm); then the window's tiles counted as k_count counts them
+//   k_count    (maps in the input order) per 64-row tile and offset, a
 //              ballot of the flags is the tile's row mask; per-group counts
 //              and per-offset totals
 //   k_scan     (ordered maps) per offset: each group's first list position
@@ -566,6 +566,68 @@ __device__ __forceinline__ uint32_t order_key(const uint32_t* __restrict__ pos_b
   return key;
 }
 
+// The count of tile t (positions t * kTileRows + lane of the row order) by
+// one wave, each lane holding the row at its position (`valid` false past
+// n): per offset k, a ballot of the rows' flags is the tile's row mask; lane
+// k mod 64 stores it to tile_mask[k][t], with tile_base[k][t], the number of
+// the tile's non-centre entries at offsets before k, and adds its population
+// to cnt[k / 64].
+template <int K>
+__device__ __forceinline__ void count_tile(const uint32_t* __restrict__ pos_bits,
+                                           const uint8_t* __restrict__ neg_flags, int64_t row, bool valid,
+                                           int64_t t, int64_t tiles, unsigned long long* __restrict__ tile_mask,
+                                           int32_t* __restrict__ tile_base, int (&cnt)[(K * K * K + 63) / 64]) {
+  constexpr int KV = K * K * K;
+  constexpr int centre = (KV - 1) / 2;
+  constexpr int NS = (KV + 63) / 64;  // offsets per lane
+  constexpr int PW = pos_words(K), NB = neg_bytes(K), NV = NB / 16;
+  const int lane = threadIdx.x & 63;
+  uint32_t pw[PW > 0 ? PW : 1];
+  uint4 nv[NV > 0 ? NV : 1];
+#pragma unroll
+  for (int w = 0; w < PW; ++w) pw[w] = pos_bits[row * PW + w];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) nv[v] = *reinterpret_cast<const uint4*>(neg_flags + row * NB + 16 * v);
+  unsigned long long mine[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) mine[s] = 0ull;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
+    for (int jj = 0; jj < 64; ++jj) {
+      const int k = s * 64 + jj;
+      if (k < KV) {
+        bool f;
+        if (k == centre) {
+          f = true;
+        } else if (k < centre) {
+          const uint4 v = nv[k / 16];
+          const uint32_t word = ((k % 16) / 4 == 0) ? v.x : ((k % 16) / 4 == 1) ? v.y : ((k % 16) / 4 == 2) ? v.z : v.w;
+          f = ((word >> (8 * (k % 4))) & 0xffu) != 0u;
+        } else {
+          const int j = k - centre - 1;
+          f = ((pw[j >> 5] >> (j & 31)) & 1u) != 0u;
+        }
+        const unsigned long long bal = __ballot(valid && f);
+        if (lane == jj) mine[s] = bal;
+      }
+    }
+  }
+  int before = 0;  // non-centre entries of the tile at offsets of earlier slots
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int k = s * 64 + lane;
+    const int c = (k < KV && k != centre) ? static_cast<int>(__popcll(mine[s])) : 0;
+    const int excl = wave_prefix_small<7>(c);
+    if (k < KV) {
+      tile_mask[static_cast<int64_t>(k) * tiles + t] = mine[s];
+      tile_base[static_cast<int64_t>(k) * tiles + t] = before + excl;
+    }
+    before += __builtin_amdgcn_readlane(excl + c, 63);
+    cnt[s] += __popcll(mine[s]);
+  }
+}
+
 // The map's row order ("TorchSparse: regular computation from irregular
 // sparsity", section "TorchSparse++: overlap memory with computation": rows
 // reordered by their neighbour bitmask, so that rows computed together need
@@ -580,14 +642,24 @@ __device__ __forceinline__ uint32_t order_key(const uint32_t* __restrict__ pos_b
 // by eight ballots, counts kept in the wave's row of the histogram), so that
 // the only workgroup barriers are those around the per-digit scan and the
 // scatter.  Rows past n sort last (key ~0 and the largest positions).
+// The sorted window is then counted in place of a separate pass: wave w
+// holds the window's tiles w E .. w E + E - 1 (position e of tile t in lane
+// e mod 64), counts each with count_tile, and the waves of each group of
+// kGroupTiles tiles add their counts through LDS into chunk_sum[k][group]
+// (one chunk per group) and the window's into the per-offset totals.
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderPerThread = kOrderWindow / kOrderThreads;
 constexpr int kOrderWaves = kOrderThreads / 64;
 constexpr int kOrderPasses = (kOrderKeyBits + 7) / 8;
+constexpr int kOrderGroups = kOrderWindow / (kTileRows * kGroupTiles);
+static_assert(kTileRows == 64 && kGroupTiles % kOrderPerThread == 0, "a wave's rounds are whole tiles of one group");
 template <int K>
 __global__ __launch_bounds__(kOrderThreads) void k_order(const uint32_t* __restrict__ pos_bits,
                                                           const uint8_t* __restrict__ neg_flags, int64_t n,
-                                                          int32_t* __restrict__ perm) {
+                                                          int32_t* __restrict__ perm, int64_t tiles, int64_t groups,
+                                                          unsigned long long* __restrict__ tile_mask,
+                                                          int32_t* __restrict__ tile_base,
+                                                          int64_t* __restrict__ chunk_sum, long long* summary) {
   constexpr int E = kOrderPerThread;
   __shared__ unsigned long long buf[kOrderWindow];
   __shared__ uint32_t hist[kOrderWaves * 256];
@@ -681,15 +753,48 @@ __global__ __launch_bounds__(kOrderThreads) void k_order(const uint32_t* __restr
     const int e = (wave * E + j) * 64 + lane;
     if (e < wn) perm[w0 + e] = static_cast<int32_t>(w0 + idx[j]);
   }
+  constexpr int KV = K * K * K, NS = (KV + 63) / 64;
+  int cnt[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) cnt[s] = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * (kOrderWindow / kTileRows) + wave * E + j;
+    if (t < tiles) {  // uniform over the wave
+      const int e = (wave * E + j) * 64 + lane;
+      const bool valid = e < wn;
+      count_tile<K>(pos_bits, neg_flags, w0 + (valid ? idx[j] : 0u), valid, t, tiles, tile_mask, tile_base, cnt);
+    }
+  }
+  // Per-wave counts through LDS (buf is free: the last pass ended on a barrier).
+  static_assert(kOrderWaves * NS * 64 * sizeof(int) <= sizeof(buf), "counts fit the sort buffer");
+  int* part = reinterpret_cast<int*>(buf);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) part[wave * NS * 64 + s * 64 + lane] = cnt[s];
+  __syncthreads();
+  constexpr int WG = kOrderWaves / kOrderGroups;  // waves per group
+  for (int k = threadIdx.x; k < KV; k += kOrderThreads) {
+    long long total = 0;
+#pragma unroll
+    for (int g = 0; g < kOrderGroups; ++g) {
+      int sum = 0;
+#pragma unroll
+      for (int w = 0; w < WG; ++w) sum += part[(g * WG + w) * NS * 64 + k];
+      const int64_t gi = static_cast<int64_t>(blockIdx.x) * kOrderGroups + g;
+      if (gi < groups) chunk_sum[static_cast<int64_t>(k) * groups + gi] = sum;
+      total += sum;
+    }
+    if (total != 0) {
+      atomicAdd(reinterpret_cast<unsigned long long*>(&summary[kSummaryHead + k]),
+                static_cast<unsigned long long>(total));
+    }
+  }
 }
 
-// One workgroup of 1024 threads (16 waves) per chunk of group_tiles tiles,
-// one tile per wave at a time (launched with chunks of one group, so each
-// wave counts one tile; tiles are over positions of the row order, whose
-// rows' flags come through perm).  Per tile and offset k, a ballot of the row
-// flags is the tile's row mask; lane k mod 64 keeps it (slot k / 64) and
-// stores it to tile_mask[k][t], with tile_base[k][t], the number of the
-// tile's non-centre entries at offsets before k.  Per-chunk counts go to
+// Maps in the input order (ordered maps are counted by k_order): one
+// workgroup of 1024 threads (16 waves) per chunk of group_tiles tiles, one
+// tile per wave at a time (launched with chunks of one group, so each wave
+// counts one tile with count_tile).  Per-chunk counts go to
 // chunk_sum[k][chunk] and are added to the per-offset totals in the summary.
 template <int K>
 __global__ __launch_bounds__(1024) void k_count(const uint32_t* __restrict__ pos_bits,
@@ -700,9 +805,7 @@ __global__ __launch_bounds__(1024) void k_count(const uint32_t* __restrict__ pos
                                                 int32_t* __restrict__ tile_base,
                                                 int64_t* __restrict__ chunk_sum, long long* summary) {
   constexpr int KV = K * K * K;
-  constexpr int centre = (KV - 1) / 2;
   constexpr int NS = (KV + 63) / 64;  // offsets per lane
-  constexpr int PW = pos_words(K), NB = neg_bytes(K), NV = NB / 16;
   const int64_t chunk = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int cnt[NS];
@@ -715,50 +818,7 @@ __global__ __launch_bounds__(1024) void k_count(const uint32_t* __restrict__ pos
     const bool valid = q < n;
     const int64_t qp = valid ? q : n - 1;
     const int64_t qs = perm != nullptr ? static_cast<int64_t>(perm[qp]) : qp;  // its row
-    uint32_t pw[PW > 0 ? PW : 1];
-    uint4 nv[NV > 0 ? NV : 1];
-#pragma unroll
-    for (int w = 0; w < PW; ++w) pw[w] = pos_bits[qs * PW + w];
-#pragma unroll
-    for (int v = 0; v < NV; ++v) nv[v] = *reinterpret_cast<const uint4*>(neg_flags + qs * NB + 16 * v);
-    unsigned long long mine[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) mine[s] = 0ull;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-#pragma unroll
-      for (int jj = 0; jj < 64; ++jj) {
-        const int k = s * 64 + jj;
-        if (k < KV) {
-          bool f;
-          if (k == centre) {
-            f = true;
-          } else if (k < centre) {
-            const uint4 v = nv[k / 16];
-            const uint32_t word = ((k % 16) / 4 == 0) ? v.x : ((k % 16) / 4 == 1) ? v.y : ((k % 16) / 4 == 2) ? v.z : v.w;
-            f = ((word >> (8 * (k % 4))) & 0xffu) != 0u;
-          } else {
-            const int j = k - centre - 1;
-            f = ((pw[j >> 5] >> (j & 31)) & 1u) != 0u;
-          }
-          const unsigned long long bal = __ballot(valid && f);
-          if (lane == jj) mine[s] = bal;
-        }
-      }
-    }
-    int before = 0;  // non-centre entries of the tile at offsets of earlier slots
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int k = s * 64 + lane;
-      const int c = (k < KV && k != centre) ? static_cast<int>(__popcll(mine[s])) : 0;
-      const int excl = wave_prefix_small<7>(c);
-      if (k < KV) {
-        tile_mask[static_cast<int64_t>(k) * tiles + t] = mine[s];
-        tile_base[static_cast<int64_t>(k) * tiles + t] = before + excl;
-      }
-      before += __builtin_amdgcn_readlane(excl + c, 63);
-      cnt[s] += __popcll(mine[s]);
-    }
+    count_tile<K>(pos_bits, neg_flags, qs, valid, t, tiles, tile_mask, tile_base, cnt);
   }
   __shared__ int part[kGroupTiles][NS * 64];
 #pragma unroll
@@ -1209,18 +1269,17 @@ void launch_probe_count(const BuildPlan& p, const int4* c4, const BuildScratch& 
                        static_cast<unsigned long long>(occ_buckets(p) - 1), s.nbr, s.pos_bits, s.neg_flags,
                        s.summary);
   }
-  const int32_t* perm = nullptr;
+  const int64_t groups = (p.tiles + kGroupTiles - 1) / kGroupTiles;
   if constexpr (K > 1) {
     if (p.ordered) {
       const unsigned windows = static_cast<unsigned>((p.n + kOrderWindow - 1) / kOrderWindow);
       hipLaunchKernelGGL((k_order<K>), dim3(windows), dim3(kOrderThreads), 0, stream, s.pos_bits, s.neg_flags, p.n,
-                         m.perm);
-      perm = m.perm;
+                         m.perm, p.tiles, groups, m.tile_mask, s.tile_base, s.chunk_sum, s.summary);
+      return;
     }
   }
-  const int64_t groups = (p.tiles + kGroupTiles - 1) / kGroupTiles;
   hipLaunchKernelGGL((k_count<K>), dim3(static_cast<unsigned>(groups)), dim3(1024), 0, stream,
-                     s.pos_bits, s.neg_flags, perm, p.n, p.tiles, static_cast<int64_t>(kGroupTiles), groups,
+                     s.pos_bits, s.neg_flags, nullptr, p.n, p.tiles, static_cast<int64_t>(kGroupTiles), groups,
                      m.tile_mask, s.tile_base, s.chunk_sum, s.summary);
 }
 
