@@ -591,6 +591,7 @@ __device__ __forceinline__ void count_tile(const uint32_t* __restrict__ pos_bits
   unsigned long long mine[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) mine[s] = 0ull;
+  const unsigned long long vmask = __ballot(valid);  // lanes holding a row
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
 #pragma unroll
@@ -608,7 +609,7 @@ __device__ __forceinline__ void count_tile(const uint32_t* __restrict__ pos_bits
           const int j = k - centre - 1;
           f = ((pw[j >> 5] >> (j & 31)) & 1u) != 0u;
         }
-        const unsigned long long bal = __ballot(valid && f);
+        const unsigned long long bal = __ballot(f) & vmask;
         if (lane == jj) mine[s] = bal;
       }
     }
