@@ -539,6 +539,24 @@ def test_map_row_order(sp, index, K, bound):
         assert ordered <= bound * plain, f"(tile, offset) pairs {ordered} vs {plain} in input order"
 
 
+def test_map_ordered_k7_ragged(sp):
+    """An ordered map at K = 7 (343 offsets, six per lane in the tile count
+    that runs inside the row-order kernel), on a cloud just above the
+    ordering threshold whose last window and last group of 16 tiles are
+    ragged: every list, count and offset equals the oracle's, and the row
+    order equals its definition."""
+    c = workloads.random_grid(91, 128, 0.14, 1)
+    n = c.shape[0]
+    assert n >= ORDER_MIN_ROWS and n % ORDER_WINDOW != 0 and ((n + 63) // 64) % 16 != 0
+    ref = oracle.build_map(c, 7)
+    kmap = _gpu_map(sp, c, 7)
+    assert_map_equal(kmap, ref)
+    a, b = _gpu_lists(kmap)
+    cen = 343 // 2
+    assert np.array_equal(b[kmap.offsets[cen]:kmap.offsets[cen + 1]], expected_row_order(ref, 7))
+    kmap.free()
+
+
 def test_map_deterministic(sp):
     c = workloads.permuted(workloads.random_grid(99, 30, 0.1, 2), 99)
     a1, b1 = _gpu_lists(_gpu_map(sp, c, 3))
